@@ -1,0 +1,163 @@
+"""Seeded synthetic inputs and workload geometry for hierarchical local attention.
+
+This module is shared by the tests, the benchmark and the oracle's callers.  It holds
+no arithmetic of the method itself: only the workload table, the seeded random draws
+and the float32 -> bfloat16 round-to-nearest-even input rounding.
+
+Workloads stand in for the pages' FLUX generation runs at 2K-8K (UltraGen [it] §3,
+[es] §4): activations are not available, so Q, K, V are iid N(0, 1) at the same token
+shapes.  The token geometry (16 pixels per latent token per axis) follows the token
+counts quoted in UltraGen [es] §1 (a 4K image is 65 536 tokens).
+
+Citation keys: [UltraGen/<lang> §n] is the gist.science summary page "UltraGen:
+Efficient Ultra-High-Resolution Image Generation with Hierarchical Local Attention"
+in the named language edition (it, fr, es, ar, ko), section n of its technical summary.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, asdict, replace
+import math
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Geometry:
+    """One attention problem.
+
+    Tensors are token-major ``[B, L, heads, head_dim]`` with ``L = N + M``: rows
+    ``0..N-1`` are the hi-res tokens of an ``H x W`` grid in raster order, rows
+    ``N..L-1`` the low-res guide tokens of an ``H_lr x W_lr`` grid in raster order.
+    """
+
+    B: int
+    heads: int
+    head_dim: int
+    H: int
+    W: int
+    w: int
+    H_lr: int
+    W_lr: int
+    rho: int = 4
+    theta: float = 10000.0
+    name: str = "custom"
+
+    @property
+    def N(self) -> int:
+        return self.H * self.W
+
+    @property
+    def M(self) -> int:
+        return self.H_lr * self.W_lr
+
+    @property
+    def L(self) -> int:
+        return self.N + self.M
+
+    @property
+    def n_windows(self) -> int:
+        return (self.H // self.w) * (self.W // self.w)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    def shape(self) -> tuple:
+        return (self.B, self.L, self.heads, self.head_dim)
+
+    def with_(self, **kw) -> "Geometry":
+        return replace(self, **kw)
+
+    def as_dict(self) -> dict:
+        return asdict(self)
+
+
+# The five workloads.  Seeds are the position in this list.
+CONFIGS = {
+    "tiny": Geometry(B=1, heads=2, head_dim=64, H=32, W=32, w=8, H_lr=8, W_lr=8, name="tiny"),
+    "2k": Geometry(B=1, heads=24, head_dim=128, H=128, W=128, w=16, H_lr=32, W_lr=32, name="2k"),
+    "4k": Geometry(B=1, heads=24, head_dim=128, H=256, W=256, w=16, H_lr=64, W_lr=64, name="4k"),
+    "nonsquare": Geometry(B=2, heads=24, head_dim=128, H=256, W=128, w=16, H_lr=64, W_lr=32,
+                          name="nonsquare"),
+    "8k": Geometry(B=1, heads=24, head_dim=128, H=512, W=512, w=16, H_lr=128, W_lr=128, name="8k"),
+}
+CONFIG_SEEDS = {name: i for i, name in enumerate(CONFIGS)}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even); return uint16 bits.
+
+    Inputs must be finite (the generators only produce finite normals).
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    lsb = (u >> 16) & np.uint32(1)
+    rounded = (u + np.uint32(0x7FFF) + lsb) >> 16
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bit patterns to float32 (exact)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bit patterns to float64 (exact)."""
+    return bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def draw_normal_f32(rng: np.random.Generator, shape, chunk: int = 1 << 24) -> np.ndarray:
+    """iid N(0, 1) float32 in C order, drawn in chunks (same stream as one draw)."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.float32)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        out[s:e] = rng.standard_normal(e - s, dtype=np.float32)
+    return out.reshape(shape)
+
+
+def make_qkv_bits(geom: Geometry, seed: int):
+    """Q, K, V as bfloat16 bit patterns, shape ``[B, L, heads, head_dim]``.
+
+    Recipe: ``numpy.random.default_rng(seed)``, iid N(0, 1) float32 drawn in C order in
+    the order Q, K, V, each rounded to bfloat16 (round to nearest even).
+    """
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(3):
+        x = draw_normal_f32(rng, geom.shape())
+        out.append(f32_to_bf16_bits(x))
+        del x
+    return tuple(out)
+
+
+def make_config_inputs(name: str):
+    """(geometry, q_bits, k_bits, v_bits) for a named workload with its fixed seed."""
+    geom = CONFIGS[name]
+    return (geom,) + make_qkv_bits(geom, CONFIG_SEEDS[name])
+
+
+def algorithmic_pairs(geom: Geometry) -> dict:
+    """Unmasked (query, key) pairs per (batch, head), by term.
+
+    Geometry bookkeeping for throughput figures: a window grid of a x b windows has
+    sum over windows of the clipped 3x3 neighbour count = (3a - 2)(3b - 2) (a, b >= 2;
+    a one-window axis contributes 1).
+    """
+    a, b = geom.H // geom.w, geom.W // geom.w
+
+    def axis(n):
+        return 1 if n == 1 else 3 * n - 2
+
+    local = axis(a) * axis(b) * geom.w ** 4
+    hi_lr = geom.N * geom.M
+    lr_lr = geom.M * geom.M
+    return {"local": local, "hi_lr": hi_lr, "lr_lr": lr_lr, "total": local + hi_lr + lr_lr}
+
+
+def algorithmic_flops(geom: Geometry) -> dict:
+    """Matrix FLOPs of the unmasked pairs: 4 * head_dim per pair (QK^T and PV), all (b, h)."""
+    p = algorithmic_pairs(geom)
+    f = 4 * geom.head_dim * geom.B * geom.heads
+    return {"hi": f * (p["local"] + p["hi_lr"]), "lr": f * p["lr_lr"], "total": f * p["total"]}

@@ -1,0 +1,224 @@
+"""Plain fp64 CPU oracle for UltraGen's hierarchical local attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, links or calls this
+module; only the tests, the smoke check and the benchmark's CPU-baseline leg do.  It
+shares no code with the HIP path: it is the method's definition written out in numpy,
+slowly and in float64, so that a reader can check it against the pages by eye.
+
+Citation keys: [UltraGen/<lang> §n] is the gist.science summary page "UltraGen:
+Efficient Ultra-High-Resolution Image Generation with Hierarchical Local Attention"
+in the named language edition (it, fr, es, ar, ko), section n of its technical summary.
+
+What the pages fix, and the readings taken where they are silent:
+
+* Window-first token order: hi-res tokens are split into fixed, non-overlapping
+  w x w windows and reordered window by window, so each attention block is one
+  spatial window ([UltraGen/it §2], [UltraGen/fr §2.A], [UltraGen/ar §2.A]).  Reading:
+  windows are enumerated row-major over the window grid, tokens raster inside a window.
+* Mask ([UltraGen/ar §2.B], [UltraGen/es §2]): a hi-res window attends to itself, to
+  its adjacent windows and to every low-res guide token; guide tokens attend to each
+  other.  Readings: "adjacent" is the clipped 3x3 neighbourhood (no wrap); guide
+  queries see no hi-res key.
+* Positions ([UltraGen/ar §2.B]): guide-token position indices are scaled by rho
+  (4) onto the hi-res grid.  Reading: integer positions (rho*i, rho*j), no offset.
+* RoPE ([UltraGen/fr §2.A]: relative positional embeddings).  Readings: 2D axial RoPE,
+  half of the head dims per axis (y first), adjacent pairs (2k, 2k+1) rotated by
+  pos * theta**(-2k/d_axis), theta = 10000; applied to Q and K, not V.
+* Attention: softmax(Q K^T / sqrt(d)) V over the allowed keys.  Every row has at least
+  w*w allowed keys, so no row is empty.
+
+parity pinned: every function here is checked by tests marked "not gpu" against brute
+force, closed forms, invariants or library routines (see tests/test_oracle_pins.py).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------------
+# Window-first permutation  ([UltraGen/it §2], [UltraGen/fr §2.A], [UltraGen/ar §2.A])
+# ---------------------------------------------------------------------------------
+
+def window_first_source_index(H: int, W: int, w: int) -> np.ndarray:
+    """r[p] = raster index of the token placed at window-first position p.
+
+    p = win * w*w + t;  win = wy * (W // w) + wx  (row-major over windows);
+    t = iy * w + ix (raster inside the window);  r = (wy*w + iy) * W + (wx*w + ix).
+    """
+    if H % w or W % w:
+        raise ValueError("window size must divide the grid")
+    p = np.arange(H * W, dtype=np.int64)
+    win, t = np.divmod(p, w * w)
+    wy, wx = np.divmod(win, W // w)
+    iy, ix = np.divmod(t, w)
+    return (wy * w + iy) * W + (wx * w + ix)
+
+
+def window_permute(x: np.ndarray, H: int, W: int, w: int) -> np.ndarray:
+    """Raster -> window-first along axis 1 (the token axis) of ``[B, N, ...]``."""
+    r = window_first_source_index(H, W, w)
+    return x[:, r]
+
+
+def window_unpermute(x: np.ndarray, H: int, W: int, w: int) -> np.ndarray:
+    """Window-first -> raster along axis 1: out[:, r[p]] = x[:, p]."""
+    r = window_first_source_index(H, W, w)
+    out = np.empty_like(x)
+    out[:, r] = x
+    return out
+
+
+# ---------------------------------------------------------------------------------
+# Positions  ([UltraGen/ar §2.B]: guide positions scaled by rho onto the hi-res grid)
+# ---------------------------------------------------------------------------------
+
+def hi_positions(H: int, W: int):
+    """(y, x) of hi-res raster tokens 0..H*W-1."""
+    r = np.arange(H * W, dtype=np.int64)
+    return r // W, r % W
+
+
+def lr_positions(H_lr: int, W_lr: int, rho: int):
+    """(y, x) of guide raster tokens: (rho * i, rho * j)."""
+    s = np.arange(H_lr * W_lr, dtype=np.int64)
+    return rho * (s // W_lr), rho * (s % W_lr)
+
+
+def token_positions(geom):
+    """(y, x) for all L tokens of the joint [hi | lr] sequence, raster in both parts."""
+    yh, xh = hi_positions(geom.H, geom.W)
+    yl, xl = lr_positions(geom.H_lr, geom.W_lr, geom.rho)
+    return np.concatenate([yh, yl]), np.concatenate([xh, xl])
+
+
+# ---------------------------------------------------------------------------------
+# 2D axial RoPE
+# ---------------------------------------------------------------------------------
+
+def rope_frequencies(head_dim: int, theta: float) -> np.ndarray:
+    """omega_k = theta ** (-2k / d_axis), k = 0 .. d_axis/2 - 1, d_axis = head_dim / 2."""
+    d_axis = head_dim // 2
+    k = np.arange(d_axis // 2, dtype=np.float64)
+    return theta ** (-2.0 * k / d_axis)
+
+
+def rope_rotate(x: np.ndarray, pos_y: np.ndarray, pos_x: np.ndarray, theta: float) -> np.ndarray:
+    """Rotate ``x[..., T, heads, d]`` (fp64) by token positions (pos_y, pos_x) of length T.
+
+    Dims [0, d/2) rotate by the y position, dims [d/2, d) by the x position.  Within an
+    axis block, pair (2k, 2k+1) = (a, b) becomes (a cos phi - b sin phi, a sin phi + b cos phi)
+    with phi = pos * omega_k.
+    """
+    d = x.shape[-1]
+    if d % 4:
+        raise ValueError("head_dim must be a multiple of 4 for 2D axial RoPE")
+    d_axis = d // 2
+    omega = rope_frequencies(d, theta)
+    out = np.empty(x.shape, dtype=np.float64)
+    for axis_block, pos in ((0, pos_y), (1, pos_x)):
+        phi = np.asarray(pos, dtype=np.float64)[:, None] * omega[None, :]  # [T, d_axis/2]
+        c = np.cos(phi)[:, None, :]  # broadcast over heads
+        s = np.sin(phi)[:, None, :]
+        lo = axis_block * d_axis
+        a = x[..., lo:lo + d_axis:2].astype(np.float64)
+        b = x[..., lo + 1:lo + d_axis:2].astype(np.float64)
+        out[..., lo:lo + d_axis:2] = a * c - b * s
+        out[..., lo + 1:lo + d_axis:2] = a * s + b * c
+    return out
+
+
+def rope_joint(x: np.ndarray, geom) -> np.ndarray:
+    """RoPE on a full ``[B, L, heads, d]`` tensor in the raster [hi | lr] layout."""
+    py, px = token_positions(geom)
+    return rope_rotate(x, py, px, geom.theta)
+
+
+# ---------------------------------------------------------------------------------
+# Mask  ([UltraGen/ar §2.B] attention-mask bullets; [UltraGen/es §2])
+# ---------------------------------------------------------------------------------
+
+def mask_rows(geom, rows: np.ndarray) -> np.ndarray:
+    """Explicit boolean mask rows (raster order over all L keys) for query rows ``rows``.
+
+    hi q -> hi k : allowed iff the windows differ by at most one in both axes;
+    hi q -> lr k : always;   lr q -> lr k : always;   lr q -> hi k : never.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    N, L, w = geom.N, geom.L, geom.w
+    key = np.arange(L, dtype=np.int64)
+    key_is_hi = key < N
+    ky, kx = np.where(key_is_hi, key // geom.W, 0), np.where(key_is_hi, key % geom.W, 0)
+    q_is_hi = rows < N
+    qy, qx = np.where(q_is_hi, rows // geom.W, 0), np.where(q_is_hi, rows % geom.W, 0)
+    near = (np.abs(qy[:, None] // w - ky[None, :] // w) <= 1) & \
+           (np.abs(qx[:, None] // w - kx[None, :] // w) <= 1)
+    hi_hi = q_is_hi[:, None] & key_is_hi[None, :] & near
+    any_lr = ~key_is_hi[None, :] & np.ones((len(rows), 1), dtype=bool)
+    return hi_hi | any_lr
+
+
+# ---------------------------------------------------------------------------------
+# Attention
+# ---------------------------------------------------------------------------------
+
+def masked_softmax_attention(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray,
+                             mask: np.ndarray, scale: float, return_probs: bool = False):
+    """Dense softmax attention for a block of query rows of one (batch, head).
+
+    q_rows [R, d], k [L, d], v [L, d], mask [R, L] (True = allowed).  S = q k^T * scale,
+    masked entries -inf, subtract row max, exp, normalise, P v.
+    """
+    s = (q_rows @ k.T) * scale
+    s = np.where(mask, s, -np.inf)
+    s = s - s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    p /= p.sum(axis=1, keepdims=True)
+    o = p @ v
+    return (o, p) if return_probs else o
+
+
+def rotated_qk(q: np.ndarray, k: np.ndarray, geom, b: int, h: int):
+    """RoPE-rotated fp64 Q and K rows of one (batch, head): [L, d] each."""
+    py, px = token_positions(geom)
+    qbh = q[b, :, h:h + 1, :].astype(np.float64)
+    kbh = k[b, :, h:h + 1, :].astype(np.float64)
+    if geom.theta > 0:
+        qbh = rope_rotate(qbh, py, px, geom.theta)
+        kbh = rope_rotate(kbh, py, px, geom.theta)
+    return qbh[:, 0, :], kbh[:, 0, :]
+
+
+def attention_rows(q, k, v, geom, b: int, h: int, rows, block: int = 512, qk=None):
+    """Oracle output rows (raster index ``rows``) of one (batch, head), fp64 ``[R, d]``.
+
+    ``qk`` may carry the already rotated (Q, K) of this (b, h) to avoid recomputing it.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    qr, kr = qk if qk is not None else rotated_qk(q, k, geom, b, h)
+    vv = v[b, :, h, :].astype(np.float64)
+    out = np.empty((len(rows), q.shape[-1]), dtype=np.float64)
+    for s in range(0, len(rows), block):
+        blk = rows[s:s + block]
+        out[s:s + len(blk)] = masked_softmax_attention(qr[blk], kr, vv, mask_rows(geom, blk),
+                                                       geom.scale)
+    return out
+
+
+def forward(q, k, v, geom, block: int = 512) -> np.ndarray:
+    """Full oracle forward: fp64 ``[B, L, heads, d]`` in the raster [hi | lr] layout.
+
+    Permute -> attend -> unpermute leaves the result in raster order, and the mask is
+    defined on positions, so the oracle attends in raster order directly.
+    """
+    B, L, Hh, d = q.shape
+    out = np.empty((B, L, Hh, d), dtype=np.float64)
+    rows = np.arange(L)
+    for b in range(B):
+        for h in range(Hh):
+            out[b, :, h, :] = attention_rows(q, k, v, geom, b, h, rows, block)
+    return out
+
+
+def allowed_key_count(geom, rows) -> np.ndarray:
+    """Number of allowed keys for each query row (from the explicit mask)."""
+    return mask_rows(geom, rows).sum(axis=1)

@@ -1,0 +1,494 @@
+"""Pins for the CPU oracle: brute force, closed forms, invariants and library routines.
+
+Each check is a function of the oracle routine under test, so the same check also runs
+against mutants with a planted mistake (a dropped term, a flipped sign, a transposed
+index) and must fail there.  Nothing here touches a GPU.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.uhla_oracle as orc
+from global_attention_image_amd.inputs import (CONFIGS, Geometry, algorithmic_pairs,
+                                                bf16_bits_to_f64, f32_to_bf16_bits,
+                                                make_qkv_bits)
+
+GOLDEN = __import__("os").path.join(__import__("os").path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------------------- helpers
+
+def small_geom(**kw):
+    base = dict(B=1, heads=1, head_dim=8, H=12, W=12, w=4, H_lr=3, W_lr=3, rho=4,
+                theta=10000.0)
+    base.update(kw)
+    return Geometry(**base)
+
+
+def rand_qkv(geom, seed=0):
+    q, k, v = make_qkv_bits(geom, seed)
+    return bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v)
+
+
+def window_tokens_by_slicing(H, W, w, wy, wx):
+    """Raster indices of window (wy, wx), read off a 2D index grid by slicing."""
+    grid = np.arange(H * W).reshape(H, W)
+    return grid[wy * w:(wy + 1) * w, wx * w:(wx + 1) * w].ravel()
+
+
+def brute_mask(geom):
+    """L x L mask built by enumerating each window's clipped 3x3 neighbour windows."""
+    H, W, w, N, L = geom.H, geom.W, geom.w, geom.N, geom.L
+    m = np.zeros((L, L), dtype=bool)
+    nwy, nwx = H // w, W // w
+    for wy in range(nwy):
+        for wx in range(nwx):
+            qt = window_tokens_by_slicing(H, W, w, wy, wx)
+            for dy in (-1, 0, 1):
+                for dx in (-1, 0, 1):
+                    ny, nx = wy + dy, wx + dx
+                    if 0 <= ny < nwy and 0 <= nx < nwx:
+                        kt = window_tokens_by_slicing(H, W, w, ny, nx)
+                        m[np.ix_(qt, kt)] = True
+            m[qt, N:] = True
+    m[N:, N:] = True
+    return m
+
+
+def complex_rope(x, pos_y, pos_x, theta):
+    """RoPE as complex multiplication: (a + ib) * exp(i * pos * omega_k) per axis block."""
+    d = x.shape[-1]
+    da = d // 2
+    out = np.empty_like(x, dtype=np.float64)
+    for blk, pos in ((0, pos_y), (1, pos_x)):
+        sub = x[..., blk * da:(blk + 1) * da]
+        z = sub[..., 0::2] + 1j * sub[..., 1::2]
+        freq = np.array([theta ** (-(2.0 * kk) / da) for kk in range(da // 2)])
+        rot = np.exp(1j * np.asarray(pos, dtype=np.float64)[:, None, None] * freq[None, None, :])
+        zr = z * rot
+        out[..., blk * da:(blk + 1) * da:2] = zr.real
+        out[..., blk * da + 1:(blk + 1) * da:2] = zr.imag
+    return out
+
+
+def loop_attention(q, k, v, geom):
+    """Pure-Python loops: RoPE with math.cos/sin, mask from brute_mask, math.exp softmax."""
+    B, L, Hh, d = q.shape
+    da = d // 2
+    yh = [r // geom.W for r in range(geom.N)] + [geom.rho * (s // geom.W_lr) for s in range(geom.M)]
+    xh = [r % geom.W for r in range(geom.N)] + [geom.rho * (s % geom.W_lr) for s in range(geom.M)]
+
+    def rot(vec, t):
+        outv = list(vec)
+        for blk, pos in ((0, yh[t]), (1, xh[t])):
+            for kk in range(da // 2):
+                ang = pos * geom.theta ** (-2.0 * kk / da)
+                a, b = vec[blk * da + 2 * kk], vec[blk * da + 2 * kk + 1]
+                outv[blk * da + 2 * kk] = a * math.cos(ang) - b * math.sin(ang)
+                outv[blk * da + 2 * kk + 1] = a * math.sin(ang) + b * math.cos(ang)
+        return outv
+
+    m = brute_mask(geom)
+    out = np.zeros_like(q)
+    sc = 1.0 / math.sqrt(d)
+    for b in range(B):
+        for h in range(Hh):
+            qr = [rot(list(q[b, t, h]), t) for t in range(L)]
+            kr = [rot(list(k[b, t, h]), t) for t in range(L)]
+            for i in range(L):
+                logits = [sum(qr[i][c] * kr[j][c] for c in range(d)) * sc if m[i, j] else None
+                          for j in range(L)]
+                mx = max(x for x in logits if x is not None)
+                wts = [math.exp(x - mx) if x is not None else 0.0 for x in logits]
+                z = sum(wts)
+                for c in range(d):
+                    out[b, i, h, c] = sum(wts[j] * v[b, j, h, c] for j in range(L)) / z
+    return out
+
+
+# ------------------------------------------------------------------ pin checks (reusable)
+
+def check_index_map(fn):
+    # hand-derived fixture: 4 x 4 grid, 2 x 2 windows
+    fixture = np.loadtxt(f"{GOLDEN}/window_first_4x4_w2.txt", dtype=np.int64)
+    assert np.array_equal(fn(4, 4, 2), fixture)
+    fixture2 = np.loadtxt(f"{GOLDEN}/window_first_4x6_w2.txt", dtype=np.int64)
+    assert np.array_equal(fn(4, 6, 2), fixture2)
+    for H, W, w in [(6, 4, 2), (12, 8, 4), (32, 32, 8), (16, 48, 16), (8, 24, 8)]:
+        r = fn(H, W, w)
+        brute = np.concatenate([window_tokens_by_slicing(H, W, w, wy, wx)
+                                for wy in range(H // w) for wx in range(W // w)])
+        assert np.array_equal(r, brute), (H, W, w)
+        # library routine: einops rearrangement of a raster index grid
+        import einops
+        ein = einops.rearrange(np.arange(H * W), "(wy iy wx ix) -> (wy wx iy ix)",
+                               iy=w, ix=w, wy=H // w, wx=W // w)
+        assert np.array_equal(r, ein), (H, W, w)
+        assert np.array_equal(np.sort(r), np.arange(H * W))  # bijection
+    # special cases: w = 1 and one window are the identity
+    assert np.array_equal(fn(5, 7, 1), np.arange(35))
+    assert np.array_equal(fn(8, 8, 8), np.arange(64))
+
+
+def check_permute_roundtrip(perm, unperm):
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((2, 12 * 8, 3, 4))
+    y = perm(x, 12, 8, 4)
+    assert np.array_equal(unperm(y, 12, 8, 4), x)
+    assert np.array_equal(perm(unperm(x, 12, 8, 4), 12, 8, 4), x)
+    # the window-first row p holds raster token r[p]
+    r = np.concatenate([window_tokens_by_slicing(12, 8, 4, wy, wx)
+                        for wy in range(3) for wx in range(2)])
+    assert np.array_equal(y, x[:, r])
+
+
+def check_rope(rot):
+    rng = np.random.default_rng(7)
+    T, Hh, d = 37, 2, 16
+    x = rng.standard_normal((T, Hh, d))
+    py = rng.integers(0, 600, T)
+    px = rng.integers(0, 600, T)
+    th = 10000.0
+    y = rot(x, py, px, th)
+    # complex-multiplication formulation
+    assert np.allclose(y, complex_rope(x, py, px, th), rtol=0, atol=1e-12)
+    # position 0 is the identity
+    assert np.allclose(rot(x, np.zeros(T, int), np.zeros(T, int), th), x, atol=0)
+    # each pair keeps its norm
+    n0 = x[..., 0::2] ** 2 + x[..., 1::2] ** 2
+    n1 = y[..., 0::2] ** 2 + y[..., 1::2] ** 2
+    assert np.allclose(n0, n1, rtol=1e-12)
+    # axis blocks: y position moves only dims [0, d/2), x position only [d/2, d)
+    y2 = rot(x, py + 3, px, th)
+    assert np.array_equal(y2[..., d // 2:], y[..., d // 2:])
+    assert not np.allclose(y2[..., :d // 2], y[..., :d // 2])
+    # relative property: <R(p) q, R(p') k> = <q, R(p' - p) k>
+    q1, k1 = x[:1], x[1:2]
+    lhs = np.sum(rot(q1, py[:1], px[:1], th) * rot(k1, py[1:2], px[1:2], th))
+    rhs = np.sum(q1 * rot(k1, py[1:2] - py[:1], px[1:2] - px[:1], th))
+    assert abs(lhs - rhs) < 1e-10
+    # hand-derived: d = 8 -> per-axis frequencies (1, theta^-1/2) = (1, 0.01); a unit
+    # vector on dim 0 at y-position 2 goes to (cos 2, sin 2); on dim 6 at x-position 100
+    # (frequency 0.01) to (cos 1, sin 1)
+    e = np.zeros((2, 1, 8))
+    e[0, 0, 0] = 1.0
+    e[1, 0, 6] = 1.0
+    r = rot(e, np.array([2, 0]), np.array([0, 100]), th)
+    assert np.allclose(r[0, 0], [math.cos(2), math.sin(2), 0, 0, 0, 0, 0, 0], atol=1e-15)
+    assert np.allclose(r[1, 0], [0, 0, 0, 0, 0, 0, math.cos(1), math.sin(1)], atol=1e-15)
+
+
+def check_positions(hi_pos, lr_pos):
+    y, x = hi_pos(3, 5)
+    assert list(y) == [0] * 5 + [1] * 5 + [2] * 5 and list(x) == list(range(5)) * 3
+    y, x = lr_pos(2, 3, 4)
+    assert list(y) == [0, 0, 0, 4, 4, 4] and list(x) == [0, 4, 8, 0, 4, 8]
+
+
+def check_mask(mask_rows_fn):
+    for g in [small_geom(), small_geom(H=8, W=16, w=4, H_lr=2, W_lr=4),
+              small_geom(H=4, W=4, w=4, H_lr=0, W_lr=0),
+              small_geom(H=20, W=8, w=4, H_lr=5, W_lr=2)]:
+        m = mask_rows_fn(g, np.arange(g.L))
+        assert np.array_equal(m, brute_mask(g)), g
+
+
+def check_pair_counts(mask_rows_fn):
+    g = CONFIGS["tiny"]
+    m = mask_rows_fn(g, np.arange(g.L))
+    cnt = m.sum(axis=1)
+    # hi rows: (number of clipped neighbour windows) * w^2 + M; corner/edge/interior
+    nbr = sorted(set(((cnt[:g.N] - g.M) // (g.w * g.w)).tolist()))
+    assert nbr == [4, 6, 9]
+    assert np.all(cnt[g.N:] == g.M)
+    assert int(m.sum()) == algorithmic_pairs(g)["total"]
+
+
+def check_attention(fwd):
+    g = small_geom()
+    q, k, v = rand_qkv(g, 11)
+    o = fwd(q, k, v, g)
+    o_loop = loop_attention(q, k, v, g)
+    assert np.max(np.abs(o - o_loop)) < 1e-12
+
+
+def check_one_window_is_full_attention(fwd):
+    # H = W = w and no guide tokens: the mask allows everything
+    for theta in (0.0, 10000.0):
+        g = small_geom(H=8, W=8, w=8, H_lr=0, W_lr=0, heads=3, head_dim=16, B=2, theta=theta)
+        q, k, v = rand_qkv(g, 3)
+        o = fwd(q, k, v, g)
+        py, px = orc.hi_positions(g.H, g.W)
+        if theta > 0:
+            qr, kr = complex_rope(q[0], py, px, theta), complex_rope(k[0], py, px, theta)
+            qr = np.stack([qr, complex_rope(q[1], py, px, theta)])
+            kr = np.stack([kr, complex_rope(k[1], py, px, theta)])
+        else:
+            qr, kr = q, k
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a.transpose(0, 2, 1, 3)))
+        ref = torch.nn.functional.scaled_dot_product_attention(t(qr), t(kr), t(v))
+        ref = ref.numpy().transpose(0, 2, 1, 3)
+        assert np.max(np.abs(o - ref)) < 1e-12
+
+
+def check_two_by_two_grid_is_dense(fwd):
+    # a 2 x 2 window grid: every hi row sees every key; guide rows see guide keys only
+    g = small_geom(H=8, W=8, w=4, H_lr=2, W_lr=2, heads=2, head_dim=8, theta=0.0)
+    q, k, v = rand_qkv(g, 4)
+    o = fwd(q, k, v, g)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a.transpose(0, 2, 1, 3)))
+    full = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v)).numpy()
+    lr = torch.nn.functional.scaled_dot_product_attention(
+        t(q[:, g.N:]), t(k[:, g.N:]), t(v[:, g.N:])).numpy()
+    assert np.max(np.abs(o[:, :g.N] - full.transpose(0, 2, 1, 3)[:, :g.N])) < 1e-12
+    assert np.max(np.abs(o[:, g.N:] - lr.transpose(0, 2, 1, 3))) < 1e-12
+
+
+def check_uniform_probe(fwd):
+    # Q = 0: every allowed key gets the same weight; O is the mean of V over the allowed set.
+    g = small_geom(H=16, W=12, w=4, H_lr=4, W_lr=3, heads=1, head_dim=8)
+    q = np.zeros(g.shape())
+    k = rand_qkv(g, 2)[1]
+    v = np.zeros(g.shape())
+    yy, xx = orc.hi_positions(g.H, g.W)
+    v[0, :g.N, 0, 0] = yy // g.w
+    v[0, :g.N, 0, 1] = xx // g.w
+    v[0, g.N:, 0, 2] = 1.0
+    o = fwd(q, k, v, g)
+    nwy, nwx = g.H // g.w, g.W // g.w
+    for r in range(g.N):
+        wy, wx = yy[r] // g.w, xx[r] // g.w
+        nb = [(a, b) for a in range(wy - 1, wy + 2) for b in range(wx - 1, wx + 2)
+              if 0 <= a < nwy and 0 <= b < nwx]
+        tot = len(nb) * g.w * g.w + g.M
+        assert abs(o[0, r, 0, 0] - sum(a for a, _ in nb) * g.w * g.w / tot) < 1e-12
+        assert abs(o[0, r, 0, 1] - sum(b for _, b in nb) * g.w * g.w / tot) < 1e-12
+        assert abs(o[0, r, 0, 2] - g.M / tot) < 1e-12
+    assert np.allclose(o[0, g.N:, 0, :2], 0) and np.allclose(o[0, g.N:, 0, 2], 1)
+
+
+# ---------------------------------------------------------------- the oracle passes them
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32),
+                        # exact ties between two bfloat16 values, both parities
+                        (np.arange(1, 2000, dtype=np.uint32) << 16 | 0x8000).view(np.float32),
+                        np.array([0.0, -0.0, 1e-40, 3e38], dtype=np.float32)])
+    ours = f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_index_map():
+    check_index_map(orc.window_first_source_index)
+
+
+def test_permute_roundtrip():
+    check_permute_roundtrip(orc.window_permute, orc.window_unpermute)
+
+
+def test_rope():
+    check_rope(orc.rope_rotate)
+
+
+def test_positions():
+    check_positions(orc.hi_positions, orc.lr_positions)
+
+
+def test_lr_rotation_equals_hi_rotation_at_scaled_position():
+    # a guide token at (i, j) rotates exactly like a hi-res token at (rho*i, rho*j)
+    g = small_geom(H=16, W=16, w=4, H_lr=4, W_lr=4, head_dim=16)
+    x = np.random.default_rng(1).standard_normal((1, g.L, 1, 16))
+    x[0, g.N:] = x[0, :g.N][[(4 * (s // 4)) * 16 + 4 * (s % 4) for s in range(16)]]
+    y = orc.rope_joint(x, g)
+    hi_idx = [(4 * (s // 4)) * 16 + 4 * (s % 4) for s in range(16)]
+    assert np.array_equal(y[0, g.N:], y[0, hi_idx])
+
+
+def test_mask():
+    check_mask(orc.mask_rows)
+
+
+def test_pair_counts():
+    check_pair_counts(orc.mask_rows)
+
+
+def test_pair_count_closed_form_matches_mask():
+    for g in [small_geom(H=20, W=8, w=4, H_lr=5, W_lr=2), CONFIGS["tiny"],
+              small_geom(H=4, W=12, w=4, H_lr=1, W_lr=3)]:
+        assert int(orc.mask_rows(g, np.arange(g.L)).sum()) == algorithmic_pairs(g)["total"]
+
+
+def test_attention_vs_loops():
+    check_attention(orc.forward)
+
+
+def test_one_window_is_full_attention():
+    check_one_window_is_full_attention(orc.forward)
+
+
+def test_two_by_two_grid_is_dense():
+    check_two_by_two_grid_is_dense(orc.forward)
+
+
+def test_uniform_probe():
+    check_uniform_probe(orc.forward)
+
+
+def test_softmax_rows_sum_to_one():
+    g = CONFIGS["tiny"]
+    q, k, v = rand_qkv(g, 0)
+    qr, kr = orc.rotated_qk(q, k, g, 0, 1)
+    rows = np.arange(0, g.L, 7)
+    _, p = orc.masked_softmax_attention(qr[rows], kr, v[0, :, 1], orc.mask_rows(g, rows),
+                                        g.scale, return_probs=True)
+    assert np.allclose(p.sum(axis=1), 1.0, atol=1e-13)
+    assert np.all(p[~orc.mask_rows(g, rows)] == 0)
+
+
+def test_constant_value_gives_constant_output():
+    g = small_geom(H=8, W=12, w=4, H_lr=2, W_lr=3, heads=2)
+    q, k, _ = rand_qkv(g, 9)
+    o = orc.forward(q, k, np.ones(g.shape()), g)
+    assert np.allclose(o, 1.0, atol=1e-14)
+
+
+def test_shift_invariance_of_positions():
+    # shifting every position by a constant leaves attention unchanged (relative RoPE)
+    g = small_geom(H=8, W=8, w=4, H_lr=2, W_lr=2, head_dim=16)
+    q, k, v = rand_qkv(g, 6)
+    py, px = orc.token_positions(g)
+    m = orc.mask_rows(g, np.arange(g.L))
+    outs = []
+    for sy, sx in ((0, 0), (17, 5)):
+        qr = orc.rope_rotate(q[0], py + sy, px + sx, g.theta)[:, 0]
+        kr = orc.rope_rotate(k[0], py + sy, px + sx, g.theta)[:, 0]
+        outs.append(orc.masked_softmax_attention(qr, kr, v[0, :, 0], m, g.scale))
+    assert np.max(np.abs(outs[0] - outs[1])) < 1e-12
+
+
+def test_identity_probe():
+    # Q = K = 4 X: the self logit dominates, so every row returns its own V row
+    g = CONFIGS["tiny"]
+    x = rand_qkv(g, 0)[0]
+    v = rand_qkv(g, 1)[2]
+    o = orc.forward(4 * x, 4 * x, v, g)
+    assert np.max(np.abs(o - v)) < 1e-12
+
+
+# --------------------------------------------------------- planted mistakes must be caught
+
+def _mut_index_transposed(H, W, w):
+    p = np.arange(H * W)
+    win, t = np.divmod(p, w * w)
+    wy, wx = np.divmod(win, W // w)
+    ix, iy = np.divmod(t, w)  # transposed inside the window
+    return (wy * w + iy) * W + (wx * w + ix)
+
+
+def _mut_index_window_colmajor(H, W, w):
+    p = np.arange(H * W)
+    win, t = np.divmod(p, w * w)
+    wx, wy = np.divmod(win, H // w)  # windows enumerated column-major
+    iy, ix = np.divmod(t, w)
+    return (wy * w + iy) * W + (wx * w + ix)
+
+
+def _mut_rope_sign(x, py, px, theta):
+    return orc.rope_rotate(x, -np.asarray(py), -np.asarray(px), theta)
+
+
+def _mut_rope_axes_swapped(x, py, px, theta):
+    return orc.rope_rotate(x, px, py, theta)
+
+
+def _mut_rope_halfdim_freq(x, py, px, theta):
+    # frequencies over the full head_dim instead of per axis
+    d = x.shape[-1]
+    out = orc.rope_rotate(x, np.zeros_like(py), np.zeros_like(px), theta)
+    da = d // 2
+    om = theta ** (-2.0 * np.arange(da // 2) / d)
+    for blk, pos in ((0, py), (1, px)):
+        phi = np.asarray(pos, float)[:, None] * om[None]
+        c, s = np.cos(phi)[:, None], np.sin(phi)[:, None]
+        a, b = x[..., blk * da:(blk + 1) * da:2], x[..., blk * da + 1:(blk + 1) * da:2]
+        out[..., blk * da:(blk + 1) * da:2] = a * c - b * s
+        out[..., blk * da + 1:(blk + 1) * da:2] = a * s + b * c
+    return out
+
+
+def _mut_lr_positions_offset(H_lr, W_lr, rho):
+    y, x = orc.lr_positions(H_lr, W_lr, rho)
+    return y + (rho - 1) // 2, x + (rho - 1) // 2
+
+
+def _mut_mask_no_diagonal(geom, rows):
+    m = orc.mask_rows(geom, rows)
+    rows = np.asarray(rows)
+    key = np.arange(geom.L)
+    hi_q, hi_k = rows < geom.N, key < geom.N
+    qy, qx = (rows // geom.W) // geom.w, (rows % geom.W) // geom.w
+    ky, kx = (key // geom.W) // geom.w, (key % geom.W) // geom.w
+    diag = (np.abs(qy[:, None] - ky[None]) == 1) & (np.abs(qx[:, None] - kx[None]) == 1)
+    return m & ~(diag & hi_q[:, None] & hi_k[None])
+
+
+def _mut_mask_lr_sees_hi(geom, rows):
+    m = orc.mask_rows(geom, rows)
+    m[np.asarray(rows) >= geom.N, :geom.N] = True
+    return m
+
+
+def _mut_mask_wrap(geom, rows):
+    # neighbourhood wraps around the grid edges
+    rows = np.asarray(rows)
+    nwy, nwx = geom.H // geom.w, geom.W // geom.w
+    m = orc.mask_rows(geom, rows)
+    key = np.arange(geom.N)
+    for i, r in enumerate(rows):
+        if r >= geom.N:
+            continue
+        qy, qx = (r // geom.W) // geom.w, (r % geom.W) // geom.w
+        ky, kx = (key // geom.W) // geom.w, (key % geom.W) // geom.w
+        dy = np.minimum((qy - ky) % nwy, (ky - qy) % nwy)
+        dx = np.minimum((qx - kx) % nwx, (kx - qx) % nwx)
+        m[i, :geom.N] = (dy <= 1) & (dx <= 1)
+    return m
+
+
+def _mut_forward_no_scale(q, k, v, geom):
+    return orc.forward(q * math.sqrt(geom.head_dim), k, v, geom)
+
+
+@pytest.mark.parametrize("mutant", [_mut_index_transposed, _mut_index_window_colmajor])
+def test_pins_catch_index_mutants(mutant):
+    with pytest.raises(AssertionError):
+        check_index_map(mutant)
+
+
+@pytest.mark.parametrize("mutant", [_mut_rope_sign, _mut_rope_axes_swapped, _mut_rope_halfdim_freq])
+def test_pins_catch_rope_mutants(mutant):
+    with pytest.raises(AssertionError):
+        check_rope(mutant)
+
+
+def test_pins_catch_position_mutant():
+    with pytest.raises(AssertionError):
+        check_positions(orc.hi_positions, _mut_lr_positions_offset)
+
+
+@pytest.mark.parametrize("mutant", [_mut_mask_no_diagonal, _mut_mask_lr_sees_hi, _mut_mask_wrap])
+def test_pins_catch_mask_mutants(mutant):
+    with pytest.raises(AssertionError):
+        check_mask(mutant)
+
+
+@pytest.mark.parametrize("mutant", [_mut_forward_no_scale])
+def test_pins_catch_forward_mutants(mutant):
+    with pytest.raises(AssertionError):
+        check_attention(mutant)
+    with pytest.raises(AssertionError):
+        check_one_window_is_full_attention(mutant)
