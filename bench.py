@@ -1,0 +1,209 @@
+"""Benchmark: hierarchical local attention forward at the 8K workload on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 8k] [--cpu-seconds S]
+
+A step is one full uhla_forward (neighbour/cos-sin tables -> permutation fused with RoPE
+-> hi-res block-sparse attention -> guide attention -> inverse permutation) over one
+batch of synthetic inputs already resident in HBM.  Prints ONE JSON line.
+
+value       effective TFLOP/s of the whole step: algorithmic FLOPs (4 * head_dim per
+            unmasked (query, key) pair) / step time.
+roofline    the dominant kernel (hi-res attention pass) against the bf16 MFMA peak:
+            its algorithmic FLOPs per launch / its mean launch duration, measured with
+            HIP events recorded on the launch stream during the timed steps.
+cpu_baseline  the fp64 oracle on a time-bounded sample of query rows of the same
+            workload, on this host's cores, in the same unit.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective TFLOP/s (unmasked blocks) + tokens/s, 8K fwd; % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+ATTN_SOURCE = os.path.join(ROOT, "global_attention_image_amd", "csrc", "attention.hip")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_hi_8k_hbm_traffic.md")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch of the hi attention kernel from the committed counter summary,
+    or None when the summary is missing or was taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_PROFILE):
+        if ":" in line and line.strip().startswith("- "):
+            k, v = line.strip()[2:].split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("attention.hip sha256[:16]") != source_hash(ATTN_SOURCE):
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(geom, q, k, v, seconds):
+    """Time the oracle on query rows of (b=0, h=0) in blocks until `seconds` elapse."""
+    import oracle.uhla_oracle as orc
+    from global_attention_image_amd.inputs import bf16_bits_to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(0)
+    t0 = time.perf_counter()
+    qs = bf16_bits_to_f64(q[0:1, :, 0:1, :])
+    ks = bf16_bits_to_f64(k[0:1, :, 0:1, :])
+    vs = bf16_bits_to_f64(v[0:1, :, 0:1, :])
+    qk = orc.rotated_qk(qs, ks, geom, 0, 0)
+    rows_done, pairs = 0, 0
+    block = 64
+    while True:
+        rows = np.sort(rng.choice(geom.L, block, replace=False))
+        orc.attention_rows(qs, ks, vs, geom, 0, 0, rows, block=block, qk=qk)
+        rows_done += block
+        pairs += int(orc.allowed_key_count(geom, rows).sum())
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    flops = 4 * geom.head_dim * pairs
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{rows_done} uniformly sampled query rows of batch 0 / head 0 of the "
+                      f"{geom.name} workload (RoPE of that head, explicit mask rows, dense fp64 "
+                      f"softmax over all {geom.L} keys); {dt:.1f} s wall; FLOPs counted as 4*d "
+                      f"per unmasked pair",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="8k")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from global_attention_image_amd import api
+    from global_attention_image_amd.inputs import (CONFIGS, CONFIG_SEEDS, algorithmic_flops,
+                                                    algorithmic_pairs, make_qkv_bits)
+
+    g = CONFIGS[args.config]
+    log(f"[bench] generating seeded inputs for {g}")
+    t0 = time.perf_counter()
+    q, k, v = make_qkv_bits(g, CONFIG_SEEDS[args.config])
+    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s; uploading")
+    dev = torch.device("cuda:0")
+    up = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+    qt, kt, vt = up(q), up(k), up(v)
+    out = torch.empty_like(qt)
+    ws = api.alloc_workspace(g.B, g.H, g.W, g.w, g.H_lr, g.W_lr, g.heads, g.head_dim, dev)
+    fwd = lambda timer=None: api.forward(qt, kt, vt, g.H, g.W, g.w, g.H_lr, g.W_lr, rho=g.rho,
+                                         theta=g.theta, out=out, workspace=ws, timer=timer)
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+    timer = api.Timer(args.steps)
+    log(f"[bench] warmup done; timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        fwd(timer)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stage_ms, calls = timer.read()
+    timer.close()
+    ms_step = elapsed * 1e3 / args.steps
+    stage_avg = {s: stage_ms[s] / calls for s in stage_ms}
+    flops = algorithmic_flops(g)
+    pairs = algorithmic_pairs(g)
+    tflops = flops["total"] / (ms_step * 1e-3) / 1e12
+    attn_hi_ms = stage_avg["attn_hi"]
+    achieved = flops["hi"] / (attn_hi_ms * 1e-3) / 1e12
+    log(f"[bench] {ms_step:.3f} ms/step; stages (ms/call): "
+        + ", ".join(f"{s}={stage_avg[s]:.3f}" for s in stage_avg))
+
+    # standalone permutation bandwidth (one of the four entry points), Q hi segment
+    pdst = torch.empty((g.B, g.N, g.heads, g.head_dim), dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        api.window_permute(qt, pdst, g.H, g.W, g.w, src_tokens_per_batch=g.L,
+                           dst_tokens_per_batch=g.N)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        api.window_permute(qt, pdst, g.H, g.W, g.w, src_tokens_per_batch=g.L,
+                           dst_tokens_per_batch=g.N)
+    e1.record()
+    torch.cuda.synchronize()
+    perm_ms = e0.elapsed_time(e1) / reps
+    perm_bytes = 2 * g.B * g.N * g.heads * g.head_dim * 2
+    perm_gbs = perm_bytes / (perm_ms * 1e-3) / 1e9
+    del pdst
+
+    traffic = read_traffic()
+    res = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": g.name, "B": g.B, "heads": g.heads, "head_dim": g.head_dim,
+                   "grid": f"{g.H}x{g.W}", "window": g.w, "guide_grid": f"{g.H_lr}x{g.W_lr}",
+                   "rho": g.rho, "rope_theta": g.theta, "tokens": g.L,
+                   "parallelism": "single GPU"},
+        "tokens_per_s": round(g.B * g.L / (ms_step * 1e-3), 1),
+        "hi_tokens_per_s": round(g.B * g.N / (ms_step * 1e-3), 1),
+        "algorithmic_flops": flops,
+        "unmasked_pairs_per_head": pairs,
+        "frac_bf16_peak_step": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "stage_ms": {s: round(x, 4) for s, x in stage_avg.items()},
+        "roofline": {"kernel": "attn_fwd_kernel<128,8> (hi-res pass)", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+        "permute": {"entry_point": "uhla_window_permute (Q hi segment, bf16)",
+                    "ms": round(perm_ms, 4), "GB/s": round(perm_gbs, 1),
+                    "frac_hbm_peak": round(perm_gbs / PEAK_HBM_GBS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU baseline: oracle for ~{args.cpu_seconds:.0f} s")
+        res["cpu_baseline"] = cpu_baseline(g, q, k, v, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

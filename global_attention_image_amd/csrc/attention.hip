@@ -1,0 +1,699 @@
+// Hierarchical local attention forward on gfx950 (bf16 MFMA, fp32 softmax).
+//
+// Mask ([UltraGen/ar §2.B], [UltraGen/es §2]): each hi-res window attends to itself, to
+// its clipped 3x3 neighbourhood of windows and to every guide token; guide tokens attend
+// to each other.  Blocks are spatial windows in window-first order ([UltraGen/it §2],
+// [UltraGen/fr §2.A]).
+//
+// Pipeline (all on the caller's stream, no allocation):
+//   1. neighbour table [nW][9] + count, and the fp64 RoPE cos/sin table [P][head_dim/4]
+//   2. prep: window-first permutation of the hi rows of Q, K, V fused with RoPE on Q, K;
+//      Q, K land head-major [B*heads][rows][D]; V lands in 64-key tiles transposed to
+//      [D][64] so the P.V contraction reads it with one 16-byte LDS load per operand.
+//      Guide rows are rotated / re-laid out the same way (no permutation).
+//   3. hi pass: one workgroup per (b, h, window, 256-query chunk); it streams the K/V
+//      tiles of its neighbour windows, then of all guide tokens, through LDS.
+//   4. guide pass: one workgroup per (b, h, 256 guide queries) over all guide keys.
+//   5. inverse permutation of the hi rows of O.
+//
+// MFMA formulation (v_mfma_f32_32x32x16_bf16, wave64).  Each wave owns 32 queries.
+// S^T = K Q^T: A = 32 keys x 16 dims from LDS, B = Q^T held in registers, so each lane
+// holds the scores of ONE query (lane & 31) for 16 keys: softmax statistics stay in the
+// lane, plus one exchange with lane ^ 32 (v_permlane32_swap).  O^T = V^T P^T: A = V^T (32 dims x 16 keys)
+// from LDS, B = P^T, which is the S^T accumulator converted to bf16 in place.
+#include "uhla_internal.h"
+
+namespace uhla {
+
+int launch_window_copy(const void* src, void* dst, int B, int H, int W, int w,
+                       int64_t row_bytes, int64_t src_tpb, int64_t dst_tpb, int inverse,
+                       hipStream_t stream);
+
+constexpr int kKeyTile = 64;     // keys per K/V tile
+constexpr int kMaxQuery = 256;   // queries per workgroup (8 waves x 32)
+
+// ------------------------------------------------------------------ geometry / layout
+
+struct Geom {
+  int B, H, W, w, H_lr, W_lr, rho, heads, D;
+  int64_t N, M, Mk, Mq;  // Mk: guide rows padded to the key tile; Mq: to the query block
+  int n_wx, n_wy, nW, P;  // P: positions covered by the cos/sin table (max(H, W))
+};
+
+static Geom make_geom(int B, int H, int W, int w, int H_lr, int W_lr, int rho, int heads,
+                      int D) {
+  Geom g;
+  g.B = B; g.H = H; g.W = W; g.w = w; g.H_lr = H_lr; g.W_lr = W_lr; g.rho = rho;
+  g.heads = heads; g.D = D;
+  g.N = static_cast<int64_t>(H) * W;
+  g.M = static_cast<int64_t>(H_lr) * W_lr;
+  g.Mk = (g.M + kKeyTile - 1) / kKeyTile * kKeyTile;
+  g.Mq = (g.M + kMaxQuery - 1) / kMaxQuery * kMaxQuery;
+  g.n_wx = W / w; g.n_wy = H / w; g.nW = g.n_wx * g.n_wy;
+  // The cos/sin table covers hi-res positions; guide positions beyond it (a guide grid
+  // reaching past the hi-res extent) are evaluated directly with the same function.
+  const int p = H > W ? H : W;
+  g.P = p;
+  return g;
+}
+
+struct Workspace {
+  int* nbr;       // [nW][9]
+  int* nbr_cnt;   // [nW]
+  double2* cs;    // [P][D/4]
+  bf16_t* q_hi;   // [B*heads][N][D]   window-first, rotated
+  bf16_t* k_hi;   // [B*heads][N][D]   window-first, rotated
+  bf16_t* v_hi;   // [B*heads][N/64][D][64]  window-first, transposed tiles
+  bf16_t* q_lr;   // [B*heads][Mq][D]  rotated, zero padded
+  bf16_t* k_lr;   // [B*heads][Mk][D]  rotated, zero padded
+  bf16_t* v_lr;   // [B*heads][Mk/64][D][64]
+  bf16_t* o_hi;   // [B][N][heads][D]  window-first output
+  size_t bytes;
+};
+
+static Workspace carve(const Geom& g, void* base) {
+  Workspace ws;
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    const size_t o = off;
+    off = align_up(off + n, 256);
+    return o;
+  };
+  const size_t bh = static_cast<size_t>(g.B) * g.heads;
+  const size_t e = sizeof(bf16_t);
+  const size_t o_nbr = take(sizeof(int) * g.nW * 9);
+  const size_t o_cnt = take(sizeof(int) * g.nW);
+  const size_t o_cs = take(sizeof(double2) * g.P * (g.D / 4));
+  const size_t o_qh = take(bh * g.N * g.D * e);
+  const size_t o_kh = take(bh * g.N * g.D * e);
+  const size_t o_vh = take(bh * g.N * g.D * e);
+  const size_t o_ql = take(bh * g.Mq * g.D * e);
+  const size_t o_kl = take(bh * g.Mk * g.D * e);
+  const size_t o_vl = take(bh * g.Mk * g.D * e);
+  const size_t o_oh = take(bh * g.N * g.D * e);
+  char* b = static_cast<char*>(base);
+  ws.nbr = reinterpret_cast<int*>(b + o_nbr);
+  ws.nbr_cnt = reinterpret_cast<int*>(b + o_cnt);
+  ws.cs = reinterpret_cast<double2*>(b + o_cs);
+  ws.q_hi = reinterpret_cast<bf16_t*>(b + o_qh);
+  ws.k_hi = reinterpret_cast<bf16_t*>(b + o_kh);
+  ws.v_hi = reinterpret_cast<bf16_t*>(b + o_vh);
+  ws.q_lr = reinterpret_cast<bf16_t*>(b + o_ql);
+  ws.k_lr = reinterpret_cast<bf16_t*>(b + o_kl);
+  ws.v_lr = reinterpret_cast<bf16_t*>(b + o_vl);
+  ws.o_hi = reinterpret_cast<bf16_t*>(b + o_oh);
+  ws.bytes = off;
+  return ws;
+}
+
+// ------------------------------------------------------------------ step 1: tables
+
+// Clipped 3x3 neighbourhood of each window, row-major (dy outer, dx inner), self included.
+__global__ void neighbour_table_kernel(int n_wy, int n_wx, int* nbr, int* cnt) {
+  const int win = blockIdx.x * blockDim.x + threadIdx.x;
+  if (win >= n_wy * n_wx) return;
+  const int wy = win / n_wx, wx = win - wy * n_wx;
+  int c = 0;
+  for (int dy = -1; dy <= 1; ++dy)
+    for (int dx = -1; dx <= 1; ++dx) {
+      const int y = wy + dy, x = wx + dx;
+      if (y >= 0 && y < n_wy && x >= 0 && x < n_wx) nbr[win * 9 + c++] = y * n_wx + x;
+    }
+  for (int j = c; j < 9; ++j) nbr[win * 9 + j] = -1;
+  cnt[win] = c;
+}
+
+__global__ void cos_sin_table_kernel(double2* cs, int P, int D, double log2_theta) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int quarter = D / 4;
+  if (i >= P * quarter) return;
+  const int pos = i / quarter, k = i - pos * quarter;
+  cs[i] = rope_cos_sin(pos, k, D / 2, log2_theta);
+}
+
+// ------------------------------------------------------------------ step 2: prep
+
+constexpr int kPrepThreads = 256;
+constexpr int kPrepRows = 4;
+
+// Q and K rows -> head-major, rotated.  Rows [0, N) of each batch are hi-res rows in
+// window-first order (source row r(p)), rows [N, N + rows_lr) are guide rows (source row
+// N + s, zero beyond M).  Q guide rows pad to Mq, K guide rows to Mk.
+__global__ __launch_bounds__(kPrepThreads) void prep_qk_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, bf16_t* q_hi, bf16_t* k_hi,
+    bf16_t* q_lr, bf16_t* k_lr, const double2* __restrict__ cs, int P, double log2_theta,
+    int64_t N, int64_t M, int64_t Mq, int64_t Mk, int W, int w, int n_wx, int W_lr, int rho,
+    int heads, int D, int rope_on) {
+  const int64_t L = N + M;
+  const int64_t rows_total = N + Mq;
+  const int64_t b = blockIdx.y;
+  const int chunks_per_head = D / 8;
+  const int chunks_per_row = heads * chunks_per_head;
+  const int quarter = D / 4;
+  for (int i = threadIdx.x; i < kPrepRows * chunks_per_row; i += kPrepThreads) {
+    const int t = i / chunks_per_row, c = i - t * chunks_per_row;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * kPrepRows + t;
+    if (row >= rows_total) continue;
+    const int h = c / chunks_per_head, j = c - h * chunks_per_head;
+    int64_t src_row;
+    int py, px;
+    bool valid = true;
+    bf16_t* dq;
+    bf16_t* dk;
+    if (row < N) {
+      const int r = window_first_to_raster(static_cast<int>(row), W, w, n_wx);
+      src_row = r;
+      py = r / W;
+      px = r - py * W;
+      const int64_t o = ((b * heads + h) * N + row) * D + j * 8;
+      dq = q_hi + o;
+      dk = k_hi + o;
+    } else {
+      const int64_t s = row - N;
+      valid = s < M;
+      src_row = N + s;
+      const int sy = valid ? static_cast<int>(s / W_lr) : 0;
+      py = rho * sy;
+      px = valid ? rho * static_cast<int>(s - static_cast<int64_t>(sy) * W_lr) : 0;
+      dq = q_lr + ((b * heads + h) * Mq + s) * D + j * 8;
+      dk = (s < Mk) ? k_lr + ((b * heads + h) * Mk + s) * D + j * 8 : nullptr;
+    }
+    uint4 qo = make_uint4(0, 0, 0, 0), ko = make_uint4(0, 0, 0, 0);
+    if (valid) {
+      const int64_t so = ((b * L + src_row) * heads + h) * D + j * 8;
+      const uint4 qi = *reinterpret_cast<const uint4*>(q + so);
+      const uint4 ki = *reinterpret_cast<const uint4*>(k + so);
+      if (rope_on) {
+        const uint32_t qw[4] = {qi.x, qi.y, qi.z, qi.w}, kw[4] = {ki.x, ki.y, ki.z, ki.w};
+        uint32_t qr[4], kr[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int pr = j * 4 + e;  // pair index inside the head
+          const int axis = pr / quarter, kk = pr - axis * quarter;
+          const int pos = axis ? px : py;
+          const double2 f = pos < P ? cs[pos * quarter + kk] : rope_cos_sin(pos, kk, D / 2, log2_theta);
+          qr[e] = rope_rotate_word(qw[e], f);
+          kr[e] = rope_rotate_word(kw[e], f);
+        }
+        qo = make_uint4(qr[0], qr[1], qr[2], qr[3]);
+        ko = make_uint4(kr[0], kr[1], kr[2], kr[3]);
+      } else {
+        qo = qi;
+        ko = ki;
+      }
+    }
+    *reinterpret_cast<uint4*>(dq) = qo;
+    if (dk) *reinterpret_cast<uint4*>(dk) = ko;
+  }
+}
+
+// Position of key `kappa` (0..63) of a tile inside the stored V^T row: within each group
+// of 16 keys the two middle quads are swapped (bits 2 and 3 of the index exchanged), so
+// that the 8 keys one lane feeds into a 32x32x16 MFMA sit in 16 contiguous bytes.
+__device__ __forceinline__ int v_slot(int kappa) {
+  return (kappa & ~12) | ((kappa & 4) << 1) | ((kappa & 8) >> 1);
+}
+
+// V rows -> 64-key tiles transposed to [D][64] (key order by v_slot).  Tile index
+// t < N/64 covers window-first hi rows [64 t, 64 t + 64); tiles beyond cover guide rows.
+__global__ __launch_bounds__(kPrepThreads) void prep_v_kernel(
+    const bf16_t* __restrict__ v, bf16_t* v_hi, bf16_t* v_lr, int64_t N, int64_t M, int64_t Mk,
+    int W, int w, int n_wx, int heads, int D) {
+  __shared__ bf16_t tile[kKeyTile][128 + 2];
+  const int64_t L = N + M;
+  const int64_t b = blockIdx.y;
+  const int64_t tile_id = blockIdx.x;
+  const int64_t n_hi_tiles = N / kKeyTile;
+  const int chunks_per_row = D / 8;
+  for (int h = 0; h < heads; ++h) {
+    // load 64 rows x D of head h (each row 16-byte chunks)
+    for (int i = threadIdx.x; i < kKeyTile * chunks_per_row; i += kPrepThreads) {
+      const int kr = i / chunks_per_row, j = i - kr * chunks_per_row;
+      int64_t src_row;
+      bool valid = true;
+      if (tile_id < n_hi_tiles) {
+        src_row = window_first_to_raster(static_cast<int>(tile_id * kKeyTile + kr), W, w, n_wx);
+      } else {
+        const int64_t s = (tile_id - n_hi_tiles) * kKeyTile + kr;
+        valid = s < M;
+        src_row = N + s;
+      }
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (valid) x = *reinterpret_cast<const uint4*>(v + ((b * L + src_row) * heads + h) * D + j * 8);
+      const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        tile[kr][j * 8 + 2 * e] = static_cast<bf16_t>(xw[e] & 0xffff);
+        tile[kr][j * 8 + 2 * e + 1] = static_cast<bf16_t>(xw[e] >> 16);
+      }
+    }
+    __syncthreads();
+    // write D rows x 64 keys; each thread writes 8 consecutive slots of one d-row
+    bf16_t* dst;
+    if (tile_id < n_hi_tiles)
+      dst = v_hi + ((b * heads + h) * n_hi_tiles + tile_id) * static_cast<int64_t>(D) * kKeyTile;
+    else
+      dst = v_lr + ((b * heads + h) * (Mk / kKeyTile) + (tile_id - n_hi_tiles)) *
+                       static_cast<int64_t>(D) * kKeyTile;
+    for (int i = threadIdx.x; i < D * (kKeyTile / 8); i += kPrepThreads) {
+      const int d = i / (kKeyTile / 8), s8 = (i - d * (kKeyTile / 8)) * 8;
+      uint32_t wv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // slot s holds key v_slot(s) (the mapping is its own inverse)
+        const uint32_t lo = tile[v_slot(s8 + 2 * e)][d];
+        const uint32_t hi = tile[v_slot(s8 + 2 * e + 1)][d];
+        wv[e] = lo | (hi << 16);
+      }
+      *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(d) * kKeyTile + s8) =
+          make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ steps 3-4: attention
+
+struct AttnArgs {
+  const bf16_t* q;        // [B*heads][q_rows][D]
+  int64_t q_rows;         // rows per (b, h) of q
+  const bf16_t* k_hi;     // [B*heads][N][D]
+  const bf16_t* v_hi;     // [B*heads][N/64][D][64]
+  const bf16_t* k_lr;     // [B*heads][Mk][D]
+  const bf16_t* v_lr;     // [B*heads][Mk/64][D][64]
+  const int* nbr;         // [nW][9]
+  const int* nbr_cnt;     // [nW]
+  bf16_t* out;            // token-major [B][out_rows][heads][D]
+  int64_t out_rows;       // rows per batch of out
+  int64_t out_row0;       // first row of this pass inside a batch of out
+  int64_t N, M, Mk;
+  int heads, w2, hi;      // hi = 1: hi pass (local + guide keys), 0: guide pass
+  int q_valid;            // valid query rows per (b, h)
+  int blocks_per_bh;
+  int total_blocks;
+  float c;                // softmax scale * log2(e)
+  float rescale_thr;      // lazy-rescale threshold in raw-score units
+};
+
+// Workgroups are dealt round-robin to the 8 XCDs; remap so that each XCD works on a
+// contiguous range of (b, h, window): neighbouring windows and the guide K/V of one head
+// then share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int i, int G) {
+  const int x = i & 7, j = i >> 3;
+  const int per = G >> 3, rem = G & 7;
+  return x < rem ? x * (per + 1) + j : rem * (per + 1) + (x - rem) * per + j;
+}
+
+// Lanes l and l ^ 32 hold the same query (different keys).  v_permlane32_swap exchanges
+// the upper half of its first operand with the lower half of its second: with both
+// operands = x, the two results hold x[l] and x[l ^ 32] in some order on every lane.
+__device__ __forceinline__ float max_with_partner32(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float sum_with_partner32(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+template <int D>
+__device__ __forceinline__ int k_swizzle(int row) {
+  // 16-byte chunk XOR swizzle so 16 lanes reading the same chunk of 16 rows hit 16
+  // distinct bank groups.
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+__device__ __forceinline__ int v_swizzle(int row) { return (row >> 1) & 7; }
+
+template <int D, int NWAVES>
+__global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
+  constexpr int NT = NWAVES * 64;
+  constexpr int TILE_BYTES = kKeyTile * D * 2;       // one K or V tile
+  constexpr int CHUNKS = TILE_BYTES / 16;
+  constexpr int CPT = CHUNKS / NT;                     // 16-byte chunks per thread
+  static_assert(CHUNKS % NT == 0, "tile must split evenly");
+  constexpr int KCH = D / 8;                           // 16-byte chunks per K row
+  __shared__ __attribute__((aligned(16))) char smem[2][2][TILE_BYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ql = lane & 31, g = lane >> 5;
+  const int blk = xcd_remap(blockIdx.x, a.total_blocks);
+  const int bh = blk / a.blocks_per_bh, qb = blk - bh * a.blocks_per_bh;
+  const int b = bh / a.heads, h = bh - b * a.heads;
+  const int qt = NWAVES * 32;
+  const int q0 = qb * qt;
+
+  // Tile list: hi pass = neighbour windows (w2/64 tiles each), then guide tiles.
+  int n_local = 0, win = 0;
+  const int tiles_per_win = a.w2 / kKeyTile;
+  if (a.hi) {
+    win = q0 / a.w2;
+    n_local = a.nbr_cnt[win] * tiles_per_win;
+  }
+  const int n_lr = static_cast<int>(a.Mk / kKeyTile);
+  const int n_tiles = n_local + n_lr;
+
+  u32x4 kreg[CPT], vreg[CPT];
+
+// Global -> registers for tile t (neighbour-window tiles first, then guide tiles).
+#define UHLA_LOAD_TILE(t, valid_out)                                                          \
+  do {                                                                                      \
+    const u32x4* kp_;                                                                       \
+    const u32x4* vp_;                                                                       \
+    if ((t) < n_local) {                                                                    \
+      const int j_ = (t) / tiles_per_win, sub_ = (t) - j_ * tiles_per_win;                  \
+      const int64_t krow_ = static_cast<int64_t>(a.nbr[win * 9 + j_]) * a.w2 + sub_ * kKeyTile; \
+      kp_ = reinterpret_cast<const u32x4*>(a.k_hi + (bh * a.N + krow_) * D);                \
+      vp_ = reinterpret_cast<const u32x4*>(a.v_hi + (bh * (a.N / kKeyTile) + krow_ / kKeyTile) * \
+                                                        static_cast<int64_t>(D) * kKeyTile); \
+      valid_out = kKeyTile;                                                                 \
+    } else {                                                                                \
+      const int j_ = (t) - n_local;                                                         \
+      kp_ = reinterpret_cast<const u32x4*>(a.k_lr + (bh * a.Mk + static_cast<int64_t>(j_) * kKeyTile) * D); \
+      vp_ = reinterpret_cast<const u32x4*>(a.v_lr + (bh * (a.Mk / kKeyTile) + j_) *         \
+                                                        static_cast<int64_t>(D) * kKeyTile); \
+      const int64_t rem_ = a.M - static_cast<int64_t>(j_) * kKeyTile;                       \
+      valid_out = rem_ < kKeyTile ? static_cast<int>(rem_) : kKeyTile;                      \
+    }                                                                                       \
+    _Pragma("unroll") for (int i_ = 0; i_ < CPT; ++i_) {                                    \
+      kreg[i_] = kp_[tid + i_ * NT];                                                        \
+      vreg[i_] = vp_[tid + i_ * NT];                                                        \
+    }                                                                                       \
+  } while (0)
+
+// Registers -> LDS buffer `buf` (swizzled).
+#define UHLA_STORE_TILE(buf)                                                                \
+  do {                                                                                      \
+    char* kb_ = smem[buf][0];                                                               \
+    char* vb_ = smem[buf][1];                                                               \
+    _Pragma("unroll") for (int i_ = 0; i_ < CPT; ++i_) {                                    \
+      const int c_ = tid + i_ * NT;                                                         \
+      const int kr_ = c_ / KCH, kc_ = c_ - kr_ * KCH;                                       \
+      *reinterpret_cast<u32x4*>(kb_ + kr_ * (D * 2) + ((kc_ ^ k_swizzle<D>(kr_)) << 4)) = kreg[i_]; \
+      const int vr_ = c_ >> 3, vc_ = c_ & 7;                                                \
+      *reinterpret_cast<u32x4*>(vb_ + vr_ * (kKeyTile * 2) + ((vc_ ^ v_swizzle(vr_)) << 4)) = vreg[i_]; \
+    }                                                                                       \
+  } while (0)
+
+  // Query fragment (B operand of S^T = K Q^T): lane holds query ql, dims 16kk + 8g .. +8.
+  bf16x8 qf[D / 16];
+  {
+    const bf16_t* qrow = a.q + (bh * a.q_rows + q0 + wave * 32 + ql) * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + 16 * kk + 8 * g);
+  }
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[dt][r] = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
+  const float c = a.c;
+
+  int valid_cur = kKeyTile, valid_next = kKeyTile;
+  UHLA_LOAD_TILE(0, valid_cur);
+  UHLA_STORE_TILE(0);
+  __syncthreads();
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < n_tiles) UHLA_LOAD_TILE(t + 1, valid_next);
+
+    // ---- S^T = K Q^T for 64 keys: two 32-key halves
+    const char* kb = smem[buf][0];
+    f32x16 s0, s1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { s0[r] = 0.0f; s1[r] = 0.0f; }
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const int ch = 2 * kk + g;
+      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kb + ql * (D * 2) + ((ch ^ k_swizzle<D>(ql)) << 4));
+      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(kb + (32 + ql) * (D * 2) + ((ch ^ k_swizzle<D>(32 + ql)) << 4));
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[kk], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[kk], s1, 0, 0, 0);
+    }
+    // lane holds keys 8*(r/4) + 4g + r%4 (s0) and 32 + that (s1)
+    if (valid_cur < kKeyTile) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 8 * (r >> 2) + 4 * g + (r & 3);
+        if (key >= valid_cur) s0[r] = -INFINITY;
+        if (key + 32 >= valid_cur) s1[r] = -INFINITY;
+      }
+    }
+
+    // ---- online softmax (base 2), lazy rescale of the running output
+    float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+    mx = max_with_partner32(mx);
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + a.rescale_thr) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      m_run = m_new;
+    }
+    const float mc = m_run * c;
+    float psum = 0.0f;
+    bf16x8 pf[4];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s0[r], c, -mc));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s0[r + 1], c, -mc));
+      const float p2 = __builtin_amdgcn_exp2f(fmaf(s1[r], c, -mc));
+      const float p3 = __builtin_amdgcn_exp2f(fmaf(s1[r + 1], c, -mc));
+      psum += (p0 + p1) + (p2 + p3);
+      // key-step ks = 2*half + r/8; slot j = r % 8
+      pf[r >> 3][r & 7] = static_cast<__bf16>(p0);
+      pf[r >> 3][(r & 7) + 1] = static_cast<__bf16>(p1);
+      pf[2 + (r >> 3)][r & 7] = static_cast<__bf16>(p2);
+      pf[2 + (r >> 3)][(r & 7) + 1] = static_cast<__bf16>(p3);
+    }
+    l_run += psum;
+
+    // ---- O^T += V^T P^T over 4 key-steps of 16 keys
+    const char* vb = smem[buf][1];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int ch = 2 * ks + g;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const int vr = dt * 32 + ql;
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vb + vr * (kKeyTile * 2) + ((ch ^ v_swizzle(vr)) << 4));
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[dt], 0, 0, 0);
+      }
+    }
+
+    if (t + 1 < n_tiles) UHLA_STORE_TILE(buf ^ 1);
+    valid_cur = valid_next;
+    __syncthreads();
+  }
+
+  // ---- epilogue: normalise and store (lane: query ql, dims dt*32 + 8*(r/4) + 4g + r%4)
+  const float lt = sum_with_partner32(l_run);
+  const float inv = 1.0f / lt;
+  const int qrow = q0 + wave * 32 + ql;
+  if (qrow < a.q_valid) {
+    bf16_t* orow = a.out + ((static_cast<int64_t>(b) * a.out_rows + a.out_row0 + qrow) * a.heads + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d0 = dt * 32 + 8 * rg + 4 * g;
+        const uint32_t w0 = pack_bf16x2(o[dt][4 * rg] * inv, o[dt][4 * rg + 1] * inv);
+        const uint32_t w1 = pack_bf16x2(o[dt][4 * rg + 2] * inv, o[dt][4 * rg + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + d0) = make_uint2(w0, w1);
+      }
+  }
+#undef UHLA_LOAD_TILE
+#undef UHLA_STORE_TILE
+}
+
+template <int D, int NWAVES>
+static void launch_attn(const AttnArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((attn_fwd_kernel<D, NWAVES>), dim3(a.total_blocks), dim3(NWAVES * 64), 0,
+                     s, a);
+}
+
+static void dispatch_attn(int D, int nwaves, const AttnArgs& a, hipStream_t s) {
+  if (D == 128) {
+    if (nwaves == 8) launch_attn<128, 8>(a, s);
+    else if (nwaves == 2) launch_attn<128, 2>(a, s);
+  } else {
+    if (nwaves == 8) launch_attn<64, 8>(a, s);
+    else if (nwaves == 2) launch_attn<64, 2>(a, s);
+  }
+}
+
+// ------------------------------------------------------------------ host side
+
+int timer_begin(uhla_timer* t, int stage, hipStream_t s);
+int timer_end(uhla_timer* t, int stage, hipStream_t s);
+int timer_commit(uhla_timer* t);
+
+static int validate_forward(const void* q, const void* k, const void* v, void* o, int B, int H,
+                            int W, int w, int H_lr, int W_lr, int rho, int heads, int D) {
+  if (!q || !k || !v || !o) return fail_arg("null pointer");
+  if (B < 1 || H < 1 || W < 1 || w < 1 || heads < 1 || D < 1 || H_lr < 0 || W_lr < 0)
+    return fail_arg("sizes out of range");
+  if (H % w || W % w) return fail_arg("w must divide H and W");
+  if ((H_lr == 0) != (W_lr == 0)) return fail_arg("H_lr and W_lr must both be zero or not");
+  if (static_cast<int64_t>(H_lr) * W_lr > 0 && rho < 1)
+    return fail_arg("rho must be >= 1 with guide tokens");
+  if (D != 64 && D != 128) return fail_unsupported("head_dim must be 64 or 128");
+  if (w % 8 || (w > 16 && w % 16)) return fail_unsupported("window size must be 8, 16 or a multiple of 16");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+       reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o)) % 16)
+    return fail_arg("tensors must be 16-byte aligned");
+  if (B > 65535) return fail_unsupported("batch too large");
+  const int64_t N = static_cast<int64_t>(H) * W, M = static_cast<int64_t>(H_lr) * W_lr;
+  const int64_t bh = static_cast<int64_t>(B) * heads;
+  // 32-bit row indices inside the kernels; 32-bit workgroup counts
+  if (N > (int64_t(1) << 30) || M > (int64_t(1) << 30) ||
+      bh * ((N > M ? N : M) / 64 + 1) > 0x7fffffff)
+    return fail_unsupported("problem too large");
+  return UHLA_OK;
+}
+
+static int forward_impl(const void* q, const void* k, const void* v, void* o, int B, int H, int W,
+                        int w, int H_lr, int W_lr, int rho, int heads, int D, float scale,
+                        float theta, void* workspace, size_t workspace_bytes, void* stream,
+                        uhla_timer* timer) {
+  int st = validate_forward(q, k, v, o, B, H, W, w, H_lr, W_lr, rho, heads, D);
+  if (st) return st;
+  const Geom g = make_geom(B, H, W, w, H_lr, W_lr, rho, heads, D);
+  const Workspace need = carve(g, nullptr);
+  if (!workspace || workspace_bytes < need.bytes)
+    return (set_detail("workspace too small"), UHLA_ERR_WORKSPACE);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail_arg("workspace must be 256-byte aligned");
+  const size_t tensor_bytes = static_cast<size_t>(B) * (g.N + g.M) * heads * D * 2;
+  if (ranges_overlap(o, tensor_bytes, q, tensor_bytes) ||
+      ranges_overlap(o, tensor_bytes, k, tensor_bytes) ||
+      ranges_overlap(o, tensor_bytes, v, tensor_bytes) ||
+      ranges_overlap(o, tensor_bytes, workspace, need.bytes))
+    return fail_arg("o overlaps an input or the workspace");
+  const Workspace ws = carve(g, workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool rope_on = theta > 0.0f;
+  const float sc = scale > 0.0f ? scale : 1.0f / sqrtf(static_cast<float>(D));
+  const int64_t L = g.N + g.M;
+  const int w2 = w * w;
+
+#define UHLA_STEP(call, name)          \
+  do {                                 \
+    call;                              \
+    st = check_launch(name);           \
+    if (st) return st;                 \
+  } while (0)
+
+  // 1. tables
+  if (timer) timer_begin(timer, UHLA_STAGE_TABLES, s);
+  UHLA_STEP(hipLaunchKernelGGL(neighbour_table_kernel, dim3((g.nW + 255) / 256), dim3(256), 0, s,
+                               g.n_wy, g.n_wx, ws.nbr, ws.nbr_cnt),
+            "neighbour_table_kernel");
+  if (rope_on) {
+    const int n = g.P * (D / 4);
+    UHLA_STEP(hipLaunchKernelGGL(cos_sin_table_kernel, dim3((n + 255) / 256), dim3(256), 0, s,
+                                 ws.cs, g.P, D, log2(static_cast<double>(theta))),
+              "cos_sin_table_kernel");
+  }
+  if (timer) timer_end(timer, UHLA_STAGE_TABLES, s);
+
+  // 2. prep: permutation + RoPE (Q, K) and permutation + tile transpose (V)
+  const bf16_t* qb = static_cast<const bf16_t*>(q);
+  const bf16_t* kb = static_cast<const bf16_t*>(k);
+  const bf16_t* vb = static_cast<const bf16_t*>(v);
+  if (timer) timer_begin(timer, UHLA_STAGE_PREP_HI, s);
+  {
+    const int64_t rows = g.N + g.Mq;
+    UHLA_STEP(hipLaunchKernelGGL(prep_qk_kernel, dim3(static_cast<unsigned>((rows + kPrepRows - 1) / kPrepRows), B),
+                                 dim3(kPrepThreads), 0, s, qb, kb, ws.q_hi, ws.k_hi, ws.q_lr, ws.k_lr,
+                                 ws.cs, g.P, rope_on ? log2(static_cast<double>(theta)) : 0.0,
+                                 g.N, g.M, g.Mq, g.Mk, W, w, g.n_wx, W_lr, rho, heads, D,
+                                 rope_on ? 1 : 0),
+              "prep_qk_kernel");
+    const int64_t tiles = g.N / kKeyTile + g.Mk / kKeyTile;
+    UHLA_STEP(hipLaunchKernelGGL(prep_v_kernel, dim3(static_cast<unsigned>(tiles), B), dim3(kPrepThreads), 0, s,
+                                 vb, ws.v_hi, ws.v_lr, g.N, g.M, g.Mk, W, w, g.n_wx, heads, D),
+              "prep_v_kernel");
+  }
+  if (timer) timer_end(timer, UHLA_STAGE_PREP_HI, s);
+  if (timer) timer_begin(timer, UHLA_STAGE_PREP_LR, s);  // guide rows are folded into step 2
+  if (timer) timer_end(timer, UHLA_STAGE_PREP_LR, s);
+
+  AttnArgs a{};
+  a.k_hi = ws.k_hi; a.v_hi = ws.v_hi; a.k_lr = ws.k_lr; a.v_lr = ws.v_lr;
+  a.nbr = ws.nbr; a.nbr_cnt = ws.nbr_cnt;
+  a.N = g.N; a.M = g.M; a.Mk = g.Mk; a.heads = heads; a.w2 = w2;
+  a.c = sc * 1.4426950408889634f;
+  a.rescale_thr = 8.0f / a.c;
+
+  // 3. hi pass
+  if (timer) timer_begin(timer, UHLA_STAGE_ATTN_HI, s);
+  {
+    const int nwaves = w2 >= kMaxQuery ? 8 : w2 / 32;
+    const int qt = nwaves * 32;
+    AttnArgs h = a;
+    h.q = ws.q_hi; h.q_rows = g.N;
+    h.out = ws.o_hi; h.out_rows = g.N; h.out_row0 = 0;
+    h.hi = 1; h.q_valid = static_cast<int>(g.N);
+    h.blocks_per_bh = static_cast<int>(g.N / qt);
+    h.total_blocks = static_cast<int>(static_cast<int64_t>(B) * heads * h.blocks_per_bh);
+    UHLA_STEP(dispatch_attn(D, nwaves, h, s), "attn_fwd_kernel(hi)");
+  }
+  if (timer) timer_end(timer, UHLA_STAGE_ATTN_HI, s);
+
+  // 4. guide pass
+  if (timer) timer_begin(timer, UHLA_STAGE_ATTN_LR, s);
+  if (g.M > 0) {
+    AttnArgs l = a;
+    l.q = ws.q_lr; l.q_rows = g.Mq;
+    l.out = static_cast<bf16_t*>(o); l.out_rows = L; l.out_row0 = g.N;
+    l.hi = 0; l.q_valid = static_cast<int>(g.M);
+    l.blocks_per_bh = static_cast<int>(g.Mq / kMaxQuery);
+    l.total_blocks = static_cast<int>(static_cast<int64_t>(B) * heads * l.blocks_per_bh);
+    UHLA_STEP(dispatch_attn(D, 8, l, s), "attn_fwd_kernel(guide)");
+  }
+  if (timer) timer_end(timer, UHLA_STAGE_ATTN_LR, s);
+
+  // 5. inverse permutation of the hi rows of O
+  if (timer) timer_begin(timer, UHLA_STAGE_UNPERMUTE, s);
+  st = launch_window_copy(ws.o_hi, o, B, H, W, w, static_cast<int64_t>(heads) * D * 2, g.N, L, 1, s);
+  if (st) return st;
+  if (timer) timer_end(timer, UHLA_STAGE_UNPERMUTE, s);
+#undef UHLA_STEP
+  if (timer) return timer_commit(timer);
+  return UHLA_OK;
+}
+
+}  // namespace uhla
+
+extern "C" size_t uhla_forward_workspace_bytes(int B, int H, int W, int w, int H_lr, int W_lr,
+                                               int heads, int head_dim) {
+  if (B < 1 || H < 1 || W < 1 || w < 1 || heads < 1 || H_lr < 0 || W_lr < 0) return 0;
+  if (H % w || W % w || (H_lr == 0) != (W_lr == 0)) return 0;
+  if (head_dim != 64 && head_dim != 128) return 0;
+  return uhla::carve(uhla::make_geom(B, H, W, w, H_lr, W_lr, 1, heads, head_dim), nullptr).bytes;
+}
+
+extern "C" int uhla_forward(const void* q, const void* k, const void* v, void* o, int B, int H,
+                            int W, int w, int H_lr, int W_lr, int rho, int heads, int head_dim,
+                            float scale, float theta, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  return uhla::forward_impl(q, k, v, o, B, H, W, w, H_lr, W_lr, rho, heads, head_dim, scale,
+                            theta, workspace, workspace_bytes, stream, nullptr);
+}
+
+extern "C" int uhla_forward_timed(const void* q, const void* k, const void* v, void* o, int B,
+                                  int H, int W, int w, int H_lr, int W_lr, int rho, int heads,
+                                  int head_dim, float scale, float theta, void* workspace,
+                                  size_t workspace_bytes, void* stream, uhla_timer* timer) {
+  if (!timer) return uhla::fail_arg("null timer");
+  return uhla::forward_impl(q, k, v, o, B, H, W, w, H_lr, W_lr, rho, heads, head_dim, scale,
+                            theta, workspace, workspace_bytes, stream, timer);
+}

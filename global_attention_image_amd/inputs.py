@@ -107,29 +107,54 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return bf16_bits_to_f32(bits).astype(np.float64)
 
 
-def draw_normal_f32(rng: np.random.Generator, shape, chunk: int = 1 << 24) -> np.ndarray:
-    """iid N(0, 1) float32 in C order, drawn in chunks (same stream as one draw)."""
+CHUNK = 1 << 22  # elements per independently seeded stream
+
+
+def _threads() -> int:
+    import os
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def normal_bf16_bits(shape, seed: int, tensor: int) -> np.ndarray:
+    """iid N(0, 1) float32 rounded to bfloat16 bits, C order, reproducible in parallel.
+
+    Element block c (CHUNK elements, C order) of tensor index ``tensor`` is drawn from
+    ``numpy.random.default_rng([seed, tensor, c]).standard_normal(..., dtype=float32)``,
+    so the values do not depend on the number of worker threads.
+    """
+    from concurrent.futures import ThreadPoolExecutor
+
     n = int(np.prod(shape))
-    out = np.empty(n, dtype=np.float32)
-    for s in range(0, n, chunk):
-        e = min(n, s + chunk)
-        out[s:e] = rng.standard_normal(e - s, dtype=np.float32)
+    out = np.empty(n, dtype=np.uint16)
+
+    def work(c):
+        s = c * CHUNK
+        e = min(n, s + CHUNK)
+        x = np.random.default_rng([seed, tensor, c]).standard_normal(e - s, dtype=np.float32)
+        out[s:e] = f32_to_bf16_bits(x)
+
+    nchunks = (n + CHUNK - 1) // CHUNK
+    if nchunks <= 1:
+        for c in range(nchunks):
+            work(c)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(work, range(nchunks)))
     return out.reshape(shape)
 
 
 def make_qkv_bits(geom: Geometry, seed: int):
     """Q, K, V as bfloat16 bit patterns, shape ``[B, L, heads, head_dim]``.
 
-    Recipe: ``numpy.random.default_rng(seed)``, iid N(0, 1) float32 drawn in C order in
-    the order Q, K, V, each rounded to bfloat16 (round to nearest even).
+    Recipe: iid N(0, 1) float32 in C order, tensor index 0, 1, 2 for Q, K, V, drawn per
+    block of CHUNK elements from ``default_rng([seed, tensor, block])`` and rounded to
+    bfloat16 (round to nearest even).
     """
-    rng = np.random.default_rng(seed)
-    out = []
-    for _ in range(3):
-        x = draw_normal_f32(rng, geom.shape())
-        out.append(f32_to_bf16_bits(x))
-        del x
-    return tuple(out)
+    return tuple(normal_bf16_bits(geom.shape(), seed, t) for t in range(3))
 
 
 def make_config_inputs(name: str):

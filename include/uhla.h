@@ -1,0 +1,167 @@
+/*
+ * uhla.h -- C ABI of the MI355X (gfx950) hierarchical local attention library.
+ *
+ * The method is UltraGen's hierarchical local attention.  Citation keys:
+ * [UltraGen/<lang> §n] is the gist.science summary page "UltraGen: Efficient
+ * Ultra-High-Resolution Image Generation with Hierarchical Local Attention" in the
+ * named language edition (it, fr, es, ar, ko), section n of its technical summary.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Token-major layout [B, L, heads, head_dim], contiguous, L = N + M.  Rows 0..N-1 are
+ *   the hi-res tokens of an H x W grid in raster order (row y = index / W); rows N..L-1
+ *   are the low-res guide tokens of an H_lr x W_lr grid in raster order.  This is the
+ *   joint [hi | guide] part of the text | image | guide sequence of [UltraGen/it §2].
+ * - Device pointers are HIP device memory owned by the caller.  The library never
+ *   allocates, frees or synchronises (except uhla_timer_read), keeps no global mutable
+ *   state and may be called from several host threads on different streams.
+ * - `stream` is a hipStream_t (NULL = the legacy default stream).  All work is enqueued
+ *   asynchronously on it.
+ * - Every function returns a uhla_status; nothing throws across the ABI.  Argument
+ *   errors are detected on the host before anything is enqueued.  UHLA_ERR_HIP means a
+ *   HIP call failed; uhla_last_error_detail() then returns the HIP message for the
+ *   calling thread.
+ * - bf16 is IEEE bfloat16 stored as 16-bit words; rounding to bf16 is round to nearest
+ *   even.
+ */
+#ifndef UHLA_H_
+#define UHLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  UHLA_OK = 0,
+  UHLA_ERR_ARG = 1,          /* invalid argument (null pointer, bad size, aliasing) */
+  UHLA_ERR_UNSUPPORTED = 2,  /* valid but not built: head_dim, elem_bytes, window size */
+  UHLA_ERR_WORKSPACE = 3,    /* workspace pointer null or smaller than required */
+  UHLA_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
+} uhla_status;
+
+/*
+ * Window-first permutation of the hi-res segment, and its exact inverse.
+ *
+ * Defined in [UltraGen/it §2], [UltraGen/fr §2.A] and [UltraGen/ar §2.A]: hi-res
+ * tokens are split into fixed, non-overlapping w x w windows and reordered window by
+ * window, so that each attention block is one spatial window.  Windows are enumerated
+ * row-major over the (H/w) x (W/w) window grid; tokens are raster inside a window:
+ *   p = win * w*w + iy * w + ix,  win = wy * (W/w) + wx,
+ *   r(p) = (wy*w + iy) * W + (wx*w + ix).
+ * uhla_window_permute:   dst[b, p] = src[b, r(p)]   for p in 0..H*W-1
+ * uhla_window_unpermute: dst[b, r(p)] = src[b, p]
+ * A "row" is heads * head_dim elements of elem_bytes bytes (2 = bf16/fp16, 4 = fp32);
+ * rows are copied bit-exactly.  Batch b of src starts at row b * src_tokens_per_batch,
+ * of dst at row b * dst_tokens_per_batch (both >= H*W), so the hi segment of a
+ * [B, N + M, heads, head_dim] tensor can be permuted in place of a copy; rows at and
+ * beyond H*W in each batch are neither read nor written.  src and dst must not overlap.
+ * Errors: UHLA_ERR_ARG for null pointers, B/H/W/w/heads/head_dim < 1, w not dividing
+ * H or W, a batch stride < H*W, overlapping src/dst; UHLA_ERR_UNSUPPORTED for
+ * elem_bytes not in {2, 4}.
+ */
+int uhla_window_permute(const void* src, void* dst, int B, int H, int W, int w,
+                        int heads, int head_dim, int elem_bytes,
+                        int64_t src_tokens_per_batch, int64_t dst_tokens_per_batch,
+                        void* stream);
+int uhla_window_unpermute(const void* src, void* dst, int B, int H, int W, int w,
+                          int heads, int head_dim, int elem_bytes,
+                          int64_t src_tokens_per_batch, int64_t dst_tokens_per_batch,
+                          void* stream);
+
+/*
+ * 2D axial RoPE on a bf16 [B, L, heads, head_dim] tensor (src may equal dst; partial
+ * overlap is an error).
+ *
+ * Positions: guide-token indices are scaled by rho onto the hi-res grid
+ * ([UltraGen/ar §2.B]): guide raster token s sits at (rho * (s / W_lr), rho * (s % W_lr)).
+ * Hi-res row i sits at (r / W, r % W) with r = i (hi_order = 0, raster) or r = r(i)
+ * of the window-first map above (hi_order = 1).
+ * Rotation: d_axis = head_dim / 2; dims [0, d_axis) rotate by y, dims [d_axis, head_dim)
+ * by x; inside an axis block the pair (2k, 2k+1) = (a, b) becomes
+ * (a cos phi - b sin phi, a sin phi + b cos phi), phi = pos * theta^(-2k / d_axis).
+ * cos/sin are evaluated in fp64 and rounded to fp32; the rotation runs in fp32 and the
+ * result is rounded to bf16.  theta <= 0 copies src to dst unchanged.
+ * Errors: UHLA_ERR_ARG (null pointers, sizes < 1, w not dividing H or W when
+ * hi_order = 1, exactly one of H_lr/W_lr zero, rho < 1 with guide tokens, hi_order not
+ * 0/1, partial overlap); UHLA_ERR_UNSUPPORTED when head_dim % 8 != 0.
+ */
+int uhla_rope_apply(const void* src, void* dst, int B, int H, int W, int w, int hi_order,
+                    int H_lr, int W_lr, int rho, int heads, int head_dim, float theta,
+                    void* stream);
+
+/*
+ * Workspace bytes uhla_forward needs for this geometry (0 on invalid geometry).
+ */
+size_t uhla_forward_workspace_bytes(int B, int H, int W, int w, int H_lr, int W_lr,
+                                    int heads, int head_dim);
+
+/*
+ * Hierarchical local attention forward.
+ *
+ * Q, K, V, O: bf16 [B, N + M, heads, head_dim] in the layout above.  The result is
+ *   O = softmax(rope(Q) rope(K)^T * scale + mask) V   per (batch, head),
+ * with the mask of [UltraGen/ar §2.B] and [UltraGen/es §2]: a hi-res token attends to
+ * every token of its own window and of the clipped 3x3 neighbourhood of windows, and to
+ * all M guide tokens; a guide token attends to all guide tokens and to no hi-res token.
+ * Steps: block-neighbour table; window-first permutation of the hi segment of Q, K, V
+ * fused with RoPE (guide rows rotated in place of permuting); block-sparse attention of
+ * each window over its neighbour windows and the guide tokens (bf16 MFMA, fp32
+ * accumulation and softmax); guide-only attention; inverse permutation of the output.
+ * scale <= 0 selects 1/sqrt(head_dim); theta <= 0 switches RoPE off; H_lr = W_lr = 0
+ * means no guide tokens.  Deterministic: no atomics, fixed reduction order.
+ * workspace: device memory of at least uhla_forward_workspace_bytes(...) bytes, 256-byte
+ *   aligned, owned by the caller; its contents are scratch.
+ * Errors: UHLA_ERR_ARG (null pointers, sizes < 1, w not dividing H or W, rho < 1 with
+ * guide tokens, exactly one of H_lr/W_lr zero, O overlapping Q, K, V or the workspace);
+ * UHLA_ERR_UNSUPPORTED (head_dim not in {64, 128}; w not a multiple of 8, or w > 16
+ * and not a multiple of 16); UHLA_ERR_WORKSPACE; UHLA_ERR_HIP.
+ */
+int uhla_forward(const void* q, const void* k, const void* v, void* o,
+                 int B, int H, int W, int w, int H_lr, int W_lr, int rho,
+                 int heads, int head_dim, float scale, float theta,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* uhla_strerror(int status);
+
+/* Detail of the last UHLA_ERR_HIP / argument error on the calling thread ("" if none). */
+const char* uhla_last_error_detail(void);
+
+/*
+ * Stage timing with HIP events (measurement only).
+ *
+ * uhla_forward_timed runs exactly uhla_forward and records a start/stop event pair on
+ * `stream` around each stage; a timer holds pairs for up to max_calls calls.
+ * uhla_timer_read waits for the recorded events and writes, for each stage s <
+ * n_stages, the summed milliseconds over the recorded calls into stage_ms[s], and the
+ * number of recorded calls into *calls.  Stages are enumerated by uhla_stage.
+ * uhla_timer_reset forgets recorded calls.  A call beyond max_calls is not timed.
+ */
+typedef enum {
+  UHLA_STAGE_TABLES = 0,    /* neighbour table + cos/sin table */
+  UHLA_STAGE_PREP_HI = 1,   /* window-first permutation of Q, K, V fused with RoPE */
+  UHLA_STAGE_PREP_LR = 2,   /* guide-token RoPE / V re-layout */
+  UHLA_STAGE_ATTN_HI = 3,   /* hi-res block-sparse attention */
+  UHLA_STAGE_ATTN_LR = 4,   /* guide-only attention */
+  UHLA_STAGE_UNPERMUTE = 5, /* inverse permutation of O */
+  UHLA_NUM_STAGES = 6
+} uhla_stage;
+
+typedef struct uhla_timer uhla_timer;
+int uhla_timer_create(int max_calls, uhla_timer** out);
+int uhla_timer_destroy(uhla_timer* timer);
+int uhla_timer_reset(uhla_timer* timer);
+int uhla_timer_read(uhla_timer* timer, double* stage_ms, int n_stages, int* calls);
+int uhla_forward_timed(const void* q, const void* k, const void* v, void* o,
+                       int B, int H, int W, int w, int H_lr, int W_lr, int rho,
+                       int heads, int head_dim, float scale, float theta,
+                       void* workspace, size_t workspace_bytes, void* stream,
+                       uhla_timer* timer);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* UHLA_H_ */

@@ -1,0 +1,175 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared symbol, and
+rejects bad arguments before anything reaches a GPU.  No compute call is made here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from global_attention_image_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "uhla.h")
+
+# Fake, 256-byte aligned device addresses: every call below must fail validation on the
+# host before these are ever dereferenced or handed to HIP.
+P = ctypes.c_void_p(0x10000000)
+P2 = ctypes.c_void_p(0x20000000)
+P3 = ctypes.c_void_p(0x30000000)
+P4 = ctypes.c_void_p(0x40000000)
+NULL = ctypes.c_void_p(0)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(uhla_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return api.load()
+
+
+def test_header_declares_the_contract_entry_points():
+    names = declared_functions()
+    for n in ("uhla_window_permute", "uhla_window_unpermute", "uhla_rope_apply", "uhla_forward",
+              "uhla_forward_workspace_bytes", "uhla_strerror"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert names
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (uhla_\w+)$", out, flags=re.M))
+    assert set(names) <= exported
+    # the binding covers the same set
+    assert set(api.EXPORTS) == set(names)
+
+
+def test_strerror(lib):
+    assert lib.uhla_strerror(0) == b"UHLA_OK"
+    for s in (1, 2, 3, 4):
+        assert lib.uhla_strerror(s).startswith(b"UHLA_ERR_")
+    assert lib.uhla_strerror(99) == b"unknown uhla status"
+
+
+def permute_args(**kw):
+    a = dict(src=P, dst=P2, B=1, H=32, W=32, w=8, heads=2, d=64, e=2, stpb=1024, dtpb=1024)
+    a.update(kw)
+    return (a["src"], a["dst"], a["B"], a["H"], a["W"], a["w"], a["heads"], a["d"], a["e"],
+            a["stpb"], a["dtpb"], NULL)
+
+
+@pytest.mark.parametrize("fn", ["uhla_window_permute", "uhla_window_unpermute"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(src=NULL), api.UHLA_ERR_ARG),
+    (dict(dst=NULL), api.UHLA_ERR_ARG),
+    (dict(B=0), api.UHLA_ERR_ARG),
+    (dict(w=0), api.UHLA_ERR_ARG),
+    (dict(w=5), api.UHLA_ERR_ARG),
+    (dict(H=30), api.UHLA_ERR_ARG),
+    (dict(heads=0), api.UHLA_ERR_ARG),
+    (dict(stpb=1000), api.UHLA_ERR_ARG),
+    (dict(dtpb=10), api.UHLA_ERR_ARG),
+    (dict(e=8), api.UHLA_ERR_UNSUPPORTED),
+    (dict(e=1), api.UHLA_ERR_UNSUPPORTED),
+    (dict(dst=ctypes.c_void_p(0x10000000 + 4096)), api.UHLA_ERR_ARG),  # overlap
+    (dict(src=ctypes.c_void_p(0x10000001)), api.UHLA_ERR_ARG),  # misaligned
+])
+def test_permute_rejects(lib, fn, kw, status):
+    assert getattr(lib, fn)(*permute_args(**kw)) == status
+    assert lib.uhla_last_error_detail() != b""
+
+
+def rope_args(**kw):
+    a = dict(src=P, dst=P2, B=1, H=32, W=32, w=8, order=0, H_lr=8, W_lr=8, rho=4, heads=2, d=64,
+             theta=10000.0)
+    a.update(kw)
+    return (a["src"], a["dst"], a["B"], a["H"], a["W"], a["w"], a["order"], a["H_lr"],
+            a["W_lr"], a["rho"], a["heads"], a["d"], a["theta"], NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(src=NULL), api.UHLA_ERR_ARG),
+    (dict(B=0), api.UHLA_ERR_ARG),
+    (dict(order=2), api.UHLA_ERR_ARG),
+    (dict(order=1, w=5), api.UHLA_ERR_ARG),
+    (dict(H_lr=0), api.UHLA_ERR_ARG),
+    (dict(rho=0), api.UHLA_ERR_ARG),
+    (dict(d=60), api.UHLA_ERR_UNSUPPORTED),
+    (dict(dst=ctypes.c_void_p(0x10000000 + 64)), api.UHLA_ERR_ARG),  # partial overlap
+    (dict(src=ctypes.c_void_p(0x10000008)), api.UHLA_ERR_ARG),  # misaligned
+])
+def test_rope_rejects(lib, kw, status):
+    assert lib.uhla_rope_apply(*rope_args(**kw)) == status
+
+
+def fwd_args(**kw):
+    a = dict(q=P, k=P2, v=P3, o=P4, B=1, H=32, W=32, w=8, H_lr=8, W_lr=8, rho=4, heads=2, d=64,
+             scale=0.0, theta=10000.0, ws=ctypes.c_void_p(0x50000000), wsb=1 << 40)
+    a.update(kw)
+    return (a["q"], a["k"], a["v"], a["o"], a["B"], a["H"], a["W"], a["w"], a["H_lr"],
+            a["W_lr"], a["rho"], a["heads"], a["d"], a["scale"], a["theta"], a["ws"], a["wsb"],
+            NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=NULL), api.UHLA_ERR_ARG),
+    (dict(o=NULL), api.UHLA_ERR_ARG),
+    (dict(B=0), api.UHLA_ERR_ARG),
+    (dict(heads=0), api.UHLA_ERR_ARG),
+    (dict(w=12), api.UHLA_ERR_ARG),
+    (dict(W_lr=0), api.UHLA_ERR_ARG),
+    (dict(rho=0), api.UHLA_ERR_ARG),
+    (dict(d=96), api.UHLA_ERR_UNSUPPORTED),
+    (dict(d=32), api.UHLA_ERR_UNSUPPORTED),
+    (dict(H=24, W=24, w=24), api.UHLA_ERR_UNSUPPORTED),
+    (dict(H=36, W=36, w=4), api.UHLA_ERR_UNSUPPORTED),
+    (dict(ws=NULL), api.UHLA_ERR_WORKSPACE),
+    (dict(wsb=1000), api.UHLA_ERR_WORKSPACE),
+    (dict(o=P), api.UHLA_ERR_ARG),  # aliases q
+    (dict(o=ctypes.c_void_p(0x30000000 + 4096)), api.UHLA_ERR_ARG),  # overlaps v
+    (dict(ws=ctypes.c_void_p(0x50000010)), api.UHLA_ERR_ARG),  # misaligned workspace
+])
+def test_forward_rejects(lib, kw, status):
+    assert lib.uhla_forward(*fwd_args(**kw)) == status
+
+
+def test_forward_timed_rejects_null_timer(lib):
+    assert lib.uhla_forward_timed(*fwd_args(), NULL) == api.UHLA_ERR_ARG
+
+
+def test_timer_create_rejects_bad_count(lib):
+    h = ctypes.c_void_p()
+    assert lib.uhla_timer_create(0, ctypes.byref(h)) == api.UHLA_ERR_ARG
+
+
+def expected_workspace(B, H, W, w, H_lr, W_lr, heads, d):
+    """Independent restatement of the workspace layout (regions 256-byte aligned)."""
+    al = lambda x: (x + 255) // 256 * 256
+    N, M = H * W, H_lr * W_lr
+    Mk, Mq = (M + 63) // 64 * 64, (M + 255) // 256 * 256
+    nW = (H // w) * (W // w)
+    e, bh = 2, B * heads
+    parts = [4 * nW * 9, 4 * nW, 16 * max(H, W) * (d // 4), bh * N * d * e, bh * N * d * e,
+             bh * N * d * e, bh * Mq * d * e, bh * Mk * d * e, bh * Mk * d * e, bh * N * d * e]
+    return sum(al(p) for p in parts)
+
+
+@pytest.mark.parametrize("g", [(1, 32, 32, 8, 8, 8, 2, 64), (1, 128, 128, 16, 32, 32, 24, 128),
+                               (2, 256, 128, 16, 64, 32, 24, 128), (1, 512, 512, 16, 128, 128, 24, 128),
+                               (1, 48, 16, 16, 5, 3, 3, 128), (1, 16, 16, 16, 0, 0, 1, 64)])
+def test_workspace_bytes(lib, g):
+    assert lib.uhla_forward_workspace_bytes(*g) == expected_workspace(*g)
+
+
+def test_workspace_bytes_invalid(lib):
+    assert lib.uhla_forward_workspace_bytes(1, 30, 32, 8, 8, 8, 2, 64) == 0
+    assert lib.uhla_forward_workspace_bytes(1, 32, 32, 8, 8, 0, 2, 64) == 0
+    assert lib.uhla_forward_workspace_bytes(1, 32, 32, 8, 8, 8, 2, 96) == 0
