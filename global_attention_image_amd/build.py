@@ -26,7 +26,7 @@ def hipcc() -> str:
 
 def flags() -> list:
     return [
-        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-shared",
         "-Wall", "-Wno-unused-function",
         # packed fp32 VALU ops stay disabled for all device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -324,7 +324,45 @@ __device__ __forceinline__ int k_swizzle(int row) {
 }
 __device__ __forceinline__ int v_swizzle(int row) { return (row >> 1) & 7; }
 
-template <int D, int NWAVES>
+constexpr int kStages = 4;  // LDS ring: tiles t, t+1 are read while t+2, t+3 land
+
+// 32-bit LDS address of a __shared__ object
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (const __attribute__((address_space(3))) char*)(p)));
+}
+
+// Asynchronous 16-byte global -> LDS copy per lane (global_load_lds_dwordx4): lane l
+// reads gbase + voff and writes LDS bytes [lds + 16 l, lds + 16 l + 16).  gbase and lds
+// are wave-uniform.  The instruction has no register results (data goes to LDS), and it
+// is issued from asm so that the compiler does not treat every later LDS read as
+// possibly overlapping it (it cannot tell the ring stages apart and would wait for all
+// in-flight tiles); completion is awaited explicitly by wait_vm_and_barrier.  M0 is
+// written by the compiler just before the block, hence the wait state.
+__device__ __forceinline__ void dma_16b(const char* gbase, int voff, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "{m0}"(lds)
+               : "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding, then
+// barrier.  The direct-to-LDS tile loads are vector-memory operations, so this makes the
+// older tiles visible to the whole workgroup while the newest ones stay in flight.  The
+// "memory" clobber keeps the compiler from moving LDS accesses across the barrier.
+template <int N>
+__device__ __forceinline__ void wait_vm_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// One workgroup = NWAVES waves x 32 queries.  Waves [0, NWAVES/2) ("A") process tile t as
+// QK^T_t -> softmax_t -> PV_t; waves [NWAVES/2, NWAVES) ("B") as softmax_t -> PV_t ->
+// QK^T_{t+1}, carrying S across the barrier.  Waves w and w + NWAVES/2 share a SIMD, so
+// while one runs MFMAs the other can run its softmax on the VALU.
+//
+// K/V tiles are copied global -> LDS by the DMA path of global_load_lds_dwordx4 (lane l of
+// a load writes LDS bytes [16 l, 16 l + 16) above the wave's base), three tiles ahead of
+// their first use.  Each lane picks the global 16-byte chunk that belongs at its LDS slot
+// under the XOR swizzle, so the LDS layout is the one the fragment reads expect.
+template <int D, int NWAVES, bool HI>
 __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   constexpr int NT = NWAVES * 64;
   constexpr int TILE_BYTES = kKeyTile * D * 2;       // one K or V tile
@@ -332,67 +370,76 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   constexpr int CPT = CHUNKS / NT;                     // 16-byte chunks per thread
   static_assert(CHUNKS % NT == 0, "tile must split evenly");
   constexpr int KCH = D / 8;                           // 16-byte chunks per K row
-  __shared__ __attribute__((aligned(16))) char smem[2][2][TILE_BYTES];
+  constexpr int LOADS_PER_TILE = 2 * CPT;              // DMA instructions per thread per tile
+  // Four separate stage buffers (K tile then V tile), always addressed with a static
+  // stage index: the compiler can then tell the stage being read from the stage the
+  // DMA is writing, and does not wait for in-flight tile loads before LDS reads.
+  __shared__ __attribute__((aligned(16))) char stage0[2 * TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char stage1[2 * TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char stage2[2 * TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char stage3[2 * TILE_BYTES];
+  __shared__ int nbr_s[9];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ql = lane & 31, g = lane >> 5;
+  const bool wave_b = wave >= NWAVES / 2;
   const int blk = xcd_remap(blockIdx.x, a.total_blocks);
   const int bh = blk / a.blocks_per_bh, qb = blk - bh * a.blocks_per_bh;
   const int b = bh / a.heads, h = bh - b * a.heads;
-  const int qt = NWAVES * 32;
-  const int q0 = qb * qt;
+  const int q0 = qb * (NWAVES * 32);
 
-  // Tile list: hi pass = neighbour windows (w2/64 tiles each), then guide tiles.
+  // Tile list: hi pass = neighbour windows (w2/64 tiles each), then guide tiles.  The
+  // window's neighbour list is staged in LDS once.
   int n_local = 0, win = 0;
   const int tiles_per_win = a.w2 / kKeyTile;
-  if (a.hi) {
+  if (HI) {
     win = q0 / a.w2;
     n_local = a.nbr_cnt[win] * tiles_per_win;
+    if (tid < 9) nbr_s[tid] = a.nbr[win * 9 + tid];
+    __syncthreads();
   }
-  const int n_lr = static_cast<int>(a.Mk / kKeyTile);
-  const int n_tiles = n_local + n_lr;
+  const int n_tiles = n_local + static_cast<int>(a.Mk / kKeyTile);
 
-  u32x4 kreg[CPT], vreg[CPT];
-
-// Global -> registers for tile t (neighbour-window tiles first, then guide tiles).
-#define UHLA_LOAD_TILE(t, valid_out)                                                          \
-  do {                                                                                      \
-    const u32x4* kp_;                                                                       \
-    const u32x4* vp_;                                                                       \
-    if ((t) < n_local) {                                                                    \
-      const int j_ = (t) / tiles_per_win, sub_ = (t) - j_ * tiles_per_win;                  \
-      const int64_t krow_ = static_cast<int64_t>(a.nbr[win * 9 + j_]) * a.w2 + sub_ * kKeyTile; \
-      kp_ = reinterpret_cast<const u32x4*>(a.k_hi + (bh * a.N + krow_) * D);                \
-      vp_ = reinterpret_cast<const u32x4*>(a.v_hi + (bh * (a.N / kKeyTile) + krow_ / kKeyTile) * \
-                                                        static_cast<int64_t>(D) * kKeyTile); \
-      valid_out = kKeyTile;                                                                 \
-    } else {                                                                                \
-      const int j_ = (t) - n_local;                                                         \
-      kp_ = reinterpret_cast<const u32x4*>(a.k_lr + (bh * a.Mk + static_cast<int64_t>(j_) * kKeyTile) * D); \
-      vp_ = reinterpret_cast<const u32x4*>(a.v_lr + (bh * (a.Mk / kKeyTile) + j_) *         \
-                                                        static_cast<int64_t>(D) * kKeyTile); \
-      const int64_t rem_ = a.M - static_cast<int64_t>(j_) * kKeyTile;                       \
-      valid_out = rem_ < kKeyTile ? static_cast<int>(rem_) : kKeyTile;                      \
-    }                                                                                       \
-    _Pragma("unroll") for (int i_ = 0; i_ < CPT; ++i_) {                                    \
-      kreg[i_] = kp_[tid + i_ * NT];                                                        \
-      vreg[i_] = vp_[tid + i_ * NT];                                                        \
-    }                                                                                       \
-  } while (0)
-
-// Registers -> LDS buffer `buf` (swizzled).
-#define UHLA_STORE_TILE(buf)                                                                \
-  do {                                                                                      \
-    char* kb_ = smem[buf][0];                                                               \
-    char* vb_ = smem[buf][1];                                                               \
-    _Pragma("unroll") for (int i_ = 0; i_ < CPT; ++i_) {                                    \
-      const int c_ = tid + i_ * NT;                                                         \
-      const int kr_ = c_ / KCH, kc_ = c_ - kr_ * KCH;                                       \
-      *reinterpret_cast<u32x4*>(kb_ + kr_ * (D * 2) + ((kc_ ^ k_swizzle<D>(kr_)) << 4)) = kreg[i_]; \
-      const int vr_ = c_ >> 3, vc_ = c_ & 7;                                                \
-      *reinterpret_cast<u32x4*>(vb_ + vr_ * (kKeyTile * 2) + ((vc_ ^ v_swizzle(vr_)) << 4)) = vreg[i_]; \
-    }                                                                                       \
-  } while (0)
+  // Per-lane source offsets (bytes inside a tile) for this thread's DMA slots.
+  int k_src[CPT], v_src[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int slot = (i * NWAVES + wave) * 64 + lane;  // 16-byte LDS slot in the tile
+    const int kr = slot / KCH, kp = slot - kr * KCH;
+    k_src[i] = kr * (D * 2) + ((kp ^ k_swizzle<D>(kr)) << 4);
+    const int vr = slot >> 3, vp = slot & 7;
+    v_src[i] = vr * (kKeyTile * 2) + ((vp ^ v_swizzle(vr)) << 4);
+  }
+  // global -> LDS stage buffer `dst` for tile t (asynchronous)
+  auto issue_tile = [&](int t, char* dst) {
+    const char* kp;
+    const char* vp;
+    if (HI && t < n_local) {
+      const int j = t / tiles_per_win, sub = t - j * tiles_per_win;
+      const int nw = __builtin_amdgcn_readfirstlane(nbr_s[j]);
+      const int64_t krow = static_cast<int64_t>(nw) * a.w2 + sub * kKeyTile;
+      kp = reinterpret_cast<const char*>(a.k_hi + (bh * a.N + krow) * D);
+      vp = reinterpret_cast<const char*>(a.v_hi + (bh * (a.N / kKeyTile) + krow / kKeyTile) *
+                                                      static_cast<int64_t>(D) * kKeyTile);
+    } else {
+      const int j = t - n_local;
+      kp = reinterpret_cast<const char*>(a.k_lr + (bh * a.Mk + static_cast<int64_t>(j) * kKeyTile) * D);
+      vp = reinterpret_cast<const char*>(a.v_lr + (bh * (a.Mk / kKeyTile) + j) *
+                                                      static_cast<int64_t>(D) * kKeyTile);
+    }
+    const uint32_t lds = lds_addr(dst);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const uint32_t base = __builtin_amdgcn_readfirstlane(lds + (i * NWAVES + wave) * 64 * 16);
+      dma_16b(kp, k_src[i], base);
+      dma_16b(vp, v_src[i], base + TILE_BYTES);
+    }
+  };
+  auto tile_valid = [&](int t) -> int {
+    if (HI && t < n_local) return kKeyTile;
+    const int64_t rem = a.M - static_cast<int64_t>(t - n_local) * kKeyTile;
+    return rem < kKeyTile ? static_cast<int>(rem) : kKeyTile;
+  };
 
   // Query fragment (B operand of S^T = K Q^T): lane holds query ql, dims 16kk + 8g .. +8.
   bf16x8 qf[D / 16];
@@ -402,6 +449,10 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
     for (int kk = 0; kk < D / 16; ++kk)
       qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + 16 * kk + 8 * g);
   }
+  // Let the Q loads complete here, in a wait the compiler sees: it cannot see the
+  // tile DMA below, and would otherwise wait for "the Q loads" inside the loop by
+  // counting vector-memory operations, which would drain the in-flight tiles.
+  __builtin_amdgcn_s_waitcnt(0);
 
   f32x16 o[D / 32];
 #pragma unroll
@@ -410,19 +461,9 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
   const float c = a.c;
+  f32x16 s0, s1;  // S^T of the current tile: lane = query ql; keys 8(r/4) + 4g + r%4 (+32)
 
-  int valid_cur = kKeyTile, valid_next = kKeyTile;
-  UHLA_LOAD_TILE(0, valid_cur);
-  UHLA_STORE_TILE(0);
-  __syncthreads();
-
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < n_tiles) UHLA_LOAD_TILE(t + 1, valid_next);
-
-    // ---- S^T = K Q^T for 64 keys: two 32-key halves
-    const char* kb = smem[buf][0];
-    f32x16 s0, s1;
+  auto qk = [&](const char* kb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) { s0[r] = 0.0f; s1[r] = 0.0f; }
 #pragma unroll
@@ -433,17 +474,19 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[kk], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[kk], s1, 0, 0, 0);
     }
-    // lane holds keys 8*(r/4) + 4g + r%4 (s0) and 32 + that (s1)
-    if (valid_cur < kKeyTile) {
+  };
+
+  // online softmax (base 2) of the current S; lazy rescale of O only when a row max
+  // grows by more than 2^8.  Produces P^T as four bf16 B operands (16 keys each).
+  auto softmax = [&](int valid, bf16x8 (&pf)[4]) {
+    if (valid < kKeyTile) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = 8 * (r >> 2) + 4 * g + (r & 3);
-        if (key >= valid_cur) s0[r] = -INFINITY;
-        if (key + 32 >= valid_cur) s1[r] = -INFINITY;
+        if (key >= valid) s0[r] = -INFINITY;
+        if (key + 32 >= valid) s1[r] = -INFINITY;
       }
     }
-
-    // ---- online softmax (base 2), lazy rescale of the running output
     float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
@@ -460,7 +503,6 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
     }
     const float mc = m_run * c;
     float psum = 0.0f;
-    bf16x8 pf[4];
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
       const float p0 = __builtin_amdgcn_exp2f(fmaf(s0[r], c, -mc));
@@ -475,9 +517,10 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
       pf[2 + (r >> 3)][(r & 7) + 1] = static_cast<__bf16>(p3);
     }
     l_run += psum;
+  };
 
-    // ---- O^T += V^T P^T over 4 key-steps of 16 keys
-    const char* vb = smem[buf][1];
+  // O^T += V^T P^T over 4 key-steps of 16 keys
+  auto pv = [&](const char* vb, const bf16x8 (&pf)[4]) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int ch = 2 * ks + g;
@@ -488,11 +531,54 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[dt], 0, 0, 0);
       }
     }
+  };
 
-    if (t + 1 < n_tiles) UHLA_STORE_TILE(buf ^ 1);
-    valid_cur = valid_next;
-    __syncthreads();
+  auto stage = [&](int i) -> char* {
+    return i == 0 ? stage0 : i == 1 ? stage1 : i == 2 ? stage2 : stage3;
+  };
+
+  // prologue: tiles 0, 1, 2 in flight; 0 and 1 must land before the first iteration
+  issue_tile(0, stage0);
+  if (n_tiles > 1) issue_tile(1, stage1);
+  if (n_tiles > 2) {
+    issue_tile(2, stage2);
+    wait_vm_and_barrier<LOADS_PER_TILE>();
+  } else {
+    wait_vm_and_barrier<0>();
   }
+  if (wave_b) qk(stage0);
+
+  // Tile t lives in stage t % 4; S is the (compile-time) stage of tile t.
+  auto step = [&]<int S>(int t) {
+    char* cur = stage(S);
+    char* nxt = stage((S + 1) & 3);
+    // stage (t+3) % 4 held tile t-1, whose last reads ended at the previous barrier
+    const bool more3 = t + 3 < n_tiles;
+    if (more3) issue_tile(t + 3, stage((S + 3) & 3));
+    bf16x8 pf[4];
+    if (!wave_b) {
+      qk(cur);
+      softmax(tile_valid(t), pf);
+      pv(cur + TILE_BYTES, pf);
+    } else {
+      softmax(tile_valid(t), pf);
+      pv(cur + TILE_BYTES, pf);
+      if (t + 1 < n_tiles) qk(nxt);
+    }
+    // tile t+2 must have landed before the next iteration reads it
+    if (more3) wait_vm_and_barrier<LOADS_PER_TILE>();
+    else wait_vm_and_barrier<0>();
+  };
+  int t = 0;
+  for (; t + 4 <= n_tiles; t += 4) {
+    step.template operator()<0>(t);
+    step.template operator()<1>(t + 1);
+    step.template operator()<2>(t + 2);
+    step.template operator()<3>(t + 3);
+  }
+  if (t < n_tiles) step.template operator()<0>(t);
+  if (t + 1 < n_tiles) step.template operator()<1>(t + 1);
+  if (t + 2 < n_tiles) step.template operator()<2>(t + 2);
 
   // ---- epilogue: normalise and store (lane: query ql, dims dt*32 + 8*(r/4) + 4g + r%4)
   const float lt = sum_with_partner32(l_run);
@@ -510,23 +596,21 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
         *reinterpret_cast<uint2*>(orow + d0) = make_uint2(w0, w1);
       }
   }
-#undef UHLA_LOAD_TILE
-#undef UHLA_STORE_TILE
 }
 
-template <int D, int NWAVES>
+template <int D, int NWAVES, bool HI>
 static void launch_attn(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, NWAVES>), dim3(a.total_blocks), dim3(NWAVES * 64), 0,
+  hipLaunchKernelGGL((attn_fwd_kernel<D, NWAVES, HI>), dim3(a.total_blocks), dim3(NWAVES * 64), 0,
                      s, a);
 }
 
-static void dispatch_attn(int D, int nwaves, const AttnArgs& a, hipStream_t s) {
+static void dispatch_attn(int D, int nwaves, bool hi, const AttnArgs& a, hipStream_t s) {
   if (D == 128) {
-    if (nwaves == 8) launch_attn<128, 8>(a, s);
-    else if (nwaves == 2) launch_attn<128, 2>(a, s);
+    if (nwaves == 8) hi ? launch_attn<128, 8, true>(a, s) : launch_attn<128, 8, false>(a, s);
+    else launch_attn<128, 2, true>(a, s);
   } else {
-    if (nwaves == 8) launch_attn<64, 8>(a, s);
-    else if (nwaves == 2) launch_attn<64, 2>(a, s);
+    if (nwaves == 8) hi ? launch_attn<64, 8, true>(a, s) : launch_attn<64, 8, false>(a, s);
+    else launch_attn<64, 2, true>(a, s);
   }
 }
 
@@ -644,7 +728,7 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
     h.hi = 1; h.q_valid = static_cast<int>(g.N);
     h.blocks_per_bh = static_cast<int>(g.N / qt);
     h.total_blocks = static_cast<int>(static_cast<int64_t>(B) * heads * h.blocks_per_bh);
-    UHLA_STEP(dispatch_attn(D, nwaves, h, s), "attn_fwd_kernel(hi)");
+    UHLA_STEP(dispatch_attn(D, nwaves, true, h, s), "attn_fwd_kernel(hi)");
   }
   if (timer) timer_end(timer, UHLA_STAGE_ATTN_HI, s);
 
@@ -657,7 +741,7 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
     l.hi = 0; l.q_valid = static_cast<int>(g.M);
     l.blocks_per_bh = static_cast<int>(g.Mq / kMaxQuery);
     l.total_blocks = static_cast<int>(static_cast<int64_t>(B) * heads * l.blocks_per_bh);
-    UHLA_STEP(dispatch_attn(D, 8, l, s), "attn_fwd_kernel(guide)");
+    UHLA_STEP(dispatch_attn(D, 8, false, l, s), "attn_fwd_kernel(guide)");
   }
   if (timer) timer_end(timer, UHLA_STAGE_ATTN_LR, s);
 

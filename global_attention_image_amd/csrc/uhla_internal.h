@@ -5,7 +5,7 @@
 #include <stdint.h>
 #include <string.h>
 
-#include "../../include/uhla.h"
+#include "uhla.h"
 
 namespace uhla {
 
