@@ -138,12 +138,14 @@ constexpr int kPrepRows = 4;
 
 // Q and K rows -> head-major, rotated.  Rows [0, N) of each batch are hi-res rows in
 // window-first order (source row r(p)), rows [N, N + rows_lr) are guide rows (source row
-// N + s, zero beyond M).  Q guide rows pad to Mq, K guide rows to Mk.
+// N + s, zero beyond M).  Q guide rows pad to Mq, K guide rows to Mk.  Q is also
+// multiplied by q_scale (the softmax scale times log2 e) before its single rounding to
+// bf16, so the attention kernel's scores come out in base-2 logits.
 __global__ __launch_bounds__(kPrepThreads) void prep_qk_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, bf16_t* q_hi, bf16_t* k_hi,
     bf16_t* q_lr, bf16_t* k_lr, const double2* __restrict__ cs, int P, double log2_theta,
     int64_t N, int64_t M, int64_t Mq, int64_t Mk, int W, int w, int n_wx, int W_lr, int rho,
-    int heads, int D, int rope_on) {
+    int heads, int D, int rope_on, double q_scale) {
   const int64_t L = N + M;
   const int64_t rows_total = N + Mq;
   const int64_t b = blockIdx.y;
@@ -192,13 +194,14 @@ __global__ __launch_bounds__(kPrepThreads) void prep_qk_kernel(
           const int axis = pr / quarter, kk = pr - axis * quarter;
           const int pos = axis ? px : py;
           const double2 f = pos < P ? cs[pos * quarter + kk] : rope_cos_sin(pos, kk, D / 2, log2_theta);
-          qr[e] = rope_rotate_word(qw[e], f);
+          qr[e] = rope_rotate_word(qw[e], f, q_scale);
           kr[e] = rope_rotate_word(kw[e], f);
         }
         qo = make_uint4(qr[0], qr[1], qr[2], qr[3]);
         ko = make_uint4(kr[0], kr[1], kr[2], kr[3]);
       } else {
-        qo = qi;
+        qo = make_uint4(scale_word(qi.x, q_scale), scale_word(qi.y, q_scale),
+                        scale_word(qi.z, q_scale), scale_word(qi.w, q_scale));
         ko = ki;
       }
     }
@@ -291,8 +294,7 @@ struct AttnArgs {
   int q_valid;            // valid query rows per (b, h)
   int blocks_per_bh;
   int total_blocks;
-  float c;                // softmax scale * log2(e)
-  float rescale_thr;      // lazy-rescale threshold in raw-score units
+  float rescale_thr;      // lazy-rescale threshold in base-2 logit units
 };
 
 // Workgroups are dealt round-robin to the 8 XCDs; remap so that each XCD works on a
@@ -459,25 +461,42 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.0f;
-  float m_run = -INFINITY, l_run = 0.0f;
-  const float c = a.c;
+  // Scores are base-2 logits (Q carries softmax scale * log2 e) measured from the running
+  // row maximum m_run: the QK^T accumulators start at -m_run (neg_m), so exp2 takes S as is.
+  float m_run = 0.0f, l_run = 0.0f;
+  bool first = true;
+  f32x16 neg_m;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) neg_m[r] = 0.0f;
   f32x16 s0, s1;  // S^T of the current tile: lane = query ql; keys 8(r/4) + 4g + r%4 (+32)
 
+  // K fragment for reduction step kk: keys ql (half 0) and 32 + ql (half 1)
+  auto k_frag = [&](const char* kb, int kk, int half) -> bf16x8 {
+    const int row = half * 32 + ql;
+    return *reinterpret_cast<const bf16x8*>(kb + row * (D * 2) + (((2 * kk + g) ^ k_swizzle<D>(row)) << 4));
+  };
+  // S^T = K Q^T - m; each step's fragments are read from LDS one step ahead of use
   auto qk = [&](const char* kb) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) { s0[r] = 0.0f; s1[r] = 0.0f; }
+    bf16x8 c0 = k_frag(kb, 0, 0), c1 = k_frag(kb, 0, 1);
+    s0 = neg_m;
+    s1 = neg_m;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      const int ch = 2 * kk + g;
-      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kb + ql * (D * 2) + ((ch ^ k_swizzle<D>(ql)) << 4));
-      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(kb + (32 + ql) * (D * 2) + ((ch ^ k_swizzle<D>(32 + ql)) << 4));
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[kk], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[kk], s1, 0, 0, 0);
+      bf16x8 n0, n1;
+      if (kk + 1 < D / 16) {
+        n0 = k_frag(kb, kk + 1, 0);
+        n1 = k_frag(kb, kk + 1, 1);
+      }
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c0, qf[kk], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c1, qf[kk], s1, 0, 0, 0);
+      c0 = n0;
+      c1 = n1;
     }
   };
 
-  // online softmax (base 2) of the current S; lazy rescale of O only when a row max
-  // grows by more than 2^8.  Produces P^T as four bf16 B operands (16 keys each).
+  // Online softmax (base 2) of the current S.  The running maximum is raised (and O, l
+  // and S rescaled) only when some row's tile maximum exceeds it by more than 2^8 (and
+  // always on the first tile), so exp2(S) <= 256.  Produces P^T as four bf16 B operands.
   auto softmax = [&](int valid, bf16x8 (&pf)[4]) {
     if (valid < kKeyTile) {
 #pragma unroll
@@ -487,28 +506,40 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
         if (key + 32 >= valid) s1[r] = -INFINITY;
       }
     }
-    float mx = fmaxf(s0[0], s1[0]);
+    float m3[4];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+    for (int i = 0; i < 4; ++i)
+      m3[i] = fmaxf(fmaxf(s0[4 * i], s0[4 * i + 1]), fmaxf(s0[4 * i + 2], s0[4 * i + 3]));
+    float mx = fmaxf(fmaxf(m3[0], m3[1]), fmaxf(m3[2], m3[3]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      mx = fmaxf(mx, fmaxf(fmaxf(s1[4 * i], s1[4 * i + 1]), fmaxf(s1[4 * i + 2], s1[4 * i + 3])));
     mx = max_with_partner32(mx);
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + a.rescale_thr) != 0) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+    if (first || __builtin_amdgcn_ballot_w64(mx > a.rescale_thr) != 0) {
+      const float delta = first ? mx : fmaxf(mx, 0.0f);
+      const float alpha = first ? 0.0f : __builtin_amdgcn_exp2f(-delta);
       l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-      m_run = m_new;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s0[r] -= delta;
+        s1[r] -= delta;
+      }
+      m_run += delta;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) neg_m[r] = -m_run;
+      first = false;
     }
-    const float mc = m_run * c;
     float psum = 0.0f;
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(s0[r], c, -mc));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(s0[r + 1], c, -mc));
-      const float p2 = __builtin_amdgcn_exp2f(fmaf(s1[r], c, -mc));
-      const float p3 = __builtin_amdgcn_exp2f(fmaf(s1[r + 1], c, -mc));
+      const float p0 = __builtin_amdgcn_exp2f(s0[r]);
+      const float p1 = __builtin_amdgcn_exp2f(s0[r + 1]);
+      const float p2 = __builtin_amdgcn_exp2f(s1[r]);
+      const float p3 = __builtin_amdgcn_exp2f(s1[r + 1]);
       psum += (p0 + p1) + (p2 + p3);
       // key-step ks = 2*half + r/8; slot j = r % 8
       pf[r >> 3][r & 7] = static_cast<__bf16>(p0);
@@ -519,17 +550,22 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
     l_run += psum;
   };
 
-  // O^T += V^T P^T over 4 key-steps of 16 keys
+  // V^T fragment for key-step ks, output dims 32 dt + ql
+  auto v_frag = [&](const char* vb, int ks, int dt) -> bf16x8 {
+    const int vr = dt * 32 + ql;
+    return *reinterpret_cast<const bf16x8*>(vb + vr * (kKeyTile * 2) + (((2 * ks + g) ^ v_swizzle(vr)) << 4));
+  };
+  // O^T += V^T P^T over 4 key-steps of 16 keys; fragments read one MFMA ahead of use
   auto pv = [&](const char* vb, const bf16x8 (&pf)[4]) {
+    constexpr int DT = D / 32;
+    bf16x8 cur = v_frag(vb, 0, 0);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int ch = 2 * ks + g;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        const int vr = dt * 32 + ql;
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vb + vr * (kKeyTile * 2) + ((ch ^ v_swizzle(vr)) << 4));
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[dt], 0, 0, 0);
-      }
+    for (int i = 0; i < 4 * DT; ++i) {
+      const int ks = i / DT, dt = i % DT;
+      bf16x8 nxt;
+      if (i + 1 < 4 * DT) nxt = v_frag(vb, (i + 1) / DT, (i + 1) % DT);
+      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, pf[ks], o[dt], 0, 0, 0);
+      cur = nxt;
     }
   };
 
@@ -699,7 +735,7 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
                                  dim3(kPrepThreads), 0, s, qb, kb, ws.q_hi, ws.k_hi, ws.q_lr, ws.k_lr,
                                  ws.cs, g.P, rope_on ? log2(static_cast<double>(theta)) : 0.0,
                                  g.N, g.M, g.Mq, g.Mk, W, w, g.n_wx, W_lr, rho, heads, D,
-                                 rope_on ? 1 : 0),
+                                 rope_on ? 1 : 0, static_cast<double>(sc) * 1.4426950408889634),
               "prep_qk_kernel");
     const int64_t tiles = g.N / kKeyTile + g.Mk / kKeyTile;
     UHLA_STEP(hipLaunchKernelGGL(prep_v_kernel, dim3(static_cast<unsigned>(tiles), B), dim3(kPrepThreads), 0, s,
@@ -714,8 +750,7 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
   a.k_hi = ws.k_hi; a.v_hi = ws.v_hi; a.k_lr = ws.k_lr; a.v_lr = ws.v_lr;
   a.nbr = ws.nbr; a.nbr_cnt = ws.nbr_cnt;
   a.N = g.N; a.M = g.M; a.Mk = g.Mk; a.heads = heads; a.w2 = w2;
-  a.c = sc * 1.4426950408889634f;
-  a.rescale_thr = 8.0f / a.c;
+  a.rescale_thr = 8.0f;
 
   // 3. hi pass
   if (timer) timer_begin(timer, UHLA_STAGE_ATTN_HI, s);

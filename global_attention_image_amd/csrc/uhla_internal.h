@@ -67,14 +67,21 @@ __device__ __forceinline__ uint32_t f64_to_bf16_bits(double x) {
 }
 
 // Rotates the pair (a, b) packed as two bf16 in one word (a in the low half) by the
-// factors cs = (cos, sin): (a cos - b sin, a sin + b cos), computed in fp64 and rounded
-// once to bf16.
-__device__ __forceinline__ uint32_t rope_rotate_word(uint32_t word, double2 cs) {
+// factors cs = (cos, sin): (a cos - b sin, a sin + b cos) times `scale`, computed in fp64
+// and rounded once to bf16 (scale = 1 is the plain rotation).
+__device__ __forceinline__ uint32_t rope_rotate_word(uint32_t word, double2 cs, double scale = 1.0) {
   const double a = static_cast<double>(__uint_as_float(word << 16));
   const double b = static_cast<double>(__uint_as_float(word & 0xffff0000u));
-  const double ra = fma(a, cs.x, -(b * cs.y));
-  const double rb = fma(a, cs.y, b * cs.x);
+  const double ra = fma(a, cs.x, -(b * cs.y)) * scale;
+  const double rb = fma(a, cs.y, b * cs.x) * scale;
   return f64_to_bf16_bits(ra) | (f64_to_bf16_bits(rb) << 16);
+}
+
+// Both bf16 halves of a word times `scale`, in fp64, rounded once to bf16.
+__device__ __forceinline__ uint32_t scale_word(uint32_t word, double scale) {
+  const double a = static_cast<double>(__uint_as_float(word << 16)) * scale;
+  const double b = static_cast<double>(__uint_as_float(word & 0xffff0000u)) * scale;
+  return f64_to_bf16_bits(a) | (f64_to_bf16_bits(b) << 16);
 }
 
 // Raster index of the token at window-first position p (hi-res grid of width W,
