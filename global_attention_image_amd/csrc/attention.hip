@@ -464,7 +464,7 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   // Scores are base-2 logits (Q carries softmax scale * log2 e) measured from the running
   // row maximum m_run: the QK^T accumulators start at -m_run (neg_m), so exp2 takes S as is.
   float m_run = 0.0f, l_run = 0.0f;
-  bool first = true;
+  bool first = true;  // no running maximum yet
   f32x16 neg_m;
 #pragma unroll
   for (int r = 0; r < 16; ++r) neg_m[r] = 0.0f;
@@ -494,9 +494,55 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
     }
   };
 
-  // Online softmax (base 2) of the current S.  The running maximum is raised (and O, l
-  // and S rescaled) only when some row's tile maximum exceeds it by more than 2^8 (and
-  // always on the first tile), so exp2(S) <= 256.  Produces P^T as four bf16 B operands.
+  // Raise the running max by delta (per lane): rescale O and l by alpha, shift the live
+  // scores, and re-seed the QK^T accumulator start value.
+  auto rescale = [&](float delta, float alpha) {
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s0[r] -= delta;
+      s1[r] -= delta;
+    }
+    m_run += delta;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) neg_m[r] = -m_run;
+  };
+  auto row_max = [&]() -> float {
+    float m3[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      m3[i] = fmaxf(fmaxf(fmaxf(s0[4 * i], s0[4 * i + 1]), fmaxf(s0[4 * i + 2], s0[4 * i + 3])),
+                    fmaxf(fmaxf(s1[4 * i], s1[4 * i + 1]), fmaxf(s1[4 * i + 2], s1[4 * i + 3])));
+    return max_with_partner32(fmaxf(fmaxf(m3[0], m3[1]), fmaxf(m3[2], m3[3])));
+  };
+  // P = exp2(S) as bf16 B operands; returns this lane's partial row sum
+  auto expo = [&](bf16x8 (&pf)[4]) -> float {
+    float ps = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(s0[r]);
+      const float p1 = __builtin_amdgcn_exp2f(s0[r + 1]);
+      const float p2 = __builtin_amdgcn_exp2f(s1[r]);
+      const float p3 = __builtin_amdgcn_exp2f(s1[r + 1]);
+      ps += (p0 + p1) + (p2 + p3);
+      // key-step ks = 2*half + r/8; slot j = r % 8
+      pf[r >> 3][r & 7] = static_cast<__bf16>(p0);
+      pf[r >> 3][(r & 7) + 1] = static_cast<__bf16>(p1);
+      pf[2 + (r >> 3)][r & 7] = static_cast<__bf16>(p2);
+      pf[2 + (r >> 3)][(r & 7) + 1] = static_cast<__bf16>(p3);
+    }
+    return ps;
+  };
+
+  // Online softmax (base 2) of the current S.  The first tile sets the running maximum.
+  // Later tiles exponentiate against the stale maximum and only look at the row max when
+  // a lane's partial sum exceeds 2^20 (some score grew by more than ~2^15 over it, or
+  // overflowed): then the maximum is raised, O and l rescaled, and P recomputed.  P stays
+  // below 2^20, far inside fp32 and bf16 range.  Produces P^T as four bf16 B operands.
   auto softmax = [&](int valid, bf16x8 (&pf)[4]) {
     if (valid < kKeyTile) {
 #pragma unroll
@@ -506,48 +552,17 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
         if (key + 32 >= valid) s1[r] = -INFINITY;
       }
     }
-    float m3[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      m3[i] = fmaxf(fmaxf(s0[4 * i], s0[4 * i + 1]), fmaxf(s0[4 * i + 2], s0[4 * i + 3]));
-    float mx = fmaxf(fmaxf(m3[0], m3[1]), fmaxf(m3[2], m3[3]));
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      mx = fmaxf(mx, fmaxf(fmaxf(s1[4 * i], s1[4 * i + 1]), fmaxf(s1[4 * i + 2], s1[4 * i + 3])));
-    mx = max_with_partner32(mx);
-    if (first || __builtin_amdgcn_ballot_w64(mx > a.rescale_thr) != 0) {
-      const float delta = first ? mx : fmaxf(mx, 0.0f);
-      const float alpha = first ? 0.0f : __builtin_amdgcn_exp2f(-delta);
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s0[r] -= delta;
-        s1[r] -= delta;
-      }
-      m_run += delta;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) neg_m[r] = -m_run;
+    if (first) {
+      rescale(row_max(), 0.0f);
       first = false;
     }
-    float psum = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(s0[r]);
-      const float p1 = __builtin_amdgcn_exp2f(s0[r + 1]);
-      const float p2 = __builtin_amdgcn_exp2f(s1[r]);
-      const float p3 = __builtin_amdgcn_exp2f(s1[r + 1]);
-      psum += (p0 + p1) + (p2 + p3);
-      // key-step ks = 2*half + r/8; slot j = r % 8
-      pf[r >> 3][r & 7] = static_cast<__bf16>(p0);
-      pf[r >> 3][(r & 7) + 1] = static_cast<__bf16>(p1);
-      pf[2 + (r >> 3)][r & 7] = static_cast<__bf16>(p2);
-      pf[2 + (r >> 3)][(r & 7) + 1] = static_cast<__bf16>(p3);
+    float ps = expo(pf);
+    if (__builtin_amdgcn_ballot_w64(!(ps <= 1048576.0f)) != 0) {
+      const float delta = fmaxf(row_max(), 0.0f);
+      rescale(delta, __builtin_amdgcn_exp2f(-delta));
+      ps = expo(pf);
     }
-    l_run += psum;
+    l_run += ps;
   };
 
   // V^T fragment for key-step ks, output dims 32 dt + ql
