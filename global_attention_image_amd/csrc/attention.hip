@@ -413,9 +413,8 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
     v_src[i] = vr * (kKeyTile * 2) + ((vp ^ v_swizzle(vr)) << 4);
   }
   // global -> LDS stage buffer `dst` for tile t (asynchronous)
-  auto issue_tile = [&](int t, char* dst) {
-    const char* kp;
-    const char* vp;
+  // Global sources of tile t (K tile, V^T tile).
+  auto tile_src = [&](int t, const char*& kp, const char*& vp) {
     if (HI && t < n_local) {
       const int j = t / tiles_per_win, sub = t - j * tiles_per_win;
       const int nw = __builtin_amdgcn_readfirstlane(nbr_s[j]);
@@ -429,13 +428,25 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
       vp = reinterpret_cast<const char*>(a.v_lr + (bh * (a.Mk / kKeyTile) + j) *
                                                       static_cast<int64_t>(D) * kKeyTile);
     }
+  };
+  // DMA instructions [p0, p1) of this thread's share of a tile into LDS stage `dst`:
+  // instruction p copies K chunk p/2 (p even) or V chunk p/2 (p odd).
+  auto issue_parts = [&](const char* kp, const char* vp, char* dst, int p0, int p1) {
     const uint32_t lds = lds_addr(dst);
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
+    for (int p = 0; p < LOADS_PER_TILE; ++p) {
+      if (p < p0 || p >= p1) continue;
+      const int i = p >> 1;
       const uint32_t base = __builtin_amdgcn_readfirstlane(lds + (i * NWAVES + wave) * 64 * 16);
-      dma_16b(kp, k_src[i], base);
-      dma_16b(vp, v_src[i], base + TILE_BYTES);
+      if (p & 1) dma_16b(vp, v_src[i], base + TILE_BYTES);
+      else dma_16b(kp, k_src[i], base);
     }
+  };
+  auto issue_tile = [&](int t, char* dst) {
+    const char* kp;
+    const char* vp;
+    tile_src(t, kp, vp);
+    issue_parts(kp, vp, dst, 0, LOADS_PER_TILE);
   };
   auto tile_valid = [&](int t) -> int {
     if (HI && t < n_local) return kKeyTile;
@@ -603,19 +614,33 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   auto step = [&]<int S>(int t) {
     char* cur = stage(S);
     char* nxt = stage((S + 1) & 3);
-    // stage (t+3) % 4 held tile t-1, whose last reads ended at the previous barrier
+    // Stage (t+3) % 4 held tile t-1, whose last reads ended at the previous barrier.  Its
+    // DMA instructions are spread over the four gaps between phases: issued all at once,
+    // the eight waves' loads back up in the vector-memory path and stall every wave.
     const bool more3 = t + 3 < n_tiles;
-    if (more3) issue_tile(t + 3, stage((S + 3) & 3));
+    const char* kp = nullptr;
+    const char* vp = nullptr;
+    char* dst = stage((S + 3) & 3);
+    if (more3) tile_src(t + 3, kp, vp);
+    auto dma_slot = [&](int slot) {
+      if (more3) issue_parts(kp, vp, dst, slot * LOADS_PER_TILE / 4, (slot + 1) * LOADS_PER_TILE / 4);
+    };
     bf16x8 pf[4];
+    dma_slot(0);
     if (!wave_b) {
       qk(cur);
+      dma_slot(1);
       softmax(tile_valid(t), pf);
+      dma_slot(2);
       pv(cur + TILE_BYTES, pf);
     } else {
       softmax(tile_valid(t), pf);
+      dma_slot(1);
       pv(cur + TILE_BYTES, pf);
+      dma_slot(2);
       if (t + 1 < n_tiles) qk(nxt);
     }
+    dma_slot(3);
     // tile t+2 must have landed before the next iteration reads it
     if (more3) wait_vm_and_barrier<LOADS_PER_TILE>();
     else wait_vm_and_barrier<0>();
