@@ -41,6 +41,11 @@ class Geometry:
     rho: int = 4
     theta: float = 10000.0
     name: str = "custom"
+    # mask options: neighbourhood radius in windows (1 = clipped 3x3) and which guide
+    # tokens a hi-res query sees (0 = all; 1 = those whose scaled position lies in the
+    # query's own window; 2 = those lying in the query's neighbourhood of windows)
+    radius: int = 1
+    guide_mode: int = 0
 
     @property
     def N(self) -> int:
@@ -163,20 +168,44 @@ def make_config_inputs(name: str):
     return (geom,) + make_qkv_bits(geom, CONFIG_SEEDS[name])
 
 
+def _axis_neighbour_sum(n: int, r: int) -> int:
+    """Sum over n positions of the number of positions within distance r (clipped)."""
+    return sum(min(n - 1, i + r) - max(0, i - r) + 1 for i in range(n))
+
+
+def _guide_cells_per_window(geom: Geometry):
+    """[n_wy, n_wx] count of guide cells whose scaled position lies in each window."""
+    a, b = geom.H // geom.w, geom.W // geom.w
+    cy = np.zeros(a, dtype=np.int64)
+    cx = np.zeros(b, dtype=np.int64)
+    for i in range(geom.H_lr):
+        if geom.rho * i < geom.H:
+            cy[(geom.rho * i) // geom.w] += 1
+    for j in range(geom.W_lr):
+        if geom.rho * j < geom.W:
+            cx[(geom.rho * j) // geom.w] += 1
+    return cy[:, None] * cx[None, :]
+
+
 def algorithmic_pairs(geom: Geometry) -> dict:
     """Unmasked (query, key) pairs per (batch, head), by term.
 
-    Geometry bookkeeping for throughput figures: a window grid of a x b windows has
-    sum over windows of the clipped 3x3 neighbour count = (3a - 2)(3b - 2) (a, b >= 2;
-    a one-window axis contributes 1).
+    Geometry bookkeeping for throughput figures: along an axis of n windows the clipped
+    neighbour counts within radius r sum to sum_i (min(n-1, i+r) - max(0, i-r) + 1)
+    (3n - 2 for r = 1); the local pairs are that product times w^4.
     """
     a, b = geom.H // geom.w, geom.W // geom.w
-
-    def axis(n):
-        return 1 if n == 1 else 3 * n - 2
-
-    local = axis(a) * axis(b) * geom.w ** 4
-    hi_lr = geom.N * geom.M
+    r = geom.radius
+    local = _axis_neighbour_sum(a, r) * _axis_neighbour_sum(b, r) * geom.w ** 4
+    if geom.guide_mode == 0:
+        hi_lr = geom.N * geom.M
+    else:
+        g = _guide_cells_per_window(geom)
+        if geom.guide_mode == 2:
+            # guide cells of every window within radius r, per query window
+            pad = np.pad(g, r)
+            g = sum(pad[dy:dy + a, dx:dx + b] for dy in range(2 * r + 1) for dx in range(2 * r + 1))
+        hi_lr = int(g.sum()) * geom.w * geom.w
     lr_lr = geom.M * geom.M
     return {"local": local, "hi_lr": hi_lr, "lr_lr": lr_lr, "total": local + hi_lr + lr_lr}
 

@@ -18,7 +18,10 @@ What the pages fix, and the readings taken where they are silent:
 * Mask ([UltraGen/ar §2.B], [UltraGen/es §2]): a hi-res window attends to itself, to
   its adjacent windows and to every low-res guide token; guide tokens attend to each
   other.  Readings: "adjacent" is the clipped 3x3 neighbourhood (no wrap); guide
-  queries see no hi-res key.
+  queries see no hi-res key.  Variants: a neighbourhood radius other than 1, and
+  [UltraGen/it §2]'s narrower wording (a window looks at the *corresponding* guide
+  tokens): the guide tokens whose scaled position lies in the window (or in its
+  neighbourhood).
 * Positions ([UltraGen/ar §2.B]): guide-token position indices are scaled by rho
   (4) onto the hi-res grid.  Reading: integer positions (rho*i, rho*j), no offset.
 * RoPE ([UltraGen/fr §2.A]: relative positional embeddings).  Readings: 2D axial RoPE,
@@ -140,21 +143,40 @@ def rope_joint(x: np.ndarray, geom) -> np.ndarray:
 def mask_rows(geom, rows: np.ndarray) -> np.ndarray:
     """Explicit boolean mask rows (raster order over all L keys) for query rows ``rows``.
 
-    hi q -> hi k : allowed iff the windows differ by at most one in both axes;
-    hi q -> lr k : always;   lr q -> lr k : always;   lr q -> hi k : never.
+    hi q -> hi k : allowed iff the windows differ by at most ``radius`` in both axes
+                   (radius 1: the clipped 3x3 neighbourhood of the pages);
+    hi q -> lr k : guide_mode 0: always; 1: iff the guide token's scaled position
+                   (rho*i, rho*j) lies in the query's window; 2: iff it lies in a window
+                   of the query's neighbourhood (scaled positions outside the hi-res grid
+                   belong to no window);
+    lr q -> lr k : always;   lr q -> hi k : never.
     """
     rows = np.asarray(rows, dtype=np.int64)
     N, L, w = geom.N, geom.L, geom.w
+    r = getattr(geom, "radius", 1)
+    mode = getattr(geom, "guide_mode", 0)
     key = np.arange(L, dtype=np.int64)
     key_is_hi = key < N
     ky, kx = np.where(key_is_hi, key // geom.W, 0), np.where(key_is_hi, key % geom.W, 0)
     q_is_hi = rows < N
     qy, qx = np.where(q_is_hi, rows // geom.W, 0), np.where(q_is_hi, rows % geom.W, 0)
-    near = (np.abs(qy[:, None] // w - ky[None, :] // w) <= 1) & \
-           (np.abs(qx[:, None] // w - kx[None, :] // w) <= 1)
+    near = (np.abs(qy[:, None] // w - ky[None, :] // w) <= r) & \
+           (np.abs(qx[:, None] // w - kx[None, :] // w) <= r)
     hi_hi = q_is_hi[:, None] & key_is_hi[None, :] & near
-    any_lr = ~key_is_hi[None, :] & np.ones((len(rows), 1), dtype=bool)
-    return hi_hi | any_lr
+    key_is_lr = ~key_is_hi
+    if mode == 0:
+        hi_lr = q_is_hi[:, None] & key_is_lr[None, :]
+    else:
+        s = np.where(key_is_lr, key - N, 0)
+        gy = geom.rho * (s // max(geom.W_lr, 1))
+        gx = geom.rho * (s % max(geom.W_lr, 1))
+        inside = key_is_lr & (gy < geom.H) & (gx < geom.W)
+        reach = 0 if mode == 1 else r
+        close = (np.abs(qy[:, None] // w - gy[None, :] // w) <= reach) & \
+                (np.abs(qx[:, None] // w - gx[None, :] // w) <= reach)
+        hi_lr = q_is_hi[:, None] & inside[None, :] & close
+    lr_lr = ~q_is_hi[:, None] & key_is_lr[None, :]
+    return hi_hi | hi_lr | lr_lr
 
 
 # ---------------------------------------------------------------------------------

@@ -39,20 +39,43 @@ def window_tokens_by_slicing(H, W, w, wy, wx):
 
 
 def brute_mask(geom):
-    """L x L mask built by enumerating each window's clipped 3x3 neighbour windows."""
+    """L x L mask built by enumeration: each window's clipped neighbour windows within the
+    radius (slices of the index grid), and guide cells assigned to windows by testing the
+    window bounds against their scaled position one window at a time."""
     H, W, w, N, L = geom.H, geom.W, geom.w, geom.N, geom.L
+    r, mode = geom.radius, geom.guide_mode
     m = np.zeros((L, L), dtype=bool)
     nwy, nwx = H // w, W // w
+
+    def cell_window(i, j):
+        y, x = geom.rho * i, geom.rho * j
+        for wy in range(nwy):
+            for wx in range(nwx):
+                if wy * w <= y < (wy + 1) * w and wx * w <= x < (wx + 1) * w:
+                    return wy, wx
+        return None
+
+    cells = [(s, cell_window(s // geom.W_lr, s % geom.W_lr)) for s in range(geom.M)]
     for wy in range(nwy):
         for wx in range(nwx):
             qt = window_tokens_by_slicing(H, W, w, wy, wx)
-            for dy in (-1, 0, 1):
-                for dx in (-1, 0, 1):
+            for dy in range(-r, r + 1):
+                for dx in range(-r, r + 1):
                     ny, nx = wy + dy, wx + dx
                     if 0 <= ny < nwy and 0 <= nx < nwx:
                         kt = window_tokens_by_slicing(H, W, w, ny, nx)
                         m[np.ix_(qt, kt)] = True
-            m[qt, N:] = True
+            for s, cw in cells:
+                if mode == 0:
+                    ok = True
+                elif cw is None:
+                    ok = False
+                elif mode == 1:
+                    ok = cw == (wy, wx)
+                else:
+                    ok = abs(cw[0] - wy) <= r and abs(cw[1] - wx) <= r
+                if ok:
+                    m[qt, N + s] = True
     m[N:, N:] = True
     return m
 
@@ -379,6 +402,72 @@ def test_identity_probe():
     assert np.max(np.abs(o - v)) < 1e-12
 
 
+# ------------------------------------------------------------------- mask variants
+
+VARIANT_GEOMS = [
+    small_geom(radius=0), small_geom(radius=2, H=20, W=16),
+    small_geom(guide_mode=1), small_geom(guide_mode=2),
+    small_geom(guide_mode=2, radius=0, H=16, W=12, H_lr=4, W_lr=3),
+    # guide grid larger than the hi-res extent / smaller than it; rho not dividing w
+    small_geom(guide_mode=1, H=8, W=12, H_lr=5, W_lr=2),
+    small_geom(guide_mode=2, H=16, W=8, H_lr=3, W_lr=3, rho=3),
+    small_geom(guide_mode=2, radius=2, H=20, W=12, H_lr=7, W_lr=4, rho=3),
+]
+
+
+def check_mask_variants(mask_rows_fn):
+    for g in VARIANT_GEOMS:
+        assert np.array_equal(mask_rows_fn(g, np.arange(g.L)), brute_mask(g)), g
+
+
+def test_mask_variants():
+    check_mask_variants(orc.mask_rows)
+
+
+def test_default_options_are_the_pages_mask():
+    g = small_geom(H=16, W=12)
+    assert g.radius == 1 and g.guide_mode == 0
+    m = orc.mask_rows(g, np.arange(g.L))
+    # radius >= the grid: every hi query sees every hi key
+    big = g.with_(radius=5)
+    mb = orc.mask_rows(big, np.arange(g.L))
+    assert mb[:g.N, :g.N].all() and np.array_equal(mb[:, g.N:], m[:, g.N:])
+
+
+def test_pair_counts_of_variants():
+    for g in VARIANT_GEOMS + [CONFIGS["tiny"].with_(guide_mode=1), CONFIGS["tiny"].with_(guide_mode=2),
+                              CONFIGS["tiny"].with_(radius=0)]:
+        assert int(orc.mask_rows(g, np.arange(g.L)).sum()) == algorithmic_pairs(g)["total"], g
+
+
+def test_attention_vs_loops_variants():
+    for g in (small_geom(guide_mode=1, radius=0), small_geom(guide_mode=2)):
+        q, k, v = rand_qkv(g, 21)
+        assert np.max(np.abs(orc.forward(q, k, v, g) - loop_attention(q, k, v, g))) < 1e-12
+
+
+def test_uniform_probe_guide_mode_1():
+    # Q = 0, V = [is guide]: a hi row's guide weight is g / (n_nbr w^2 + g), g = the number
+    # of guide cells whose scaled position falls in the row's window (counted here by hand)
+    g = small_geom(H=16, W=12, w=4, H_lr=4, W_lr=3, guide_mode=1, radius=1)
+    q = np.zeros(g.shape())
+    v = np.zeros(g.shape())
+    v[0, g.N:, 0, 0] = 1.0
+    o = orc.forward(q, rand_qkv(g, 2)[1], v, g)
+    nwy, nwx = g.H // g.w, g.W // g.w
+    cnt = np.zeros((nwy, nwx), dtype=int)
+    for i in range(g.H_lr):
+        for j in range(g.W_lr):
+            cnt[(4 * i) // 4, (4 * j) // 4] += 1  # rho = w = 4: one cell per window
+    yy, xx = orc.hi_positions(g.H, g.W)
+    for rr in range(g.N):
+        wy, wx = yy[rr] // g.w, xx[rr] // g.w
+        nb = sum(1 for a in range(wy - 1, wy + 2) for b in range(wx - 1, wx + 2)
+                 if 0 <= a < nwy and 0 <= b < nwx)
+        tot = nb * g.w * g.w + cnt[wy, wx]
+        assert abs(o[0, rr, 0, 0] - cnt[wy, wx] / tot) < 1e-12
+
+
 # --------------------------------------------------------- planted mistakes must be caught
 
 def _mut_index_transposed(H, W, w):
@@ -457,6 +546,39 @@ def _mut_mask_wrap(geom, rows):
         dx = np.minimum((qx - kx) % nwx, (kx - qx) % nwx)
         m[i, :geom.N] = (dy <= 1) & (dx <= 1)
     return m
+
+
+def _mut_variant_unscaled_cells(geom, rows):
+    # guide cells mapped to windows by their unscaled index
+    return orc.mask_rows(geom.with_(rho=1), rows) if geom.guide_mode else orc.mask_rows(geom, rows)
+
+
+def _mut_variant_radius_off_by_one(geom, rows):
+    return orc.mask_rows(geom.with_(radius=geom.radius + 1), rows)
+
+
+def _mut_variant_outside_cells_clamped(geom, rows):
+    # guide cells beyond the hi-res grid wrongly assigned to the border windows
+    m = orc.mask_rows(geom, rows)
+    if geom.guide_mode:
+        rows = np.asarray(rows)
+        s = np.arange(geom.M)
+        gy = np.minimum(geom.rho * (s // geom.W_lr), geom.H - 1)
+        gx = np.minimum(geom.rho * (s % geom.W_lr), geom.W - 1)
+        for i, rr in enumerate(rows):
+            if rr >= geom.N:
+                continue
+            qy, qx = (rr // geom.W) // geom.w, (rr % geom.W) // geom.w
+            reach = 0 if geom.guide_mode == 1 else geom.radius
+            m[i, geom.N:] = (np.abs(gy // geom.w - qy) <= reach) & (np.abs(gx // geom.w - qx) <= reach)
+    return m
+
+
+@pytest.mark.parametrize("mutant", [_mut_variant_unscaled_cells, _mut_variant_radius_off_by_one,
+                                     _mut_variant_outside_cells_clamped])
+def test_pins_catch_variant_mutants(mutant):
+    with pytest.raises(AssertionError):
+        check_mask_variants(mutant)
 
 
 def _mut_forward_no_scale(q, k, v, geom):
