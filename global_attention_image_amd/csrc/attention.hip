@@ -327,6 +327,8 @@ __device__ __forceinline__ int k_swizzle(int row) {
 __device__ __forceinline__ int v_swizzle(int row) { return (row >> 1) & 7; }
 
 constexpr int kStages = 4;  // LDS ring: tiles t, t+1 are read while t+2, t+3 land
+constexpr int kQkAhead = 3;  // K fragment reads in flight ahead of the QK^T MFMAs (steps)
+constexpr int kPvAhead = 4;  // V fragment reads in flight ahead of the PV MFMAs
 
 // 32-bit LDS address of a __shared__ object
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -479,6 +481,7 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   f32x16 neg_m;
 #pragma unroll
   for (int r = 0; r < 16; ++r) neg_m[r] = 0.0f;
+  asm volatile("" : "+v"(neg_m));
   f32x16 s0, s1;  // S^T of the current tile: lane = query ql; keys 8(r/4) + 4g + r%4 (+32)
 
   // K fragment for reduction step kk: keys ql (half 0) and 32 + ql (half 1)
@@ -486,23 +489,30 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
     const int row = half * 32 + ql;
     return *reinterpret_cast<const bf16x8*>(kb + row * (D * 2) + (((2 * kk + g) ^ k_swizzle<D>(row)) << 4));
   };
-  // S^T = K Q^T - m; each step's fragments are read from LDS one step ahead of use
+  // S^T = K Q^T - m.  K fragments are read kQkAhead reduction steps ahead of their MFMAs;
+  // the scheduling barriers keep the compiler from sinking each read next to its use,
+  // which would expose the full LDS latency at every step.
   auto qk = [&](const char* kb) {
-    bf16x8 c0 = k_frag(kb, 0, 0), c1 = k_frag(kb, 0, 1);
+    constexpr int KS = D / 16, AH = kQkAhead < KS ? kQkAhead : KS;
+    bf16x8 f0[KS], f1[KS];
+#pragma unroll
+    for (int kk = 0; kk < AH; ++kk) {
+      f0[kk] = k_frag(kb, kk, 0);
+      f1[kk] = k_frag(kb, kk, 1);
+    }
     s0 = neg_m;
     s1 = neg_m;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      bf16x8 n0, n1;
-      if (kk + 1 < D / 16) {
-        n0 = k_frag(kb, kk + 1, 0);
-        n1 = k_frag(kb, kk + 1, 1);
+    for (int kk = 0; kk < KS; ++kk) {
+      __builtin_amdgcn_sched_barrier(0);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0[kk], qf[kk], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1[kk], qf[kk], s1, 0, 0, 0);
+      if (kk + AH < KS) {
+        f0[kk + AH] = k_frag(kb, kk + AH, 0);
+        f1[kk + AH] = k_frag(kb, kk + AH, 1);
       }
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c0, qf[kk], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c1, qf[kk], s1, 0, 0, 0);
-      c0 = n0;
-      c1 = n1;
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // Raise the running max by delta (per lane): rescale O and l by alpha, shift the live
@@ -521,6 +531,7 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
     m_run += delta;
 #pragma unroll
     for (int r = 0; r < 16; ++r) neg_m[r] = -m_run;
+    asm volatile("" : "+v"(neg_m));
   };
   auto row_max = [&]() -> float {
     float m3[4];
@@ -530,23 +541,27 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
                     fmaxf(fmaxf(s1[4 * i], s1[4 * i + 1]), fmaxf(s1[4 * i + 2], s1[4 * i + 3])));
     return max_with_partner32(fmaxf(fmaxf(m3[0], m3[1]), fmaxf(m3[2], m3[3])));
   };
-  // P = exp2(S) as bf16 B operands; returns this lane's partial row sum
+  // P = exp2(S) as bf16 B operands; returns this lane's partial row sum.  The sum is taken
+  // over the bf16-rounded P (two at a time with v_dot2_f32_bf16 against (1, 1)), so the
+  // normaliser counts exactly the weights that multiply V.
   auto expo = [&](bf16x8 (&pf)[4]) -> float {
-    float ps = 0.0f;
+    const bf16x2 one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    float ps0 = 0.0f, ps1 = 0.0f;
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(s0[r]);
-      const float p1 = __builtin_amdgcn_exp2f(s0[r + 1]);
-      const float p2 = __builtin_amdgcn_exp2f(s1[r]);
-      const float p3 = __builtin_amdgcn_exp2f(s1[r + 1]);
-      ps += (p0 + p1) + (p2 + p3);
+      const bf16x2 a = {static_cast<__bf16>(__builtin_amdgcn_exp2f(s0[r])),
+                        static_cast<__bf16>(__builtin_amdgcn_exp2f(s0[r + 1]))};
+      const bf16x2 c = {static_cast<__bf16>(__builtin_amdgcn_exp2f(s1[r])),
+                        static_cast<__bf16>(__builtin_amdgcn_exp2f(s1[r + 1]))};
+      ps0 = __builtin_amdgcn_fdot2_f32_bf16(a, one, ps0, false);
+      ps1 = __builtin_amdgcn_fdot2_f32_bf16(c, one, ps1, false);
       // key-step ks = 2*half + r/8; slot j = r % 8
-      pf[r >> 3][r & 7] = static_cast<__bf16>(p0);
-      pf[r >> 3][(r & 7) + 1] = static_cast<__bf16>(p1);
-      pf[2 + (r >> 3)][r & 7] = static_cast<__bf16>(p2);
-      pf[2 + (r >> 3)][(r & 7) + 1] = static_cast<__bf16>(p3);
+      pf[r >> 3][r & 7] = a[0];
+      pf[r >> 3][(r & 7) + 1] = a[1];
+      pf[2 + (r >> 3)][r & 7] = c[0];
+      pf[2 + (r >> 3)][(r & 7) + 1] = c[1];
     }
-    return ps;
+    return ps0 + ps1;
   };
 
   // Online softmax (base 2) of the current S.  The first tile sets the running maximum.
@@ -556,11 +571,14 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   // below 2^20, far inside fp32 and bf16 range.  Produces P^T as four bf16 B operands.
   auto softmax = [&](int valid, bf16x8 (&pf)[4]) {
     if (valid < kKeyTile) {
+      // key 8(r/4) + 4g + r%4 (+32) is past the end iff its g-free part reaches valid - 4g;
+      // comparing against that compile-time part keeps 32 key indices out of registers
+      const int lim = valid - 4 * g;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = 8 * (r >> 2) + 4 * g + (r & 3);
-        if (key >= valid) s0[r] = -INFINITY;
-        if (key + 32 >= valid) s1[r] = -INFINITY;
+        const int kc = 8 * (r >> 2) + (r & 3);
+        if (kc >= lim) s0[r] = -INFINITY;
+        if (kc + 32 >= lim) s1[r] = -INFINITY;
       }
     }
     if (first) {
@@ -581,18 +599,19 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
     const int vr = dt * 32 + ql;
     return *reinterpret_cast<const bf16x8*>(vb + vr * (kKeyTile * 2) + (((2 * ks + g) ^ v_swizzle(vr)) << 4));
   };
-  // O^T += V^T P^T over 4 key-steps of 16 keys; fragments read one MFMA ahead of use
+  // O^T += V^T P^T over 4 key-steps of 16 keys; V fragments are read kPvAhead MFMAs ahead
   auto pv = [&](const char* vb, const bf16x8 (&pf)[4]) {
-    constexpr int DT = D / 32;
-    bf16x8 cur = v_frag(vb, 0, 0);
+    constexpr int DT = D / 32, NI = 4 * DT, AH = kPvAhead < NI ? kPvAhead : NI;
+    bf16x8 f[NI];
 #pragma unroll
-    for (int i = 0; i < 4 * DT; ++i) {
-      const int ks = i / DT, dt = i % DT;
-      bf16x8 nxt;
-      if (i + 1 < 4 * DT) nxt = v_frag(vb, (i + 1) / DT, (i + 1) % DT);
-      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, pf[ks], o[dt], 0, 0, 0);
-      cur = nxt;
+    for (int i = 0; i < AH; ++i) f[i] = v_frag(vb, i / DT, i % DT);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      o[i % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[i], pf[i / DT], o[i % DT], 0, 0, 0);
+      if (i + AH < NI) f[i + AH] = v_frag(vb, (i + AH) / DT, (i + AH) % DT);
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   auto stage = [&](int i) -> char* {
