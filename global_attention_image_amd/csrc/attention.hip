@@ -357,13 +357,14 @@ __device__ __forceinline__ void wait_vm_and_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// One workgroup = NWAVES waves x 32 queries.  Waves [0, NWAVES/2) ("A") process tile t as
-// QK^T_t -> softmax_t -> PV_t; waves [NWAVES/2, NWAVES) ("B") as softmax_t -> PV_t ->
-// QK^T_{t+1}, carrying S across the barrier.  Waves w and w + NWAVES/2 share a SIMD, so
-// while one runs MFMAs the other can run its softmax on the VALU.
+// One workgroup = NWAVES waves x 32 queries.  Waves [0, NWAVES/2) ("A") and
+// [NWAVES/2, NWAVES) ("B") are offset by half an iteration: in iteration t, A runs
+// PV_{t-1}, QK^T_t, softmax_t and B runs softmax_t, PV_t, QK^T_{t+1}.  Waves w and
+// w + NWAVES/2 share a SIMD, so while one runs its block of MFMAs the other runs its
+// softmax on the VALU.
 //
 // K/V tiles are copied global -> LDS by the DMA path of global_load_lds_dwordx4 (lane l of
-// a load writes LDS bytes [16 l, 16 l + 16) above the wave's base), three tiles ahead of
+// a load writes LDS bytes [16 l, 16 l + 16) above the wave's base), two iterations ahead of
 // their first use.  Each lane picks the global 16-byte chunk that belongs at its LDS slot
 // under the XOR swizzle, so the LDS layout is the one the fragment reads expect.
 template <int D, int NWAVES, bool HI>
@@ -416,7 +417,7 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   }
   // global -> LDS stage buffer `dst` for tile t (asynchronous)
   // Global sources of tile t (K tile, V^T tile).
-  auto tile_src = [&](int t, const char*& kp, const char*& vp) {
+  auto tile_src = [&](int t, const char*& kp, const char*& vp) __attribute__((always_inline)) {
     if (HI && t < n_local) {
       const int j = t / tiles_per_win, sub = t - j * tiles_per_win;
       const int nw = __builtin_amdgcn_readfirstlane(nbr_s[j]);
@@ -431,26 +432,36 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
                                                       static_cast<int64_t>(D) * kKeyTile);
     }
   };
-  // DMA instructions [p0, p1) of this thread's share of a tile into LDS stage `dst`:
-  // instruction p copies K chunk p/2 (p even) or V chunk p/2 (p odd).
-  auto issue_parts = [&](const char* kp, const char* vp, char* dst, int p0, int p1) {
-    const uint32_t lds = lds_addr(dst);
+  // DMA instructions [p0, p1) of this thread's share of one K tile and one V tile:
+  // instruction p copies K chunk p/2 (p even) from kp into the K half of stage `kdst`, or
+  // V chunk p/2 (p odd) from vp into the V half of stage `vdst`; a null source is skipped.
+  auto issue_parts = [&](const char* kp, const char* vp, char* kdst, char* vdst, int p0, int p1) __attribute__((always_inline)) {
+    const uint32_t klds = lds_addr(kdst), vlds = lds_addr(vdst) + TILE_BYTES;
 #pragma unroll
     for (int p = 0; p < LOADS_PER_TILE; ++p) {
       if (p < p0 || p >= p1) continue;
       const int i = p >> 1;
-      const uint32_t base = __builtin_amdgcn_readfirstlane(lds + (i * NWAVES + wave) * 64 * 16);
-      if (p & 1) dma_16b(vp, v_src[i], base + TILE_BYTES);
-      else dma_16b(kp, k_src[i], base);
+      const uint32_t off = (i * NWAVES + wave) * 64 * 16;
+      if (p & 1) {
+        if (vp) dma_16b(vp, v_src[i], __builtin_amdgcn_readfirstlane(vlds + off));
+      } else {
+        if (kp) dma_16b(kp, k_src[i], __builtin_amdgcn_readfirstlane(klds + off));
+      }
     }
   };
-  auto issue_tile = [&](int t, char* dst) {
+  auto issue_k = [&](int t, char* dst) __attribute__((always_inline)) {
     const char* kp;
     const char* vp;
     tile_src(t, kp, vp);
-    issue_parts(kp, vp, dst, 0, LOADS_PER_TILE);
+    issue_parts(kp, nullptr, dst, dst, 0, LOADS_PER_TILE);
   };
-  auto tile_valid = [&](int t) -> int {
+  auto issue_v = [&](int t, char* dst) __attribute__((always_inline)) {
+    const char* kp;
+    const char* vp;
+    tile_src(t, kp, vp);
+    issue_parts(nullptr, vp, dst, dst, 0, LOADS_PER_TILE);
+  };
+  auto tile_valid = [&](int t) __attribute__((always_inline)) -> int {
     if (HI && t < n_local) return kKeyTile;
     const int64_t rem = a.M - static_cast<int64_t>(t - n_local) * kKeyTile;
     return rem < kKeyTile ? static_cast<int>(rem) : kKeyTile;
@@ -485,14 +496,14 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   f32x16 s0, s1;  // S^T of the current tile: lane = query ql; keys 8(r/4) + 4g + r%4 (+32)
 
   // K fragment for reduction step kk: keys ql (half 0) and 32 + ql (half 1)
-  auto k_frag = [&](const char* kb, int kk, int half) -> bf16x8 {
+  auto k_frag = [&](const char* kb, int kk, int half) __attribute__((always_inline)) -> bf16x8 {
     const int row = half * 32 + ql;
     return *reinterpret_cast<const bf16x8*>(kb + row * (D * 2) + (((2 * kk + g) ^ k_swizzle<D>(row)) << 4));
   };
   // S^T = K Q^T - m.  K fragments are read kQkAhead reduction steps ahead of their MFMAs;
   // the scheduling barriers keep the compiler from sinking each read next to its use,
   // which would expose the full LDS latency at every step.
-  auto qk = [&](const char* kb) {
+  auto qk = [&](const char* kb) __attribute__((always_inline)) {
     constexpr int KS = D / 16, AH = kQkAhead < KS ? kQkAhead : KS;
     bf16x8 f0[KS], f1[KS];
 #pragma unroll
@@ -517,7 +528,7 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
 
   // Raise the running max by delta (per lane): rescale O and l by alpha, shift the live
   // scores, and re-seed the QK^T accumulator start value.
-  auto rescale = [&](float delta, float alpha) {
+  auto rescale = [&](float delta, float alpha) __attribute__((always_inline)) {
     l_run *= alpha;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
@@ -533,7 +544,7 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
     for (int r = 0; r < 16; ++r) neg_m[r] = -m_run;
     asm volatile("" : "+v"(neg_m));
   };
-  auto row_max = [&]() -> float {
+  auto row_max = [&]() __attribute__((always_inline)) -> float {
     float m3[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -541,20 +552,19 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
                     fmaxf(fmaxf(s1[4 * i], s1[4 * i + 1]), fmaxf(s1[4 * i + 2], s1[4 * i + 3])));
     return max_with_partner32(fmaxf(fmaxf(m3[0], m3[1]), fmaxf(m3[2], m3[3])));
   };
-  // P = exp2(S) as bf16 B operands; returns this lane's partial row sum.  The sum is taken
-  // over the bf16-rounded P (two at a time with v_dot2_f32_bf16 against (1, 1)), so the
-  // normaliser counts exactly the weights that multiply V.
-  auto expo = [&](bf16x8 (&pf)[4]) -> float {
-    const bf16x2 one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  // P = exp2(S) as bf16 B operands; returns this lane's partial row sum.  The softmax uses
+  // only one- and two-operand VALU instructions (exp, add, cvt): on gfx950 these issue
+  // beside the SIMD partner's MFMAs, while three-operand ones (fma, dot2) mostly wait.
+  auto expo = [&](bf16x8 (&pf)[4]) __attribute__((always_inline)) -> float {
     float ps0 = 0.0f, ps1 = 0.0f;
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      const bf16x2 a = {static_cast<__bf16>(__builtin_amdgcn_exp2f(s0[r])),
-                        static_cast<__bf16>(__builtin_amdgcn_exp2f(s0[r + 1]))};
-      const bf16x2 c = {static_cast<__bf16>(__builtin_amdgcn_exp2f(s1[r])),
-                        static_cast<__bf16>(__builtin_amdgcn_exp2f(s1[r + 1]))};
-      ps0 = __builtin_amdgcn_fdot2_f32_bf16(a, one, ps0, false);
-      ps1 = __builtin_amdgcn_fdot2_f32_bf16(c, one, ps1, false);
+      const float e0 = __builtin_amdgcn_exp2f(s0[r]), e1 = __builtin_amdgcn_exp2f(s0[r + 1]);
+      const float e2 = __builtin_amdgcn_exp2f(s1[r]), e3 = __builtin_amdgcn_exp2f(s1[r + 1]);
+      const bf16x2 a = {static_cast<__bf16>(e0), static_cast<__bf16>(e1)};
+      const bf16x2 c = {static_cast<__bf16>(e2), static_cast<__bf16>(e3)};
+      ps0 += e0 + e1;
+      ps1 += e2 + e3;
       // key-step ks = 2*half + r/8; slot j = r % 8
       pf[r >> 3][r & 7] = a[0];
       pf[r >> 3][(r & 7) + 1] = a[1];
@@ -569,7 +579,7 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   // a lane's partial sum exceeds 2^20 (some score grew by more than ~2^15 over it, or
   // overflowed): then the maximum is raised, O and l rescaled, and P recomputed.  P stays
   // below 2^20, far inside fp32 and bf16 range.  Produces P^T as four bf16 B operands.
-  auto softmax = [&](int valid, bf16x8 (&pf)[4]) {
+  auto softmax = [&](int valid, bf16x8 (&pf)[4]) __attribute__((always_inline)) {
     if (valid < kKeyTile) {
       // key 8(r/4) + 4g + r%4 (+32) is past the end iff its g-free part reaches valid - 4g;
       // comparing against that compile-time part keeps 32 key indices out of registers
@@ -595,12 +605,12 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   };
 
   // V^T fragment for key-step ks, output dims 32 dt + ql
-  auto v_frag = [&](const char* vb, int ks, int dt) -> bf16x8 {
+  auto v_frag = [&](const char* vb, int ks, int dt) __attribute__((always_inline)) -> bf16x8 {
     const int vr = dt * 32 + ql;
     return *reinterpret_cast<const bf16x8*>(vb + vr * (kKeyTile * 2) + (((2 * ks + g) ^ v_swizzle(vr)) << 4));
   };
   // O^T += V^T P^T over 4 key-steps of 16 keys; V fragments are read kPvAhead MFMAs ahead
-  auto pv = [&](const char* vb, const bf16x8 (&pf)[4]) {
+  auto pv = [&](const char* vb, const bf16x8 (&pf)[4]) __attribute__((always_inline)) {
     constexpr int DT = D / 32, NI = 4 * DT, AH = kPvAhead < NI ? kPvAhead : NI;
     bf16x8 f[NI];
 #pragma unroll
@@ -614,54 +624,72 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  auto stage = [&](int i) -> char* {
+  auto stage = [&](int i) __attribute__((always_inline)) -> char* {
     return i == 0 ? stage0 : i == 1 ? stage1 : i == 2 ? stage2 : stage3;
   };
 
-  // prologue: tiles 0, 1, 2 in flight; 0 and 1 must land before the first iteration
-  issue_tile(0, stage0);
-  if (n_tiles > 1) issue_tile(1, stage1);
-  if (n_tiles > 2) {
-    issue_tile(2, stage2);
-    wait_vm_and_barrier<LOADS_PER_TILE>();
-  } else {
-    wait_vm_and_barrier<0>();
-  }
+  // Iteration t (one barrier each): wave A runs PV_{t-1}, QK^T_t, softmax_t and carries P_t
+  // to the next iteration; wave B runs softmax_t, PV_t, QK^T_{t+1} and carries S.  Each wave
+  // thus alternates one block of 32 MFMAs with one softmax, half an iteration apart from its
+  // SIMD partner, so one wave's softmax runs under the other wave's MFMAs.
+  // Iteration t reads K_t, K_{t+1}, V_{t-1}, V_t; it copies K_{t+3} into the K half of stage
+  // (t+3) % 4 (K_{t-1} was last read before the previous barrier) and V_{t+2} into the V
+  // half of stage (t+2) % 4 (V_{t-2} likewise), and at its barrier waits for the copies
+  // issued one iteration earlier (K_{t+2}, V_{t+1}).
+  // Prologue: K_0, V_0, K_1 must land before iteration 0; K_2 and V_1 stay in flight.
+  issue_k(0, stage0);
+  issue_v(0, stage0);
+  if (n_tiles > 1) issue_k(1, stage1);
+  if (n_tiles > 2) issue_k(2, stage2);
+  if (n_tiles > 1) issue_v(1, stage1);
+  if (n_tiles > 2) wait_vm_and_barrier<LOADS_PER_TILE>();
+  else if (n_tiles > 1) wait_vm_and_barrier<LOADS_PER_TILE / 2>();
+  else wait_vm_and_barrier<0>();
   if (wave_b) qk(stage0);
 
+  bf16x8 pa[4];  // wave A: P of the previous tile, consumed by the next iteration's PV
   // Tile t lives in stage t % 4; S is the (compile-time) stage of tile t.
-  auto step = [&]<int S>(int t) {
+  auto step = [&]<int S>(int t) __attribute__((always_inline)) {
     char* cur = stage(S);
     char* nxt = stage((S + 1) & 3);
-    // Stage (t+3) % 4 held tile t-1, whose last reads ended at the previous barrier.  Its
-    // DMA instructions are spread over the four gaps between phases: issued all at once,
-    // the eight waves' loads back up in the vector-memory path and stall every wave.
-    const bool more3 = t + 3 < n_tiles;
+    char* prv = stage((S + 3) & 3);
+    // The copies are spread over the four gaps between phases: issued all at once, the
+    // eight waves' loads back up in the vector-memory path and stall every wave.
+    const bool k3 = t + 3 < n_tiles, v2 = t + 2 < n_tiles;
     const char* kp = nullptr;
     const char* vp = nullptr;
-    char* dst = stage((S + 3) & 3);
-    if (more3) tile_src(t + 3, kp, vp);
-    auto dma_slot = [&](int slot) {
-      if (more3) issue_parts(kp, vp, dst, slot * LOADS_PER_TILE / 4, (slot + 1) * LOADS_PER_TILE / 4);
+    const char* unused;
+    if (k3) tile_src(t + 3, kp, unused);
+    if (v2) tile_src(t + 2, unused, vp);
+    char* kdst = stage((S + 3) & 3);
+    char* vdst = stage((S + 2) & 3);
+    auto dma_slot = [&](int slot) __attribute__((always_inline)) {
+      issue_parts(kp, vp, kdst, vdst, slot * LOADS_PER_TILE / 4, (slot + 1) * LOADS_PER_TILE / 4);
     };
-    bf16x8 pf[4];
+    // The wave in its MFMA block runs at raised issue priority, so the SIMD's arbiter keeps
+    // the matrix pipe fed and the partner's softmax fills the remaining issue cycles.
     dma_slot(0);
     if (!wave_b) {
-      qk(cur);
+      __builtin_amdgcn_s_setprio(1);
+      if (t > 0) pv(prv + TILE_BYTES, pa);
       dma_slot(1);
-      softmax(tile_valid(t), pf);
+      qk(cur);
+      __builtin_amdgcn_s_setprio(0);
       dma_slot(2);
-      pv(cur + TILE_BYTES, pf);
+      softmax(tile_valid(t), pa);
     } else {
+      bf16x8 pf[4];
       softmax(tile_valid(t), pf);
+      __builtin_amdgcn_s_setprio(1);
       dma_slot(1);
       pv(cur + TILE_BYTES, pf);
       dma_slot(2);
       if (t + 1 < n_tiles) qk(nxt);
+      __builtin_amdgcn_s_setprio(0);
     }
     dma_slot(3);
-    // tile t+2 must have landed before the next iteration reads it
-    if (more3) wait_vm_and_barrier<LOADS_PER_TILE>();
+    if (k3) wait_vm_and_barrier<LOADS_PER_TILE>();
+    else if (v2) wait_vm_and_barrier<LOADS_PER_TILE / 2>();
     else wait_vm_and_barrier<0>();
   };
   int t = 0;
@@ -674,6 +702,15 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   if (t < n_tiles) step.template operator()<0>(t);
   if (t + 1 < n_tiles) step.template operator()<1>(t + 1);
   if (t + 2 < n_tiles) step.template operator()<2>(t + 2);
+  // wave A's last PV (no copies are in flight any more)
+  if (!wave_b) {
+    switch ((n_tiles - 1) & 3) {
+      case 0: pv(stage0 + TILE_BYTES, pa); break;
+      case 1: pv(stage1 + TILE_BYTES, pa); break;
+      case 2: pv(stage2 + TILE_BYTES, pa); break;
+      default: pv(stage3 + TILE_BYTES, pa); break;
+    }
+  }
 
   // ---- epilogue: normalise and store (lane: query ql, dims dt*32 + 8*(r/4) + 4g + r%4)
   const float lt = sum_with_partner32(l_run);
