@@ -31,6 +31,7 @@ int launch_window_copy(const void* src, void* dst, int B, int H, int W, int w,
 
 constexpr int kKeyTile = 64;     // keys per K/V tile
 constexpr int kMaxQuery = 256;   // queries per workgroup (8 waves x 32)
+constexpr int kMaxLocalTiles = 1024;  // neighbour-window key tiles per query window
 
 // ------------------------------------------------------------------ geometry / layout
 
@@ -383,7 +384,7 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char stage1[2 * TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char stage2[2 * TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char stage3[2 * TILE_BYTES];
-  __shared__ int nbr_s[9];
+  __shared__ uint32_t tile_off_s[HI ? kMaxLocalTiles : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ql = lane & 31, g = lane >> 5;
@@ -393,14 +394,18 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   const int b = bh / a.heads, h = bh - b * a.heads;
   const int q0 = qb * (NWAVES * 32);
 
-  // Tile list: hi pass = neighbour windows (w2/64 tiles each), then guide tiles.  The
-  // window's neighbour list is staged in LDS once.
-  int n_local = 0, win = 0;
-  const int tiles_per_win = a.w2 / kKeyTile;
+  // Tile list: hi pass = neighbour windows (w2/64 tiles each), then guide tiles.  The byte
+  // offsets of the neighbour tiles (inside this (b, h)'s K and V^T buffers) are staged in
+  // LDS once, so that picking a tile costs one LDS read and the loop keeps few scalars live.
+  int n_local = 0;
   if (HI) {
-    win = q0 / a.w2;
+    const int tiles_per_win = a.w2 / kKeyTile;
+    const int win = q0 / a.w2;
     n_local = a.nbr_cnt[win] * tiles_per_win;
-    if (tid < 9) nbr_s[tid] = a.nbr[win * 9 + tid];
+    for (int i = tid; i < n_local; i += NT) {
+      const int j = i / tiles_per_win, sub = i - j * tiles_per_win;
+      tile_off_s[i] = static_cast<uint32_t>(a.nbr[win * 9 + j] * a.w2 + sub * kKeyTile) * (D * 2);
+    }
     __syncthreads();
   }
   const int n_tiles = n_local + static_cast<int>(a.Mk / kKeyTile);
@@ -415,21 +420,21 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
     const int vr = slot >> 3, vp = slot & 7;
     v_src[i] = vr * (kKeyTile * 2) + ((vp ^ v_swizzle(vr)) << 4);
   }
-  // global -> LDS stage buffer `dst` for tile t (asynchronous)
-  // Global sources of tile t (K tile, V^T tile).
+  // Global sources of tile t (K tile, V^T tile).  A V^T tile of 64 keys holds as many bytes
+  // as the K tile of the same keys, so one offset serves both.
+  const char* k_hi_b = reinterpret_cast<const char*>(a.k_hi) + static_cast<int64_t>(bh) * a.N * (D * 2);
+  const char* v_hi_b = reinterpret_cast<const char*>(a.v_hi) + static_cast<int64_t>(bh) * a.N * (D * 2);
+  const char* k_lr_b = reinterpret_cast<const char*>(a.k_lr) + static_cast<int64_t>(bh) * a.Mk * (D * 2);
+  const char* v_lr_b = reinterpret_cast<const char*>(a.v_lr) + static_cast<int64_t>(bh) * a.Mk * (D * 2);
   auto tile_src = [&](int t, const char*& kp, const char*& vp) __attribute__((always_inline)) {
     if (HI && t < n_local) {
-      const int j = t / tiles_per_win, sub = t - j * tiles_per_win;
-      const int nw = __builtin_amdgcn_readfirstlane(nbr_s[j]);
-      const int64_t krow = static_cast<int64_t>(nw) * a.w2 + sub * kKeyTile;
-      kp = reinterpret_cast<const char*>(a.k_hi + (bh * a.N + krow) * D);
-      vp = reinterpret_cast<const char*>(a.v_hi + (bh * (a.N / kKeyTile) + krow / kKeyTile) *
-                                                      static_cast<int64_t>(D) * kKeyTile);
+      const uint32_t off = __builtin_amdgcn_readfirstlane(tile_off_s[t]);
+      kp = k_hi_b + off;
+      vp = v_hi_b + off;
     } else {
-      const int j = t - n_local;
-      kp = reinterpret_cast<const char*>(a.k_lr + (bh * a.Mk + static_cast<int64_t>(j) * kKeyTile) * D);
-      vp = reinterpret_cast<const char*>(a.v_lr + (bh * (a.Mk / kKeyTile) + j) *
-                                                      static_cast<int64_t>(D) * kKeyTile);
+      const uint32_t off = static_cast<uint32_t>(t - n_local) * TILE_BYTES;
+      kp = k_lr_b + off;
+      vp = v_lr_b + off;
     }
   };
   // DMA instructions [p0, p1) of this thread's share of one K tile and one V tile:
@@ -645,72 +650,69 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   if (n_tiles > 2) wait_vm_and_barrier<LOADS_PER_TILE>();
   else if (n_tiles > 1) wait_vm_and_barrier<LOADS_PER_TILE / 2>();
   else wait_vm_and_barrier<0>();
-  if (wave_b) qk(stage0);
-
   bf16x8 pa[4];  // wave A: P of the previous tile, consumed by the next iteration's PV
-  // Tile t lives in stage t % 4; S is the (compile-time) stage of tile t.
-  auto step = [&]<int S>(int t) __attribute__((always_inline)) {
-    char* cur = stage(S);
-    char* nxt = stage((S + 1) & 3);
-    char* prv = stage((S + 3) & 3);
-    // The copies are spread over the four gaps between phases: issued all at once, the
-    // eight waves' loads back up in the vector-memory path and stall every wave.
-    const bool k3 = t + 3 < n_tiles, v2 = t + 2 < n_tiles;
-    const char* kp = nullptr;
-    const char* vp = nullptr;
-    const char* unused;
-    if (k3) tile_src(t + 3, kp, unused);
-    if (v2) tile_src(t + 2, unused, vp);
-    char* kdst = stage((S + 3) & 3);
-    char* vdst = stage((S + 2) & 3);
-    auto dma_slot = [&](int slot) __attribute__((always_inline)) {
-      issue_parts(kp, vp, kdst, vdst, slot * LOADS_PER_TILE / 4, (slot + 1) * LOADS_PER_TILE / 4);
+  // One copy of the loop per role (B = wave B), so that neither carries the other's state.
+  auto run = [&]<bool B>() __attribute__((always_inline)) {
+    if (B) qk(stage0);
+    // Tile t lives in stage t % 4; S is the (compile-time) stage of tile t.
+    auto step = [&]<int S>(int t) __attribute__((always_inline)) {
+      char* cur = stage(S);
+      const bool k3 = t + 3 < n_tiles, v2 = t + 2 < n_tiles;
+      const char* kp = nullptr;
+      const char* vp = nullptr;
+      const char* unused;
+      if (k3) tile_src(t + 3, kp, unused);
+      if (v2) tile_src(t + 2, unused, vp);
+      char* kdst = stage((S + 3) & 3);
+      char* vdst = stage((S + 2) & 3);
+      auto dma_slot = [&](int slot) __attribute__((always_inline)) {
+        issue_parts(kp, vp, kdst, vdst, slot * LOADS_PER_TILE / 4, (slot + 1) * LOADS_PER_TILE / 4);
+      };
+      dma_slot(0);
+      if constexpr (!B) {
+        __builtin_amdgcn_s_setprio(1);
+        if (t > 0) pv(stage((S + 3) & 3) + TILE_BYTES, pa);
+        dma_slot(1);
+        qk(cur);
+        __builtin_amdgcn_s_setprio(0);
+        dma_slot(2);
+        softmax(tile_valid(t), pa);
+      } else {
+        bf16x8 pf[4];
+        softmax(tile_valid(t), pf);
+        __builtin_amdgcn_s_setprio(1);
+        dma_slot(1);
+        pv(cur + TILE_BYTES, pf);
+        dma_slot(2);
+        if (t + 1 < n_tiles) qk(stage((S + 1) & 3));
+        __builtin_amdgcn_s_setprio(0);
+      }
+      dma_slot(3);
+      if (k3) wait_vm_and_barrier<LOADS_PER_TILE>();
+      else if (v2) wait_vm_and_barrier<LOADS_PER_TILE / 2>();
+      else wait_vm_and_barrier<0>();
     };
-    // The wave in its MFMA block runs at raised issue priority, so the SIMD's arbiter keeps
-    // the matrix pipe fed and the partner's softmax fills the remaining issue cycles.
-    dma_slot(0);
-    if (!wave_b) {
-      __builtin_amdgcn_s_setprio(1);
-      if (t > 0) pv(prv + TILE_BYTES, pa);
-      dma_slot(1);
-      qk(cur);
-      __builtin_amdgcn_s_setprio(0);
-      dma_slot(2);
-      softmax(tile_valid(t), pa);
-    } else {
-      bf16x8 pf[4];
-      softmax(tile_valid(t), pf);
-      __builtin_amdgcn_s_setprio(1);
-      dma_slot(1);
-      pv(cur + TILE_BYTES, pf);
-      dma_slot(2);
-      if (t + 1 < n_tiles) qk(nxt);
-      __builtin_amdgcn_s_setprio(0);
+    int t = 0;
+    for (; t + 4 <= n_tiles; t += 4) {
+      step.template operator()<0>(t);
+      step.template operator()<1>(t + 1);
+      step.template operator()<2>(t + 2);
+      step.template operator()<3>(t + 3);
     }
-    dma_slot(3);
-    if (k3) wait_vm_and_barrier<LOADS_PER_TILE>();
-    else if (v2) wait_vm_and_barrier<LOADS_PER_TILE / 2>();
-    else wait_vm_and_barrier<0>();
+    if (t < n_tiles) step.template operator()<0>(t);
+    if (t + 1 < n_tiles) step.template operator()<1>(t + 1);
+    if (t + 2 < n_tiles) step.template operator()<2>(t + 2);
+    if (!B) {
+      switch ((n_tiles - 1) & 3) {
+        case 0: pv(stage0 + TILE_BYTES, pa); break;
+        case 1: pv(stage1 + TILE_BYTES, pa); break;
+        case 2: pv(stage2 + TILE_BYTES, pa); break;
+        default: pv(stage3 + TILE_BYTES, pa); break;
+      }
+    }
   };
-  int t = 0;
-  for (; t + 4 <= n_tiles; t += 4) {
-    step.template operator()<0>(t);
-    step.template operator()<1>(t + 1);
-    step.template operator()<2>(t + 2);
-    step.template operator()<3>(t + 3);
-  }
-  if (t < n_tiles) step.template operator()<0>(t);
-  if (t + 1 < n_tiles) step.template operator()<1>(t + 1);
-  if (t + 2 < n_tiles) step.template operator()<2>(t + 2);
-  // wave A's last PV (no copies are in flight any more)
-  if (!wave_b) {
-    switch ((n_tiles - 1) & 3) {
-      case 0: pv(stage0 + TILE_BYTES, pa); break;
-      case 1: pv(stage1 + TILE_BYTES, pa); break;
-      case 2: pv(stage2 + TILE_BYTES, pa); break;
-      default: pv(stage3 + TILE_BYTES, pa); break;
-    }
-  }
+  if (wave_b) run.template operator()<true>();
+  else run.template operator()<false>();
 
   // ---- epilogue: normalise and store (lane: query ql, dims dt*32 + 8*(r/4) + 4g + r%4)
   const float lt = sum_with_partner32(l_run);
@@ -763,6 +765,7 @@ static int validate_forward(const void* q, const void* k, const void* v, void* o
     return fail_arg("rho must be >= 1 with guide tokens");
   if (D != 64 && D != 128) return fail_unsupported("head_dim must be 64 or 128");
   if (w % 8 || (w > 16 && w % 16)) return fail_unsupported("window size must be 8, 16 or a multiple of 16");
+  if (9 * (w * w / kKeyTile) > kMaxLocalTiles) return fail_unsupported("window size above 80");
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
        reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o)) % 16)
     return fail_arg("tensors must be 16-byte aligned");

@@ -117,7 +117,7 @@ size_t uhla_forward_workspace_bytes(int B, int H, int W, int w, int H_lr, int W_
  * Errors: UHLA_ERR_ARG (null pointers, sizes < 1, w not dividing H or W, rho < 1 with
  * guide tokens, exactly one of H_lr/W_lr zero, O overlapping Q, K, V or the workspace);
  * UHLA_ERR_UNSUPPORTED (head_dim not in {64, 128}; w not a multiple of 8, or w > 16
- * and not a multiple of 16); UHLA_ERR_WORKSPACE; UHLA_ERR_HIP.
+ * and not a multiple of 16, or w > 80); UHLA_ERR_WORKSPACE; UHLA_ERR_HIP.
  */
 int uhla_forward(const void* q, const void* k, const void* v, void* o,
                  int B, int H, int W, int w, int H_lr, int W_lr, int rho,

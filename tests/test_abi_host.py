@@ -131,6 +131,7 @@ def fwd_args(**kw):
     (dict(d=32), api.UHLA_ERR_UNSUPPORTED),
     (dict(H=24, W=24, w=24), api.UHLA_ERR_UNSUPPORTED),
     (dict(H=36, W=36, w=4), api.UHLA_ERR_UNSUPPORTED),
+    (dict(H=96, W=96, w=96, H_lr=0, W_lr=0), api.UHLA_ERR_UNSUPPORTED),
     (dict(ws=NULL), api.UHLA_ERR_WORKSPACE),
     (dict(wsb=1000), api.UHLA_ERR_WORKSPACE),
     (dict(o=P), api.UHLA_ERR_ARG),  # aliases q
