@@ -12,9 +12,9 @@
 //      [D][64] so the P.V contraction reads it with one 16-byte LDS load per operand.
 //      Guide rows are rotated / re-laid out the same way (no permutation).
 //   3. hi pass: one workgroup per (b, h, window, 256-query chunk); it streams the K/V
-//      tiles of its neighbour windows, then of all guide tokens, through LDS.
+//      tiles of its neighbour windows, then of all guide tokens, through LDS, and stores
+//      each output row at its raster position (the inverse permutation, fused).
 //   4. guide pass: one workgroup per (b, h, 256 guide queries) over all guide keys.
-//   5. inverse permutation of the hi rows of O.
 //
 // MFMA formulation (v_mfma_f32_32x32x16_bf16, wave64).  Each wave owns 32 queries.
 // S^T = K Q^T: A = 32 keys x 16 dims from LDS, B = Q^T held in registers, so each lane
@@ -24,10 +24,6 @@
 #include "uhla_internal.h"
 
 namespace uhla {
-
-int launch_window_copy(const void* src, void* dst, int B, int H, int W, int w,
-                       int64_t row_bytes, int64_t src_tpb, int64_t dst_tpb, int inverse,
-                       hipStream_t stream);
 
 constexpr int kKeyTile = 64;     // keys per K/V tile
 constexpr int kMaxQuery = 256;   // queries per workgroup (8 waves x 32)
@@ -68,7 +64,6 @@ struct Workspace {
   bf16_t* q_lr;   // [B*heads][Mq][D]  rotated, zero padded
   bf16_t* k_lr;   // [B*heads][Mk][D]  rotated, zero padded
   bf16_t* v_lr;   // [B*heads][Mk/64][D][64]
-  bf16_t* o_hi;   // [B][N][heads][D]  window-first output
   size_t bytes;
 };
 
@@ -91,7 +86,6 @@ static Workspace carve(const Geom& g, void* base) {
   const size_t o_ql = take(bh * g.Mq * g.D * e);
   const size_t o_kl = take(bh * g.Mk * g.D * e);
   const size_t o_vl = take(bh * g.Mk * g.D * e);
-  const size_t o_oh = take(bh * g.N * g.D * e);
   char* b = static_cast<char*>(base);
   ws.nbr = reinterpret_cast<int*>(b + o_nbr);
   ws.nbr_cnt = reinterpret_cast<int*>(b + o_cnt);
@@ -102,7 +96,6 @@ static Workspace carve(const Geom& g, void* base) {
   ws.q_lr = reinterpret_cast<bf16_t*>(b + o_ql);
   ws.k_lr = reinterpret_cast<bf16_t*>(b + o_kl);
   ws.v_lr = reinterpret_cast<bf16_t*>(b + o_vl);
-  ws.o_hi = reinterpret_cast<bf16_t*>(b + o_oh);
   ws.bytes = off;
   return ws;
 }
@@ -292,6 +285,7 @@ struct AttnArgs {
   int64_t out_row0;       // first row of this pass inside a batch of out
   int64_t N, M, Mk;
   int heads, w2, hi;      // hi = 1: hi pass (local + guide keys), 0: guide pass
+  int W, w, n_wx;         // hi pass: query row p (window-first) is written to raster row r(p)
   int q_valid;            // valid query rows per (b, h)
   int blocks_per_bh;
   int total_blocks;
@@ -719,7 +713,10 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   const float inv = 1.0f / lt;
   const int qrow = q0 + wave * 32 + ql;
   if (qrow < a.q_valid) {
-    bf16_t* orow = a.out + ((static_cast<int64_t>(b) * a.out_rows + a.out_row0 + qrow) * a.heads + h) * D;
+    // The hi pass undoes the window-first permutation here: window-first row qrow goes to
+    // its raster row, so O needs no separate inverse-permutation pass.
+    const int orow_idx = HI ? window_first_to_raster(qrow, a.W, a.w, a.n_wx) : qrow;
+    bf16_t* orow = a.out + ((static_cast<int64_t>(b) * a.out_rows + a.out_row0 + orow_idx) * a.heads + h) * D;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -858,7 +855,8 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
     const int qt = nwaves * 32;
     AttnArgs h = a;
     h.q = ws.q_hi; h.q_rows = g.N;
-    h.out = ws.o_hi; h.out_rows = g.N; h.out_row0 = 0;
+    h.out = static_cast<bf16_t*>(o); h.out_rows = L; h.out_row0 = 0;
+    h.W = W; h.w = w; h.n_wx = g.n_wx;
     h.hi = 1; h.q_valid = static_cast<int>(g.N);
     h.blocks_per_bh = static_cast<int>(g.N / qt);
     h.total_blocks = static_cast<int>(static_cast<int64_t>(B) * heads * h.blocks_per_bh);
@@ -880,9 +878,8 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
   if (timer) timer_end(timer, UHLA_STAGE_ATTN_LR, s);
 
   // 5. inverse permutation of the hi rows of O
+  // 5. the inverse permutation of O is fused into the hi pass's stores (stage left empty)
   if (timer) timer_begin(timer, UHLA_STAGE_UNPERMUTE, s);
-  st = launch_window_copy(ws.o_hi, o, B, H, W, w, static_cast<int64_t>(heads) * D * 2, g.N, L, 1, s);
-  if (st) return st;
   if (timer) timer_end(timer, UHLA_STAGE_UNPERMUTE, s);
 #undef UHLA_STEP
   if (timer) return timer_commit(timer);

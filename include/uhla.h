@@ -109,7 +109,8 @@ size_t uhla_forward_workspace_bytes(int B, int H, int W, int w, int H_lr, int W_
  * Steps: block-neighbour table; window-first permutation of the hi segment of Q, K, V
  * fused with RoPE (guide rows rotated in place of permuting); block-sparse attention of
  * each window over its neighbour windows and the guide tokens (bf16 MFMA, fp32
- * accumulation and softmax); guide-only attention; inverse permutation of the output.
+ * accumulation and softmax) whose stores put each output row back at its raster
+ * position (the inverse permutation, fused); guide-only attention.
  * scale <= 0 selects 1/sqrt(head_dim); theta <= 0 switches RoPE off; H_lr = W_lr = 0
  * means no guide tokens.  Deterministic: no atomics, fixed reduction order.
  * workspace: device memory of at least uhla_forward_workspace_bytes(...) bytes, 256-byte
@@ -146,7 +147,7 @@ typedef enum {
   UHLA_STAGE_PREP_LR = 2,   /* guide-token RoPE / V re-layout */
   UHLA_STAGE_ATTN_HI = 3,   /* hi-res block-sparse attention */
   UHLA_STAGE_ATTN_LR = 4,   /* guide-only attention */
-  UHLA_STAGE_UNPERMUTE = 5, /* inverse permutation of O */
+  UHLA_STAGE_UNPERMUTE = 5, /* inverse permutation of O (fused into the hi pass: empty) */
   UHLA_NUM_STAGES = 6
 } uhla_stage;
 

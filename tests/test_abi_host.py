@@ -159,7 +159,7 @@ def expected_workspace(B, H, W, w, H_lr, W_lr, heads, d):
     nW = (H // w) * (W // w)
     e, bh = 2, B * heads
     parts = [4 * nW * 9, 4 * nW, 16 * max(H, W) * (d // 4), bh * N * d * e, bh * N * d * e,
-             bh * N * d * e, bh * Mq * d * e, bh * Mk * d * e, bh * Mk * d * e, bh * N * d * e]
+             bh * N * d * e, bh * Mq * d * e, bh * Mk * d * e, bh * Mk * d * e]
     return sum(al(p) for p in parts)
 
 
