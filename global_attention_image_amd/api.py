@@ -27,6 +27,10 @@ EXPORTS = {
     "uhla_forward": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_int] * 9
                      + [ctypes.c_float, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t,
                         ctypes.c_void_p]),
+    "uhla_forward_masked_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 11),
+    "uhla_forward_masked": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_int] * 9
+                            + [ctypes.c_float, ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                               ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "uhla_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "uhla_last_error_detail": (ctypes.c_char_p, []),
     "uhla_timer_create": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_void_p)]),
@@ -142,9 +146,20 @@ def forward_workspace_bytes(B, H, W, w, H_lr, W_lr, heads, head_dim) -> int:
     return int(load().uhla_forward_workspace_bytes(B, H, W, w, H_lr, W_lr, heads, head_dim))
 
 
-def alloc_workspace(B, H, W, w, H_lr, W_lr, heads, head_dim, device="cuda"):
+def forward_masked_workspace_bytes(B, H, W, w, H_lr, W_lr, rho, heads, head_dim, radius,
+                                   guide_mode) -> int:
+    return int(load().uhla_forward_masked_workspace_bytes(B, H, W, w, H_lr, W_lr, rho, heads,
+                                                          head_dim, radius, guide_mode))
+
+
+def alloc_workspace(B, H, W, w, H_lr, W_lr, heads, head_dim, device="cuda", rho=4, radius=1,
+                    guide_mode=0):
     import torch
-    n = forward_workspace_bytes(B, H, W, w, H_lr, W_lr, heads, head_dim)
+    if radius == 1 and guide_mode == 0:
+        n = forward_workspace_bytes(B, H, W, w, H_lr, W_lr, heads, head_dim)
+    else:
+        n = forward_masked_workspace_bytes(B, H, W, w, H_lr, W_lr, rho, heads, head_dim, radius,
+                                           guide_mode)
     if n == 0:
         raise ValueError("invalid geometry")
     return torch.empty(n, dtype=torch.uint8, device=device)
@@ -180,8 +195,11 @@ class Timer:
 
 
 def forward(q, k, v, H, W, w, H_lr, W_lr, rho=4, scale=0.0, theta=10000.0, out=None,
-            workspace=None, timer: Timer | None = None):
-    """Hierarchical local attention forward on bf16 [B, H*W + H_lr*W_lr, heads, d] tensors."""
+            workspace=None, timer: Timer | None = None, radius=1, guide_mode=0):
+    """Hierarchical local attention forward on bf16 [B, H*W + H_lr*W_lr, heads, d] tensors.
+
+    radius / guide_mode select the mask variants of uhla_forward_masked; the defaults are
+    the mask of uhla_forward, which is the entry point called for them."""
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _require(t, n, torch.bfloat16)
@@ -194,13 +212,21 @@ def forward(q, k, v, H, W, w, H_lr, W_lr, rho=4, scale=0.0, theta=10000.0, out=N
         out = torch.empty_like(q)
     _require(out, "out", torch.bfloat16)
     if workspace is None:
-        workspace = alloc_workspace(B, H, W, w, H_lr, W_lr, Hh, d, q.device)
+        workspace = alloc_workspace(B, H, W, w, H_lr, W_lr, Hh, d, q.device, rho=rho,
+                                    radius=radius, guide_mode=guide_mode)
     lib = load()
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, W, w, H_lr, W_lr, rho, Hh, d,
-            float(scale), float(theta), _ptr(workspace), workspace.numel(), _stream(q))
+            float(scale), float(theta))
+    tail = (_ptr(workspace), workspace.numel(), _stream(q))
+    if radius != 1 or guide_mode != 0:
+        if timer is not None:
+            raise ValueError("stage timing covers the default mask only")
+        st = lib.uhla_forward_masked(*args, int(radius), int(guide_mode), *tail)
+        _check(st, "uhla_forward_masked")
+        return out
     if timer is None:
-        st = lib.uhla_forward(*args)
+        st = lib.uhla_forward(*args, *tail)
     else:
-        st = lib.uhla_forward_timed(*args, timer.h)
+        st = lib.uhla_forward_timed(*args, *tail, timer.h)
     _check(st, "uhla_forward")
     return out

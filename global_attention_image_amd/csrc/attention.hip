@@ -21,27 +21,32 @@
 // holds the scores of ONE query (lane & 31) for 16 keys: softmax statistics stay in the
 // lane, plus one exchange with lane ^ 32 (v_permlane32_swap).  O^T = V^T P^T: A = V^T (32 dims x 16 keys)
 // from LDS, B = P^T, which is the S^T accumulator converted to bf16 in place.
+#include <algorithm>
+
 #include "uhla_internal.h"
 
 namespace uhla {
 
 constexpr int kKeyTile = 64;     // keys per K/V tile
 constexpr int kMaxQuery = 256;   // queries per workgroup (8 waves x 32)
-constexpr int kMaxLocalTiles = 1024;  // neighbour-window key tiles per query window
+constexpr int kMaxTableTiles = 1024;  // table-driven key tiles (neighbour + cell-block) per window
 
 // ------------------------------------------------------------------ geometry / layout
 
 struct Geom {
   int B, H, W, w, H_lr, W_lr, rho, heads, D;
-  int64_t N, M, Mk, Mq;  // Mk: guide rows padded to the key tile; Mq: to the query block
-  int n_wx, n_wy, nW, P;  // P: positions covered by the cos/sin table (max(H, W))
+  int radius, guide_mode;  // neighbourhood radius in windows; guide tokens seen (0 all, 1, 2)
+  int64_t N, M, Mk, Mq;    // Mk: guide rows padded to the key tile; Mq: to the query block
+  int n_wx, n_wy, nW, P;   // P: positions covered by the cos/sin table (max(H, W))
+  int nbi, nbj;            // guide grid in 8x8 cell blocks (rows, columns)
+  int64_t Mb;              // guide cells in block order, padded: nbi * nbj * 64 (0 if unused)
 };
 
 static Geom make_geom(int B, int H, int W, int w, int H_lr, int W_lr, int rho, int heads,
-                      int D) {
+                      int D, int radius, int guide_mode) {
   Geom g;
   g.B = B; g.H = H; g.W = W; g.w = w; g.H_lr = H_lr; g.W_lr = W_lr; g.rho = rho;
-  g.heads = heads; g.D = D;
+  g.heads = heads; g.D = D; g.radius = radius; g.guide_mode = guide_mode;
   g.N = static_cast<int64_t>(H) * W;
   g.M = static_cast<int64_t>(H_lr) * W_lr;
   g.Mk = (g.M + kKeyTile - 1) / kKeyTile * kKeyTile;
@@ -51,12 +56,13 @@ static Geom make_geom(int B, int H, int W, int w, int H_lr, int W_lr, int rho, i
   // reaching past the hi-res extent) are evaluated directly with the same function.
   const int p = H > W ? H : W;
   g.P = p;
+  g.nbi = (H_lr + 7) / 8;
+  g.nbj = (W_lr + 7) / 8;
+  g.Mb = (guide_mode != 0 && g.M > 0) ? static_cast<int64_t>(g.nbi) * g.nbj * kKeyTile : 0;
   return g;
 }
 
 struct Workspace {
-  int* nbr;       // [nW][9]
-  int* nbr_cnt;   // [nW]
   double2* cs;    // [P][D/4]
   bf16_t* q_hi;   // [B*heads][N][D]   window-first, rotated
   bf16_t* k_hi;   // [B*heads][N][D]   window-first, rotated
@@ -64,6 +70,8 @@ struct Workspace {
   bf16_t* q_lr;   // [B*heads][Mq][D]  rotated, zero padded
   bf16_t* k_lr;   // [B*heads][Mk][D]  rotated, zero padded
   bf16_t* v_lr;   // [B*heads][Mk/64][D][64]
+  bf16_t* k_gb;   // [B*heads][Mb][D]  guide K in 8x8 cell blocks (guide modes 1, 2)
+  bf16_t* v_gb;   // [B*heads][Mb/64][D][64]
   size_t bytes;
 };
 
@@ -77,8 +85,6 @@ static Workspace carve(const Geom& g, void* base) {
   };
   const size_t bh = static_cast<size_t>(g.B) * g.heads;
   const size_t e = sizeof(bf16_t);
-  const size_t o_nbr = take(sizeof(int) * g.nW * 9);
-  const size_t o_cnt = take(sizeof(int) * g.nW);
   const size_t o_cs = take(sizeof(double2) * g.P * (g.D / 4));
   const size_t o_qh = take(bh * g.N * g.D * e);
   const size_t o_kh = take(bh * g.N * g.D * e);
@@ -86,9 +92,9 @@ static Workspace carve(const Geom& g, void* base) {
   const size_t o_ql = take(bh * g.Mq * g.D * e);
   const size_t o_kl = take(bh * g.Mk * g.D * e);
   const size_t o_vl = take(bh * g.Mk * g.D * e);
+  const size_t o_kb = take(bh * g.Mb * g.D * e);
+  const size_t o_vb = take(bh * g.Mb * g.D * e);
   char* b = static_cast<char*>(base);
-  ws.nbr = reinterpret_cast<int*>(b + o_nbr);
-  ws.nbr_cnt = reinterpret_cast<int*>(b + o_cnt);
   ws.cs = reinterpret_cast<double2*>(b + o_cs);
   ws.q_hi = reinterpret_cast<bf16_t*>(b + o_qh);
   ws.k_hi = reinterpret_cast<bf16_t*>(b + o_kh);
@@ -96,26 +102,22 @@ static Workspace carve(const Geom& g, void* base) {
   ws.q_lr = reinterpret_cast<bf16_t*>(b + o_ql);
   ws.k_lr = reinterpret_cast<bf16_t*>(b + o_kl);
   ws.v_lr = reinterpret_cast<bf16_t*>(b + o_vl);
+  ws.k_gb = reinterpret_cast<bf16_t*>(b + o_kb);
+  ws.v_gb = reinterpret_cast<bf16_t*>(b + o_vb);
   ws.bytes = off;
   return ws;
 }
 
-// ------------------------------------------------------------------ step 1: tables
-
-// Clipped 3x3 neighbourhood of each window, row-major (dy outer, dx inner), self included.
-__global__ void neighbour_table_kernel(int n_wy, int n_wx, int* nbr, int* cnt) {
-  const int win = blockIdx.x * blockDim.x + threadIdx.x;
-  if (win >= n_wy * n_wx) return;
-  const int wy = win / n_wx, wx = win - wy * n_wx;
-  int c = 0;
-  for (int dy = -1; dy <= 1; ++dy)
-    for (int dx = -1; dx <= 1; ++dx) {
-      const int y = wy + dy, x = wx + dx;
-      if (y >= 0 && y < n_wy && x >= 0 && x < n_wx) nbr[win * 9 + c++] = y * n_wx + x;
-    }
-  for (int j = c; j < 9; ++j) nbr[win * 9 + j] = -1;
-  cnt[win] = c;
+// Guide cell of slot `slot` in block order: block slot/64 = (BI, BJ) row-major over an
+// nbj-wide block grid, cell (8 BI + k/8, 8 BJ + k%8) with k = slot % 64.
+__device__ __forceinline__ void block_cell(int64_t slot, int nbj, int& i, int& j) {
+  const int blk = static_cast<int>(slot / kKeyTile), k = static_cast<int>(slot % kKeyTile);
+  const int bi = blk / nbj, bj = blk - bi * nbj;
+  i = 8 * bi + (k >> 3);
+  j = 8 * bj + (k & 7);
 }
+
+// ------------------------------------------------------------------ step 1: tables
 
 __global__ void cos_sin_table_kernel(double2* cs, int P, int D, double log2_theta) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -131,17 +133,20 @@ constexpr int kPrepThreads = 256;
 constexpr int kPrepRows = 4;
 
 // Q and K rows -> head-major, rotated.  Rows [0, N) of each batch are hi-res rows in
-// window-first order (source row r(p)), rows [N, N + rows_lr) are guide rows (source row
-// N + s, zero beyond M).  Q guide rows pad to Mq, K guide rows to Mk.  Q is also
+// window-first order (source row r(p)), rows [N, N + Mq) are guide rows (source row
+// N + s, zero beyond M); Q guide rows pad to Mq, K guide rows to Mk.  Rows
+// [N + Mq, N + Mq + Mb) are a second copy of the guide K rows in 8x8 cell-block order
+// (zero for cells outside the guide grid), used by the guide-locality masks.  Q is also
 // multiplied by q_scale (the softmax scale times log2 e) before its single rounding to
 // bf16, so the attention kernel's scores come out in base-2 logits.
 __global__ __launch_bounds__(kPrepThreads) void prep_qk_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, bf16_t* q_hi, bf16_t* k_hi,
-    bf16_t* q_lr, bf16_t* k_lr, const double2* __restrict__ cs, int P, double log2_theta,
-    int64_t N, int64_t M, int64_t Mq, int64_t Mk, int W, int w, int n_wx, int W_lr, int rho,
-    int heads, int D, int rope_on, double q_scale) {
+    bf16_t* q_lr, bf16_t* k_lr, bf16_t* k_gb, const double2* __restrict__ cs, int P,
+    double log2_theta, int64_t N, int64_t M, int64_t Mq, int64_t Mk, int64_t Mb, int W, int w,
+    int n_wx, int H_lr, int W_lr, int nbj, int rho, int heads, int D, int rope_on,
+    double q_scale) {
   const int64_t L = N + M;
-  const int64_t rows_total = N + Mq;
+  const int64_t rows_total = N + Mq + Mb;
   const int64_t b = blockIdx.y;
   const int chunks_per_head = D / 8;
   const int chunks_per_row = heads * chunks_per_head;
@@ -164,7 +169,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_qk_kernel(
       const int64_t o = ((b * heads + h) * N + row) * D + j * 8;
       dq = q_hi + o;
       dk = k_hi + o;
-    } else {
+    } else if (row < N + Mq) {
       const int64_t s = row - N;
       valid = s < M;
       src_row = N + s;
@@ -173,6 +178,16 @@ __global__ __launch_bounds__(kPrepThreads) void prep_qk_kernel(
       px = valid ? rho * static_cast<int>(s - static_cast<int64_t>(sy) * W_lr) : 0;
       dq = q_lr + ((b * heads + h) * Mq + s) * D + j * 8;
       dk = (s < Mk) ? k_lr + ((b * heads + h) * Mk + s) * D + j * 8 : nullptr;
+    } else {
+      const int64_t slot = row - N - Mq;
+      int ci, cj;
+      block_cell(slot, nbj, ci, cj);
+      valid = ci < H_lr && cj < W_lr;
+      src_row = valid ? N + static_cast<int64_t>(ci) * W_lr + cj : 0;
+      py = rho * ci;
+      px = rho * cj;
+      dq = nullptr;
+      dk = k_gb + ((b * heads + h) * Mb + slot) * D + j * 8;
     }
     uint4 qo = make_uint4(0, 0, 0, 0), ko = make_uint4(0, 0, 0, 0);
     if (valid) {
@@ -199,7 +214,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_qk_kernel(
         ko = ki;
       }
     }
-    *reinterpret_cast<uint4*>(dq) = qo;
+    if (dq) *reinterpret_cast<uint4*>(dq) = qo;
     if (dk) *reinterpret_cast<uint4*>(dk) = ko;
   }
 }
@@ -212,10 +227,12 @@ __device__ __forceinline__ int v_slot(int kappa) {
 }
 
 // V rows -> 64-key tiles transposed to [D][64] (key order by v_slot).  Tile index
-// t < N/64 covers window-first hi rows [64 t, 64 t + 64); tiles beyond cover guide rows.
+// t < N/64 covers window-first hi rows [64 t, 64 t + 64); the next Mk/64 tiles cover guide
+// rows in raster order, and the last Mb/64 tiles the guide cells in 8x8 block order.
 __global__ __launch_bounds__(kPrepThreads) void prep_v_kernel(
-    const bf16_t* __restrict__ v, bf16_t* v_hi, bf16_t* v_lr, int64_t N, int64_t M, int64_t Mk,
-    int W, int w, int n_wx, int heads, int D) {
+    const bf16_t* __restrict__ v, bf16_t* v_hi, bf16_t* v_lr, bf16_t* v_gb, int64_t N,
+    int64_t M, int64_t Mk, int64_t Mb, int W, int w, int n_wx, int H_lr, int W_lr, int nbj,
+    int heads, int D) {
   __shared__ bf16_t tile[kKeyTile][128 + 2];
   const int64_t L = N + M;
   const int64_t b = blockIdx.y;
@@ -230,10 +247,15 @@ __global__ __launch_bounds__(kPrepThreads) void prep_v_kernel(
       bool valid = true;
       if (tile_id < n_hi_tiles) {
         src_row = window_first_to_raster(static_cast<int>(tile_id * kKeyTile + kr), W, w, n_wx);
-      } else {
+      } else if (tile_id < n_hi_tiles + Mk / kKeyTile) {
         const int64_t s = (tile_id - n_hi_tiles) * kKeyTile + kr;
         valid = s < M;
         src_row = N + s;
+      } else {
+        int ci, cj;
+        block_cell((tile_id - n_hi_tiles - Mk / kKeyTile) * kKeyTile + kr, nbj, ci, cj);
+        valid = ci < H_lr && cj < W_lr;
+        src_row = valid ? N + static_cast<int64_t>(ci) * W_lr + cj : 0;
       }
       uint4 x = make_uint4(0, 0, 0, 0);
       if (valid) x = *reinterpret_cast<const uint4*>(v + ((b * L + src_row) * heads + h) * D + j * 8);
@@ -249,8 +271,11 @@ __global__ __launch_bounds__(kPrepThreads) void prep_v_kernel(
     bf16_t* dst;
     if (tile_id < n_hi_tiles)
       dst = v_hi + ((b * heads + h) * n_hi_tiles + tile_id) * static_cast<int64_t>(D) * kKeyTile;
-    else
+    else if (tile_id < n_hi_tiles + Mk / kKeyTile)
       dst = v_lr + ((b * heads + h) * (Mk / kKeyTile) + (tile_id - n_hi_tiles)) *
+                       static_cast<int64_t>(D) * kKeyTile;
+    else
+      dst = v_gb + ((b * heads + h) * (Mb / kKeyTile) + (tile_id - n_hi_tiles - Mk / kKeyTile)) *
                        static_cast<int64_t>(D) * kKeyTile;
     for (int i = threadIdx.x; i < D * (kKeyTile / 8); i += kPrepThreads) {
       const int d = i / (kKeyTile / 8), s8 = (i - d * (kKeyTile / 8)) * 8;
@@ -276,20 +301,21 @@ struct AttnArgs {
   int64_t q_rows;         // rows per (b, h) of q
   const bf16_t* k_hi;     // [B*heads][N][D]
   const bf16_t* v_hi;     // [B*heads][N/64][D][64]
-  const bf16_t* k_lr;     // [B*heads][Mk][D]
-  const bf16_t* v_lr;     // [B*heads][Mk/64][D][64]
-  const int* nbr;         // [nW][9]
-  const int* nbr_cnt;     // [nW]
+  const bf16_t* k_lr;     // [B*heads][Mk][D]        guide K (cell-block copy with RECT)
+  const bf16_t* v_lr;     // [B*heads][Mk/64][D][64] guide V^T (likewise)
   bf16_t* out;            // token-major [B][out_rows][heads][D]
   int64_t out_rows;       // rows per batch of out
   int64_t out_row0;       // first row of this pass inside a batch of out
   int64_t N, M, Mk;
   int heads, w2, hi;      // hi = 1: hi pass (local + guide keys), 0: guide pass
-  int W, w, n_wx;         // hi pass: query row p (window-first) is written to raster row r(p)
+  int W, w, n_wx, n_wy;   // hi pass: query row p (window-first) is written to raster row r(p)
+  int radius;             // hi pass: windows within this distance (per axis) are visible
+  int reach;              // RECT: the guide cells whose scaled position lies within `reach`
+                          // windows of the query window are visible
+  int rho, H_lr, W_lr, nbj;
   int q_valid;            // valid query rows per (b, h)
   int blocks_per_bh;
   int total_blocks;
-  float rescale_thr;      // lazy-rescale threshold in base-2 logit units
 };
 
 // Workgroups are dealt round-robin to the 8 XCDs; remap so that each XCD works on a
@@ -362,7 +388,7 @@ __device__ __forceinline__ void wait_vm_and_barrier() {
 // a load writes LDS bytes [16 l, 16 l + 16) above the wave's base), two iterations ahead of
 // their first use.  Each lane picks the global 16-byte chunk that belongs at its LDS slot
 // under the XOR swizzle, so the LDS layout is the one the fragment reads expect.
-template <int D, int NWAVES, bool HI>
+template <int D, int NWAVES, bool HI, bool RECT>
 __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   constexpr int NT = NWAVES * 64;
   constexpr int TILE_BYTES = kKeyTile * D * 2;       // one K or V tile
@@ -378,7 +404,8 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char stage1[2 * TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char stage2[2 * TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char stage3[2 * TILE_BYTES];
-  __shared__ uint32_t tile_off_s[HI ? kMaxLocalTiles : 1];
+  __shared__ uint32_t tile_off_s[HI ? kMaxTableTiles : 1];
+  __shared__ uint32_t tile_mask_s[RECT ? kMaxTableTiles : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ql = lane & 31, g = lane >> 5;
@@ -388,21 +415,52 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   const int b = bh / a.heads, h = bh - b * a.heads;
   const int q0 = qb * (NWAVES * 32);
 
-  // Tile list: hi pass = neighbour windows (w2/64 tiles each), then guide tiles.  The byte
-  // offsets of the neighbour tiles (inside this (b, h)'s K and V^T buffers) are staged in
-  // LDS once, so that picking a tile costs one LDS read and the loop keeps few scalars live.
-  int n_local = 0;
+  // Tile list.  Hi pass: the key tiles (w2/64 each) of the windows within `radius` of the
+  // query window, clipped to the grid, row-major; then the guide tiles: all of them in
+  // raster order, or (rect) the 8x8 cell blocks that meet the window's guide rectangle,
+  // each with a row/column mask.  Byte offsets of the table-driven tiles are staged in LDS
+  // once, so that picking a tile costs one LDS read and the loop keeps few scalars live.
+  int n_local = 0, n_guide = static_cast<int>(a.Mk / kKeyTile);
   if (HI) {
     const int tiles_per_win = a.w2 / kKeyTile;
     const int win = q0 / a.w2;
-    n_local = a.nbr_cnt[win] * tiles_per_win;
+    const int wy = win / a.n_wx, wx = win - wy * a.n_wx;
+    const int y0 = max(0, wy - a.radius), y1 = min(a.n_wy - 1, wy + a.radius);
+    const int x0 = max(0, wx - a.radius), x1 = min(a.n_wx - 1, wx + a.radius);
+    const int nx = x1 - x0 + 1;
+    n_local = (y1 - y0 + 1) * nx * tiles_per_win;
     for (int i = tid; i < n_local; i += NT) {
       const int j = i / tiles_per_win, sub = i - j * tiles_per_win;
-      tile_off_s[i] = static_cast<uint32_t>(a.nbr[win * 9 + j] * a.w2 + sub * kKeyTile) * (D * 2);
+      const int jy = j / nx, nw = (y0 + jy) * a.n_wx + x0 + (j - jy * nx);
+      tile_off_s[i] = static_cast<uint32_t>(nw * a.w2 + sub * kKeyTile) * (D * 2);
+    }
+    if (RECT) {
+      // guide cells (i, j) whose scaled position (rho i, rho j) lies in the windows within
+      // `reach` of the query window: i in [ceil(gy0 w / rho), ceil((gy1 + 1) w / rho))
+      const int gy0 = max(0, wy - a.reach), gy1 = min(a.n_wy - 1, wy + a.reach);
+      const int gx0 = max(0, wx - a.reach), gx1 = min(a.n_wx - 1, wx + a.reach);
+      const int i0 = (gy0 * a.w + a.rho - 1) / a.rho, i1 = min(a.H_lr, ((gy1 + 1) * a.w + a.rho - 1) / a.rho);
+      const int j0 = (gx0 * a.w + a.rho - 1) / a.rho, j1 = min(a.W_lr, ((gx1 + 1) * a.w + a.rho - 1) / a.rho);
+      int ng = 0;
+      if (i0 < i1 && j0 < j1) {
+        const int bi0 = i0 >> 3, bj0 = j0 >> 3, nbx = ((j1 - 1) >> 3) - bj0 + 1;
+        ng = (((i1 - 1) >> 3) - bi0 + 1) * nbx;
+        for (int k = tid; k < ng; k += NT) {
+          const int ky = k / nbx, bi = bi0 + ky, bj = bj0 + (k - ky * nbx);
+          uint32_t rows = 0, cols = 0;
+          for (int e = 0; e < 8; ++e) {
+            rows |= static_cast<uint32_t>(8 * bi + e >= i0 && 8 * bi + e < i1) << e;
+            cols |= static_cast<uint32_t>(8 * bj + e >= j0 && 8 * bj + e < j1) << e;
+          }
+          tile_off_s[n_local + k] = static_cast<uint32_t>(bi * a.nbj + bj) * TILE_BYTES;
+          tile_mask_s[n_local + k] = rows | (cols << 8);
+        }
+      }
+      n_guide = ng;
     }
     __syncthreads();
   }
-  const int n_tiles = n_local + static_cast<int>(a.Mk / kKeyTile);
+  const int n_tiles = n_local + n_guide;
 
   // Per-lane source offsets (bytes inside a tile) for this thread's DMA slots.
   int k_src[CPT], v_src[CPT];
@@ -420,11 +478,16 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   const char* v_hi_b = reinterpret_cast<const char*>(a.v_hi) + static_cast<int64_t>(bh) * a.N * (D * 2);
   const char* k_lr_b = reinterpret_cast<const char*>(a.k_lr) + static_cast<int64_t>(bh) * a.Mk * (D * 2);
   const char* v_lr_b = reinterpret_cast<const char*>(a.v_lr) + static_cast<int64_t>(bh) * a.Mk * (D * 2);
+  // (with RECT, k_lr / v_lr / Mk describe the cell-block copy of the guide K / V^T)
   auto tile_src = [&](int t, const char*& kp, const char*& vp) __attribute__((always_inline)) {
     if (HI && t < n_local) {
       const uint32_t off = __builtin_amdgcn_readfirstlane(tile_off_s[t]);
       kp = k_hi_b + off;
       vp = v_hi_b + off;
+    } else if (RECT) {
+      const uint32_t off = __builtin_amdgcn_readfirstlane(tile_off_s[t]);
+      kp = k_lr_b + off;
+      vp = v_lr_b + off;
     } else {
       const uint32_t off = static_cast<uint32_t>(t - n_local) * TILE_BYTES;
       kp = k_lr_b + off;
@@ -460,10 +523,17 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
     tile_src(t, kp, vp);
     issue_parts(nullptr, vp, dst, dst, 0, LOADS_PER_TILE);
   };
+  // Keys of tile t that exist (a prefix; the raster guide list ends in a partial tile) ...
   auto tile_valid = [&](int t) __attribute__((always_inline)) -> int {
-    if (HI && t < n_local) return kKeyTile;
+    if (HI && (t < n_local || RECT)) return kKeyTile;
     const int64_t rem = a.M - static_cast<int64_t>(t - n_local) * kKeyTile;
     return rem < kKeyTile ? static_cast<int>(rem) : kKeyTile;
+  };
+  // ... and, for a cell-block guide tile, which of its 8x8 cells are visible: bits 0-7 the
+  // rows, bits 8-15 the columns (0xffff: all).
+  auto tile_mask = [&](int t) __attribute__((always_inline)) -> uint32_t {
+    if (RECT && t >= n_local) return __builtin_amdgcn_readfirstlane(tile_mask_s[t]);
+    return 0xffffu;
   };
 
   // Query fragment (B operand of S^T = K Q^T): lane holds query ql, dims 16kk + 8g .. +8.
@@ -578,7 +648,7 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   // a lane's partial sum exceeds 2^20 (some score grew by more than ~2^15 over it, or
   // overflowed): then the maximum is raised, O and l rescaled, and P recomputed.  P stays
   // below 2^20, far inside fp32 and bf16 range.  Produces P^T as four bf16 B operands.
-  auto softmax = [&](int valid, bf16x8 (&pf)[4]) __attribute__((always_inline)) {
+  auto softmax = [&](int valid, uint32_t cells, bf16x8 (&pf)[4]) __attribute__((always_inline)) {
     if (valid < kKeyTile) {
       // key 8(r/4) + 4g + r%4 (+32) is past the end iff its g-free part reaches valid - 4g;
       // comparing against that compile-time part keeps 32 key indices out of registers
@@ -588,6 +658,16 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
         const int kc = 8 * (r >> 2) + (r & 3);
         if (kc >= lim) s0[r] = -INFINITY;
         if (kc + 32 >= lim) s1[r] = -INFINITY;
+      }
+    } else if (cells != 0xffffu) {
+      // cell-block tile: key k is cell (k / 8, k % 8) of the block, i.e. row r/4 (+4 in the
+      // second half) and column 4g + r%4
+      const uint32_t cols = (cells >> (8 + 4 * g)) & 15u;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool col_ok = (cols >> (r & 3)) & 1u;
+        if (!(col_ok && ((cells >> (r >> 2)) & 1u))) s0[r] = -INFINITY;
+        if (!(col_ok && ((cells >> (4 + (r >> 2))) & 1u))) s1[r] = -INFINITY;
       }
     }
     if (first) {
@@ -670,10 +750,10 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
         qk(cur);
         __builtin_amdgcn_s_setprio(0);
         dma_slot(2);
-        softmax(tile_valid(t), pa);
+        softmax(tile_valid(t), tile_mask(t), pa);
       } else {
         bf16x8 pf[4];
-        softmax(tile_valid(t), pf);
+        softmax(tile_valid(t), tile_mask(t), pf);
         __builtin_amdgcn_s_setprio(1);
         dma_slot(1);
         pv(cur + TILE_BYTES, pf);
@@ -729,20 +809,23 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   }
 }
 
-template <int D, int NWAVES, bool HI>
+template <int D, int NWAVES, bool HI, bool RECT>
 static void launch_attn(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, NWAVES, HI>), dim3(a.total_blocks), dim3(NWAVES * 64), 0,
-                     s, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, NWAVES, HI, RECT>), dim3(a.total_blocks), dim3(NWAVES * 64),
+                     0, s, a);
 }
 
-static void dispatch_attn(int D, int nwaves, bool hi, const AttnArgs& a, hipStream_t s) {
-  if (D == 128) {
-    if (nwaves == 8) hi ? launch_attn<128, 8, true>(a, s) : launch_attn<128, 8, false>(a, s);
-    else launch_attn<128, 2, true>(a, s);
-  } else {
-    if (nwaves == 8) hi ? launch_attn<64, 8, true>(a, s) : launch_attn<64, 8, false>(a, s);
-    else launch_attn<64, 2, true>(a, s);
-  }
+// hi: hi pass (else guide pass); rect: guide tokens restricted to a per-window rectangle
+template <int D>
+static void dispatch_attn_d(int nwaves, bool hi, bool rect, const AttnArgs& a, hipStream_t s) {
+  if (!hi) launch_attn<D, 8, false, false>(a, s);
+  else if (nwaves == 8) rect ? launch_attn<D, 8, true, true>(a, s) : launch_attn<D, 8, true, false>(a, s);
+  else rect ? launch_attn<D, 2, true, true>(a, s) : launch_attn<D, 2, true, false>(a, s);
+}
+
+static void dispatch_attn(int D, int nwaves, bool hi, bool rect, const AttnArgs& a, hipStream_t s) {
+  if (D == 128) dispatch_attn_d<128>(nwaves, hi, rect, a, s);
+  else dispatch_attn_d<64>(nwaves, hi, rect, a, s);
 }
 
 // ------------------------------------------------------------------ host side
@@ -751,8 +834,32 @@ int timer_begin(uhla_timer* t, int stage, hipStream_t s);
 int timer_end(uhla_timer* t, int stage, hipStream_t s);
 int timer_commit(uhla_timer* t);
 
+// Largest number of table-driven tiles (neighbour-window tiles plus cell-block guide
+// tiles) over all windows; mirrors the tile-list construction of the hi pass.
+static int64_t max_table_tiles(const Geom& g) {
+  const int tpw = g.w * g.w / kKeyTile;
+  const int reach = g.guide_mode == 1 ? 0 : g.radius;
+  int64_t best = 0;
+  for (int wy = 0; wy < g.n_wy; ++wy)
+    for (int wx = 0; wx < g.n_wx; ++wx) {
+      auto span = [](int c, int r, int n) { return std::min(n - 1, c + r) - std::max(0, c - r) + 1; };
+      int64_t n = static_cast<int64_t>(span(wy, g.radius, g.n_wy)) * span(wx, g.radius, g.n_wx) * tpw;
+      if (g.guide_mode != 0 && g.M > 0) {
+        const int gy0 = std::max(0, wy - reach), gy1 = std::min(g.n_wy - 1, wy + reach);
+        const int gx0 = std::max(0, wx - reach), gx1 = std::min(g.n_wx - 1, wx + reach);
+        const int i0 = (gy0 * g.w + g.rho - 1) / g.rho, i1 = std::min(g.H_lr, ((gy1 + 1) * g.w + g.rho - 1) / g.rho);
+        const int j0 = (gx0 * g.w + g.rho - 1) / g.rho, j1 = std::min(g.W_lr, ((gx1 + 1) * g.w + g.rho - 1) / g.rho);
+        if (i0 < i1 && j0 < j1)
+          n += static_cast<int64_t>(((i1 - 1) >> 3) - (i0 >> 3) + 1) * (((j1 - 1) >> 3) - (j0 >> 3) + 1);
+      }
+      best = std::max(best, n);
+    }
+  return best;
+}
+
 static int validate_forward(const void* q, const void* k, const void* v, void* o, int B, int H,
-                            int W, int w, int H_lr, int W_lr, int rho, int heads, int D) {
+                            int W, int w, int H_lr, int W_lr, int rho, int heads, int D,
+                            int radius, int guide_mode) {
   if (!q || !k || !v || !o) return fail_arg("null pointer");
   if (B < 1 || H < 1 || W < 1 || w < 1 || heads < 1 || D < 1 || H_lr < 0 || W_lr < 0)
     return fail_arg("sizes out of range");
@@ -760,9 +867,10 @@ static int validate_forward(const void* q, const void* k, const void* v, void* o
   if ((H_lr == 0) != (W_lr == 0)) return fail_arg("H_lr and W_lr must both be zero or not");
   if (static_cast<int64_t>(H_lr) * W_lr > 0 && rho < 1)
     return fail_arg("rho must be >= 1 with guide tokens");
+  if (radius < 0) return fail_arg("radius must be >= 0");
+  if (guide_mode < 0 || guide_mode > 2) return fail_arg("guide_mode must be 0, 1 or 2");
   if (D != 64 && D != 128) return fail_unsupported("head_dim must be 64 or 128");
   if (w % 8 || (w > 16 && w % 16)) return fail_unsupported("window size must be 8, 16 or a multiple of 16");
-  if (9 * (w * w / kKeyTile) > kMaxLocalTiles) return fail_unsupported("window size above 80");
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
        reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o)) % 16)
     return fail_arg("tensors must be 16-byte aligned");
@@ -773,16 +881,22 @@ static int validate_forward(const void* q, const void* k, const void* v, void* o
   if (N > (int64_t(1) << 30) || M > (int64_t(1) << 30) ||
       bh * ((N > M ? N : M) / 64 + 1) > 0x7fffffff)
     return fail_unsupported("problem too large");
+  // radius capped so that the neighbourhood span stays far inside int range
+  if (max_table_tiles(make_geom(B, H, W, w, H_lr, W_lr, rho, heads, D,
+                                std::min(radius, H / w + W / w), guide_mode)) > kMaxTableTiles)
+    return fail_unsupported("too many key tiles per window (window size or radius too large)");
   return UHLA_OK;
 }
 
 static int forward_impl(const void* q, const void* k, const void* v, void* o, int B, int H, int W,
                         int w, int H_lr, int W_lr, int rho, int heads, int D, float scale,
-                        float theta, void* workspace, size_t workspace_bytes, void* stream,
-                        uhla_timer* timer) {
-  int st = validate_forward(q, k, v, o, B, H, W, w, H_lr, W_lr, rho, heads, D);
+                        float theta, int radius, int guide_mode, void* workspace,
+                        size_t workspace_bytes, void* stream, uhla_timer* timer) {
+  int st = validate_forward(q, k, v, o, B, H, W, w, H_lr, W_lr, rho, heads, D, radius, guide_mode);
   if (st) return st;
-  const Geom g = make_geom(B, H, W, w, H_lr, W_lr, rho, heads, D);
+  // a radius reaching past the grid is the whole grid
+  radius = std::min(radius, H / w + W / w);
+  const Geom g = make_geom(B, H, W, w, H_lr, W_lr, rho, heads, D, radius, guide_mode);
   const Workspace need = carve(g, nullptr);
   if (!workspace || workspace_bytes < need.bytes)
     return (set_detail("workspace too small"), UHLA_ERR_WORKSPACE);
@@ -807,11 +921,8 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
     if (st) return st;                 \
   } while (0)
 
-  // 1. tables
+  // 1. tables (the neighbour windows are a clipped rectangle, computed in the hi pass)
   if (timer) timer_begin(timer, UHLA_STAGE_TABLES, s);
-  UHLA_STEP(hipLaunchKernelGGL(neighbour_table_kernel, dim3((g.nW + 255) / 256), dim3(256), 0, s,
-                               g.n_wy, g.n_wx, ws.nbr, ws.nbr_cnt),
-            "neighbour_table_kernel");
   if (rope_on) {
     const int n = g.P * (D / 4);
     UHLA_STEP(hipLaunchKernelGGL(cos_sin_table_kernel, dim3((n + 255) / 256), dim3(256), 0, s,
@@ -826,16 +937,17 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
   const bf16_t* vb = static_cast<const bf16_t*>(v);
   if (timer) timer_begin(timer, UHLA_STAGE_PREP_HI, s);
   {
-    const int64_t rows = g.N + g.Mq;
+    const int64_t rows = g.N + g.Mq + g.Mb;
     UHLA_STEP(hipLaunchKernelGGL(prep_qk_kernel, dim3(static_cast<unsigned>((rows + kPrepRows - 1) / kPrepRows), B),
                                  dim3(kPrepThreads), 0, s, qb, kb, ws.q_hi, ws.k_hi, ws.q_lr, ws.k_lr,
-                                 ws.cs, g.P, rope_on ? log2(static_cast<double>(theta)) : 0.0,
-                                 g.N, g.M, g.Mq, g.Mk, W, w, g.n_wx, W_lr, rho, heads, D,
-                                 rope_on ? 1 : 0, static_cast<double>(sc) * 1.4426950408889634),
+                                 ws.k_gb, ws.cs, g.P, rope_on ? log2(static_cast<double>(theta)) : 0.0,
+                                 g.N, g.M, g.Mq, g.Mk, g.Mb, W, w, g.n_wx, H_lr, W_lr, g.nbj, rho,
+                                 heads, D, rope_on ? 1 : 0, static_cast<double>(sc) * 1.4426950408889634),
               "prep_qk_kernel");
-    const int64_t tiles = g.N / kKeyTile + g.Mk / kKeyTile;
+    const int64_t tiles = (g.N + g.Mk + g.Mb) / kKeyTile;
     UHLA_STEP(hipLaunchKernelGGL(prep_v_kernel, dim3(static_cast<unsigned>(tiles), B), dim3(kPrepThreads), 0, s,
-                                 vb, ws.v_hi, ws.v_lr, g.N, g.M, g.Mk, W, w, g.n_wx, heads, D),
+                                 vb, ws.v_hi, ws.v_lr, ws.v_gb, g.N, g.M, g.Mk, g.Mb, W, w, g.n_wx,
+                                 H_lr, W_lr, g.nbj, heads, D),
               "prep_v_kernel");
   }
   if (timer) timer_end(timer, UHLA_STAGE_PREP_HI, s);
@@ -844,9 +956,7 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
 
   AttnArgs a{};
   a.k_hi = ws.k_hi; a.v_hi = ws.v_hi; a.k_lr = ws.k_lr; a.v_lr = ws.v_lr;
-  a.nbr = ws.nbr; a.nbr_cnt = ws.nbr_cnt;
   a.N = g.N; a.M = g.M; a.Mk = g.Mk; a.heads = heads; a.w2 = w2;
-  a.rescale_thr = 8.0f;
 
   // 3. hi pass
   if (timer) timer_begin(timer, UHLA_STAGE_ATTN_HI, s);
@@ -856,11 +966,18 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
     AttnArgs h = a;
     h.q = ws.q_hi; h.q_rows = g.N;
     h.out = static_cast<bf16_t*>(o); h.out_rows = L; h.out_row0 = 0;
-    h.W = W; h.w = w; h.n_wx = g.n_wx;
+    h.W = W; h.w = w; h.n_wx = g.n_wx; h.n_wy = g.n_wy;
+    h.radius = radius;
+    const bool rect = guide_mode != 0 && g.M > 0;
+    if (rect) {
+      h.k_lr = ws.k_gb; h.v_lr = ws.v_gb; h.Mk = g.Mb;
+    }
+    h.reach = guide_mode == 1 ? 0 : radius;
+    h.rho = rho; h.H_lr = H_lr; h.W_lr = W_lr; h.nbj = g.nbj;
     h.hi = 1; h.q_valid = static_cast<int>(g.N);
     h.blocks_per_bh = static_cast<int>(g.N / qt);
     h.total_blocks = static_cast<int>(static_cast<int64_t>(B) * heads * h.blocks_per_bh);
-    UHLA_STEP(dispatch_attn(D, nwaves, true, h, s), "attn_fwd_kernel(hi)");
+    UHLA_STEP(dispatch_attn(D, nwaves, true, rect, h, s), "attn_fwd_kernel(hi)");
   }
   if (timer) timer_end(timer, UHLA_STAGE_ATTN_HI, s);
 
@@ -873,11 +990,10 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
     l.hi = 0; l.q_valid = static_cast<int>(g.M);
     l.blocks_per_bh = static_cast<int>(g.Mq / kMaxQuery);
     l.total_blocks = static_cast<int>(static_cast<int64_t>(B) * heads * l.blocks_per_bh);
-    UHLA_STEP(dispatch_attn(D, 8, false, l, s), "attn_fwd_kernel(guide)");
+    UHLA_STEP(dispatch_attn(D, 8, false, false, l, s), "attn_fwd_kernel(guide)");
   }
   if (timer) timer_end(timer, UHLA_STAGE_ATTN_LR, s);
 
-  // 5. inverse permutation of the hi rows of O
   // 5. the inverse permutation of O is fused into the hi pass's stores (stage left empty)
   if (timer) timer_begin(timer, UHLA_STAGE_UNPERMUTE, s);
   if (timer) timer_end(timer, UHLA_STAGE_UNPERMUTE, s);
@@ -886,14 +1002,27 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
   return UHLA_OK;
 }
 
+static size_t workspace_bytes(int B, int H, int W, int w, int H_lr, int W_lr, int rho, int heads,
+                              int head_dim, int radius, int guide_mode) {
+  if (B < 1 || H < 1 || W < 1 || w < 1 || heads < 1 || H_lr < 0 || W_lr < 0) return 0;
+  if (H % w || W % w || (H_lr == 0) != (W_lr == 0)) return 0;
+  if (head_dim != 64 && head_dim != 128) return 0;
+  if (radius < 0 || guide_mode < 0 || guide_mode > 2) return 0;
+  if (static_cast<int64_t>(H_lr) * W_lr > 0 && rho < 1) return 0;
+  return carve(make_geom(B, H, W, w, H_lr, W_lr, rho, heads, head_dim, radius, guide_mode), nullptr).bytes;
+}
+
 }  // namespace uhla
 
 extern "C" size_t uhla_forward_workspace_bytes(int B, int H, int W, int w, int H_lr, int W_lr,
                                                int heads, int head_dim) {
-  if (B < 1 || H < 1 || W < 1 || w < 1 || heads < 1 || H_lr < 0 || W_lr < 0) return 0;
-  if (H % w || W % w || (H_lr == 0) != (W_lr == 0)) return 0;
-  if (head_dim != 64 && head_dim != 128) return 0;
-  return uhla::carve(uhla::make_geom(B, H, W, w, H_lr, W_lr, 1, heads, head_dim), nullptr).bytes;
+  return uhla::workspace_bytes(B, H, W, w, H_lr, W_lr, 1, heads, head_dim, 1, 0);
+}
+
+extern "C" size_t uhla_forward_masked_workspace_bytes(int B, int H, int W, int w, int H_lr,
+                                                      int W_lr, int rho, int heads, int head_dim,
+                                                      int radius, int guide_mode) {
+  return uhla::workspace_bytes(B, H, W, w, H_lr, W_lr, rho, heads, head_dim, radius, guide_mode);
 }
 
 extern "C" int uhla_forward(const void* q, const void* k, const void* v, void* o, int B, int H,
@@ -901,7 +1030,16 @@ extern "C" int uhla_forward(const void* q, const void* k, const void* v, void* o
                             float scale, float theta, void* workspace, size_t workspace_bytes,
                             void* stream) {
   return uhla::forward_impl(q, k, v, o, B, H, W, w, H_lr, W_lr, rho, heads, head_dim, scale,
-                            theta, workspace, workspace_bytes, stream, nullptr);
+                            theta, 1, 0, workspace, workspace_bytes, stream, nullptr);
+}
+
+extern "C" int uhla_forward_masked(const void* q, const void* k, const void* v, void* o, int B,
+                                   int H, int W, int w, int H_lr, int W_lr, int rho, int heads,
+                                   int head_dim, float scale, float theta, int radius,
+                                   int guide_mode, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  return uhla::forward_impl(q, k, v, o, B, H, W, w, H_lr, W_lr, rho, heads, head_dim, scale,
+                            theta, radius, guide_mode, workspace, workspace_bytes, stream, nullptr);
 }
 
 extern "C" int uhla_forward_timed(const void* q, const void* k, const void* v, void* o, int B,
@@ -910,5 +1048,5 @@ extern "C" int uhla_forward_timed(const void* q, const void* k, const void* v, v
                                   size_t workspace_bytes, void* stream, uhla_timer* timer) {
   if (!timer) return uhla::fail_arg("null timer");
   return uhla::forward_impl(q, k, v, o, B, H, W, w, H_lr, W_lr, rho, heads, head_dim, scale,
-                            theta, workspace, workspace_bytes, stream, timer);
+                            theta, 1, 0, workspace, workspace_bytes, stream, timer);
 }

@@ -106,8 +106,7 @@ size_t uhla_forward_workspace_bytes(int B, int H, int W, int w, int H_lr, int W_
  * with the mask of [UltraGen/ar §2.B] and [UltraGen/es §2]: a hi-res token attends to
  * every token of its own window and of the clipped 3x3 neighbourhood of windows, and to
  * all M guide tokens; a guide token attends to all guide tokens and to no hi-res token.
- * Steps: block-neighbour table; window-first permutation of the hi segment of Q, K, V
- * fused with RoPE (guide rows rotated in place of permuting); block-sparse attention of
+ * Steps: window-first permutation of the hi segment of Q, K, V fused with RoPE (guide rows rotated in place of permuting); block-sparse attention of
  * each window over its neighbour windows and the guide tokens (bf16 MFMA, fp32
  * accumulation and softmax) whose stores put each output row back at its raster
  * position (the inverse permutation, fused); guide-only attention.
@@ -118,12 +117,40 @@ size_t uhla_forward_workspace_bytes(int B, int H, int W, int w, int H_lr, int W_
  * Errors: UHLA_ERR_ARG (null pointers, sizes < 1, w not dividing H or W, rho < 1 with
  * guide tokens, exactly one of H_lr/W_lr zero, O overlapping Q, K, V or the workspace);
  * UHLA_ERR_UNSUPPORTED (head_dim not in {64, 128}; w not a multiple of 8, or w > 16
- * and not a multiple of 16, or w > 80); UHLA_ERR_WORKSPACE; UHLA_ERR_HIP.
+ * and not a multiple of 16; more than 1024 key tiles of 64 keys per window, counting
+ * the neighbour windows' tiles and, in the masked variant, the guide cell blocks);
+ * UHLA_ERR_WORKSPACE; UHLA_ERR_HIP.
  */
 int uhla_forward(const void* q, const void* k, const void* v, void* o,
                  int B, int H, int W, int w, int H_lr, int W_lr, int rho,
                  int heads, int head_dim, float scale, float theta,
                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Mask variants the pages leave open ([UltraGen/it §2]: a window looks at the guide
+ * tokens that correspond to it; [UltraGen/ar §2.B]: the neighbourhood of adjacent
+ * windows).  Same as uhla_forward except for the hi-res rows of the mask:
+ *   radius >= 0: a hi-res token sees the windows within `radius` windows along each axis
+ *     (clipped to the grid; 1 is the 3x3 neighbourhood of uhla_forward, 0 its own window);
+ *   guide_mode 0: every guide token (as uhla_forward);
+ *   guide_mode 1: the guide tokens (i, j) whose scaled position (rho*i, rho*j) lies in the
+ *     query's window;
+ *   guide_mode 2: those whose scaled position lies in one of the query's `radius`
+ *     neighbourhood windows.
+ *   A scaled position outside the hi-res grid lies in no window.  Guide rows of O are as
+ *   in uhla_forward.  uhla_forward(...) == uhla_forward_masked(..., 1, 0, ...).
+ * workspace: at least uhla_forward_masked_workspace_bytes(...) bytes (0 on invalid
+ *   arguments); guide modes 1 and 2 add a cell-block copy of the guide K and V.
+ * Errors: as uhla_forward, plus UHLA_ERR_ARG for radius < 0 or guide_mode not in {0,1,2}.
+ */
+size_t uhla_forward_masked_workspace_bytes(int B, int H, int W, int w, int H_lr, int W_lr,
+                                           int rho, int heads, int head_dim, int radius,
+                                           int guide_mode);
+int uhla_forward_masked(const void* q, const void* k, const void* v, void* o,
+                        int B, int H, int W, int w, int H_lr, int W_lr, int rho,
+                        int heads, int head_dim, float scale, float theta,
+                        int radius, int guide_mode,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* uhla_strerror(int status);
@@ -142,7 +169,7 @@ const char* uhla_last_error_detail(void);
  * uhla_timer_reset forgets recorded calls.  A call beyond max_calls is not timed.
  */
 typedef enum {
-  UHLA_STAGE_TABLES = 0,    /* neighbour table + cos/sin table */
+  UHLA_STAGE_TABLES = 0,    /* RoPE cos/sin table */
   UHLA_STAGE_PREP_HI = 1,   /* window-first permutation of Q, K, V fused with RoPE */
   UHLA_STAGE_PREP_LR = 2,   /* guide-token RoPE / V re-layout */
   UHLA_STAGE_ATTN_HI = 3,   /* hi-res block-sparse attention */

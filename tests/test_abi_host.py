@@ -131,7 +131,8 @@ def fwd_args(**kw):
     (dict(d=32), api.UHLA_ERR_UNSUPPORTED),
     (dict(H=24, W=24, w=24), api.UHLA_ERR_UNSUPPORTED),
     (dict(H=36, W=36, w=4), api.UHLA_ERR_UNSUPPORTED),
-    (dict(H=96, W=96, w=96, H_lr=0, W_lr=0), api.UHLA_ERR_UNSUPPORTED),
+    # 3x3 windows of 96x96 tokens: 9 * 144 key tiles per window, above the 1024-tile table
+    (dict(H=384, W=384, w=96, H_lr=0, W_lr=0), api.UHLA_ERR_UNSUPPORTED),
     (dict(ws=NULL), api.UHLA_ERR_WORKSPACE),
     (dict(wsb=1000), api.UHLA_ERR_WORKSPACE),
     (dict(o=P), api.UHLA_ERR_ARG),  # aliases q
@@ -151,23 +152,62 @@ def test_timer_create_rejects_bad_count(lib):
     assert lib.uhla_timer_create(0, ctypes.byref(h)) == api.UHLA_ERR_ARG
 
 
-def expected_workspace(B, H, W, w, H_lr, W_lr, heads, d):
-    """Independent restatement of the workspace layout (regions 256-byte aligned)."""
+@pytest.mark.parametrize("radius,mode,kw,status", [
+    (-1, 0, {}, api.UHLA_ERR_ARG),
+    (1, 3, {}, api.UHLA_ERR_ARG),
+    (1, -1, {}, api.UHLA_ERR_ARG),
+    (1, 1, dict(q=NULL), api.UHLA_ERR_ARG),
+    (1, 2, dict(d=96), api.UHLA_ERR_UNSUPPORTED),
+    (1, 1, dict(wsb=1000), api.UHLA_ERR_WORKSPACE),
+    # radius 4 on a 16x16-window grid: 9x9 windows of 4 tiles = 324 tiles, fine; with 64x64
+    # windows (64 tiles each) the 3x3 neighbourhood is 576 and radius 2 is 1600 > 1024
+    (2, 0, dict(H=320, W=320, w=64, H_lr=0, W_lr=0), api.UHLA_ERR_UNSUPPORTED),
+])
+def test_forward_masked_rejects(lib, radius, mode, kw, status):
+    a = fwd_args(**kw)
+    assert lib.uhla_forward_masked(*a[:15], radius, mode, *a[15:]) == status
+
+
+def expected_workspace(B, H, W, w, H_lr, W_lr, heads, d, guide_mode=0):
+    """Independent restatement of the workspace layout (regions 256-byte aligned): cos/sin
+    table, Q/K/V hi rows, Q guide rows (256-padded), K/V guide rows (64-padded), and for
+    guide modes 1 and 2 a copy of the guide K/V in 8x8 cell blocks."""
     al = lambda x: (x + 255) // 256 * 256
     N, M = H * W, H_lr * W_lr
     Mk, Mq = (M + 63) // 64 * 64, (M + 255) // 256 * 256
-    nW = (H // w) * (W // w)
+    Mb = ((H_lr + 7) // 8) * ((W_lr + 7) // 8) * 64 if (guide_mode and M) else 0
     e, bh = 2, B * heads
-    parts = [4 * nW * 9, 4 * nW, 16 * max(H, W) * (d // 4), bh * N * d * e, bh * N * d * e,
-             bh * N * d * e, bh * Mq * d * e, bh * Mk * d * e, bh * Mk * d * e]
+    parts = [16 * max(H, W) * (d // 4), bh * N * d * e, bh * N * d * e,
+             bh * N * d * e, bh * Mq * d * e, bh * Mk * d * e, bh * Mk * d * e,
+             bh * Mb * d * e, bh * Mb * d * e]
     return sum(al(p) for p in parts)
 
 
-@pytest.mark.parametrize("g", [(1, 32, 32, 8, 8, 8, 2, 64), (1, 128, 128, 16, 32, 32, 24, 128),
-                               (2, 256, 128, 16, 64, 32, 24, 128), (1, 512, 512, 16, 128, 128, 24, 128),
-                               (1, 48, 16, 16, 5, 3, 3, 128), (1, 16, 16, 16, 0, 0, 1, 64)])
+GEOMS = [(1, 32, 32, 8, 8, 8, 2, 64), (1, 128, 128, 16, 32, 32, 24, 128),
+         (2, 256, 128, 16, 64, 32, 24, 128), (1, 512, 512, 16, 128, 128, 24, 128),
+         (1, 48, 16, 16, 5, 3, 3, 128), (1, 16, 16, 16, 0, 0, 1, 64)]
+
+
+@pytest.mark.parametrize("g", GEOMS)
 def test_workspace_bytes(lib, g):
     assert lib.uhla_forward_workspace_bytes(*g) == expected_workspace(*g)
+
+
+@pytest.mark.parametrize("g", GEOMS)
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_masked_workspace_bytes(lib, g, mode):
+    B, H, W, w, H_lr, W_lr, heads, d = g
+    got = lib.uhla_forward_masked_workspace_bytes(B, H, W, w, H_lr, W_lr, 4, heads, d, 2, mode)
+    assert got == expected_workspace(*g, guide_mode=mode)
+    if mode == 0:
+        assert got == lib.uhla_forward_workspace_bytes(*g)
+
+
+def test_masked_workspace_bytes_invalid(lib):
+    f = lib.uhla_forward_masked_workspace_bytes
+    assert f(1, 32, 32, 8, 8, 8, 4, 2, 64, -1, 0) == 0
+    assert f(1, 32, 32, 8, 8, 8, 4, 2, 64, 1, 3) == 0
+    assert f(1, 32, 32, 8, 8, 8, 0, 2, 64, 1, 1) == 0
 
 
 def test_workspace_bytes_invalid(lib):
