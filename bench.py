@@ -1,13 +1,15 @@
 """Benchmark: hierarchical local attention forward at the 8K workload on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 8k] [--cpu-seconds S]
+                    [--radius R] [--guide-mode M]
 
 A step is one full uhla_forward (neighbour/cos-sin tables -> permutation fused with RoPE
 -> hi-res block-sparse attention -> guide attention -> inverse permutation) over one
 batch of synthetic inputs already resident in HBM.  Prints ONE JSON line.
 
 value       effective TFLOP/s of the whole step: algorithmic FLOPs (4 * head_dim per
-            unmasked (query, key) pair) / step time.
+            unmasked (query, key) pair) / step time.  --radius / --guide-mode measure the
+            mask variants of uhla_forward_masked instead (default: the pages' mask).
 roofline    the dominant kernel (hi-res attention pass) against the bf16 MFMA peak:
             its algorithmic FLOPs per launch / its mean launch duration, measured with
             HIP events recorded on the launch stream during the timed steps.
@@ -103,6 +105,8 @@ def main():
     ap.add_argument("--config", default="8k")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--radius", type=int, default=1)
+    ap.add_argument("--guide-mode", type=int, default=0, choices=(0, 1, 2))
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -114,7 +118,8 @@ def main():
     from global_attention_image_amd.inputs import (CONFIGS, CONFIG_SEEDS, algorithmic_flops,
                                                     algorithmic_pairs, make_qkv_bits)
 
-    g = CONFIGS[args.config]
+    g = CONFIGS[args.config].with_(radius=args.radius, guide_mode=args.guide_mode)
+    variant = args.radius != 1 or args.guide_mode != 0
     log(f"[bench] generating seeded inputs for {g}")
     t0 = time.perf_counter()
     q, k, v = make_qkv_bits(g, CONFIG_SEEDS[args.config])
@@ -123,9 +128,11 @@ def main():
     up = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
     qt, kt, vt = up(q), up(k), up(v)
     out = torch.empty_like(qt)
-    ws = api.alloc_workspace(g.B, g.H, g.W, g.w, g.H_lr, g.W_lr, g.heads, g.head_dim, dev)
+    ws = api.alloc_workspace(g.B, g.H, g.W, g.w, g.H_lr, g.W_lr, g.heads, g.head_dim, dev,
+                             rho=g.rho, radius=g.radius, guide_mode=g.guide_mode)
     fwd = lambda timer=None: api.forward(qt, kt, vt, g.H, g.W, g.w, g.H_lr, g.W_lr, rho=g.rho,
-                                         theta=g.theta, out=out, workspace=ws, timer=timer)
+                                         theta=g.theta, out=out, workspace=ws, timer=timer,
+                                         radius=g.radius, guide_mode=g.guide_mode)
     for _ in range(args.warmup):
         fwd()
     torch.cuda.synchronize()
@@ -167,7 +174,7 @@ def main():
     perm_gbs = perm_bytes / (perm_ms * 1e-3) / 1e9
     del pdst
 
-    traffic = read_traffic()
+    traffic = None if variant else read_traffic()
     res = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -184,6 +191,7 @@ def main():
         "config": {"workload": g.name, "B": g.B, "heads": g.heads, "head_dim": g.head_dim,
                    "grid": f"{g.H}x{g.W}", "window": g.w, "guide_grid": f"{g.H_lr}x{g.W_lr}",
                    "rho": g.rho, "rope_theta": g.theta, "tokens": g.L,
+                   "neighbourhood_radius": g.radius, "guide_mode": g.guide_mode,
                    "parallelism": "single GPU"},
         "tokens_per_s": round(g.B * g.L / (ms_step * 1e-3), 1),
         "hi_tokens_per_s": round(g.B * g.N / (ms_step * 1e-3), 1),
@@ -191,7 +199,7 @@ def main():
         "unmasked_pairs_per_head": pairs,
         "frac_bf16_peak_step": round(tflops / PEAK_BF16_TFLOPS, 4),
         "stage_ms": {s: round(x, 4) for s, x in stage_avg.items()},
-        "roofline": {"kernel": "attn_fwd_kernel<128,8> (hi-res pass)", "bound": "mfma",
+        "roofline": {"kernel": "attn_fwd_kernel<128, 8, hi> (hi-res pass)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},

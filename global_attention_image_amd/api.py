@@ -31,6 +31,10 @@ EXPORTS = {
     "uhla_forward_masked": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_int] * 9
                             + [ctypes.c_float, ctypes.c_float, ctypes.c_int, ctypes.c_int,
                                ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "uhla_forward_masked_timed": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_int] * 9
+                                  + [ctypes.c_float, ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                     ctypes.c_void_p]),
     "uhla_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "uhla_last_error_detail": (ctypes.c_char_p, []),
     "uhla_timer_create": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_void_p)]),
@@ -199,7 +203,8 @@ def forward(q, k, v, H, W, w, H_lr, W_lr, rho=4, scale=0.0, theta=10000.0, out=N
     """Hierarchical local attention forward on bf16 [B, H*W + H_lr*W_lr, heads, d] tensors.
 
     radius / guide_mode select the mask variants of uhla_forward_masked; the defaults are
-    the mask of uhla_forward, which is the entry point called for them."""
+    the mask of uhla_forward, which is the entry point called for them.  A timer records
+    per-stage durations (uhla_forward_timed / uhla_forward_masked_timed)."""
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _require(t, n, torch.bfloat16)
@@ -219,9 +224,11 @@ def forward(q, k, v, H, W, w, H_lr, W_lr, rho=4, scale=0.0, theta=10000.0, out=N
             float(scale), float(theta))
     tail = (_ptr(workspace), workspace.numel(), _stream(q))
     if radius != 1 or guide_mode != 0:
-        if timer is not None:
-            raise ValueError("stage timing covers the default mask only")
-        st = lib.uhla_forward_masked(*args, int(radius), int(guide_mode), *tail)
+        if timer is None:
+            st = lib.uhla_forward_masked(*args, int(radius), int(guide_mode), *tail)
+        else:
+            st = lib.uhla_forward_masked_timed(*args, int(radius), int(guide_mode), *tail,
+                                               timer.h)
         _check(st, "uhla_forward_masked")
         return out
     if timer is None:

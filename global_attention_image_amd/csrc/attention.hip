@@ -1050,3 +1050,13 @@ extern "C" int uhla_forward_timed(const void* q, const void* k, const void* v, v
   return uhla::forward_impl(q, k, v, o, B, H, W, w, H_lr, W_lr, rho, heads, head_dim, scale,
                             theta, 1, 0, workspace, workspace_bytes, stream, timer);
 }
+
+extern "C" int uhla_forward_masked_timed(const void* q, const void* k, const void* v, void* o,
+                                         int B, int H, int W, int w, int H_lr, int W_lr, int rho,
+                                         int heads, int head_dim, float scale, float theta,
+                                         int radius, int guide_mode, void* workspace,
+                                         size_t workspace_bytes, void* stream, uhla_timer* timer) {
+  if (!timer) return uhla::fail_arg("null timer");
+  return uhla::forward_impl(q, k, v, o, B, H, W, w, H_lr, W_lr, rho, heads, head_dim, scale,
+                            theta, radius, guide_mode, workspace, workspace_bytes, stream, timer);
+}

@@ -161,7 +161,8 @@ const char* uhla_last_error_detail(void);
 /*
  * Stage timing with HIP events (measurement only).
  *
- * uhla_forward_timed runs exactly uhla_forward and records a start/stop event pair on
+ * uhla_forward_timed runs exactly uhla_forward (uhla_forward_masked_timed exactly
+ * uhla_forward_masked) and records a start/stop event pair on
  * `stream` around each stage; a timer holds pairs for up to max_calls calls.
  * uhla_timer_read waits for the recorded events and writes, for each stage s <
  * n_stages, the summed milliseconds over the recorded calls into stage_ms[s], and the
@@ -188,6 +189,13 @@ int uhla_forward_timed(const void* q, const void* k, const void* v, void* o,
                        int heads, int head_dim, float scale, float theta,
                        void* workspace, size_t workspace_bytes, void* stream,
                        uhla_timer* timer);
+/* uhla_forward_masked with the same stage timing. */
+int uhla_forward_masked_timed(const void* q, const void* k, const void* v, void* o,
+                              int B, int H, int W, int w, int H_lr, int W_lr, int rho,
+                              int heads, int head_dim, float scale, float theta,
+                              int radius, int guide_mode,
+                              void* workspace, size_t workspace_bytes, void* stream,
+                              uhla_timer* timer);
 
 #ifdef __cplusplus
 }

@@ -145,6 +145,8 @@ def test_forward_rejects(lib, kw, status):
 
 def test_forward_timed_rejects_null_timer(lib):
     assert lib.uhla_forward_timed(*fwd_args(), NULL) == api.UHLA_ERR_ARG
+    a = fwd_args()
+    assert lib.uhla_forward_masked_timed(*a[:15], 1, 1, *a[15:], NULL) == api.UHLA_ERR_ARG
 
 
 def test_timer_create_rejects_bad_count(lib):
