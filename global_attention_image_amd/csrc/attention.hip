@@ -139,83 +139,110 @@ constexpr int kPrepRows = 4;
 // (zero for cells outside the guide grid), used by the guide-locality masks.  Q is also
 // multiplied by q_scale (the softmax scale times log2 e) before its single rounding to
 // bf16, so the attention kernel's scores come out in base-2 logits.
+template <int D>
 __global__ __launch_bounds__(kPrepThreads) void prep_qk_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, bf16_t* q_hi, bf16_t* k_hi,
-    bf16_t* q_lr, bf16_t* k_lr, bf16_t* k_gb, const double2* __restrict__ cs, int P,
-    double log2_theta, int64_t N, int64_t M, int64_t Mq, int64_t Mk, int64_t Mb, int W, int w,
-    int n_wx, int H_lr, int W_lr, int nbj, int rho, int heads, int D, int rope_on,
-    double q_scale) {
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, bf16_t* __restrict__ q_hi,
+    bf16_t* __restrict__ k_hi, bf16_t* __restrict__ q_lr, bf16_t* __restrict__ k_lr,
+    bf16_t* __restrict__ k_gb, const double2* __restrict__ cs, int P, double log2_theta,
+    int64_t N, int64_t M, int64_t Mq, int64_t Mk, int64_t Mb, int W, int w, int n_wx, int H_lr,
+    int W_lr, int nbj, int rho, int heads, int rope_on, double q_scale) {
+  constexpr int CPH = D / 8;      // 16-byte chunks per head row
+  constexpr int QUARTER = D / 4;  // rotation pairs per axis
+  // Per row of this block: source row (-1: zero row), destination rows of Q and K (-1:
+  // none), and the RoPE factors of its y and x positions.
+  __shared__ int64_t src_s[kPrepRows], dq_s[kPrepRows], dk_s[kPrepRows];
+  __shared__ int pos_s[kPrepRows][2];
+  __shared__ double2 cs_s[kPrepRows][2][QUARTER];
   const int64_t L = N + M;
-  const int64_t rows_total = N + Mq + Mb;
   const int64_t b = blockIdx.y;
-  const int chunks_per_head = D / 8;
-  const int chunks_per_row = heads * chunks_per_head;
-  const int quarter = D / 4;
-  for (int i = threadIdx.x; i < kPrepRows * chunks_per_row; i += kPrepThreads) {
-    const int t = i / chunks_per_row, c = i - t * chunks_per_row;
-    const int64_t row = static_cast<int64_t>(blockIdx.x) * kPrepRows + t;
-    if (row >= rows_total) continue;
-    const int h = c / chunks_per_head, j = c - h * chunks_per_head;
-    int64_t src_row;
-    int py, px;
-    bool valid = true;
-    bf16_t* dq;
-    bf16_t* dk;
+  const int tid = threadIdx.x;
+  if (tid < kPrepRows) {
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * kPrepRows + tid;
+    int64_t src = -1, dq = -1, dk = -1;
+    int py = 0, px = 0;
     if (row < N) {
       const int r = window_first_to_raster(static_cast<int>(row), W, w, n_wx);
-      src_row = r;
+      src = r;
       py = r / W;
       px = r - py * W;
-      const int64_t o = ((b * heads + h) * N + row) * D + j * 8;
-      dq = q_hi + o;
-      dk = k_hi + o;
+      dq = row;  // hi rows: q_hi / k_hi row index
+      dk = row;
     } else if (row < N + Mq) {
       const int64_t s = row - N;
-      valid = s < M;
-      src_row = N + s;
-      const int sy = valid ? static_cast<int>(s / W_lr) : 0;
-      py = rho * sy;
-      px = valid ? rho * static_cast<int>(s - static_cast<int64_t>(sy) * W_lr) : 0;
-      dq = q_lr + ((b * heads + h) * Mq + s) * D + j * 8;
-      dk = (s < Mk) ? k_lr + ((b * heads + h) * Mk + s) * D + j * 8 : nullptr;
-    } else {
+      if (s < M) {
+        src = N + s;
+        const int sy = static_cast<int>(s / W_lr);
+        py = rho * sy;
+        px = rho * static_cast<int>(s - static_cast<int64_t>(sy) * W_lr);
+      }
+      dq = N + s;                       // guide rows: q_lr row s
+      dk = s < Mk ? N + s : -1;         // k_lr row s
+    } else if (row < N + Mq + Mb) {
       const int64_t slot = row - N - Mq;
       int ci, cj;
       block_cell(slot, nbj, ci, cj);
-      valid = ci < H_lr && cj < W_lr;
-      src_row = valid ? N + static_cast<int64_t>(ci) * W_lr + cj : 0;
+      if (ci < H_lr && cj < W_lr) src = N + static_cast<int64_t>(ci) * W_lr + cj;
       py = rho * ci;
       px = rho * cj;
-      dq = nullptr;
-      dk = k_gb + ((b * heads + h) * Mb + slot) * D + j * 8;
+      dk = N + Mq + slot;               // k_gb row slot
     }
+    src_s[tid] = src;
+    dq_s[tid] = dq;
+    dk_s[tid] = dk;
+    pos_s[tid][0] = py;
+    pos_s[tid][1] = px;
+  }
+  __syncthreads();
+  if (rope_on) {
+    for (int e = tid; e < kPrepRows * 2 * QUARTER; e += kPrepThreads) {
+      const int rt = e / (2 * QUARTER), axis = (e / QUARTER) & 1, kk = e % QUARTER;
+      const int pos = pos_s[rt][axis];
+      cs_s[rt][axis][kk] = pos < P ? cs[pos * QUARTER + kk] : rope_cos_sin(pos, kk, D / 2, log2_theta);
+    }
+    __syncthreads();
+  }
+
+  const int cpr = heads * CPH;  // chunks per row
+  auto dst_ptr = [&](int64_t d, int h, int j, bool is_q) -> bf16_t* {
+    if (d < 0) return nullptr;
+    const int64_t bh = b * heads + h;
+    if (d < N) return (is_q ? q_hi : k_hi) + (bh * N + d) * D + j * 8;
+    if (d < N + Mq) return (is_q ? q_lr + (bh * Mq + (d - N)) * D : k_lr + (bh * Mk + (d - N)) * D) + j * 8;
+    return k_gb + (bh * Mb + (d - N - Mq)) * D + j * 8;
+  };
+  // task i = (row t, chunk c); t and c advance without divisions
+  int t = tid / cpr, c = tid - (tid / cpr) * cpr;
+  for (; t < kPrepRows; ) {
+    const int h = c / CPH, j = c % CPH;
+    const int64_t src = src_s[t];
     uint4 qo = make_uint4(0, 0, 0, 0), ko = make_uint4(0, 0, 0, 0);
-    if (valid) {
-      const int64_t so = ((b * L + src_row) * heads + h) * D + j * 8;
+    if (src >= 0) {
+      const int64_t so = ((b * L + src) * heads + h) * D + j * 8;
       const uint4 qi = *reinterpret_cast<const uint4*>(q + so);
       const uint4 ki = *reinterpret_cast<const uint4*>(k + so);
       if (rope_on) {
-        const uint32_t qw[4] = {qi.x, qi.y, qi.z, qi.w}, kw[4] = {ki.x, ki.y, ki.z, ki.w};
-        uint32_t qr[4], kr[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int pr = j * 4 + e;  // pair index inside the head
-          const int axis = pr / quarter, kk = pr - axis * quarter;
-          const int pos = axis ? px : py;
-          const double2 f = pos < P ? cs[pos * quarter + kk] : rope_cos_sin(pos, kk, D / 2, log2_theta);
-          qr[e] = rope_rotate_word(qw[e], f, q_scale);
-          kr[e] = rope_rotate_word(kw[e], f);
-        }
-        qo = make_uint4(qr[0], qr[1], qr[2], qr[3]);
-        ko = make_uint4(kr[0], kr[1], kr[2], kr[3]);
+        // pairs 4j .. 4j+3 lie on one axis (y for the first D/4 pairs)
+        const int axis = (4 * j) / QUARTER, k0 = 4 * j - axis * QUARTER;
+        const double2* f = &cs_s[t][axis][k0];
+        qo = make_uint4(rope_rotate_word(qi.x, f[0], q_scale), rope_rotate_word(qi.y, f[1], q_scale),
+                        rope_rotate_word(qi.z, f[2], q_scale), rope_rotate_word(qi.w, f[3], q_scale));
+        ko = make_uint4(rope_rotate_word(ki.x, f[0]), rope_rotate_word(ki.y, f[1]),
+                        rope_rotate_word(ki.z, f[2]), rope_rotate_word(ki.w, f[3]));
       } else {
         qo = make_uint4(scale_word(qi.x, q_scale), scale_word(qi.y, q_scale),
                         scale_word(qi.z, q_scale), scale_word(qi.w, q_scale));
         ko = ki;
       }
     }
+    bf16_t* dq = dst_ptr(dq_s[t], h, j, true);
+    bf16_t* dk = dst_ptr(dk_s[t], h, j, false);
     if (dq) *reinterpret_cast<uint4*>(dq) = qo;
     if (dk) *reinterpret_cast<uint4*>(dk) = ko;
+    c += kPrepThreads;
+    while (c >= cpr) {
+      c -= cpr;
+      ++t;
+    }
   }
 }
 
@@ -938,12 +965,19 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
   if (timer) timer_begin(timer, UHLA_STAGE_PREP_HI, s);
   {
     const int64_t rows = g.N + g.Mq + g.Mb;
-    UHLA_STEP(hipLaunchKernelGGL(prep_qk_kernel, dim3(static_cast<unsigned>((rows + kPrepRows - 1) / kPrepRows), B),
-                                 dim3(kPrepThreads), 0, s, qb, kb, ws.q_hi, ws.k_hi, ws.q_lr, ws.k_lr,
-                                 ws.k_gb, ws.cs, g.P, rope_on ? log2(static_cast<double>(theta)) : 0.0,
-                                 g.N, g.M, g.Mq, g.Mk, g.Mb, W, w, g.n_wx, H_lr, W_lr, g.nbj, rho,
-                                 heads, D, rope_on ? 1 : 0, static_cast<double>(sc) * 1.4426950408889634),
-              "prep_qk_kernel");
+    const dim3 grid(static_cast<unsigned>((rows + kPrepRows - 1) / kPrepRows), B);
+    const double l2t = rope_on ? log2(static_cast<double>(theta)) : 0.0;
+    const double qs = static_cast<double>(sc) * 1.4426950408889634;
+    if (D == 128)
+      hipLaunchKernelGGL(prep_qk_kernel<128>, grid, dim3(kPrepThreads), 0, s, qb, kb, ws.q_hi,
+                         ws.k_hi, ws.q_lr, ws.k_lr, ws.k_gb, ws.cs, g.P, l2t, g.N, g.M, g.Mq, g.Mk,
+                         g.Mb, W, w, g.n_wx, H_lr, W_lr, g.nbj, rho, heads, rope_on ? 1 : 0, qs);
+    else
+      hipLaunchKernelGGL(prep_qk_kernel<64>, grid, dim3(kPrepThreads), 0, s, qb, kb, ws.q_hi,
+                         ws.k_hi, ws.q_lr, ws.k_lr, ws.k_gb, ws.cs, g.P, l2t, g.N, g.M, g.Mq, g.Mk,
+                         g.Mb, W, w, g.n_wx, H_lr, W_lr, g.nbj, rho, heads, rope_on ? 1 : 0, qs);
+    st = check_launch("prep_qk_kernel");
+    if (st) return st;
     const int64_t tiles = (g.N + g.Mk + g.Mb) / kKeyTile;
     UHLA_STEP(hipLaunchKernelGGL(prep_v_kernel, dim3(static_cast<unsigned>(tiles), B), dim3(kPrepThreads), 0, s,
                                  vb, ws.v_hi, ws.v_lr, ws.v_gb, g.N, g.M, g.Mk, g.Mb, W, w, g.n_wx,
