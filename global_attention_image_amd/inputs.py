@@ -25,9 +25,10 @@ import numpy as np
 class Geometry:
     """One attention problem.
 
-    Tensors are token-major ``[B, L, heads, head_dim]`` with ``L = N + M``: rows
-    ``0..N-1`` are the hi-res tokens of an ``H x W`` grid in raster order, rows
-    ``N..L-1`` the low-res guide tokens of an ``H_lr x W_lr`` grid in raster order.
+    Tensors are token-major ``[B, L, heads, head_dim]`` with ``L = T + N + M``: rows
+    ``0..T-1`` are text tokens (none unless T > 0), then the hi-res tokens of an ``H x W``
+    grid in raster order, then the low-res guide tokens of an ``H_lr x W_lr`` grid in
+    raster order.
     """
 
     B: int
@@ -46,6 +47,8 @@ class Geometry:
     # query's own window; 2 = those lying in the query's neighbourhood of windows)
     radius: int = 1
     guide_mode: int = 0
+    # text tokens at the front of the joint sequence (text | hi | guide)
+    T: int = 0
 
     @property
     def N(self) -> int:
@@ -57,7 +60,7 @@ class Geometry:
 
     @property
     def L(self) -> int:
-        return self.N + self.M
+        return self.T + self.N + self.M
 
     @property
     def n_windows(self) -> int:
@@ -207,11 +210,17 @@ def algorithmic_pairs(geom: Geometry) -> dict:
             g = sum(pad[dy:dy + a, dx:dx + b] for dy in range(2 * r + 1) for dx in range(2 * r + 1))
         hi_lr = int(g.sum()) * geom.w * geom.w
     lr_lr = geom.M * geom.M
-    return {"local": local, "hi_lr": hi_lr, "lr_lr": lr_lr, "total": local + hi_lr + lr_lr}
+    # text: text queries see every key; every other query also sees every text key
+    text = geom.T * geom.L + (geom.N + geom.M) * geom.T
+    return {"local": local, "hi_lr": hi_lr, "lr_lr": lr_lr, "text": text,
+            "total": local + hi_lr + lr_lr + text}
 
 
 def algorithmic_flops(geom: Geometry) -> dict:
     """Matrix FLOPs of the unmasked pairs: 4 * head_dim per pair (QK^T and PV), all (b, h)."""
     p = algorithmic_pairs(geom)
     f = 4 * geom.head_dim * geom.B * geom.heads
-    return {"hi": f * (p["local"] + p["hi_lr"]), "lr": f * p["lr_lr"], "total": f * p["total"]}
+    hi_text = geom.N * geom.T
+    lr_text = geom.M * geom.T
+    return {"hi": f * (p["local"] + p["hi_lr"] + hi_text), "lr": f * (p["lr_lr"] + lr_text),
+            "text": f * geom.T * geom.L, "total": f * p["total"]}

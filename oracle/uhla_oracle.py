@@ -27,6 +27,10 @@ What the pages fix, and the readings taken where they are silent:
 * RoPE ([UltraGen/fr §2.A]: relative positional embeddings).  Readings: 2D axial RoPE,
   half of the head dims per axis (y first), adjacent pairs (2k, 2k+1) rotated by
   pos * theta**(-2k/d_axis), theta = 10000; applied to Q and K, not V.
+* Text tokens (optional, T > 0): the joint sequence is text | hi-res | guide
+  ([UltraGen/it §2], [UltraGen/fr §2.C]).  Readings (the plain MMDiT joint attention):
+  text queries attend to every key, every query attends to every text key; text tokens
+  sit at position (0, 0), so RoPE leaves them unrotated.
 * Attention: softmax(Q K^T / sqrt(d)) V over the allowed keys.  Every row has at least
   w*w allowed keys, so no row is empty.
 
@@ -88,10 +92,13 @@ def lr_positions(H_lr: int, W_lr: int, rho: int):
 
 
 def token_positions(geom):
-    """(y, x) for all L tokens of the joint [hi | lr] sequence, raster in both parts."""
+    """(y, x) for all L tokens of the joint [text | hi | lr] sequence: text tokens at
+    (0, 0), hi and guide tokens raster."""
+    T = getattr(geom, "T", 0)
     yh, xh = hi_positions(geom.H, geom.W)
     yl, xl = lr_positions(geom.H_lr, geom.W_lr, geom.rho)
-    return np.concatenate([yh, yl]), np.concatenate([xh, xl])
+    z = np.zeros(T, dtype=np.int64)
+    return np.concatenate([z, yh, yl]), np.concatenate([z, xh, xl])
 
 
 # ---------------------------------------------------------------------------------
@@ -131,7 +138,7 @@ def rope_rotate(x: np.ndarray, pos_y: np.ndarray, pos_x: np.ndarray, theta: floa
 
 
 def rope_joint(x: np.ndarray, geom) -> np.ndarray:
-    """RoPE on a full ``[B, L, heads, d]`` tensor in the raster [hi | lr] layout."""
+    """RoPE on a full ``[B, L, heads, d]`` tensor in the [text | hi | lr] layout."""
     py, px = token_positions(geom)
     return rope_rotate(x, py, px, geom.theta)
 
@@ -141,7 +148,8 @@ def rope_joint(x: np.ndarray, geom) -> np.ndarray:
 # ---------------------------------------------------------------------------------
 
 def mask_rows(geom, rows: np.ndarray) -> np.ndarray:
-    """Explicit boolean mask rows (raster order over all L keys) for query rows ``rows``.
+    """Explicit boolean mask rows (over all L keys of the [text | hi | lr] sequence) for
+    query rows ``rows``.
 
     hi q -> hi k : allowed iff the windows differ by at most ``radius`` in both axes
                    (radius 1: the clipped 3x3 neighbourhood of the pages);
@@ -149,25 +157,32 @@ def mask_rows(geom, rows: np.ndarray) -> np.ndarray:
                    (rho*i, rho*j) lies in the query's window; 2: iff it lies in a window
                    of the query's neighbourhood (scaled positions outside the hi-res grid
                    belong to no window);
-    lr q -> lr k : always;   lr q -> hi k : never.
+    lr q -> lr k : always;   lr q -> hi k : never;
+    text q -> any k, and any q -> text k : always.
     """
     rows = np.asarray(rows, dtype=np.int64)
+    T = getattr(geom, "T", 0)
     N, L, w = geom.N, geom.L, geom.w
     r = getattr(geom, "radius", 1)
     mode = getattr(geom, "guide_mode", 0)
     key = np.arange(L, dtype=np.int64)
-    key_is_hi = key < N
-    ky, kx = np.where(key_is_hi, key // geom.W, 0), np.where(key_is_hi, key % geom.W, 0)
-    q_is_hi = rows < N
-    qy, qx = np.where(q_is_hi, rows // geom.W, 0), np.where(q_is_hi, rows % geom.W, 0)
+    key_is_text = key < T
+    key_is_hi = (key >= T) & (key < T + N)
+    key_is_lr = key >= T + N
+    kh = np.where(key_is_hi, key - T, 0)
+    ky, kx = kh // geom.W, kh % geom.W
+    q_is_text = rows < T
+    q_is_hi = (rows >= T) & (rows < T + N)
+    q_is_lr = rows >= T + N
+    qh = np.where(q_is_hi, rows - T, 0)
+    qy, qx = qh // geom.W, qh % geom.W
     near = (np.abs(qy[:, None] // w - ky[None, :] // w) <= r) & \
            (np.abs(qx[:, None] // w - kx[None, :] // w) <= r)
     hi_hi = q_is_hi[:, None] & key_is_hi[None, :] & near
-    key_is_lr = ~key_is_hi
     if mode == 0:
         hi_lr = q_is_hi[:, None] & key_is_lr[None, :]
     else:
-        s = np.where(key_is_lr, key - N, 0)
+        s = np.where(key_is_lr, key - T - N, 0)
         gy = geom.rho * (s // max(geom.W_lr, 1))
         gx = geom.rho * (s % max(geom.W_lr, 1))
         inside = key_is_lr & (gy < geom.H) & (gx < geom.W)
@@ -175,8 +190,9 @@ def mask_rows(geom, rows: np.ndarray) -> np.ndarray:
         close = (np.abs(qy[:, None] // w - gy[None, :] // w) <= reach) & \
                 (np.abs(qx[:, None] // w - gx[None, :] // w) <= reach)
         hi_lr = q_is_hi[:, None] & inside[None, :] & close
-    lr_lr = ~q_is_hi[:, None] & key_is_lr[None, :]
-    return hi_hi | hi_lr | lr_lr
+    lr_lr = q_is_lr[:, None] & key_is_lr[None, :]
+    text = q_is_text[:, None] | key_is_text[None, :]
+    return hi_hi | hi_lr | lr_lr | text
 
 
 # ---------------------------------------------------------------------------------
@@ -227,7 +243,7 @@ def attention_rows(q, k, v, geom, b: int, h: int, rows, block: int = 512, qk=Non
 
 
 def forward(q, k, v, geom, block: int = 512) -> np.ndarray:
-    """Full oracle forward: fp64 ``[B, L, heads, d]`` in the raster [hi | lr] layout.
+    """Full oracle forward: fp64 ``[B, L, heads, d]`` in the [text | hi | lr] layout.
 
     Permute -> attend -> unpermute leaves the result in raster order, and the mask is
     defined on positions, so the oracle attends in raster order directly.

@@ -41,7 +41,13 @@ def window_tokens_by_slicing(H, W, w, wy, wx):
 def brute_mask(geom):
     """L x L mask built by enumeration: each window's clipped neighbour windows within the
     radius (slices of the index grid), and guide cells assigned to windows by testing the
-    window bounds against their scaled position one window at a time."""
+    window bounds against their scaled position one window at a time; text tokens (the
+    first T rows) see and are seen by every token."""
+    T = geom.T
+    if T:
+        m = np.ones((geom.L, geom.L), dtype=bool)
+        m[T:, T:] = brute_mask(geom.with_(T=0))
+        return m
     H, W, w, N, L = geom.H, geom.W, geom.w, geom.N, geom.L
     r, mode = geom.radius, geom.guide_mode
     m = np.zeros((L, L), dtype=bool)
@@ -100,8 +106,11 @@ def loop_attention(q, k, v, geom):
     """Pure-Python loops: RoPE with math.cos/sin, mask from brute_mask, math.exp softmax."""
     B, L, Hh, d = q.shape
     da = d // 2
-    yh = [r // geom.W for r in range(geom.N)] + [geom.rho * (s // geom.W_lr) for s in range(geom.M)]
-    xh = [r % geom.W for r in range(geom.N)] + [geom.rho * (s % geom.W_lr) for s in range(geom.M)]
+    # text tokens sit at (0, 0), then hi raster, then guide raster at (rho i, rho j)
+    yh = [0] * geom.T + [r // geom.W for r in range(geom.N)] + \
+        [geom.rho * (s // geom.W_lr) for s in range(geom.M)]
+    xh = [0] * geom.T + [r % geom.W for r in range(geom.N)] + \
+        [geom.rho * (s % geom.W_lr) for s in range(geom.M)]
 
     def rot(vec, t):
         outv = list(vec)
@@ -466,6 +475,96 @@ def test_uniform_probe_guide_mode_1():
                  if 0 <= a < nwy and 0 <= b < nwx)
         tot = nb * g.w * g.w + cnt[wy, wx]
         assert abs(o[0, rr, 0, 0] - cnt[wy, wx] / tot) < 1e-12
+
+
+# ------------------------------------------------------------------- text tokens
+
+TEXT_GEOMS = [small_geom(T=1), small_geom(T=5, guide_mode=1), small_geom(T=70, radius=0),
+              small_geom(T=3, H=16, W=8, H_lr=3, W_lr=3, rho=3, guide_mode=2),
+              small_geom(T=9, H_lr=0, W_lr=0)]
+
+
+def check_text_mask(mask_rows_fn):
+    for g in TEXT_GEOMS:
+        assert np.array_equal(mask_rows_fn(g, np.arange(g.L)), brute_mask(g)), g
+
+
+def test_text_mask():
+    check_text_mask(orc.mask_rows)
+
+
+def test_text_pair_counts():
+    for g in TEXT_GEOMS + [CONFIGS["tiny"].with_(T=77)]:
+        assert int(orc.mask_rows(g, np.arange(g.L)).sum()) == algorithmic_pairs(g)["total"], g
+
+
+def test_text_attention_vs_loops():
+    g = small_geom(T=3, guide_mode=1, H=8, W=8, H_lr=2, W_lr=2)
+    q, k, v = rand_qkv(g, 31)
+    assert np.max(np.abs(orc.forward(q, k, v, g) - loop_attention(q, k, v, g))) < 1e-12
+
+
+def test_text_rows_unrotated_and_rest_unchanged():
+    g = small_geom(T=6)
+    x = rand_qkv(g, 3)[0]
+    y = orc.rope_joint(x, g)
+    assert np.array_equal(y[:, :g.T], x[:, :g.T])
+    # the hi/guide rows rotate exactly as without text tokens
+    assert np.array_equal(y[:, g.T:], orc.rope_joint(x[:, g.T:], g.with_(T=0)))
+
+
+def test_text_queries_are_dense_attention():
+    """Text query rows: unmasked softmax attention over every (rotated) key, checked with
+    torch's scaled_dot_product_attention in fp64."""
+    import torch
+    g = small_geom(T=4, head_dim=16, guide_mode=2)
+    q, k, v = rand_qkv(g, 8)
+    o = orc.forward(q, k, v, g)
+    qr, kr = orc.rope_joint(q, g), orc.rope_joint(k, g)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(qr[0, :g.T, 0][None]), torch.from_numpy(kr[0, :, 0][None]),
+        torch.from_numpy(v[0, :, 0][None])).numpy()[0]
+    assert np.max(np.abs(o[0, :g.T, 0] - ref)) < 1e-12
+
+
+def _mut_text_queries_skip_hi(geom, rows):
+    m = orc.mask_rows(geom, rows)
+    rows = np.asarray(rows)
+    m[np.ix_(rows < geom.T, np.arange(geom.T, geom.T + geom.N))] = False
+    return m
+
+
+def _mut_guide_queries_skip_text(geom, rows):
+    m = orc.mask_rows(geom, rows)
+    rows = np.asarray(rows)
+    m[np.ix_(rows >= geom.T + geom.N, np.arange(geom.T))] = False
+    return m
+
+
+@pytest.mark.parametrize("mutant", [_mut_text_queries_skip_hi, _mut_guide_queries_skip_text])
+def test_pins_catch_text_mutants(mutant):
+    with pytest.raises(AssertionError):
+        check_text_mask(mutant)
+
+
+def test_pins_catch_rotated_text():
+    # text tokens placed at (1, 1) instead of (0, 0): the loop oracle must disagree
+    g = small_geom(T=2, H=8, W=8, H_lr=2, W_lr=2)
+    q, k, v = rand_qkv(g, 5)
+    real = orc.token_positions
+
+    def shifted(geom):
+        y, x = real(geom)
+        y, x = y.copy(), x.copy()
+        y[:geom.T] = 1
+        x[:geom.T] = 1
+        return y, x
+    orc.token_positions = shifted
+    try:
+        bad = orc.forward(q, k, v, g)
+    finally:
+        orc.token_positions = real
+    assert np.max(np.abs(bad - loop_attention(q, k, v, g))) > 1e-6
 
 
 # --------------------------------------------------------- planted mistakes must be caught
