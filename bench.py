@@ -1,7 +1,7 @@
 """Benchmark: hierarchical local attention forward at the 8K workload on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 8k] [--cpu-seconds S]
-                    [--radius R] [--guide-mode M]
+                    [--radius R] [--guide-mode M] [--text T]
 
 A step is one full uhla_forward (neighbour/cos-sin tables -> permutation fused with RoPE
 -> hi-res block-sparse attention -> guide attention -> inverse permutation) over one
@@ -9,7 +9,8 @@ batch of synthetic inputs already resident in HBM.  Prints ONE JSON line.
 
 value       effective TFLOP/s of the whole step: algorithmic FLOPs (4 * head_dim per
             unmasked (query, key) pair) / step time.  --radius / --guide-mode measure the
-            mask variants of uhla_forward_masked instead (default: the pages' mask).
+            mask variants of uhla_forward_masked instead (default: the pages' mask), and
+            --text T a joint sequence with T text tokens (uhla_forward_text).
 roofline    the dominant kernel (hi-res attention pass) against the bf16 MFMA peak:
             its algorithmic FLOPs per launch / its mean launch duration, measured with
             HIP events recorded on the launch stream during the timed steps.
@@ -107,6 +108,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--radius", type=int, default=1)
     ap.add_argument("--guide-mode", type=int, default=0, choices=(0, 1, 2))
+    ap.add_argument("--text", type=int, default=0, help="text tokens in the joint sequence")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -118,8 +120,8 @@ def main():
     from global_attention_image_amd.inputs import (CONFIGS, CONFIG_SEEDS, algorithmic_flops,
                                                     algorithmic_pairs, make_qkv_bits)
 
-    g = CONFIGS[args.config].with_(radius=args.radius, guide_mode=args.guide_mode)
-    variant = args.radius != 1 or args.guide_mode != 0
+    g = CONFIGS[args.config].with_(radius=args.radius, guide_mode=args.guide_mode, T=args.text)
+    variant = args.radius != 1 or args.guide_mode != 0 or args.text != 0
     log(f"[bench] generating seeded inputs for {g}")
     t0 = time.perf_counter()
     q, k, v = make_qkv_bits(g, CONFIG_SEEDS[args.config])
@@ -129,10 +131,10 @@ def main():
     qt, kt, vt = up(q), up(k), up(v)
     out = torch.empty_like(qt)
     ws = api.alloc_workspace(g.B, g.H, g.W, g.w, g.H_lr, g.W_lr, g.heads, g.head_dim, dev,
-                             rho=g.rho, radius=g.radius, guide_mode=g.guide_mode)
+                             rho=g.rho, radius=g.radius, guide_mode=g.guide_mode, T=g.T)
     fwd = lambda timer=None: api.forward(qt, kt, vt, g.H, g.W, g.w, g.H_lr, g.W_lr, rho=g.rho,
                                          theta=g.theta, out=out, workspace=ws, timer=timer,
-                                         radius=g.radius, guide_mode=g.guide_mode)
+                                         radius=g.radius, guide_mode=g.guide_mode, T=g.T)
     for _ in range(args.warmup):
         fwd()
     torch.cuda.synchronize()
@@ -192,6 +194,7 @@ def main():
                    "grid": f"{g.H}x{g.W}", "window": g.w, "guide_grid": f"{g.H_lr}x{g.W_lr}",
                    "rho": g.rho, "rope_theta": g.theta, "tokens": g.L,
                    "neighbourhood_radius": g.radius, "guide_mode": g.guide_mode,
+                   "text_tokens": g.T,
                    "parallelism": "single GPU"},
         "tokens_per_s": round(g.B * g.L / (ms_step * 1e-3), 1),
         "hi_tokens_per_s": round(g.B * g.N / (ms_step * 1e-3), 1),

@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libuhla.so")
 
 UHLA_OK, UHLA_ERR_ARG, UHLA_ERR_UNSUPPORTED, UHLA_ERR_WORKSPACE, UHLA_ERR_HIP = range(5)
-STAGES = ("tables", "prep_hi", "prep_lr", "attn_hi", "attn_lr", "unpermute")
+STAGES = ("tables", "prep_hi", "prep_lr", "attn_hi", "attn_lr", "unpermute", "attn_text")
 
 EXPORTS = {
     # name: (restype, argtypes)
@@ -35,6 +35,10 @@ EXPORTS = {
                                   + [ctypes.c_float, ctypes.c_float, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                      ctypes.c_void_p]),
+    "uhla_forward_text_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 12),
+    "uhla_forward_text": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_int] * 10
+                          + [ctypes.c_float, ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                             ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
     "uhla_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "uhla_last_error_detail": (ctypes.c_char_p, []),
     "uhla_timer_create": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_void_p)]),
@@ -156,10 +160,19 @@ def forward_masked_workspace_bytes(B, H, W, w, H_lr, W_lr, rho, heads, head_dim,
                                                           head_dim, radius, guide_mode))
 
 
+def forward_text_workspace_bytes(B, T, H, W, w, H_lr, W_lr, rho, heads, head_dim, radius,
+                                 guide_mode) -> int:
+    return int(load().uhla_forward_text_workspace_bytes(B, T, H, W, w, H_lr, W_lr, rho, heads,
+                                                        head_dim, radius, guide_mode))
+
+
 def alloc_workspace(B, H, W, w, H_lr, W_lr, heads, head_dim, device="cuda", rho=4, radius=1,
-                    guide_mode=0):
+                    guide_mode=0, T=0):
     import torch
-    if radius == 1 and guide_mode == 0:
+    if T:
+        n = forward_text_workspace_bytes(B, T, H, W, w, H_lr, W_lr, rho, heads, head_dim, radius,
+                                         guide_mode)
+    elif radius == 1 and guide_mode == 0:
         n = forward_workspace_bytes(B, H, W, w, H_lr, W_lr, heads, head_dim)
     else:
         n = forward_masked_workspace_bytes(B, H, W, w, H_lr, W_lr, rho, heads, head_dim, radius,
@@ -199,30 +212,36 @@ class Timer:
 
 
 def forward(q, k, v, H, W, w, H_lr, W_lr, rho=4, scale=0.0, theta=10000.0, out=None,
-            workspace=None, timer: Timer | None = None, radius=1, guide_mode=0):
-    """Hierarchical local attention forward on bf16 [B, H*W + H_lr*W_lr, heads, d] tensors.
+            workspace=None, timer: Timer | None = None, radius=1, guide_mode=0, T=0):
+    """Hierarchical local attention forward on bf16 [B, T + H*W + H_lr*W_lr, heads, d] tensors.
 
-    radius / guide_mode select the mask variants of uhla_forward_masked; the defaults are
-    the mask of uhla_forward, which is the entry point called for them.  A timer records
-    per-stage durations (uhla_forward_timed / uhla_forward_masked_timed)."""
+    radius / guide_mode select the mask variants of uhla_forward_masked and T > 0 the text
+    tokens of uhla_forward_text (rows 0..T-1); with the defaults uhla_forward is called.
+    A timer records per-stage durations (uhla_forward_timed / uhla_forward_masked_timed /
+    uhla_forward_text)."""
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _require(t, n, torch.bfloat16)
     if not (q.shape == k.shape == v.shape) or q.dim() != 4:
         raise ValueError("q, k, v must share one [B, L, heads, head_dim] shape")
     B, L, Hh, d = q.shape
-    if L != H * W + H_lr * W_lr:
+    if L != T + H * W + H_lr * W_lr:
         raise ValueError("token count does not match the grids")
     if out is None:
         out = torch.empty_like(q)
     _require(out, "out", torch.bfloat16)
     if workspace is None:
         workspace = alloc_workspace(B, H, W, w, H_lr, W_lr, Hh, d, q.device, rho=rho,
-                                    radius=radius, guide_mode=guide_mode)
+                                    radius=radius, guide_mode=guide_mode, T=T)
     lib = load()
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, W, w, H_lr, W_lr, rho, Hh, d,
             float(scale), float(theta))
     tail = (_ptr(workspace), workspace.numel(), _stream(q))
+    if T:
+        st = lib.uhla_forward_text(*args[:5], int(T), *args[5:], int(radius), int(guide_mode),
+                                   *tail, timer.h if timer is not None else None)
+        _check(st, "uhla_forward_text")
+        return out
     if radius != 1 or guide_mode != 0:
         if timer is None:
             st = lib.uhla_forward_masked(*args, int(radius), int(guide_mode), *tail)

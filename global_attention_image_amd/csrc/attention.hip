@@ -36,21 +36,29 @@ constexpr int kMaxTableTiles = 1024;  // table-driven key tiles (neighbour + cel
 struct Geom {
   int B, H, W, w, H_lr, W_lr, rho, heads, D;
   int radius, guide_mode;  // neighbourhood radius in windows; guide tokens seen (0 all, 1, 2)
+  int64_t T;               // text tokens at the front of the joint sequence
   int64_t N, M, Mk, Mq;    // Mk: guide rows padded to the key tile; Mq: to the query block
+  int64_t Tk, Tq;          // text rows padded to the key tile / the query block
+  int64_t Mg;              // rows of the global-key buffer: guide (Mk) then text (Tk)
   int n_wx, n_wy, nW, P;   // P: positions covered by the cos/sin table (max(H, W))
   int nbi, nbj;            // guide grid in 8x8 cell blocks (rows, columns)
   int64_t Mb;              // guide cells in block order, padded: nbi * nbj * 64 (0 if unused)
+  int64_t Mbg;             // rows of the cell-block buffer: Mb then (if Mb > 0) the text rows
+  int splits;              // key-range splits of the text-query pass
 };
 
 static Geom make_geom(int B, int H, int W, int w, int H_lr, int W_lr, int rho, int heads,
-                      int D, int radius, int guide_mode) {
+                      int D, int radius, int guide_mode, int64_t T) {
   Geom g;
   g.B = B; g.H = H; g.W = W; g.w = w; g.H_lr = H_lr; g.W_lr = W_lr; g.rho = rho;
-  g.heads = heads; g.D = D; g.radius = radius; g.guide_mode = guide_mode;
+  g.heads = heads; g.D = D; g.radius = radius; g.guide_mode = guide_mode; g.T = T;
   g.N = static_cast<int64_t>(H) * W;
   g.M = static_cast<int64_t>(H_lr) * W_lr;
   g.Mk = (g.M + kKeyTile - 1) / kKeyTile * kKeyTile;
   g.Mq = (g.M + kMaxQuery - 1) / kMaxQuery * kMaxQuery;
+  g.Tk = (T + kKeyTile - 1) / kKeyTile * kKeyTile;
+  g.Tq = (T + kMaxQuery - 1) / kMaxQuery * kMaxQuery;
+  g.Mg = g.Mk + g.Tk;
   g.n_wx = W / w; g.n_wy = H / w; g.nW = g.n_wx * g.n_wy;
   // The cos/sin table covers hi-res positions; guide positions beyond it (a guide grid
   // reaching past the hi-res extent) are evaluated directly with the same function.
@@ -59,6 +67,17 @@ static Geom make_geom(int B, int H, int W, int w, int H_lr, int W_lr, int rho, i
   g.nbi = (H_lr + 7) / 8;
   g.nbj = (W_lr + 7) / 8;
   g.Mb = (guide_mode != 0 && g.M > 0) ? static_cast<int64_t>(g.nbi) * g.nbj * kKeyTile : 0;
+  g.Mbg = g.Mb > 0 ? g.Mb + g.Tk : 0;
+  // Text queries attend to all N + M + T keys: few query blocks, so the key range is split
+  // to give the GPU about 1024 workgroups, each split at least 8 tiles long.
+  g.splits = 0;
+  if (T > 0) {
+    const int64_t qblocks = static_cast<int64_t>(B) * heads * (g.Tq / kMaxQuery);
+    const int64_t tiles = (g.N + g.Mg) / kKeyTile;
+    int64_t sp = (1024 + qblocks - 1) / qblocks;
+    sp = std::min(sp, std::max<int64_t>(1, tiles / 8));
+    g.splits = static_cast<int>(std::max<int64_t>(1, sp));
+  }
   return g;
 }
 
@@ -68,10 +87,13 @@ struct Workspace {
   bf16_t* k_hi;   // [B*heads][N][D]   window-first, rotated
   bf16_t* v_hi;   // [B*heads][N/64][D][64]  window-first, transposed tiles
   bf16_t* q_lr;   // [B*heads][Mq][D]  rotated, zero padded
-  bf16_t* k_lr;   // [B*heads][Mk][D]  rotated, zero padded
-  bf16_t* v_lr;   // [B*heads][Mk/64][D][64]
-  bf16_t* k_gb;   // [B*heads][Mb][D]  guide K in 8x8 cell blocks (guide modes 1, 2)
-  bf16_t* v_gb;   // [B*heads][Mb/64][D][64]
+  bf16_t* k_lr;   // [B*heads][Mg][D]  global keys: guide rows (Mk, zero padded), text rows (Tk)
+  bf16_t* v_lr;   // [B*heads][Mg/64][D][64]
+  bf16_t* k_gb;   // [B*heads][Mbg][D] guide K in 8x8 cell blocks, then text (guide modes 1, 2)
+  bf16_t* v_gb;   // [B*heads][Mbg/64][D][64]
+  bf16_t* q_tx;   // [B*heads][Tq][D]  text queries (scaled, zero padded)
+  float* o_part;  // [splits][B*heads][Tq][D]  text-query partial outputs (unnormalised)
+  float2* ml_part;  // [splits][B*heads][Tq]   their (running max, sum)
   size_t bytes;
 };
 
@@ -90,10 +112,13 @@ static Workspace carve(const Geom& g, void* base) {
   const size_t o_kh = take(bh * g.N * g.D * e);
   const size_t o_vh = take(bh * g.N * g.D * e);
   const size_t o_ql = take(bh * g.Mq * g.D * e);
-  const size_t o_kl = take(bh * g.Mk * g.D * e);
-  const size_t o_vl = take(bh * g.Mk * g.D * e);
-  const size_t o_kb = take(bh * g.Mb * g.D * e);
-  const size_t o_vb = take(bh * g.Mb * g.D * e);
+  const size_t o_kl = take(bh * g.Mg * g.D * e);
+  const size_t o_vl = take(bh * g.Mg * g.D * e);
+  const size_t o_kb = take(bh * g.Mbg * g.D * e);
+  const size_t o_vb = take(bh * g.Mbg * g.D * e);
+  const size_t o_qt = take(bh * g.Tq * g.D * e);
+  const size_t o_op = take(static_cast<size_t>(g.splits) * bh * g.Tq * g.D * sizeof(float));
+  const size_t o_ml = take(static_cast<size_t>(g.splits) * bh * g.Tq * sizeof(float2));
   char* b = static_cast<char*>(base);
   ws.cs = reinterpret_cast<double2*>(b + o_cs);
   ws.q_hi = reinterpret_cast<bf16_t*>(b + o_qh);
@@ -104,6 +129,9 @@ static Workspace carve(const Geom& g, void* base) {
   ws.v_lr = reinterpret_cast<bf16_t*>(b + o_vl);
   ws.k_gb = reinterpret_cast<bf16_t*>(b + o_kb);
   ws.v_gb = reinterpret_cast<bf16_t*>(b + o_vb);
+  ws.q_tx = reinterpret_cast<bf16_t*>(b + o_qt);
+  ws.o_part = reinterpret_cast<float*>(b + o_op);
+  ws.ml_part = reinterpret_cast<float2*>(b + o_ml);
   ws.bytes = off;
   return ws;
 }
@@ -132,63 +160,87 @@ __global__ void cos_sin_table_kernel(double2* cs, int P, int D, double log2_thet
 constexpr int kPrepThreads = 256;
 constexpr int kPrepRows = 4;
 
-// Q and K rows -> head-major, rotated.  Rows [0, N) of each batch are hi-res rows in
-// window-first order (source row r(p)), rows [N, N + Mq) are guide rows (source row
-// N + s, zero beyond M); Q guide rows pad to Mq, K guide rows to Mk.  Rows
-// [N + Mq, N + Mq + Mb) are a second copy of the guide K rows in 8x8 cell-block order
-// (zero for cells outside the guide grid), used by the guide-locality masks.  Q is also
-// multiplied by q_scale (the softmax scale times log2 e) before its single rounding to
-// bf16, so the attention kernel's scores come out in base-2 logits.
+// Q and K rows -> head-major, rotated.  The input rows are [text | hi | guide].  Prep rows
+// of a batch:
+//   [0, N)            hi-res rows in window-first order (source row T + r(p)) -> q_hi, k_hi;
+//   [N, N + Mq)       guide rows s (source T + N + s, zero beyond M) -> q_lr row s, and
+//                     k_lr row s for s < Mk;
+//   [.., + Mb)        guide cells in 8x8 block order (zero outside the grid) -> k_gb, used
+//                     by the guide-locality masks;
+//   [.., + Tq)        text rows x (source x, zero beyond T; position (0, 0), so RoPE is the
+//                     identity) -> q_tx row x, k_lr row Mk + x and, with cell blocks,
+//                     k_gb row Mb + x.
+// Q is also multiplied by q_scale (the softmax scale times log2 e) before its single
+// rounding to bf16, so the attention kernel's scores come out in base-2 logits.
 template <int D>
 __global__ __launch_bounds__(kPrepThreads) void prep_qk_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, bf16_t* __restrict__ q_hi,
     bf16_t* __restrict__ k_hi, bf16_t* __restrict__ q_lr, bf16_t* __restrict__ k_lr,
-    bf16_t* __restrict__ k_gb, const double2* __restrict__ cs, int P, double log2_theta,
-    int64_t N, int64_t M, int64_t Mq, int64_t Mk, int64_t Mb, int W, int w, int n_wx, int H_lr,
-    int W_lr, int nbj, int rho, int heads, int rope_on, double q_scale) {
+    bf16_t* __restrict__ k_gb, bf16_t* __restrict__ q_tx, const double2* __restrict__ cs,
+    int P, double log2_theta, int64_t T, int64_t N, int64_t M, int64_t Mq, int64_t Mk,
+    int64_t Mg, int64_t Mb, int64_t Mbg, int64_t Tk, int64_t Tq, int W, int w, int n_wx,
+    int H_lr, int W_lr, int nbj, int rho, int heads, int rope_on, double q_scale) {
   constexpr int CPH = D / 8;      // 16-byte chunks per head row
   constexpr int QUARTER = D / 4;  // rotation pairs per axis
-  // Per row of this block: source row (-1: zero row), destination rows of Q and K (-1:
-  // none), and the RoPE factors of its y and x positions.
-  __shared__ int64_t src_s[kPrepRows], dq_s[kPrepRows], dk_s[kPrepRows];
+  // Per row of this block: source row (-1: zero row), destinations (buffer row offsets in
+  // elements of one head row, -1: none), and the RoPE factors of its y and x positions.
+  __shared__ int64_t src_s[kPrepRows];
+  __shared__ bf16_t* dq_s[kPrepRows];
+  __shared__ bf16_t* dk_s[kPrepRows];
+  __shared__ bf16_t* dk2_s[kPrepRows];
+  __shared__ int64_t qst_s[kPrepRows], kst_s[kPrepRows], k2st_s[kPrepRows];  // per-head strides
   __shared__ int pos_s[kPrepRows][2];
   __shared__ double2 cs_s[kPrepRows][2][QUARTER];
-  const int64_t L = N + M;
+  const int64_t L = T + N + M;
   const int64_t b = blockIdx.y;
   const int tid = threadIdx.x;
   if (tid < kPrepRows) {
     const int64_t row = static_cast<int64_t>(blockIdx.x) * kPrepRows + tid;
-    int64_t src = -1, dq = -1, dk = -1;
+    const int64_t bh0 = b * heads;  // first (b, h) of this batch
+    int64_t src = -1;
+    bf16_t* dq = nullptr;
+    bf16_t* dk = nullptr;
+    bf16_t* dk2 = nullptr;
+    int64_t qst = 0, kst = 0, k2st = 0;
     int py = 0, px = 0;
     if (row < N) {
       const int r = window_first_to_raster(static_cast<int>(row), W, w, n_wx);
-      src = r;
+      src = T + r;
       py = r / W;
       px = r - py * W;
-      dq = row;  // hi rows: q_hi / k_hi row index
-      dk = row;
+      dq = q_hi + (bh0 * N + row) * D;  qst = N * D;
+      dk = k_hi + (bh0 * N + row) * D;  kst = N * D;
     } else if (row < N + Mq) {
       const int64_t s = row - N;
       if (s < M) {
-        src = N + s;
+        src = T + N + s;
         const int sy = static_cast<int>(s / W_lr);
         py = rho * sy;
         px = rho * static_cast<int>(s - static_cast<int64_t>(sy) * W_lr);
       }
-      dq = N + s;                       // guide rows: q_lr row s
-      dk = s < Mk ? N + s : -1;         // k_lr row s
+      dq = q_lr + (bh0 * Mq + s) * D;  qst = Mq * D;
+      if (s < Mk) { dk = k_lr + (bh0 * Mg + s) * D;  kst = Mg * D; }
     } else if (row < N + Mq + Mb) {
       const int64_t slot = row - N - Mq;
       int ci, cj;
       block_cell(slot, nbj, ci, cj);
-      if (ci < H_lr && cj < W_lr) src = N + static_cast<int64_t>(ci) * W_lr + cj;
+      if (ci < H_lr && cj < W_lr) src = T + N + static_cast<int64_t>(ci) * W_lr + cj;
       py = rho * ci;
       px = rho * cj;
-      dk = N + Mq + slot;               // k_gb row slot
+      dk = k_gb + (bh0 * Mbg + slot) * D;  kst = Mbg * D;
+    } else if (row < N + Mq + Mb + Tq) {
+      const int64_t x = row - N - Mq - Mb;
+      if (x < T) src = x;
+      dq = q_tx + (bh0 * Tq + x) * D;  qst = Tq * D;
+      if (x < Tk) {
+        dk = k_lr + (bh0 * Mg + Mk + x) * D;  kst = Mg * D;
+        if (Mb > 0) { dk2 = k_gb + (bh0 * Mbg + Mb + x) * D;  k2st = Mbg * D; }
+      }
     }
     src_s[tid] = src;
-    dq_s[tid] = dq;
-    dk_s[tid] = dk;
+    dq_s[tid] = dq;  qst_s[tid] = qst;
+    dk_s[tid] = dk;  kst_s[tid] = kst;
+    dk2_s[tid] = dk2;  k2st_s[tid] = k2st;
     pos_s[tid][0] = py;
     pos_s[tid][1] = px;
   }
@@ -203,13 +255,6 @@ __global__ __launch_bounds__(kPrepThreads) void prep_qk_kernel(
   }
 
   const int cpr = heads * CPH;  // chunks per row
-  auto dst_ptr = [&](int64_t d, int h, int j, bool is_q) -> bf16_t* {
-    if (d < 0) return nullptr;
-    const int64_t bh = b * heads + h;
-    if (d < N) return (is_q ? q_hi : k_hi) + (bh * N + d) * D + j * 8;
-    if (d < N + Mq) return (is_q ? q_lr + (bh * Mq + (d - N)) * D : k_lr + (bh * Mk + (d - N)) * D) + j * 8;
-    return k_gb + (bh * Mb + (d - N - Mq)) * D + j * 8;
-  };
   // task i = (row t, chunk c); t and c advance without divisions
   int t = tid / cpr, c = tid - (tid / cpr) * cpr;
   for (; t < kPrepRows; ) {
@@ -234,10 +279,12 @@ __global__ __launch_bounds__(kPrepThreads) void prep_qk_kernel(
         ko = ki;
       }
     }
-    bf16_t* dq = dst_ptr(dq_s[t], h, j, true);
-    bf16_t* dk = dst_ptr(dk_s[t], h, j, false);
-    if (dq) *reinterpret_cast<uint4*>(dq) = qo;
-    if (dk) *reinterpret_cast<uint4*>(dk) = ko;
+    bf16_t* dq = dq_s[t];
+    bf16_t* dk = dk_s[t];
+    bf16_t* dk2 = dk2_s[t];
+    if (dq) *reinterpret_cast<uint4*>(dq + h * qst_s[t] + j * 8) = qo;
+    if (dk) *reinterpret_cast<uint4*>(dk + h * kst_s[t] + j * 8) = ko;
+    if (dk2) *reinterpret_cast<uint4*>(dk2 + h * k2st_s[t] + j * 8) = ko;
     c += kPrepThreads;
     while (c >= cpr) {
       c -= cpr;
@@ -253,39 +300,42 @@ __device__ __forceinline__ int v_slot(int kappa) {
   return (kappa & ~12) | ((kappa & 4) << 1) | ((kappa & 8) >> 1);
 }
 
-// V rows -> 64-key tiles transposed to [D][64] (key order by v_slot).  Tile index
-// t < N/64 covers window-first hi rows [64 t, 64 t + 64); the next Mk/64 tiles cover guide
-// rows in raster order, and the last Mb/64 tiles the guide cells in 8x8 block order.
+// V rows -> 64-key tiles transposed to [D][64] (key order by v_slot).  Tiles of a batch:
+// [0, N/64) window-first hi rows -> v_hi; the next Mg/64 the global keys -> v_lr (guide
+// rows in raster order, zero padded to Mk, then text rows); the last Mbg/64 the cell-block
+// buffer -> v_gb (guide cells in 8x8 block order, then text rows).  Input rows are
+// [text | hi | guide].
 __global__ __launch_bounds__(kPrepThreads) void prep_v_kernel(
-    const bf16_t* __restrict__ v, bf16_t* v_hi, bf16_t* v_lr, bf16_t* v_gb, int64_t N,
-    int64_t M, int64_t Mk, int64_t Mb, int W, int w, int n_wx, int H_lr, int W_lr, int nbj,
-    int heads, int D) {
+    const bf16_t* __restrict__ v, bf16_t* v_hi, bf16_t* v_lr, bf16_t* v_gb, int64_t T,
+    int64_t N, int64_t M, int64_t Mk, int64_t Mg, int64_t Mb, int64_t Mbg, int W, int w,
+    int n_wx, int H_lr, int W_lr, int nbj, int heads, int D) {
   __shared__ bf16_t tile[kKeyTile][128 + 2];
-  const int64_t L = N + M;
+  const int64_t L = T + N + M;
   const int64_t b = blockIdx.y;
   const int64_t tile_id = blockIdx.x;
-  const int64_t n_hi_tiles = N / kKeyTile;
+  const int64_t n_hi = N / kKeyTile, n_g = Mg / kKeyTile;
   const int chunks_per_row = D / 8;
+  // source row (or -1) of key kr of this tile
+  auto source = [&](int kr) -> int64_t {
+    if (tile_id < n_hi) return T + window_first_to_raster(static_cast<int>(tile_id * kKeyTile + kr), W, w, n_wx);
+    if (tile_id < n_hi + n_g) {
+      const int64_t r = (tile_id - n_hi) * kKeyTile + kr;
+      if (r < Mk) return r < M ? T + N + r : -1;
+      return r - Mk < T ? r - Mk : -1;
+    }
+    const int64_t r = (tile_id - n_hi - n_g) * kKeyTile + kr;
+    if (r >= Mb) return r - Mb < T ? r - Mb : -1;
+    int ci, cj;
+    block_cell(r, nbj, ci, cj);
+    return (ci < H_lr && cj < W_lr) ? T + N + static_cast<int64_t>(ci) * W_lr + cj : -1;
+  };
   for (int h = 0; h < heads; ++h) {
     // load 64 rows x D of head h (each row 16-byte chunks)
     for (int i = threadIdx.x; i < kKeyTile * chunks_per_row; i += kPrepThreads) {
       const int kr = i / chunks_per_row, j = i - kr * chunks_per_row;
-      int64_t src_row;
-      bool valid = true;
-      if (tile_id < n_hi_tiles) {
-        src_row = window_first_to_raster(static_cast<int>(tile_id * kKeyTile + kr), W, w, n_wx);
-      } else if (tile_id < n_hi_tiles + Mk / kKeyTile) {
-        const int64_t s = (tile_id - n_hi_tiles) * kKeyTile + kr;
-        valid = s < M;
-        src_row = N + s;
-      } else {
-        int ci, cj;
-        block_cell((tile_id - n_hi_tiles - Mk / kKeyTile) * kKeyTile + kr, nbj, ci, cj);
-        valid = ci < H_lr && cj < W_lr;
-        src_row = valid ? N + static_cast<int64_t>(ci) * W_lr + cj : 0;
-      }
+      const int64_t src_row = source(kr);
       uint4 x = make_uint4(0, 0, 0, 0);
-      if (valid) x = *reinterpret_cast<const uint4*>(v + ((b * L + src_row) * heads + h) * D + j * 8);
+      if (src_row >= 0) x = *reinterpret_cast<const uint4*>(v + ((b * L + src_row) * heads + h) * D + j * 8);
       const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -295,15 +345,11 @@ __global__ __launch_bounds__(kPrepThreads) void prep_v_kernel(
     }
     __syncthreads();
     // write D rows x 64 keys; each thread writes 8 consecutive slots of one d-row
+    const int64_t bh = b * heads + h, tsz = static_cast<int64_t>(D) * kKeyTile;
     bf16_t* dst;
-    if (tile_id < n_hi_tiles)
-      dst = v_hi + ((b * heads + h) * n_hi_tiles + tile_id) * static_cast<int64_t>(D) * kKeyTile;
-    else if (tile_id < n_hi_tiles + Mk / kKeyTile)
-      dst = v_lr + ((b * heads + h) * (Mk / kKeyTile) + (tile_id - n_hi_tiles)) *
-                       static_cast<int64_t>(D) * kKeyTile;
-    else
-      dst = v_gb + ((b * heads + h) * (Mb / kKeyTile) + (tile_id - n_hi_tiles - Mk / kKeyTile)) *
-                       static_cast<int64_t>(D) * kKeyTile;
+    if (tile_id < n_hi) dst = v_hi + (bh * n_hi + tile_id) * tsz;
+    else if (tile_id < n_hi + n_g) dst = v_lr + (bh * n_g + (tile_id - n_hi)) * tsz;
+    else dst = v_gb + (bh * (Mbg / kKeyTile) + (tile_id - n_hi - n_g)) * tsz;
     for (int i = threadIdx.x; i < D * (kKeyTile / 8); i += kPrepThreads) {
       const int d = i / (kKeyTile / 8), s8 = (i - d * (kKeyTile / 8)) * 8;
       uint32_t wv[4];
@@ -328,13 +374,13 @@ struct AttnArgs {
   int64_t q_rows;         // rows per (b, h) of q
   const bf16_t* k_hi;     // [B*heads][N][D]
   const bf16_t* v_hi;     // [B*heads][N/64][D][64]
-  const bf16_t* k_lr;     // [B*heads][Mk][D]        guide K (cell-block copy with RECT)
-  const bf16_t* v_lr;     // [B*heads][Mk/64][D][64] guide V^T (likewise)
+  const bf16_t* k_lr;     // [B*heads][Mg][D]        global keys: guide rows, then text rows
+  const bf16_t* v_lr;     // [B*heads][Mg/64][D][64] (RECT: the cell-block buffer, Mg = Mbg)
   bf16_t* out;            // token-major [B][out_rows][heads][D]
   int64_t out_rows;       // rows per batch of out
   int64_t out_row0;       // first row of this pass inside a batch of out
-  int64_t N, M, Mk;
-  int heads, w2, hi;      // hi = 1: hi pass (local + guide keys), 0: guide pass
+  int64_t N, M, Mk, Mg, T, Mb;
+  int heads, w2;
   int W, w, n_wx, n_wy;   // hi pass: query row p (window-first) is written to raster row r(p)
   int radius;             // hi pass: windows within this distance (per axis) are visible
   int reach;              // RECT: the guide cells whose scaled position lies within `reach`
@@ -343,6 +389,9 @@ struct AttnArgs {
   int q_valid;            // valid query rows per (b, h)
   int blocks_per_bh;
   int total_blocks;
+  int splits;             // TEXT: key-range splits per query block
+  float* o_part;          // TEXT: [splits][B*heads][q_rows][D] unnormalised partial outputs
+  float2* ml_part;        // TEXT: [splits][B*heads][q_rows] (running max, sum)
 };
 
 // Workgroups are dealt round-robin to the 8 XCDs; remap so that each XCD works on a
@@ -415,7 +464,7 @@ __device__ __forceinline__ void wait_vm_and_barrier() {
 // a load writes LDS bytes [16 l, 16 l + 16) above the wave's base), two iterations ahead of
 // their first use.  Each lane picks the global 16-byte chunk that belongs at its LDS slot
 // under the XOR swizzle, so the LDS layout is the one the fragment reads expect.
-template <int D, int NWAVES, bool HI, bool RECT>
+template <int D, int NWAVES, bool HI, bool RECT, bool TEXT>
 __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   constexpr int NT = NWAVES * 64;
   constexpr int TILE_BYTES = kKeyTile * D * 2;       // one K or V tile
@@ -438,16 +487,28 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   const int ql = lane & 31, g = lane >> 5;
   const bool wave_b = wave >= NWAVES / 2;
   const int blk = xcd_remap(blockIdx.x, a.total_blocks);
-  const int bh = blk / a.blocks_per_bh, qb = blk - bh * a.blocks_per_bh;
+  const int bh = blk / a.blocks_per_bh;
+  const int rem_blk = blk - bh * a.blocks_per_bh;
+  const int qb = TEXT ? rem_blk / a.splits : rem_blk;
+  const int split = TEXT ? rem_blk - qb * a.splits : 0;
   const int b = bh / a.heads, h = bh - b * a.heads;
   const int q0 = qb * (NWAVES * 32);
 
   // Tile list.  Hi pass: the key tiles (w2/64 each) of the windows within `radius` of the
-  // query window, clipped to the grid, row-major; then the guide tiles: all of them in
-  // raster order, or (rect) the 8x8 cell blocks that meet the window's guide rectangle,
-  // each with a row/column mask.  Byte offsets of the table-driven tiles are staged in LDS
-  // once, so that picking a tile costs one LDS read and the loop keeps few scalars live.
-  int n_local = 0, n_guide = static_cast<int>(a.Mk / kKeyTile);
+  // query window, clipped to the grid, row-major; then the global tiles: guide tiles (all
+  // of them in raster order, or with RECT the 8x8 cell blocks that meet the window's
+  // guide rectangle, each with a row/column mask), then text tiles.  Guide pass: the
+  // global tiles.  Text pass: this split's share of all hi tiles followed by the global
+  // tiles.  Byte offsets of the table-driven tiles are staged in LDS once, so that
+  // picking a tile costs one LDS read and the loop keeps few scalars live.
+  const int n_hi_tiles = static_cast<int>(a.N / kKeyTile);
+  const int n_text_tiles = static_cast<int>((a.T + kKeyTile - 1) / kKeyTile);
+  int n_local = 0, n_rect = 0, n_guide = static_cast<int>(a.Mg / kKeyTile), t_base = 0;
+  if (TEXT) {
+    const int total = n_hi_tiles + static_cast<int>(a.Mg / kKeyTile);
+    t_base = static_cast<int>(static_cast<int64_t>(split) * total / a.splits);
+    n_guide = static_cast<int>(static_cast<int64_t>(split + 1) * total / a.splits) - t_base;
+  }
   if (HI) {
     const int tiles_per_win = a.w2 / kKeyTile;
     const int win = q0 / a.w2;
@@ -483,7 +544,13 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
           tile_mask_s[n_local + k] = rows | (cols << 8);
         }
       }
-      n_guide = ng;
+      // the text tiles follow the cell blocks in the same buffer
+      for (int x = tid; x < n_text_tiles; x += NT) {
+        tile_off_s[n_local + ng + x] = static_cast<uint32_t>(a.Mb / kKeyTile + x) * TILE_BYTES;
+        tile_mask_s[n_local + ng + x] = 0xffffu;
+      }
+      n_rect = ng;
+      n_guide = ng + n_text_tiles;
     }
     __syncthreads();
   }
@@ -503,9 +570,9 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   // as the K tile of the same keys, so one offset serves both.
   const char* k_hi_b = reinterpret_cast<const char*>(a.k_hi) + static_cast<int64_t>(bh) * a.N * (D * 2);
   const char* v_hi_b = reinterpret_cast<const char*>(a.v_hi) + static_cast<int64_t>(bh) * a.N * (D * 2);
-  const char* k_lr_b = reinterpret_cast<const char*>(a.k_lr) + static_cast<int64_t>(bh) * a.Mk * (D * 2);
-  const char* v_lr_b = reinterpret_cast<const char*>(a.v_lr) + static_cast<int64_t>(bh) * a.Mk * (D * 2);
-  // (with RECT, k_lr / v_lr / Mk describe the cell-block copy of the guide K / V^T)
+  const char* k_lr_b = reinterpret_cast<const char*>(a.k_lr) + static_cast<int64_t>(bh) * a.Mg * (D * 2);
+  const char* v_lr_b = reinterpret_cast<const char*>(a.v_lr) + static_cast<int64_t>(bh) * a.Mg * (D * 2);
+  // (with RECT, k_lr / v_lr / Mg describe the cell-block buffer)
   auto tile_src = [&](int t, const char*& kp, const char*& vp) __attribute__((always_inline)) {
     if (HI && t < n_local) {
       const uint32_t off = __builtin_amdgcn_readfirstlane(tile_off_s[t]);
@@ -515,8 +582,12 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
       const uint32_t off = __builtin_amdgcn_readfirstlane(tile_off_s[t]);
       kp = k_lr_b + off;
       vp = v_lr_b + off;
+    } else if (TEXT && t + t_base < n_hi_tiles) {
+      const uint32_t off = static_cast<uint32_t>(t + t_base) * TILE_BYTES;
+      kp = k_hi_b + off;
+      vp = v_hi_b + off;
     } else {
-      const uint32_t off = static_cast<uint32_t>(t - n_local) * TILE_BYTES;
+      const uint32_t off = static_cast<uint32_t>(t + t_base - (TEXT ? n_hi_tiles : n_local)) * TILE_BYTES;
       kp = k_lr_b + off;
       vp = v_lr_b + off;
     }
@@ -550,11 +621,21 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
     tile_src(t, kp, vp);
     issue_parts(nullptr, vp, dst, dst, 0, LOADS_PER_TILE);
   };
-  // Keys of tile t that exist (a prefix; the raster guide list ends in a partial tile) ...
-  auto tile_valid = [&](int t) __attribute__((always_inline)) -> int {
-    if (HI && (t < n_local || RECT)) return kKeyTile;
-    const int64_t rem = a.M - static_cast<int64_t>(t - n_local) * kKeyTile;
+  // Keys of tile t that exist (a prefix: the guide rows and the text rows of the global
+  // buffer each end in a partial tile) ...
+  auto global_valid = [&](int64_t r) __attribute__((always_inline)) -> int {
+    const int64_t rem = r < a.Mk ? a.M - r : a.T - (r - a.Mk);
     return rem < kKeyTile ? static_cast<int>(rem) : kKeyTile;
+  };
+  auto tile_valid = [&](int t) __attribute__((always_inline)) -> int {
+    if (HI && t < n_local) return kKeyTile;
+    if (RECT) {
+      if (t < n_local + n_rect) return kKeyTile;  // cell blocks: the cell mask decides
+      const int64_t rem = a.T - static_cast<int64_t>(t - n_local - n_rect) * kKeyTile;
+      return rem < kKeyTile ? static_cast<int>(rem) : kKeyTile;
+    }
+    if (TEXT && t + t_base < n_hi_tiles) return kKeyTile;
+    return global_valid(static_cast<int64_t>(t + t_base - (TEXT ? n_hi_tiles : n_local)) * kKeyTile);
   };
   // ... and, for a cell-block guide tile, which of its 8x8 cells are visible: bits 0-7 the
   // rows, bits 8-15 the columns (0xffff: all).
@@ -815,10 +896,27 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   if (wave_b) run.template operator()<true>();
   else run.template operator()<false>();
 
-  // ---- epilogue: normalise and store (lane: query ql, dims dt*32 + 8*(r/4) + 4g + r%4)
+  // ---- epilogue (lane: query ql, dims dt*32 + 8*(r/4) + 4g + r%4)
   const float lt = sum_with_partner32(l_run);
-  const float inv = 1.0f / lt;
   const int qrow = q0 + wave * 32 + ql;
+  if (TEXT) {
+    // partial result of this key range: unnormalised O, the running max and the sum, all
+    // relative to that max (base-2 logits); text_combine_kernel merges the splits
+    const int64_t prow = (static_cast<int64_t>(split) * a.total_blocks / a.blocks_per_bh + bh) *
+                             a.q_rows + qrow;
+    float* op = a.o_part + prow * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d0 = dt * 32 + 8 * rg + 4 * g;
+        *reinterpret_cast<f32x4*>(op + d0) =
+            f32x4{o[dt][4 * rg], o[dt][4 * rg + 1], o[dt][4 * rg + 2], o[dt][4 * rg + 3]};
+      }
+    if (g == 0) a.ml_part[prow] = make_float2(m_run, lt);
+    return;
+  }
+  const float inv = 1.0f / lt;
   if (qrow < a.q_valid) {
     // The hi pass undoes the window-first permutation here: window-first row qrow goes to
     // its raster row, so O needs no separate inverse-permutation pass.
@@ -836,23 +934,54 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   }
 }
 
-template <int D, int NWAVES, bool HI, bool RECT>
+// Merges the key-range splits of the text-query pass: with m* the largest running max,
+// O = sum_s 2^(m_s - m*) O_s / sum_s 2^(m_s - m*) l_s, stored as bf16 in text row x of
+// (b, h).  One thread per pair of dims.
+__global__ void text_combine_kernel(const float* __restrict__ o_part, const float2* __restrict__ ml,
+                                    bf16_t* out, int splits, int64_t bh_total, int64_t Tq,
+                                    int64_t out_rows, int heads, int D) {
+  const int64_t x = blockIdx.x, bh = blockIdx.y;
+  const int d = 2 * threadIdx.x;
+  if (d >= D) return;
+  float mx = -INFINITY;
+  for (int sp = 0; sp < splits; ++sp) mx = fmaxf(mx, ml[(sp * bh_total + bh) * Tq + x].x);
+  float l = 0.0f, o0 = 0.0f, o1 = 0.0f;
+  for (int sp = 0; sp < splits; ++sp) {
+    const int64_t prow = (sp * bh_total + bh) * Tq + x;
+    const float2 m = ml[prow];
+    const float f = exp2f(m.x - mx);
+    l += f * m.y;
+    o0 += f * o_part[prow * D + d];
+    o1 += f * o_part[prow * D + d + 1];
+  }
+  const int64_t b = bh / heads, h = bh - b * heads;
+  *reinterpret_cast<uint32_t*>(out + ((b * out_rows + x) * heads + h) * D + d) = pack_bf16x2(o0 / l, o1 / l);
+}
+
+template <int D, int NWAVES, bool HI, bool RECT, bool TEXT>
 static void launch_attn(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, NWAVES, HI, RECT>), dim3(a.total_blocks), dim3(NWAVES * 64),
-                     0, s, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, NWAVES, HI, RECT, TEXT>), dim3(a.total_blocks),
+                     dim3(NWAVES * 64), 0, s, a);
 }
 
-// hi: hi pass (else guide pass); rect: guide tokens restricted to a per-window rectangle
+enum PassKind { kPassHi = 0, kPassHiRect = 1, kPassGuide = 2, kPassText = 3 };
+
 template <int D>
-static void dispatch_attn_d(int nwaves, bool hi, bool rect, const AttnArgs& a, hipStream_t s) {
-  if (!hi) launch_attn<D, 8, false, false>(a, s);
-  else if (nwaves == 8) rect ? launch_attn<D, 8, true, true>(a, s) : launch_attn<D, 8, true, false>(a, s);
-  else rect ? launch_attn<D, 2, true, true>(a, s) : launch_attn<D, 2, true, false>(a, s);
+static void dispatch_attn_d(int nwaves, PassKind kind, const AttnArgs& a, hipStream_t s) {
+  switch (kind) {
+    case kPassGuide: launch_attn<D, 8, false, false, false>(a, s); break;
+    case kPassText: launch_attn<D, 8, false, false, true>(a, s); break;
+    case kPassHiRect:
+      nwaves == 8 ? launch_attn<D, 8, true, true, false>(a, s) : launch_attn<D, 2, true, true, false>(a, s);
+      break;
+    default:
+      nwaves == 8 ? launch_attn<D, 8, true, false, false>(a, s) : launch_attn<D, 2, true, false, false>(a, s);
+  }
 }
 
-static void dispatch_attn(int D, int nwaves, bool hi, bool rect, const AttnArgs& a, hipStream_t s) {
-  if (D == 128) dispatch_attn_d<128>(nwaves, hi, rect, a, s);
-  else dispatch_attn_d<64>(nwaves, hi, rect, a, s);
+static void dispatch_attn(int D, int nwaves, PassKind kind, const AttnArgs& a, hipStream_t s) {
+  if (D == 128) dispatch_attn_d<128>(nwaves, kind, a, s);
+  else dispatch_attn_d<64>(nwaves, kind, a, s);
 }
 
 // ------------------------------------------------------------------ host side
@@ -866,29 +995,31 @@ int timer_commit(uhla_timer* t);
 static int64_t max_table_tiles(const Geom& g) {
   const int tpw = g.w * g.w / kKeyTile;
   const int reach = g.guide_mode == 1 ? 0 : g.radius;
+  const bool rect = g.guide_mode != 0 && g.M > 0;
   int64_t best = 0;
   for (int wy = 0; wy < g.n_wy; ++wy)
     for (int wx = 0; wx < g.n_wx; ++wx) {
       auto span = [](int c, int r, int n) { return std::min(n - 1, c + r) - std::max(0, c - r) + 1; };
       int64_t n = static_cast<int64_t>(span(wy, g.radius, g.n_wy)) * span(wx, g.radius, g.n_wx) * tpw;
-      if (g.guide_mode != 0 && g.M > 0) {
+      if (rect) {
         const int gy0 = std::max(0, wy - reach), gy1 = std::min(g.n_wy - 1, wy + reach);
         const int gx0 = std::max(0, wx - reach), gx1 = std::min(g.n_wx - 1, wx + reach);
         const int i0 = (gy0 * g.w + g.rho - 1) / g.rho, i1 = std::min(g.H_lr, ((gy1 + 1) * g.w + g.rho - 1) / g.rho);
         const int j0 = (gx0 * g.w + g.rho - 1) / g.rho, j1 = std::min(g.W_lr, ((gx1 + 1) * g.w + g.rho - 1) / g.rho);
         if (i0 < i1 && j0 < j1)
           n += static_cast<int64_t>(((i1 - 1) >> 3) - (i0 >> 3) + 1) * (((j1 - 1) >> 3) - (j0 >> 3) + 1);
+        n += g.Tk / kKeyTile;  // text tiles follow the cell blocks in the table
       }
       best = std::max(best, n);
     }
   return best;
 }
 
-static int validate_forward(const void* q, const void* k, const void* v, void* o, int B, int H,
-                            int W, int w, int H_lr, int W_lr, int rho, int heads, int D,
-                            int radius, int guide_mode) {
+static int validate_forward(const void* q, const void* k, const void* v, void* o, int B,
+                            int64_t T, int H, int W, int w, int H_lr, int W_lr, int rho,
+                            int heads, int D, int radius, int guide_mode) {
   if (!q || !k || !v || !o) return fail_arg("null pointer");
-  if (B < 1 || H < 1 || W < 1 || w < 1 || heads < 1 || D < 1 || H_lr < 0 || W_lr < 0)
+  if (B < 1 || H < 1 || W < 1 || w < 1 || heads < 1 || D < 1 || H_lr < 0 || W_lr < 0 || T < 0)
     return fail_arg("sizes out of range");
   if (H % w || W % w) return fail_arg("w must divide H and W");
   if ((H_lr == 0) != (W_lr == 0)) return fail_arg("H_lr and W_lr must both be zero or not");
@@ -904,31 +1035,32 @@ static int validate_forward(const void* q, const void* k, const void* v, void* o
   if (B > 65535) return fail_unsupported("batch too large");
   const int64_t N = static_cast<int64_t>(H) * W, M = static_cast<int64_t>(H_lr) * W_lr;
   const int64_t bh = static_cast<int64_t>(B) * heads;
-  // 32-bit row indices inside the kernels; 32-bit workgroup counts
-  if (N > (int64_t(1) << 30) || M > (int64_t(1) << 30) ||
-      bh * ((N > M ? N : M) / 64 + 1) > 0x7fffffff)
+  // 32-bit row indices and tile byte offsets inside the kernels; 32-bit workgroup counts
+  if (N > (int64_t(1) << 26) || M > (int64_t(1) << 26) || T > (int64_t(1) << 24) ||
+      bh * ((N + M + T) / 64 + 1) > 0x7fffffff)
     return fail_unsupported("problem too large");
   // radius capped so that the neighbourhood span stays far inside int range
   if (max_table_tiles(make_geom(B, H, W, w, H_lr, W_lr, rho, heads, D,
-                                std::min(radius, H / w + W / w), guide_mode)) > kMaxTableTiles)
-    return fail_unsupported("too many key tiles per window (window size or radius too large)");
+                                std::min(radius, H / w + W / w), guide_mode, T)) > kMaxTableTiles)
+    return fail_unsupported("too many key tiles per window (window size, radius or text too large)");
   return UHLA_OK;
 }
 
-static int forward_impl(const void* q, const void* k, const void* v, void* o, int B, int H, int W,
-                        int w, int H_lr, int W_lr, int rho, int heads, int D, float scale,
-                        float theta, int radius, int guide_mode, void* workspace,
+static int forward_impl(const void* q, const void* k, const void* v, void* o, int B, int64_t T,
+                        int H, int W, int w, int H_lr, int W_lr, int rho, int heads, int D,
+                        float scale, float theta, int radius, int guide_mode, void* workspace,
                         size_t workspace_bytes, void* stream, uhla_timer* timer) {
-  int st = validate_forward(q, k, v, o, B, H, W, w, H_lr, W_lr, rho, heads, D, radius, guide_mode);
+  int st = validate_forward(q, k, v, o, B, T, H, W, w, H_lr, W_lr, rho, heads, D, radius, guide_mode);
   if (st) return st;
   // a radius reaching past the grid is the whole grid
   radius = std::min(radius, H / w + W / w);
-  const Geom g = make_geom(B, H, W, w, H_lr, W_lr, rho, heads, D, radius, guide_mode);
+  const Geom g = make_geom(B, H, W, w, H_lr, W_lr, rho, heads, D, radius, guide_mode, T);
   const Workspace need = carve(g, nullptr);
   if (!workspace || workspace_bytes < need.bytes)
     return (set_detail("workspace too small"), UHLA_ERR_WORKSPACE);
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail_arg("workspace must be 256-byte aligned");
-  const size_t tensor_bytes = static_cast<size_t>(B) * (g.N + g.M) * heads * D * 2;
+  const int64_t L = T + g.N + g.M;
+  const size_t tensor_bytes = static_cast<size_t>(B) * L * heads * D * 2;
   if (ranges_overlap(o, tensor_bytes, q, tensor_bytes) ||
       ranges_overlap(o, tensor_bytes, k, tensor_bytes) ||
       ranges_overlap(o, tensor_bytes, v, tensor_bytes) ||
@@ -938,7 +1070,6 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool rope_on = theta > 0.0f;
   const float sc = scale > 0.0f ? scale : 1.0f / sqrtf(static_cast<float>(D));
-  const int64_t L = g.N + g.M;
   const int w2 = w * w;
 
 #define UHLA_STEP(call, name)          \
@@ -964,24 +1095,26 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
   const bf16_t* vb = static_cast<const bf16_t*>(v);
   if (timer) timer_begin(timer, UHLA_STAGE_PREP_HI, s);
   {
-    const int64_t rows = g.N + g.Mq + g.Mb;
+    const int64_t rows = g.N + g.Mq + g.Mb + g.Tq;
     const dim3 grid(static_cast<unsigned>((rows + kPrepRows - 1) / kPrepRows), B);
     const double l2t = rope_on ? log2(static_cast<double>(theta)) : 0.0;
     const double qs = static_cast<double>(sc) * 1.4426950408889634;
     if (D == 128)
       hipLaunchKernelGGL(prep_qk_kernel<128>, grid, dim3(kPrepThreads), 0, s, qb, kb, ws.q_hi,
-                         ws.k_hi, ws.q_lr, ws.k_lr, ws.k_gb, ws.cs, g.P, l2t, g.N, g.M, g.Mq, g.Mk,
-                         g.Mb, W, w, g.n_wx, H_lr, W_lr, g.nbj, rho, heads, rope_on ? 1 : 0, qs);
+                         ws.k_hi, ws.q_lr, ws.k_lr, ws.k_gb, ws.q_tx, ws.cs, g.P, l2t, T, g.N,
+                         g.M, g.Mq, g.Mk, g.Mg, g.Mb, g.Mbg, g.Tk, g.Tq, W, w, g.n_wx, H_lr, W_lr,
+                         g.nbj, rho, heads, rope_on ? 1 : 0, qs);
     else
       hipLaunchKernelGGL(prep_qk_kernel<64>, grid, dim3(kPrepThreads), 0, s, qb, kb, ws.q_hi,
-                         ws.k_hi, ws.q_lr, ws.k_lr, ws.k_gb, ws.cs, g.P, l2t, g.N, g.M, g.Mq, g.Mk,
-                         g.Mb, W, w, g.n_wx, H_lr, W_lr, g.nbj, rho, heads, rope_on ? 1 : 0, qs);
+                         ws.k_hi, ws.q_lr, ws.k_lr, ws.k_gb, ws.q_tx, ws.cs, g.P, l2t, T, g.N,
+                         g.M, g.Mq, g.Mk, g.Mg, g.Mb, g.Mbg, g.Tk, g.Tq, W, w, g.n_wx, H_lr, W_lr,
+                         g.nbj, rho, heads, rope_on ? 1 : 0, qs);
     st = check_launch("prep_qk_kernel");
     if (st) return st;
-    const int64_t tiles = (g.N + g.Mk + g.Mb) / kKeyTile;
+    const int64_t tiles = (g.N + g.Mg + g.Mbg) / kKeyTile;
     UHLA_STEP(hipLaunchKernelGGL(prep_v_kernel, dim3(static_cast<unsigned>(tiles), B), dim3(kPrepThreads), 0, s,
-                                 vb, ws.v_hi, ws.v_lr, ws.v_gb, g.N, g.M, g.Mk, g.Mb, W, w, g.n_wx,
-                                 H_lr, W_lr, g.nbj, heads, D),
+                                 vb, ws.v_hi, ws.v_lr, ws.v_gb, T, g.N, g.M, g.Mk, g.Mg, g.Mb, g.Mbg,
+                                 W, w, g.n_wx, H_lr, W_lr, g.nbj, heads, D),
               "prep_v_kernel");
   }
   if (timer) timer_end(timer, UHLA_STAGE_PREP_HI, s);
@@ -990,7 +1123,10 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
 
   AttnArgs a{};
   a.k_hi = ws.k_hi; a.v_hi = ws.v_hi; a.k_lr = ws.k_lr; a.v_lr = ws.v_lr;
-  a.N = g.N; a.M = g.M; a.Mk = g.Mk; a.heads = heads; a.w2 = w2;
+  a.N = g.N; a.M = g.M; a.Mk = g.Mk; a.Mg = g.Mg; a.T = T; a.Mb = g.Mb;
+  a.heads = heads; a.w2 = w2;
+  a.out = static_cast<bf16_t*>(o); a.out_rows = L;
+  const int64_t BH = static_cast<int64_t>(B) * heads;
 
   // 3. hi pass
   if (timer) timer_begin(timer, UHLA_STAGE_ATTN_HI, s);
@@ -999,71 +1135,96 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
     const int qt = nwaves * 32;
     AttnArgs h = a;
     h.q = ws.q_hi; h.q_rows = g.N;
-    h.out = static_cast<bf16_t*>(o); h.out_rows = L; h.out_row0 = 0;
+    h.out_row0 = T;
     h.W = W; h.w = w; h.n_wx = g.n_wx; h.n_wy = g.n_wy;
     h.radius = radius;
     const bool rect = guide_mode != 0 && g.M > 0;
     if (rect) {
-      h.k_lr = ws.k_gb; h.v_lr = ws.v_gb; h.Mk = g.Mb;
+      h.k_lr = ws.k_gb; h.v_lr = ws.v_gb; h.Mg = g.Mbg;
     }
     h.reach = guide_mode == 1 ? 0 : radius;
     h.rho = rho; h.H_lr = H_lr; h.W_lr = W_lr; h.nbj = g.nbj;
-    h.hi = 1; h.q_valid = static_cast<int>(g.N);
+    h.q_valid = static_cast<int>(g.N);
     h.blocks_per_bh = static_cast<int>(g.N / qt);
-    h.total_blocks = static_cast<int>(static_cast<int64_t>(B) * heads * h.blocks_per_bh);
-    UHLA_STEP(dispatch_attn(D, nwaves, true, rect, h, s), "attn_fwd_kernel(hi)");
+    h.total_blocks = static_cast<int>(BH * h.blocks_per_bh);
+    UHLA_STEP(dispatch_attn(D, nwaves, rect ? kPassHiRect : kPassHi, h, s), "attn_fwd_kernel(hi)");
   }
   if (timer) timer_end(timer, UHLA_STAGE_ATTN_HI, s);
 
-  // 4. guide pass
+  // 4. guide pass (guide keys, then text keys)
   if (timer) timer_begin(timer, UHLA_STAGE_ATTN_LR, s);
   if (g.M > 0) {
     AttnArgs l = a;
     l.q = ws.q_lr; l.q_rows = g.Mq;
-    l.out = static_cast<bf16_t*>(o); l.out_rows = L; l.out_row0 = g.N;
-    l.hi = 0; l.q_valid = static_cast<int>(g.M);
+    l.out_row0 = T + g.N;
+    l.q_valid = static_cast<int>(g.M);
     l.blocks_per_bh = static_cast<int>(g.Mq / kMaxQuery);
-    l.total_blocks = static_cast<int>(static_cast<int64_t>(B) * heads * l.blocks_per_bh);
-    UHLA_STEP(dispatch_attn(D, 8, false, false, l, s), "attn_fwd_kernel(guide)");
+    l.total_blocks = static_cast<int>(BH * l.blocks_per_bh);
+    UHLA_STEP(dispatch_attn(D, 8, kPassGuide, l, s), "attn_fwd_kernel(guide)");
   }
   if (timer) timer_end(timer, UHLA_STAGE_ATTN_LR, s);
 
   // 5. the inverse permutation of O is fused into the hi pass's stores (stage left empty)
   if (timer) timer_begin(timer, UHLA_STAGE_UNPERMUTE, s);
   if (timer) timer_end(timer, UHLA_STAGE_UNPERMUTE, s);
+
+  // 6. text queries: every key, split over the key range, then merged
+  if (timer) timer_begin(timer, UHLA_STAGE_ATTN_TEXT, s);
+  if (T > 0) {
+    AttnArgs x = a;
+    x.q = ws.q_tx; x.q_rows = g.Tq;
+    x.q_valid = static_cast<int>(T);
+    x.splits = g.splits;
+    x.blocks_per_bh = static_cast<int>(g.Tq / kMaxQuery) * g.splits;
+    x.total_blocks = static_cast<int>(BH * x.blocks_per_bh);
+    x.o_part = ws.o_part; x.ml_part = ws.ml_part;
+    UHLA_STEP(dispatch_attn(D, 8, kPassText, x, s), "attn_fwd_kernel(text)");
+    UHLA_STEP(hipLaunchKernelGGL(text_combine_kernel, dim3(static_cast<unsigned>(T), static_cast<unsigned>(BH)),
+                                 dim3(D / 2), 0, s, ws.o_part, ws.ml_part, static_cast<bf16_t*>(o),
+                                 g.splits, BH, g.Tq, L, heads, D),
+              "text_combine_kernel");
+  }
+  if (timer) timer_end(timer, UHLA_STAGE_ATTN_TEXT, s);
 #undef UHLA_STEP
   if (timer) return timer_commit(timer);
   return UHLA_OK;
 }
 
-static size_t workspace_bytes(int B, int H, int W, int w, int H_lr, int W_lr, int rho, int heads,
-                              int head_dim, int radius, int guide_mode) {
-  if (B < 1 || H < 1 || W < 1 || w < 1 || heads < 1 || H_lr < 0 || W_lr < 0) return 0;
+static size_t workspace_bytes(int B, int64_t T, int H, int W, int w, int H_lr, int W_lr, int rho,
+                              int heads, int head_dim, int radius, int guide_mode) {
+  if (B < 1 || H < 1 || W < 1 || w < 1 || heads < 1 || H_lr < 0 || W_lr < 0 || T < 0) return 0;
   if (H % w || W % w || (H_lr == 0) != (W_lr == 0)) return 0;
   if (head_dim != 64 && head_dim != 128) return 0;
   if (radius < 0 || guide_mode < 0 || guide_mode > 2) return 0;
   if (static_cast<int64_t>(H_lr) * W_lr > 0 && rho < 1) return 0;
-  return carve(make_geom(B, H, W, w, H_lr, W_lr, rho, heads, head_dim, radius, guide_mode), nullptr).bytes;
+  return carve(make_geom(B, H, W, w, H_lr, W_lr, rho, heads, head_dim, radius, guide_mode, T),
+               nullptr).bytes;
 }
 
 }  // namespace uhla
 
 extern "C" size_t uhla_forward_workspace_bytes(int B, int H, int W, int w, int H_lr, int W_lr,
                                                int heads, int head_dim) {
-  return uhla::workspace_bytes(B, H, W, w, H_lr, W_lr, 1, heads, head_dim, 1, 0);
+  return uhla::workspace_bytes(B, 0, H, W, w, H_lr, W_lr, 1, heads, head_dim, 1, 0);
 }
 
 extern "C" size_t uhla_forward_masked_workspace_bytes(int B, int H, int W, int w, int H_lr,
                                                       int W_lr, int rho, int heads, int head_dim,
                                                       int radius, int guide_mode) {
-  return uhla::workspace_bytes(B, H, W, w, H_lr, W_lr, rho, heads, head_dim, radius, guide_mode);
+  return uhla::workspace_bytes(B, 0, H, W, w, H_lr, W_lr, rho, heads, head_dim, radius, guide_mode);
+}
+
+extern "C" size_t uhla_forward_text_workspace_bytes(int B, int T, int H, int W, int w, int H_lr,
+                                                    int W_lr, int rho, int heads, int head_dim,
+                                                    int radius, int guide_mode) {
+  return uhla::workspace_bytes(B, T, H, W, w, H_lr, W_lr, rho, heads, head_dim, radius, guide_mode);
 }
 
 extern "C" int uhla_forward(const void* q, const void* k, const void* v, void* o, int B, int H,
                             int W, int w, int H_lr, int W_lr, int rho, int heads, int head_dim,
                             float scale, float theta, void* workspace, size_t workspace_bytes,
                             void* stream) {
-  return uhla::forward_impl(q, k, v, o, B, H, W, w, H_lr, W_lr, rho, heads, head_dim, scale,
+  return uhla::forward_impl(q, k, v, o, B, 0, H, W, w, H_lr, W_lr, rho, heads, head_dim, scale,
                             theta, 1, 0, workspace, workspace_bytes, stream, nullptr);
 }
 
@@ -1072,8 +1233,17 @@ extern "C" int uhla_forward_masked(const void* q, const void* k, const void* v, 
                                    int head_dim, float scale, float theta, int radius,
                                    int guide_mode, void* workspace, size_t workspace_bytes,
                                    void* stream) {
-  return uhla::forward_impl(q, k, v, o, B, H, W, w, H_lr, W_lr, rho, heads, head_dim, scale,
+  return uhla::forward_impl(q, k, v, o, B, 0, H, W, w, H_lr, W_lr, rho, heads, head_dim, scale,
                             theta, radius, guide_mode, workspace, workspace_bytes, stream, nullptr);
+}
+
+extern "C" int uhla_forward_text(const void* q, const void* k, const void* v, void* o, int B,
+                                 int T, int H, int W, int w, int H_lr, int W_lr, int rho,
+                                 int heads, int head_dim, float scale, float theta, int radius,
+                                 int guide_mode, void* workspace, size_t workspace_bytes,
+                                 void* stream, uhla_timer* timer) {
+  return uhla::forward_impl(q, k, v, o, B, T, H, W, w, H_lr, W_lr, rho, heads, head_dim, scale,
+                            theta, radius, guide_mode, workspace, workspace_bytes, stream, timer);
 }
 
 extern "C" int uhla_forward_timed(const void* q, const void* k, const void* v, void* o, int B,
@@ -1081,7 +1251,7 @@ extern "C" int uhla_forward_timed(const void* q, const void* k, const void* v, v
                                   int head_dim, float scale, float theta, void* workspace,
                                   size_t workspace_bytes, void* stream, uhla_timer* timer) {
   if (!timer) return uhla::fail_arg("null timer");
-  return uhla::forward_impl(q, k, v, o, B, H, W, w, H_lr, W_lr, rho, heads, head_dim, scale,
+  return uhla::forward_impl(q, k, v, o, B, 0, H, W, w, H_lr, W_lr, rho, heads, head_dim, scale,
                             theta, 1, 0, workspace, workspace_bytes, stream, timer);
 }
 
@@ -1091,6 +1261,6 @@ extern "C" int uhla_forward_masked_timed(const void* q, const void* k, const voi
                                          int radius, int guide_mode, void* workspace,
                                          size_t workspace_bytes, void* stream, uhla_timer* timer) {
   if (!timer) return uhla::fail_arg("null timer");
-  return uhla::forward_impl(q, k, v, o, B, H, W, w, H_lr, W_lr, rho, heads, head_dim, scale,
+  return uhla::forward_impl(q, k, v, o, B, 0, H, W, w, H_lr, W_lr, rho, heads, head_dim, scale,
                             theta, radius, guide_mode, workspace, workspace_bytes, stream, timer);
 }

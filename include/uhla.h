@@ -42,6 +42,9 @@ typedef enum {
   UHLA_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
 } uhla_status;
 
+/* Stage timer (measurement only; see uhla_timer_create below). */
+typedef struct uhla_timer uhla_timer;
+
 /*
  * Window-first permutation of the hi-res segment, and its exact inverse.
  *
@@ -152,6 +155,32 @@ int uhla_forward_masked(const void* q, const void* k, const void* v, void* o,
                         int radius, int guide_mode,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Text tokens in the joint sequence ([UltraGen/it §2], [UltraGen/fr §2.C]: the DiT input is
+ * text | hi-res | guide).  Q, K, V, O: bf16 [B, T + N + M, heads, head_dim], rows 0..T-1
+ * the text tokens, then the hi-res rows and the guide rows as in uhla_forward.  The mask
+ * of uhla_forward_masked (radius, guide_mode) is extended by the plain joint-attention
+ * reading: a text query attends to every key, and every query attends to every text key.
+ * Text tokens sit at position (0, 0), so RoPE leaves them unrotated.  T = 0 is
+ * uhla_forward_masked.  The text queries run as one extra pass over all keys, split into
+ * key ranges whose partial results are merged (log-sum-exp) before the bf16 store.
+ * timer: NULL, or a timer as for uhla_forward_timed (stage UHLA_STAGE_ATTN_TEXT times the
+ *   text pass).
+ * workspace: at least uhla_forward_text_workspace_bytes(...) bytes (0 on invalid
+ *   arguments).
+ * Errors: as uhla_forward_masked, plus UHLA_ERR_ARG for T < 0 and UHLA_ERR_UNSUPPORTED for
+ * T > 2^24.
+ */
+size_t uhla_forward_text_workspace_bytes(int B, int T, int H, int W, int w, int H_lr,
+                                         int W_lr, int rho, int heads, int head_dim, int radius,
+                                         int guide_mode);
+int uhla_forward_text(const void* q, const void* k, const void* v, void* o,
+                      int B, int T, int H, int W, int w, int H_lr, int W_lr, int rho,
+                      int heads, int head_dim, float scale, float theta,
+                      int radius, int guide_mode,
+                      void* workspace, size_t workspace_bytes, void* stream,
+                      uhla_timer* timer);
+
 /* Human-readable name of a status code (static storage). */
 const char* uhla_strerror(int status);
 
@@ -176,10 +205,10 @@ typedef enum {
   UHLA_STAGE_ATTN_HI = 3,   /* hi-res block-sparse attention */
   UHLA_STAGE_ATTN_LR = 4,   /* guide-only attention */
   UHLA_STAGE_UNPERMUTE = 5, /* inverse permutation of O (fused into the hi pass: empty) */
-  UHLA_NUM_STAGES = 6
+  UHLA_STAGE_ATTN_TEXT = 6, /* text queries over all keys (uhla_forward_text), merge */
+  UHLA_NUM_STAGES = 7
 } uhla_stage;
 
-typedef struct uhla_timer uhla_timer;
 int uhla_timer_create(int max_calls, uhla_timer** out);
 int uhla_timer_destroy(uhla_timer* timer);
 int uhla_timer_reset(uhla_timer* timer);

@@ -205,6 +205,41 @@ def test_masked_workspace_bytes(lib, g, mode):
         assert got == lib.uhla_forward_workspace_bytes(*g)
 
 
+def expected_text_extra(B, T, H, W, w, H_lr, W_lr, heads, d, guide_mode):
+    """Extra workspace bytes with T text tokens: text rows appended to the global-key
+    buffers (and to the cell-block buffers), text queries, and the split partial results
+    (splits = min(ceil(1024 / query blocks), max(1, key tiles // 8)))."""
+    al = lambda x: (x + 255) // 256 * 256
+    N, M = H * W, H_lr * W_lr
+    Mk, Tk, Tq = (M + 63) // 64 * 64, (T + 63) // 64 * 64, (T + 255) // 256 * 256
+    Mb = ((H_lr + 7) // 8) * ((W_lr + 7) // 8) * 64 if (guide_mode and M) else 0
+    e, bh = 2, B * heads
+    qblocks = bh * (Tq // 256)
+    splits = min(-(-1024 // qblocks), max(1, (N + Mk + Tk) // 64 // 8)) if T else 0
+    grown = [(bh * (Mk + Tk) * d * e, bh * Mk * d * e)] * 2 + \
+        [(bh * (Mb + (Tk if Mb else 0)) * d * e, bh * Mb * d * e)] * 2
+    extra = sum(al(a) - al(b) for a, b in grown)
+    return extra + al(bh * Tq * d * e) + al(splits * bh * Tq * d * 4) + al(splits * bh * Tq * 8)
+
+
+@pytest.mark.parametrize("g", GEOMS)
+@pytest.mark.parametrize("T,mode", [(0, 0), (1, 0), (77, 1), (512, 2)])
+def test_text_workspace_bytes(lib, g, T, mode):
+    B, H, W, w, H_lr, W_lr, heads, d = g
+    got = lib.uhla_forward_text_workspace_bytes(B, T, H, W, w, H_lr, W_lr, 4, heads, d, 1, mode)
+    assert got == expected_workspace(*g, guide_mode=mode) + \
+        expected_text_extra(B, T, H, W, w, H_lr, W_lr, heads, d, mode)
+
+
+def test_forward_text_rejects(lib):
+    a = fwd_args()
+    f = lib.uhla_forward_text
+    assert f(*a[:5], -1, *a[5:15], 1, 0, *a[15:], NULL) == api.UHLA_ERR_ARG
+    assert f(*a[:5], 1 << 25, *a[5:15], 1, 0, *a[15:], NULL) == api.UHLA_ERR_UNSUPPORTED
+    assert f(*a[:5], 8, *a[5:15], 1, 5, *a[15:], NULL) == api.UHLA_ERR_ARG
+    assert lib.uhla_forward_text_workspace_bytes(1, -1, 32, 32, 8, 8, 8, 4, 2, 64, 1, 0) == 0
+
+
 def test_masked_workspace_bytes_invalid(lib):
     f = lib.uhla_forward_masked_workspace_bytes
     assert f(1, 32, 32, 8, 8, 8, 4, 2, 64, -1, 0) == 0
