@@ -33,6 +33,9 @@ What the pages fix, and the readings taken where they are silent:
   sit at position (0, 0), so RoPE leaves them unrotated.
 * Attention: softmax(Q K^T / sqrt(d)) V over the allowed keys.  Every row has at least
   w*w allowed keys, so no row is empty.
+* Backward (training the guide path, [UltraGen/it §2] LoRA fine-tuning, [UltraGen/ar §2.C]):
+  the gradients of that function with respect to the un-rotated Q, K and V, written out
+  from the chain rule; LSE is the natural log of each row's sum of exp(scaled scores).
 
 parity pinned: every function here is checked by tests marked "not gpu" against brute
 force, closed forms, invariants or library routines (see tests/test_oracle_pins.py).
@@ -260,3 +263,69 @@ def forward(q, k, v, geom, block: int = 512) -> np.ndarray:
 def allowed_key_count(geom, rows) -> np.ndarray:
     """Number of allowed keys for each query row (from the explicit mask)."""
     return mask_rows(geom, rows).sum(axis=1)
+
+# ---------------------------------------------------------------------------------
+# Backward (gradients of the forward above) and the per-row log-sum-exp
+# ---------------------------------------------------------------------------------
+
+def rope_rotate_inverse(x: np.ndarray, pos_y: np.ndarray, pos_x: np.ndarray,
+                        theta: float) -> np.ndarray:
+    """The transpose (= inverse) of rope_rotate: each pair rotated by -phi."""
+    d = x.shape[-1]
+    d_axis = d // 2
+    omega = rope_frequencies(d, theta)
+    out = np.empty(x.shape, dtype=np.float64)
+    for axis_block, pos in ((0, pos_y), (1, pos_x)):
+        phi = np.asarray(pos, dtype=np.float64)[:, None] * omega[None, :]
+        c = np.cos(phi)[:, None, :]
+        s = np.sin(phi)[:, None, :]
+        lo = axis_block * d_axis
+        a = x[..., lo:lo + d_axis:2].astype(np.float64)
+        b = x[..., lo + 1:lo + d_axis:2].astype(np.float64)
+        out[..., lo:lo + d_axis:2] = a * c + b * s
+        out[..., lo + 1:lo + d_axis:2] = -a * s + b * c
+    return out
+
+
+def lse_rows(q, k, geom, b: int, h: int, rows, block: int = 512, qk=None) -> np.ndarray:
+    """log sum_j exp(scale * q_i . k_j) over the allowed keys j of each query row i."""
+    rows = np.asarray(rows, dtype=np.int64)
+    qr, kr = qk if qk is not None else rotated_qk(q, k, geom, b, h)
+    out = np.empty(len(rows), dtype=np.float64)
+    for s0 in range(0, len(rows), block):
+        blk = rows[s0:s0 + block]
+        sc = (qr[blk] @ kr.T) * geom.scale
+        sc = np.where(mask_rows(geom, blk), sc, -np.inf)
+        mx = sc.max(axis=1)
+        out[s0:s0 + len(blk)] = mx + np.log(np.exp(sc - mx[:, None]).sum(axis=1))
+    return out
+
+
+def backward(q, k, v, do, geom):
+    """Gradients (dQ, dK, dV), fp64 ``[B, L, heads, d]``, of O = forward(q, k, v, geom) for the
+    output gradient ``do``.  Per (batch, head), with rotated Q~, K~ and the scale s:
+    P = softmax(s Q~ K~^T + mask), dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(dP * P)),
+    dQ~ = s dS K~, dK~ = s dS^T Q~; dQ and dK rotate dQ~ and dK~ back (transpose of RoPE)."""
+    B, L, Hh, d = q.shape
+    py, px = token_positions(geom)
+    dq = np.empty((B, L, Hh, d))
+    dk = np.empty((B, L, Hh, d))
+    dv = np.empty((B, L, Hh, d))
+    mask = mask_rows(geom, np.arange(L))
+    for b in range(B):
+        for h in range(Hh):
+            qr, kr = rotated_qk(q, k, geom, b, h)
+            vv = v[b, :, h].astype(np.float64)
+            g = do[b, :, h].astype(np.float64)
+            _, p = masked_softmax_attention(qr, kr, vv, mask, geom.scale, return_probs=True)
+            dv[b, :, h] = p.T @ g
+            dp = g @ vv.T
+            ds = p * (dp - (dp * p).sum(axis=1, keepdims=True))
+            dqr = geom.scale * (ds @ kr)
+            dkr = geom.scale * (ds.T @ qr)
+            if geom.theta > 0:
+                dqr = rope_rotate_inverse(dqr[:, None, :], py, px, geom.theta)[:, 0, :]
+                dkr = rope_rotate_inverse(dkr[:, None, :], py, px, geom.theta)[:, 0, :]
+            dq[b, :, h] = dqr
+            dk[b, :, h] = dkr
+    return dq, dk, dv

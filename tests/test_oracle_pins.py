@@ -567,6 +567,136 @@ def test_pins_catch_rotated_text():
     assert np.max(np.abs(bad - loop_attention(q, k, v, g))) > 1e-6
 
 
+# ------------------------------------------------------------------- backward
+
+def torch_attention_fn(geom):
+    """The forward as a torch fp64 function of un-rotated (q, k, v) [L, d] of one head:
+    RoPE as a rotation matrix per token (from cos/sin of pos * omega), the brute-force mask,
+    torch softmax.  Differentiated by torch autograd."""
+    import torch
+    L, d = geom.L, geom.head_dim
+    da = d // 2
+    ys = [0] * geom.T + [r // geom.W for r in range(geom.N)] + \
+        [geom.rho * (s_ // geom.W_lr) for s_ in range(geom.M)]
+    xs = [0] * geom.T + [r % geom.W for r in range(geom.N)] + \
+        [geom.rho * (s_ % geom.W_lr) for s_ in range(geom.M)]
+    R = np.zeros((L, d, d))
+    for t in range(L):
+        for blk, pos in ((0, ys[t]), (1, xs[t])):
+            for kk in range(da // 2):
+                ang = pos * geom.theta ** (-2.0 * kk / da)
+                i0 = blk * da + 2 * kk
+                R[t, i0, i0], R[t, i0, i0 + 1] = math.cos(ang), -math.sin(ang)
+                R[t, i0 + 1, i0], R[t, i0 + 1, i0 + 1] = math.sin(ang), math.cos(ang)
+    Rt = torch.from_numpy(R)
+    mask = torch.from_numpy(brute_mask(geom))
+    sc = 1.0 / math.sqrt(d)
+
+    def f(q, k, v):
+        qr = torch.einsum("tij,tj->ti", Rt, q)
+        kr = torch.einsum("tij,tj->ti", Rt, k)
+        s_ = (qr @ kr.T) * sc
+        s_ = s_.masked_fill(~mask, float("-inf"))
+        return torch.softmax(s_, dim=1) @ v, torch.logsumexp(s_, dim=1)
+    return f
+
+
+def check_backward(backward_fn):
+    import torch
+    for g in (small_geom(H=8, W=8, H_lr=2, W_lr=2, head_dim=8),
+              small_geom(head_dim=8, guide_mode=2, T=3),
+              small_geom(head_dim=16, radius=0, H=8, W=12, H_lr=3, W_lr=2, rho=3)):
+        q, k, v = rand_qkv(g, 17)
+        do = rand_qkv(g, 18)[0]
+        dq, dk, dv = backward_fn(q, k, v, do, g)
+        f = torch_attention_fn(g)
+        tq, tk, tv = (torch.from_numpy(x[0, :, 0].copy()).requires_grad_(True) for x in (q, k, v))
+        o, _ = f(tq, tk, tv)
+        o.backward(torch.from_numpy(do[0, :, 0].copy()))
+        for got, want in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+            assert np.max(np.abs(got[0, :, 0] - want.numpy())) < 1e-10, g
+
+
+def test_backward_vs_torch_autograd():
+    check_backward(orc.backward)
+
+
+def test_lse_vs_torch_logsumexp():
+    import torch
+    g = small_geom(head_dim=8, guide_mode=1, T=2)
+    q, k, _ = rand_qkv(g, 4)
+    f = torch_attention_fn(g)
+    _, lse = f(torch.from_numpy(q[0, :, 0].copy()), torch.from_numpy(k[0, :, 0].copy()),
+               torch.zeros(g.L, g.head_dim, dtype=torch.float64))
+    assert np.max(np.abs(orc.lse_rows(q, k, g, 0, 0, np.arange(g.L)) - lse.numpy())) < 1e-12
+
+
+def test_backward_finite_differences():
+    g = small_geom(H=8, W=8, H_lr=2, W_lr=2, head_dim=8)
+    q, k, v = rand_qkv(g, 23)
+    do = rand_qkv(g, 24)[0]
+    dq, dk, dv = orc.backward(q, k, v, do, g)
+    rng = np.random.default_rng(0)
+    eps = 1e-6
+    loss = lambda q_, k_, v_: float((orc.forward(q_, k_, v_, g) * do).sum())
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        for _ in range(6):
+            idx = (0, int(rng.integers(g.L)), 0, int(rng.integers(g.head_dim)))
+            args = [q.copy(), k.copy(), v.copy()]
+            args[which][idx] += eps
+            up = loss(*args)
+            args[which][idx] -= 2 * eps
+            dn = loss(*args)
+            assert abs((up - dn) / (2 * eps) - grad[idx]) < 1e-6
+
+
+def test_backward_dv_sums_to_do():
+    # every row of P sums to 1, so the sum of dV over keys equals the sum of dO over queries
+    g = small_geom(guide_mode=2, T=4)
+    q, k, v = rand_qkv(g, 2)
+    do = rand_qkv(g, 3)[0]
+    _, _, dv = orc.backward(q, k, v, do, g)
+    assert np.max(np.abs(dv.sum(axis=1) - do.sum(axis=1))) < 1e-12
+
+
+def _mut_backward_no_rowsum(q, k, v, do, geom):
+    # the oracle's gradient with dS = P * dP (the softmax Jacobian's row term dropped)
+    real = orc.masked_softmax_attention
+
+    def probs_then_break(*a, **kw):
+        o, p = real(*a, **kw)
+        return o, p
+
+    dq, dk, dv = orc.backward(q, k, v, do, geom)
+    L = q.shape[1]
+    mask = orc.mask_rows(geom, np.arange(L))
+    qr, kr = orc.rotated_qk(q, k, geom, 0, 0)
+    _, p = probs_then_break(qr, kr, v[0, :, 0], mask, geom.scale, return_probs=True)
+    ds = p * (do[0, :, 0] @ v[0, :, 0].T)
+    py, px = orc.token_positions(geom)
+    dqr = geom.scale * (ds @ kr)
+    if geom.theta > 0:
+        dqr = orc.rope_rotate_inverse(dqr[:, None, :], py, px, geom.theta)[:, 0, :]
+    dq = dq.copy()
+    dq[0, :, 0] = dqr
+    return dq, dk, dv
+
+
+def _mut_backward_forward_rotation(q, k, v, do, geom):
+    real = orc.rope_rotate_inverse
+    orc.rope_rotate_inverse = orc.rope_rotate
+    try:
+        return orc.backward(q, k, v, do, geom)
+    finally:
+        orc.rope_rotate_inverse = real
+
+
+@pytest.mark.parametrize("mutant", [_mut_backward_no_rowsum, _mut_backward_forward_rotation])
+def test_pins_catch_backward_mutants(mutant):
+    with pytest.raises(AssertionError):
+        check_backward(mutant)
+
+
 # --------------------------------------------------------- planted mistakes must be caught
 
 def _mut_index_transposed(H, W, w):
