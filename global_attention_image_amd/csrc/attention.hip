@@ -23,11 +23,10 @@
 // from LDS, B = P^T, which is the S^T accumulator converted to bf16 in place.
 #include <algorithm>
 
-#include "uhla_internal.h"
+#include "tile_common.h"
 
 namespace uhla {
 
-constexpr int kKeyTile = 64;     // keys per K/V tile
 constexpr int kMaxQuery = 256;   // queries per workgroup (8 waves x 32)
 constexpr int kMaxTableTiles = 1024;  // table-driven key tiles (neighbour + cell-block) per window
 
@@ -293,13 +292,6 @@ __global__ __launch_bounds__(kPrepThreads) void prep_qk_kernel(
   }
 }
 
-// Position of key `kappa` (0..63) of a tile inside the stored V^T row: within each group
-// of 16 keys the two middle quads are swapped (bits 2 and 3 of the index exchanged), so
-// that the 8 keys one lane feeds into a 32x32x16 MFMA sit in 16 contiguous bytes.
-__device__ __forceinline__ int v_slot(int kappa) {
-  return (kappa & ~12) | ((kappa & 4) << 1) | ((kappa & 8) >> 1);
-}
-
 // V rows -> 64-key tiles transposed to [D][64] (key order by v_slot).  Tiles of a batch:
 // [0, N/64) window-first hi rows -> v_hi; the next Mg/64 the global keys -> v_lr (guide
 // rows in raster order, zero padded to Mk, then text rows); the last Mbg/64 the cell-block
@@ -394,65 +386,9 @@ struct AttnArgs {
   float2* ml_part;        // TEXT: [splits][B*heads][q_rows] (running max, sum)
 };
 
-// Workgroups are dealt round-robin to the 8 XCDs; remap so that each XCD works on a
-// contiguous range of (b, h, window): neighbouring windows and the guide K/V of one head
-// then share that XCD's L2.
-__device__ __forceinline__ int xcd_remap(int i, int G) {
-  const int x = i & 7, j = i >> 3;
-  const int per = G >> 3, rem = G & 7;
-  return x < rem ? x * (per + 1) + j : rem * (per + 1) + (x - rem) * per + j;
-}
-
-// Lanes l and l ^ 32 hold the same query (different keys).  v_permlane32_swap exchanges
-// the upper half of its first operand with the lower half of its second: with both
-// operands = x, the two results hold x[l] and x[l ^ 32] in some order on every lane.
-__device__ __forceinline__ float max_with_partner32(float x) {
-  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
-}
-__device__ __forceinline__ float sum_with_partner32(float x) {
-  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-}
-
-template <int D>
-__device__ __forceinline__ int k_swizzle(int row) {
-  // 16-byte chunk XOR swizzle so 16 lanes reading the same chunk of 16 rows hit 16
-  // distinct bank groups.
-  return D == 128 ? (row & 15) : ((row >> 1) & 7);
-}
-__device__ __forceinline__ int v_swizzle(int row) { return (row >> 1) & 7; }
-
 constexpr int kStages = 4;  // LDS ring: tiles t, t+1 are read while t+2, t+3 land
 constexpr int kQkAhead = 3;  // K fragment reads in flight ahead of the QK^T MFMAs (steps)
 constexpr int kPvAhead = 4;  // V fragment reads in flight ahead of the PV MFMAs
-
-// 32-bit LDS address of a __shared__ object
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-      (const __attribute__((address_space(3))) char*)(p)));
-}
-
-// Asynchronous 16-byte global -> LDS copy per lane (global_load_lds_dwordx4): lane l
-// reads gbase + voff and writes LDS bytes [lds + 16 l, lds + 16 l + 16).  gbase and lds
-// are wave-uniform.  The instruction has no register results (data goes to LDS), and it
-// is issued from asm so that the compiler does not treat every later LDS read as
-// possibly overlapping it (it cannot tell the ring stages apart and would wait for all
-// in-flight tiles); completion is awaited explicitly by wait_vm_and_barrier.  M0 is
-// written by the compiler just before the block, hence the wait state.
-__device__ __forceinline__ void dma_16b(const char* gbase, int voff, uint32_t lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "{m0}"(lds)
-               : "memory");
-}
-
-// Wait until at most N vector-memory operations of this wave are outstanding, then
-// barrier.  The direct-to-LDS tile loads are vector-memory operations, so this makes the
-// older tiles visible to the whole workgroup while the newest ones stay in flight.  The
-// "memory" clobber keeps the compiler from moving LDS accesses across the barrier.
-template <int N>
-__device__ __forceinline__ void wait_vm_and_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
-}
 
 // One workgroup = NWAVES waves x 32 queries.  Waves [0, NWAVES/2) ("A") and
 // [NWAVES/2, NWAVES) ("B") are offset by half an iteration: in iteration t, A runs
