@@ -39,6 +39,13 @@ EXPORTS = {
     "uhla_forward_text": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_int] * 10
                           + [ctypes.c_float, ctypes.c_float, ctypes.c_int, ctypes.c_int,
                              ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
+    "uhla_forward_lse": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int] * 10
+                         + [ctypes.c_float, ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                            ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "uhla_backward_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 10),
+    "uhla_backward": (ctypes.c_int, [ctypes.c_void_p] * 9 + [ctypes.c_int] * 9
+                      + [ctypes.c_float, ctypes.c_float, ctypes.c_int,
+                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "uhla_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "uhla_last_error_detail": (ctypes.c_char_p, []),
     "uhla_timer_create": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_void_p)]),
@@ -256,3 +263,53 @@ def forward(q, k, v, H, W, w, H_lr, W_lr, rho=4, scale=0.0, theta=10000.0, out=N
         st = lib.uhla_forward_timed(*args, *tail, timer.h)
     _check(st, "uhla_forward")
     return out
+
+
+def forward_lse(q, k, v, H, W, w, H_lr, W_lr, rho=4, scale=0.0, theta=10000.0, radius=1,
+                guide_mode=0, T=0, out=None, lse=None, workspace=None):
+    """uhla_forward_lse: the forward plus the per-row natural-log sum of exp of the scaled
+    scores, fp32 [B, heads, L].  Returns (out, lse)."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, n, torch.bfloat16)
+    B, L, Hh, d = q.shape
+    if L != T + H * W + H_lr * W_lr:
+        raise ValueError("token count does not match the grids")
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, Hh, L), dtype=torch.float32, device=q.device) if lse is None else lse
+    _require(out, "out", torch.bfloat16)
+    _require(lse, "lse", torch.float32)
+    if workspace is None:
+        workspace = alloc_workspace(B, H, W, w, H_lr, W_lr, Hh, d, q.device, rho=rho,
+                                    radius=radius, guide_mode=guide_mode, T=T)
+    st = load().uhla_forward_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, T, H, W, w,
+                                 H_lr, W_lr, rho, Hh, d, float(scale), float(theta), int(radius),
+                                 int(guide_mode), _ptr(workspace), workspace.numel(), _stream(q))
+    _check(st, "uhla_forward_lse")
+    return out, lse
+
+
+def backward(q, k, v, o, do, lse, H, W, w, H_lr, W_lr, rho=4, scale=0.0, theta=10000.0,
+             radius=1, dq=None, dk=None, dv=None, workspace=None):
+    """uhla_backward: (dq, dk, dv) bf16 for the output gradient do (guide mode 0, no text)."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _require(t, n, torch.bfloat16)
+    _require(lse, "lse", torch.float32)
+    B, L, Hh, d = q.shape
+    if L != H * W + H_lr * W_lr:
+        raise ValueError("token count does not match the grids")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    if workspace is None:
+        n = int(load().uhla_backward_workspace_bytes(B, H, W, w, H_lr, W_lr, rho, Hh, d, radius))
+        if n == 0:
+            raise ValueError("invalid geometry")
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    st = load().uhla_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                              _ptr(dk), _ptr(dv), B, H, W, w, H_lr, W_lr, rho, Hh, d, float(scale),
+                              float(theta), int(radius), _ptr(workspace), workspace.numel(),
+                              _stream(q))
+    _check(st, "uhla_backward")
+    return dq, dk, dv

@@ -384,6 +384,7 @@ struct AttnArgs {
   int splits;             // TEXT: key-range splits per query block
   float* o_part;          // TEXT: [splits][B*heads][q_rows][D] unnormalised partial outputs
   float2* ml_part;        // TEXT: [splits][B*heads][q_rows] (running max, sum)
+  float* lse;             // optional [B*heads][out_rows]: natural-log sum of exp(scaled scores)
 };
 
 constexpr int kStages = 4;  // LDS ring: tiles t, t+1 are read while t+2, t+3 land
@@ -857,6 +858,9 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
     // The hi pass undoes the window-first permutation here: window-first row qrow goes to
     // its raster row, so O needs no separate inverse-permutation pass.
     const int orow_idx = HI ? window_first_to_raster(qrow, a.W, a.w, a.n_wx) : qrow;
+    if (a.lse && g == 0)  // scores are base-2 logits: ln(sum e^s) = ln 2 (m + log2 l)
+      a.lse[static_cast<int64_t>(bh) * a.out_rows + a.out_row0 + orow_idx] =
+          (m_run + __log2f(lt)) * 0.69314718055994531f;
     bf16_t* orow = a.out + ((static_cast<int64_t>(b) * a.out_rows + a.out_row0 + orow_idx) * a.heads + h) * D;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
@@ -874,8 +878,8 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
 // O = sum_s 2^(m_s - m*) O_s / sum_s 2^(m_s - m*) l_s, stored as bf16 in text row x of
 // (b, h).  One thread per pair of dims.
 __global__ void text_combine_kernel(const float* __restrict__ o_part, const float2* __restrict__ ml,
-                                    bf16_t* out, int splits, int64_t bh_total, int64_t Tq,
-                                    int64_t out_rows, int heads, int D) {
+                                    bf16_t* out, float* lse, int splits, int64_t bh_total,
+                                    int64_t Tq, int64_t out_rows, int heads, int D) {
   const int64_t x = blockIdx.x, bh = blockIdx.y;
   const int d = 2 * threadIdx.x;
   if (d >= D) return;
@@ -892,6 +896,7 @@ __global__ void text_combine_kernel(const float* __restrict__ o_part, const floa
   }
   const int64_t b = bh / heads, h = bh - b * heads;
   *reinterpret_cast<uint32_t*>(out + ((b * out_rows + x) * heads + h) * D + d) = pack_bf16x2(o0 / l, o1 / l);
+  if (lse && d == 0) lse[bh * out_rows + x] = (mx + __log2f(l)) * 0.69314718055994531f;
 }
 
 template <int D, int NWAVES, bool HI, bool RECT, bool TEXT>
@@ -985,7 +990,8 @@ static int validate_forward(const void* q, const void* k, const void* v, void* o
 static int forward_impl(const void* q, const void* k, const void* v, void* o, int B, int64_t T,
                         int H, int W, int w, int H_lr, int W_lr, int rho, int heads, int D,
                         float scale, float theta, int radius, int guide_mode, void* workspace,
-                        size_t workspace_bytes, void* stream, uhla_timer* timer) {
+                        size_t workspace_bytes, void* stream, uhla_timer* timer,
+                        float* lse = nullptr) {
   int st = validate_forward(q, k, v, o, B, T, H, W, w, H_lr, W_lr, rho, heads, D, radius, guide_mode);
   if (st) return st;
   // a radius reaching past the grid is the whole grid
@@ -1002,6 +1008,10 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
       ranges_overlap(o, tensor_bytes, v, tensor_bytes) ||
       ranges_overlap(o, tensor_bytes, workspace, need.bytes))
     return fail_arg("o overlaps an input or the workspace");
+  const size_t lse_bytes = static_cast<size_t>(B) * heads * L * sizeof(float);
+  if (lse && (reinterpret_cast<uintptr_t>(lse) % 4 || ranges_overlap(lse, lse_bytes, o, tensor_bytes) ||
+              ranges_overlap(lse, lse_bytes, workspace, need.bytes)))
+    return fail_arg("lse misaligned or overlapping o or the workspace");
   const Workspace ws = carve(g, workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool rope_on = theta > 0.0f;
@@ -1062,6 +1072,7 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
   a.N = g.N; a.M = g.M; a.Mk = g.Mk; a.Mg = g.Mg; a.T = T; a.Mb = g.Mb;
   a.heads = heads; a.w2 = w2;
   a.out = static_cast<bf16_t*>(o); a.out_rows = L;
+  a.lse = lse;
   const int64_t BH = static_cast<int64_t>(B) * heads;
 
   // 3. hi pass
@@ -1117,7 +1128,7 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
     UHLA_STEP(dispatch_attn(D, 8, kPassText, x, s), "attn_fwd_kernel(text)");
     UHLA_STEP(hipLaunchKernelGGL(text_combine_kernel, dim3(static_cast<unsigned>(T), static_cast<unsigned>(BH)),
                                  dim3(D / 2), 0, s, ws.o_part, ws.ml_part, static_cast<bf16_t*>(o),
-                                 g.splits, BH, g.Tq, L, heads, D),
+                                 lse, g.splits, BH, g.Tq, L, heads, D),
               "text_combine_kernel");
   }
   if (timer) timer_end(timer, UHLA_STAGE_ATTN_TEXT, s);
@@ -1199,4 +1210,15 @@ extern "C" int uhla_forward_masked_timed(const void* q, const void* k, const voi
   if (!timer) return uhla::fail_arg("null timer");
   return uhla::forward_impl(q, k, v, o, B, 0, H, W, w, H_lr, W_lr, rho, heads, head_dim, scale,
                             theta, radius, guide_mode, workspace, workspace_bytes, stream, timer);
+}
+
+extern "C" int uhla_forward_lse(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, int T, int H, int W, int w, int H_lr, int W_lr, int rho,
+                                int heads, int head_dim, float scale, float theta, int radius,
+                                int guide_mode, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (!lse) return uhla::fail_arg("null lse");
+  return uhla::forward_impl(q, k, v, o, B, T, H, W, w, H_lr, W_lr, rho, heads, head_dim, scale,
+                            theta, radius, guide_mode, workspace, workspace_bytes, stream, nullptr,
+                            lse);
 }

@@ -1,0 +1,785 @@
+// Hierarchical local attention backward on gfx950: dQ, dK, dV for the mask of uhla_forward
+// with any neighbourhood radius (all guide tokens visible to hi-res queries, guide queries
+// seeing guide keys only), from Q, K, V, O, dO and the forward's per-row log-sum-exp.
+//
+// Math per (batch, head), rotated Q~ K~, scale s: P = exp(s Q~ K~^T - lse) on the allowed
+// pairs, dV = P^T dO, dP = dO V^T, dS = P (dP - D) with D = rowsum(dO O), dQ~ = s dS K~,
+// dK~ = s dS^T Q~; dQ and dK rotate dQ~ and dK~ back (the transpose of RoPE).
+//
+// Pipeline (caller's stream, no allocation):
+//   1. fp64 cos/sin table (as the forward);
+//   2. bwd_rows_kernel: per (b, h) buffers with hi rows window-first then guide rows,
+//      padded to 128: Qb = rope(Q) * s * log2 e (the forward's base-2 query), Kb = rope(K),
+//      Vb, dOb; bwd_aux_kernel: per 64-row tile, lse2 = lse * log2 e (pad rows +inf) and D;
+//      bwd_transpose_kernel: Q, K, dO as 64-row tiles transposed to [D][64];
+//   3. bwd_dq_kernel (query-outer, the forward's tile lists): per key tile S, dP (two
+//      32x32x16 MFMA chains from K and V tiles), dS, and dQ^T += K^T dS^T;
+//   4. bwd_dkv_kernel (key-outer, the transposed mask: a hi window's keys are seen by the
+//      queries of its neighbour windows, a guide key by every hi and guide query):
+//      per query tile S, dP, dS and dV^T += dO^T P, dK^T += Q^T dS.
+// Both write bf16 gradients in the caller's raster layout, undoing RoPE in the epilogue.
+#include <algorithm>
+
+#include "tile_common.h"
+
+namespace uhla {
+
+namespace {
+
+constexpr int kBwdRowsPerBlock = 4;
+constexpr int kBwdThreads = 256;
+constexpr int kBwdMaxTiles = 1024;  // neighbour-window tiles per window (table in LDS)
+constexpr int kAuxBytes = 2 * kKeyTile * 4;  // per tile: 64 lse2 then 64 D values
+
+struct BwdGeom {
+  int B, H, W, w, H_lr, W_lr, rho, heads, D, radius;
+  int64_t N, M, R;  // R: rows per (b, h) = N + guide rows padded to 128
+  int n_wx, n_wy, P;
+};
+
+BwdGeom make_bwd_geom(int B, int H, int W, int w, int H_lr, int W_lr, int rho, int heads, int D,
+                      int radius) {
+  BwdGeom g;
+  g.B = B; g.H = H; g.W = W; g.w = w; g.H_lr = H_lr; g.W_lr = W_lr; g.rho = rho;
+  g.heads = heads; g.D = D; g.radius = radius;
+  g.N = static_cast<int64_t>(H) * W;
+  g.M = static_cast<int64_t>(H_lr) * W_lr;
+  g.R = g.N + (g.M + 127) / 128 * 128;
+  g.n_wx = W / w; g.n_wy = H / w;
+  g.P = H > W ? H : W;
+  return g;
+}
+
+struct BwdWorkspace {
+  double2* cs;
+  bf16_t *qb, *kb, *vb, *dob;  // [B*heads][R][D]
+  bf16_t *qt, *kt, *dot;       // [B*heads][R/64][D][64]
+  float* aux;                  // [B*heads][R/64][128]
+  size_t bytes;
+};
+
+BwdWorkspace carve_bwd(const BwdGeom& g, void* base) {
+  BwdWorkspace ws;
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    const size_t o = off;
+    off = align_up(off + n, 256);
+    return o;
+  };
+  const size_t rows = static_cast<size_t>(g.B) * g.heads * g.R;
+  const size_t mat = rows * g.D * sizeof(bf16_t);
+  const size_t o_cs = take(sizeof(double2) * g.P * (g.D / 4));
+  size_t o_m[7];
+  for (auto& x : o_m) x = take(mat);
+  const size_t o_aux = take(rows / kKeyTile * kAuxBytes);
+  char* b = static_cast<char*>(base);
+  ws.cs = reinterpret_cast<double2*>(b + o_cs);
+  bf16_t** mats[7] = {&ws.qb, &ws.kb, &ws.vb, &ws.dob, &ws.qt, &ws.kt, &ws.dot};
+  for (int i = 0; i < 7; ++i) *mats[i] = reinterpret_cast<bf16_t*>(b + o_m[i]);
+  ws.aux = reinterpret_cast<float*>(b + o_aux);
+  ws.bytes = off;
+  return ws;
+}
+
+}  // namespace
+
+__global__ void bwd_cos_sin_kernel(double2* cs, int P, int D, double log2_theta) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int quarter = D / 4;
+  if (i >= P * quarter) return;
+  const int pos = i / quarter, k = i - pos * quarter;
+  cs[i] = rope_cos_sin(pos, k, D / 2, log2_theta);
+}
+
+// Raster source row and RoPE position of buffer row `row` (hi rows window-first, then guide
+// rows); -1 for padding rows.
+__device__ __forceinline__ int64_t bwd_source(int64_t row, int64_t N, int64_t M, int W, int w,
+                                              int n_wx, int W_lr, int rho, int& py, int& px) {
+  if (row < N) {
+    const int r = window_first_to_raster(static_cast<int>(row), W, w, n_wx);
+    py = r / W;
+    px = r - py * W;
+    return r;
+  }
+  const int64_t s = row - N;
+  if (s >= M) {
+    py = px = 0;
+    return -1;
+  }
+  const int sy = static_cast<int>(s / W_lr);
+  py = rho * sy;
+  px = rho * static_cast<int>(s - static_cast<int64_t>(sy) * W_lr);
+  return N + s;
+}
+
+// Q, K, V, dO rows -> per (b, h) buffers [R][D]: Q rotated and scaled by q_scale in fp64
+// and rounded once (as the forward), K rotated, V and dO copied; zero padding rows.
+template <int D>
+__global__ __launch_bounds__(kBwdThreads) void bwd_rows_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const bf16_t* __restrict__ dout, bf16_t* __restrict__ qb, bf16_t* __restrict__ kb,
+    bf16_t* __restrict__ vb, bf16_t* __restrict__ dob, const double2* __restrict__ cs, int P,
+    double log2_theta, int64_t N, int64_t M, int64_t R, int W, int w, int n_wx, int W_lr,
+    int rho, int heads, int rope_on, double q_scale) {
+  constexpr int CPH = D / 8, QUARTER = D / 4;
+  __shared__ int64_t src_s[kBwdRowsPerBlock];
+  __shared__ int pos_s[kBwdRowsPerBlock][2];
+  __shared__ double2 cs_s[kBwdRowsPerBlock][2][QUARTER];
+  const int64_t L = N + M, b = blockIdx.y;
+  const int tid = threadIdx.x;
+  if (tid < kBwdRowsPerBlock) {
+    int py, px;
+    src_s[tid] = bwd_source(static_cast<int64_t>(blockIdx.x) * kBwdRowsPerBlock + tid, N, M, W, w,
+                            n_wx, W_lr, rho, py, px);
+    pos_s[tid][0] = py;
+    pos_s[tid][1] = px;
+  }
+  __syncthreads();
+  if (rope_on) {
+    for (int e = tid; e < kBwdRowsPerBlock * 2 * QUARTER; e += kBwdThreads) {
+      const int rt = e / (2 * QUARTER), axis = (e / QUARTER) & 1, kk = e % QUARTER;
+      const int pos = pos_s[rt][axis];
+      cs_s[rt][axis][kk] = pos < P ? cs[pos * QUARTER + kk] : rope_cos_sin(pos, kk, D / 2, log2_theta);
+    }
+    __syncthreads();
+  }
+  const int cpr = heads * CPH;
+  for (int i = tid; i < kBwdRowsPerBlock * cpr; i += kBwdThreads) {
+    const int t = i / cpr, c = i - t * cpr;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * kBwdRowsPerBlock + t;
+    if (row >= R) continue;
+    const int h = c / CPH, j = c % CPH;
+    const int64_t src = src_s[t];
+    uint4 qo = make_uint4(0, 0, 0, 0), ko = qo, vo = qo, go = qo;
+    if (src >= 0) {
+      const int64_t so = ((b * L + src) * heads + h) * D + j * 8;
+      const uint4 qi = *reinterpret_cast<const uint4*>(q + so);
+      const uint4 ki = *reinterpret_cast<const uint4*>(k + so);
+      vo = *reinterpret_cast<const uint4*>(v + so);
+      go = *reinterpret_cast<const uint4*>(dout + so);
+      if (rope_on) {
+        const int axis = (4 * j) / QUARTER, k0 = 4 * j - axis * QUARTER;
+        const double2* f = &cs_s[t][axis][k0];
+        qo = make_uint4(rope_rotate_word(qi.x, f[0], q_scale), rope_rotate_word(qi.y, f[1], q_scale),
+                        rope_rotate_word(qi.z, f[2], q_scale), rope_rotate_word(qi.w, f[3], q_scale));
+        ko = make_uint4(rope_rotate_word(ki.x, f[0]), rope_rotate_word(ki.y, f[1]),
+                        rope_rotate_word(ki.z, f[2]), rope_rotate_word(ki.w, f[3]));
+      } else {
+        qo = make_uint4(scale_word(qi.x, q_scale), scale_word(qi.y, q_scale),
+                        scale_word(qi.z, q_scale), scale_word(qi.w, q_scale));
+        ko = ki;
+      }
+    }
+    const int64_t o = ((b * heads + h) * R + row) * D + j * 8;
+    *reinterpret_cast<uint4*>(qb + o) = qo;
+    *reinterpret_cast<uint4*>(kb + o) = ko;
+    *reinterpret_cast<uint4*>(vb + o) = vo;
+    *reinterpret_cast<uint4*>(dob + o) = go;
+  }
+}
+
+// Per buffer row: lse2 = lse * log2 e (+inf for padding, so those rows get P = 0) and
+// D = sum_d dO * O in fp32, stored per 64-row tile as [64 lse2][64 D].
+__global__ void bwd_aux_kernel(const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout,
+                               const float* __restrict__ lse, float* __restrict__ aux, int64_t N,
+                               int64_t M, int64_t R, int W, int w, int n_wx, int W_lr, int rho,
+                               int heads, int D, int64_t bh_total) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= bh_total * R) return;
+  const int64_t bh = i / R, row = i - bh * R;
+  const int64_t b = bh / heads, h = bh - b * heads;
+  int py, px;
+  const int64_t src = bwd_source(row, N, M, W, w, n_wx, W_lr, rho, py, px);
+  float l2 = INFINITY, dd = 0.0f;
+  if (src >= 0) {
+    l2 = lse[bh * (N + M) + src] * 1.4426950408889634f;
+    const bf16_t* orow = o + ((b * (N + M) + src) * heads + h) * D;
+    const bf16_t* grow = dout + ((b * (N + M) + src) * heads + h) * D;
+    for (int d = 0; d < D; d += 8) {
+      const uint4 a = *reinterpret_cast<const uint4*>(orow + d);
+      const uint4 c = *reinterpret_cast<const uint4*>(grow + d);
+      const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, cw[4] = {c.x, c.y, c.z, c.w};
+      for (int e = 0; e < 4; ++e)
+        dd += __uint_as_float(aw[e] << 16) * __uint_as_float(cw[e] << 16) +
+              __uint_as_float(aw[e] & 0xffff0000u) * __uint_as_float(cw[e] & 0xffff0000u);
+    }
+  }
+  float* t = aux + (bh * (R / kKeyTile) + row / kKeyTile) * (2 * kKeyTile);
+  t[row % kKeyTile] = l2;
+  t[kKeyTile + row % kKeyTile] = dd;
+}
+
+// [bh][R][D] row-major -> [bh][R/64][D][64] tiles, rows within a tile in v_slot order.
+__global__ __launch_bounds__(kBwdThreads) void bwd_transpose_kernel(const bf16_t* __restrict__ src,
+                                                                    bf16_t* __restrict__ dst,
+                                                                    int64_t R, int D) {
+  __shared__ bf16_t tile[kKeyTile][128 + 2];
+  const int64_t bh = blockIdx.y, t = blockIdx.x;
+  const int cpr = D / 8;
+  const bf16_t* s = src + (bh * R + t * kKeyTile) * D;
+  for (int i = threadIdx.x; i < kKeyTile * cpr; i += kBwdThreads) {
+    const int r = i / cpr, j = i - r * cpr;
+    const uint4 x = *reinterpret_cast<const uint4*>(s + static_cast<int64_t>(r) * D + j * 8);
+    const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+    for (int e = 0; e < 4; ++e) {
+      tile[r][j * 8 + 2 * e] = static_cast<bf16_t>(xw[e] & 0xffff);
+      tile[r][j * 8 + 2 * e + 1] = static_cast<bf16_t>(xw[e] >> 16);
+    }
+  }
+  __syncthreads();
+  bf16_t* d = dst + (bh * (R / kKeyTile) + t) * static_cast<int64_t>(D) * kKeyTile;
+  for (int i = threadIdx.x; i < D * (kKeyTile / 8); i += kBwdThreads) {
+    const int dd = i / (kKeyTile / 8), s8 = (i - dd * (kKeyTile / 8)) * 8;
+    uint32_t wv[4];
+    for (int e = 0; e < 4; ++e)
+      wv[e] = static_cast<uint32_t>(tile[v_slot(s8 + 2 * e)][dd]) |
+              (static_cast<uint32_t>(tile[v_slot(s8 + 2 * e + 1)][dd]) << 16);
+    *reinterpret_cast<uint4*>(d + static_cast<int64_t>(dd) * kKeyTile + s8) =
+        make_uint4(wv[0], wv[1], wv[2], wv[3]);
+  }
+}
+
+struct BwdArgs {
+  const bf16_t *qb, *kb, *vb, *dob, *qt, *kt, *dot;
+  const float* aux;
+  const double2* cs;
+  bf16_t* out0;  // dQ (dq kernel) or dK (dkv kernel), raster [B][N+M][heads][D]
+  bf16_t* out1;  // dV (dkv kernel)
+  int64_t N, M, R;
+  int heads, w2, W, w, n_wx, n_wy, radius, rho, W_lr, P;
+  int rope_on;
+  double log2_theta;
+  float out_scale;  // scale (dQ) or ln 2 (dK)
+  int blocks_per_bh, total_blocks;
+};
+
+// Inverse RoPE of the pair (a, b) at pair index pr of a row at position (py, px), in fp32
+// from the fp64 factors, then bf16.
+__device__ __forceinline__ uint32_t unrotate_pair(float a, float b, int pr, int py, int px,
+                                                  const BwdArgs& A, int D) {
+  if (!A.rope_on) return pack_bf16x2(a, b);
+  const int quarter = D / 4, axis = pr / quarter, kk = pr - axis * quarter;
+  const int pos = axis ? px : py;
+  const double2 f = pos < A.P ? A.cs[pos * quarter + kk] : rope_cos_sin(pos, kk, D / 2, A.log2_theta);
+  const float c = static_cast<float>(f.x), s = static_cast<float>(f.y);
+  return pack_bf16x2(a * c + b * s, b * c - a * s);
+}
+
+// Raster row and position of buffer row `row` (hi rows window-first, then guide rows).
+__device__ __forceinline__ int64_t raster_row(int64_t row, const BwdArgs& A, int& py, int& px) {
+  if (row < A.N) {
+    const int r = window_first_to_raster(static_cast<int>(row), A.W, A.w, A.n_wx);
+    py = r / A.W;
+    px = r - py * A.W;
+    return r;
+  }
+  const int64_t s = row - A.N;
+  const int sy = static_cast<int>(s / A.W_lr);
+  py = A.rho * sy;
+  px = A.rho * static_cast<int>(s - static_cast<int64_t>(sy) * A.W_lr);
+  return A.N + s;
+}
+
+// Tile list of a block of rows (queries for dQ, keys for dK/dV): for hi rows the tiles of
+// the windows within `radius` of the row's window (the mask is symmetric there), then for
+// dQ the guide key tiles; for guide rows: dQ the guide key tiles, dK/dV every hi query tile
+// and then the guide query tiles.  Local tiles come from an LDS table of tile indices.
+template <int NT>
+__device__ int build_local_table(const BwdArgs& A, int r0, uint32_t* tab) {
+  const int tpw = A.w2 / kKeyTile;
+  const int win = r0 / A.w2;
+  const int wy = win / A.n_wx, wx = win - wy * A.n_wx;
+  const int y0 = max(0, wy - A.radius), y1 = min(A.n_wy - 1, wy + A.radius);
+  const int x0 = max(0, wx - A.radius), x1 = min(A.n_wx - 1, wx + A.radius);
+  const int nx = x1 - x0 + 1;
+  const int n = (y1 - y0 + 1) * nx * tpw;
+  for (int i = threadIdx.x; i < n; i += NT) {
+    const int j = i / tpw, sub = i - j * tpw;
+    const int jy = j / nx, nw = (y0 + jy) * A.n_wx + x0 + (j - jy * nx);
+    tab[i] = static_cast<uint32_t>(nw * tpw + sub);
+  }
+  return n;
+}
+
+// ---------------------------------------------------------------- dQ (query-outer)
+//
+// Wave = 32 queries (lane & 31), as the forward: S^T = K Q^T and dP^T = V dO^T (A = K / V
+// tile rows from LDS, B = Q / dO held in registers), so each lane holds one query's
+// scores; dS^T converted to bf16 in place is the B operand of dQ^T += K~^T dS^T with
+// A = the transposed K tile.
+template <int D, int NWAVES, bool HI>
+__global__ __launch_bounds__(NWAVES * 64) void bwd_dq_kernel(BwdArgs A) {
+  constexpr int NT = NWAVES * 64;
+  constexpr int TILE = kKeyTile * D * 2;
+  constexpr int CPT = TILE / 16 / NT;
+  constexpr int KCH = D / 8;
+  constexpr int STAGE = 3 * TILE;  // K, V, K^T
+  __shared__ __attribute__((aligned(16))) char ring[2 * STAGE];
+  __shared__ uint32_t tab[HI ? kBwdMaxTiles : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ql = lane & 31, g = lane >> 5;
+  const int blk = xcd_remap(blockIdx.x, A.total_blocks);
+  const int bh = blk / A.blocks_per_bh, qb = blk - bh * A.blocks_per_bh;
+  const int b = bh / A.heads, h = bh - b * A.heads;
+  const int64_t r0 = HI ? static_cast<int64_t>(qb) * NWAVES * 32 : A.N + static_cast<int64_t>(qb) * NWAVES * 32;
+  const int n_guide = static_cast<int>((A.M + kKeyTile - 1) / kKeyTile);
+  int n_local = 0;
+  if (HI) {
+    n_local = build_local_table<NT>(A, static_cast<int>(r0), tab);
+    __syncthreads();
+  }
+  const int n_tiles = n_local + n_guide;
+  const int n_hi_tiles = static_cast<int>(A.N / kKeyTile);
+  const int64_t mat = static_cast<int64_t>(bh) * A.R * D * 2;
+  const char* kbase = reinterpret_cast<const char*>(A.kb) + mat;
+  const char* vbase = reinterpret_cast<const char*>(A.vb) + mat;
+  const char* tbase = reinterpret_cast<const char*>(A.kt) + mat;
+  auto tile_index = [&](int t) -> int {
+    if (HI && t < n_local) return __builtin_amdgcn_readfirstlane(tab[t]);
+    return n_hi_tiles + (t - n_local);
+  };
+  auto tile_valid = [&](int t) -> int {
+    if (HI && t < n_local) return kKeyTile;
+    const int64_t rem = A.M - static_cast<int64_t>(t - n_local) * kKeyTile;
+    return rem < kKeyTile ? static_cast<int>(rem) : kKeyTile;
+  };
+  int k_src[CPT], t_src[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int slot = (i * NWAVES + wave) * 64 + lane;
+    const int kr = slot / KCH, kp = slot - kr * KCH;
+    k_src[i] = kr * (D * 2) + ((kp ^ k_swizzle<D>(kr)) << 4);
+    const int vr = slot >> 3, vp = slot & 7;
+    t_src[i] = vr * (kKeyTile * 2) + ((vp ^ v_swizzle(vr)) << 4);
+  }
+  auto issue = [&](int t, int st) {
+    const int64_t off = static_cast<int64_t>(tile_index(t)) * TILE;
+    const uint32_t base = lds_addr(ring + st * STAGE);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const uint32_t o = __builtin_amdgcn_readfirstlane(base + (i * NWAVES + wave) * 64 * 16);
+      dma_16b(kbase + off, k_src[i], o);
+      dma_16b(vbase + off, k_src[i], o + TILE);
+      dma_16b(tbase + off, t_src[i], o + 2 * TILE);
+    }
+  };
+
+  // query fragments (B operands): Q (base-2 scaled) and dO; per-lane lse2 and D
+  const int64_t qrow = r0 + wave * 32 + ql;
+  bf16x8 qf[D / 16], gf[D / 16];
+  {
+    const bf16_t* qp = A.qb + (static_cast<int64_t>(bh) * A.R + qrow) * D;
+    const bf16_t* gp = A.dob + (static_cast<int64_t>(bh) * A.R + qrow) * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      qf[kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk + 8 * g);
+      gf[kk] = *reinterpret_cast<const bf16x8*>(gp + 16 * kk + 8 * g);
+    }
+  }
+  const float* at = A.aux + (static_cast<int64_t>(bh) * (A.R / kKeyTile) + qrow / kKeyTile) * (2 * kKeyTile);
+  const float lse2 = at[qrow % kKeyTile], dd = at[kKeyTile + qrow % kKeyTile];
+  __builtin_amdgcn_s_waitcnt(0);
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.0f;
+
+  auto k_frag = [&](const char* tb, int kk, int half) -> bf16x8 {
+    const int row = half * 32 + ql;
+    return *reinterpret_cast<const bf16x8*>(tb + row * (D * 2) + (((2 * kk + g) ^ k_swizzle<D>(row)) << 4));
+  };
+  auto t_frag = [&](const char* tb, int ks, int dt) -> bf16x8 {
+    const int vr = dt * 32 + ql;
+    return *reinterpret_cast<const bf16x8*>(tb + vr * (kKeyTile * 2) + (((2 * ks + g) ^ v_swizzle(vr)) << 4));
+  };
+
+  issue(0, 0);
+  wait_vm_and_barrier<0>();
+  for (int t = 0; t < n_tiles; ++t) {
+    const int st = t & 1;
+    if (t + 1 < n_tiles) issue(t + 1, st ^ 1);
+    const char* kt_ = ring + st * STAGE;
+    const char* vt_ = kt_ + TILE;
+    const char* tt_ = kt_ + 2 * TILE;
+    f32x16 s0 = {}, s1 = {}, p0 = {}, p1 = {};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(kt_, kk, 0), qf[kk], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(kt_, kk, 1), qf[kk], s1, 0, 0, 0);
+      p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(vt_, kk, 0), gf[kk], p0, 0, 0, 0);
+      p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(vt_, kk, 1), gf[kk], p1, 0, 0, 0);
+    }
+    const int valid = tile_valid(t);
+    bf16x8 dsb[4];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 8 * (r >> 2) + 4 * g + (r & 3);
+      const float a0 = key < valid ? __builtin_amdgcn_exp2f(s0[r] - lse2) : 0.0f;
+      const float a1 = key + 32 < valid ? __builtin_amdgcn_exp2f(s1[r] - lse2) : 0.0f;
+      dsb[r >> 3][r & 7] = static_cast<__bf16>(a0 * (p0[r] - dd));
+      dsb[2 + (r >> 3)][r & 7] = static_cast<__bf16>(a1 * (p1[r] - dd));
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t_frag(tt_, ks, dt), dsb[ks], acc[dt], 0, 0, 0);
+    wait_vm_and_barrier<0>();
+  }
+
+  // epilogue: dQ~ = scale * acc (lane: query ql, dims dt*32 + 8*(r/4) + 4g + r%4), unrotate
+  if (!HI && qrow - A.N >= A.M) return;
+  int py, px;
+  const int64_t rr = raster_row(qrow, A, py, px);
+  bf16_t* orow = A.out0 + ((static_cast<int64_t>(b) * (A.N + A.M) + rr) * A.heads + h) * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d0 = dt * 32 + 8 * rg + 4 * g;
+      const uint32_t w0 = unrotate_pair(A.out_scale * acc[dt][4 * rg], A.out_scale * acc[dt][4 * rg + 1], d0 / 2, py, px, A, D);
+      const uint32_t w1 = unrotate_pair(A.out_scale * acc[dt][4 * rg + 2], A.out_scale * acc[dt][4 * rg + 3], d0 / 2 + 1, py, px, A, D);
+      *reinterpret_cast<uint2*>(orow + d0) = make_uint2(w0, w1);
+    }
+}
+
+// ---------------------------------------------------------------- dK, dV (key-outer)
+//
+// Wave = 32 keys (lane & 31).  Per 64-query tile, in halves of 32 queries: S = Q K~^T and
+// dP = dO V^T (A = Q / dO tile rows from LDS, B = K / V held in registers), so a lane holds
+// one key's scores for 16 queries; P and dS converted to bf16 in place are the B operands
+// of dV^T += dO^T P and dK^T += Q^T dS with A = the transposed dO / Q tiles.
+template <int D, int NWAVES, bool HI>
+__global__ __launch_bounds__(NWAVES * 64) void bwd_dkv_kernel(BwdArgs A) {
+  constexpr int NT = NWAVES * 64;
+  constexpr int TILE = kKeyTile * D * 2;
+  constexpr int CPT = TILE / 16 / NT;
+  constexpr int KCH = D / 8;
+  constexpr int STAGE = 4 * TILE + kAuxBytes;  // Q, Q^T, dO, dO^T, aux
+  __shared__ __attribute__((aligned(16))) char ring[2 * STAGE];
+  __shared__ uint32_t tab[HI ? kBwdMaxTiles : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ql = lane & 31, g = lane >> 5;
+  const int blk = xcd_remap(blockIdx.x, A.total_blocks);
+  const int bh = blk / A.blocks_per_bh, kb_ = blk - bh * A.blocks_per_bh;
+  const int b = bh / A.heads, h = bh - b * A.heads;
+  const int64_t r0 = HI ? static_cast<int64_t>(kb_) * NWAVES * 32 : A.N + static_cast<int64_t>(kb_) * NWAVES * 32;
+  const int n_hi_tiles = static_cast<int>(A.N / kKeyTile);
+  const int n_guide_q = static_cast<int>((A.M + kKeyTile - 1) / kKeyTile);
+  int n_tiles;
+  if (HI) {
+    n_tiles = build_local_table<NT>(A, static_cast<int>(r0), tab);
+    __syncthreads();
+  } else {
+    n_tiles = n_hi_tiles + n_guide_q;  // every query tile: hi, then guide
+  }
+  const int64_t mat = static_cast<int64_t>(bh) * A.R * D * 2;
+  const char* qbase = reinterpret_cast<const char*>(A.qb) + mat;
+  const char* qtbase = reinterpret_cast<const char*>(A.qt) + mat;
+  const char* gbase = reinterpret_cast<const char*>(A.dob) + mat;
+  const char* gtbase = reinterpret_cast<const char*>(A.dot) + mat;
+  const char* abase = reinterpret_cast<const char*>(A.aux) + static_cast<int64_t>(bh) * (A.R / kKeyTile) * kAuxBytes;
+  auto tile_index = [&](int t) -> int {
+    if (HI) return __builtin_amdgcn_readfirstlane(tab[t]);
+    return t;
+  };
+  int k_src[CPT], t_src[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int slot = (i * NWAVES + wave) * 64 + lane;
+    const int kr = slot / KCH, kp = slot - kr * KCH;
+    k_src[i] = kr * (D * 2) + ((kp ^ k_swizzle<D>(kr)) << 4);
+    const int vr = slot >> 3, vp = slot & 7;
+    t_src[i] = vr * (kKeyTile * 2) + ((vp ^ v_swizzle(vr)) << 4);
+  }
+  auto issue = [&](int t, int st) {
+    const int ti = tile_index(t);
+    const int64_t off = static_cast<int64_t>(ti) * TILE;
+    const uint32_t base = lds_addr(ring + st * STAGE);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const uint32_t o = __builtin_amdgcn_readfirstlane(base + (i * NWAVES + wave) * 64 * 16);
+      dma_16b(qbase + off, k_src[i], o);
+      dma_16b(qtbase + off, t_src[i], o + TILE);
+      dma_16b(gbase + off, k_src[i], o + 2 * TILE);
+      dma_16b(gtbase + off, t_src[i], o + 3 * TILE);
+    }
+    if (wave == 0 && lane < kAuxBytes / 16)
+      dma_16b(abase + static_cast<int64_t>(ti) * kAuxBytes, lane * 16, __builtin_amdgcn_readfirstlane(base + 4 * TILE));
+  };
+
+  // key fragments (B operands): K~ and V rows of this lane's key
+  const int64_t krow = r0 + wave * 32 + ql;
+  bf16x8 kf[D / 16], vf[D / 16];
+  {
+    const bf16_t* kp = A.kb + (static_cast<int64_t>(bh) * A.R + krow) * D;
+    const bf16_t* vp = A.vb + (static_cast<int64_t>(bh) * A.R + krow) * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      kf[kk] = *reinterpret_cast<const bf16x8*>(kp + 16 * kk + 8 * g);
+      vf[kk] = *reinterpret_cast<const bf16x8*>(vp + 16 * kk + 8 * g);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dk[dt][r] = dv[dt][r] = 0.0f;
+
+  auto k_frag = [&](const char* tb, int kk, int half) -> bf16x8 {
+    const int row = half * 32 + ql;
+    return *reinterpret_cast<const bf16x8*>(tb + row * (D * 2) + (((2 * kk + g) ^ k_swizzle<D>(row)) << 4));
+  };
+  auto t_frag = [&](const char* tb, int ks, int dt) -> bf16x8 {
+    const int vr = dt * 32 + ql;
+    return *reinterpret_cast<const bf16x8*>(tb + vr * (kKeyTile * 2) + (((2 * ks + g) ^ v_swizzle(vr)) << 4));
+  };
+
+  issue(0, 0);
+  wait_vm_and_barrier<0>();
+  for (int t = 0; t < n_tiles; ++t) {
+    const int st = t & 1;
+    if (t + 1 < n_tiles) issue(t + 1, st ^ 1);
+    const char* qt_ = ring + st * STAGE;
+    const char* qtt = qt_ + TILE;
+    const char* gt_ = qt_ + 2 * TILE;
+    const char* gtt = qt_ + 3 * TILE;
+    const float* aux = reinterpret_cast<const float*>(qt_ + 4 * TILE);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      f32x16 s = {}, p = {};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(qt_, kk, half), kf[kk], s, 0, 0, 0);
+        p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(gt_, kk, half), vf[kk], p, 0, 0, 0);
+      }
+      // rows are queries 32 half + 8(r/4) + 4g + r%4 of the tile; lanes are keys
+      bf16x8 pb[2], db[2];
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int q0 = 32 * half + 8 * rq + 4 * g;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(aux + q0);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(aux + kKeyTile + q0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * rq + e;
+          const float pr = __builtin_amdgcn_exp2f(s[r] - l4[e]);
+          pb[r >> 3][r & 7] = static_cast<__bf16>(pr);
+          db[r >> 3][r & 7] = static_cast<__bf16>(pr * (p[r] - d4[e]));
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t_frag(gtt, 2 * half + j, dt), pb[j], dv[dt], 0, 0, 0);
+          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t_frag(qtt, 2 * half + j, dt), db[j], dk[dt], 0, 0, 0);
+        }
+    }
+    wait_vm_and_barrier<0>();
+  }
+
+  // epilogue: dK~ = ln2 * dk (Q carried scale * log2 e), unrotated; dV = dv
+  if (!HI && krow - A.N >= A.M) return;
+  int py, px;
+  const int64_t rr = raster_row(krow, A, py, px);
+  const int64_t ro = ((static_cast<int64_t>(b) * (A.N + A.M) + rr) * A.heads + h) * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d0 = dt * 32 + 8 * rg + 4 * g;
+      const float c = A.out_scale;
+      const uint32_t k0 = unrotate_pair(c * dk[dt][4 * rg], c * dk[dt][4 * rg + 1], d0 / 2, py, px, A, D);
+      const uint32_t k1 = unrotate_pair(c * dk[dt][4 * rg + 2], c * dk[dt][4 * rg + 3], d0 / 2 + 1, py, px, A, D);
+      *reinterpret_cast<uint2*>(A.out0 + ro + d0) = make_uint2(k0, k1);
+      *reinterpret_cast<uint2*>(A.out1 + ro + d0) =
+          make_uint2(pack_bf16x2(dv[dt][4 * rg], dv[dt][4 * rg + 1]),
+                     pack_bf16x2(dv[dt][4 * rg + 2], dv[dt][4 * rg + 3]));
+    }
+}
+
+// ------------------------------------------------------------------ host side
+
+namespace {
+
+int validate_backward(const void* const* ptrs, int n_ptrs, int B, int H, int W, int w, int H_lr,
+                      int W_lr, int rho, int heads, int D, int radius) {
+  for (int i = 0; i < n_ptrs; ++i) {
+    if (!ptrs[i]) return fail_arg("null pointer");
+    if (reinterpret_cast<uintptr_t>(ptrs[i]) % 16) return fail_arg("tensors must be 16-byte aligned");
+  }
+  if (B < 1 || H < 1 || W < 1 || w < 1 || heads < 1 || H_lr < 0 || W_lr < 0)
+    return fail_arg("sizes out of range");
+  if (H % w || W % w) return fail_arg("w must divide H and W");
+  if ((H_lr == 0) != (W_lr == 0)) return fail_arg("H_lr and W_lr must both be zero or not");
+  if (static_cast<int64_t>(H_lr) * W_lr > 0 && rho < 1) return fail_arg("rho must be >= 1 with guide tokens");
+  if (radius < 0) return fail_arg("radius must be >= 0");
+  if (D != 64 && D != 128) return fail_unsupported("head_dim must be 64 or 128");
+  if (w % 8 || (w > 16 && w % 16)) return fail_unsupported("window size must be 8, 16 or a multiple of 16");
+  if (B > 65535) return fail_unsupported("batch too large");
+  const int64_t N = static_cast<int64_t>(H) * W, M = static_cast<int64_t>(H_lr) * W_lr;
+  if (N > (int64_t(1) << 26) || M > (int64_t(1) << 26) ||
+      static_cast<int64_t>(B) * heads * ((N + M) / 64 + 2) > 0x7fffffff)
+    return fail_unsupported("problem too large");
+  const int r = std::min(radius, H / w + W / w);
+  const int64_t tiles = static_cast<int64_t>(std::min(2 * r + 1, H / w)) * std::min(2 * r + 1, W / w) *
+                        (w * w / kKeyTile);
+  if (tiles > kBwdMaxTiles) return fail_unsupported("too many key tiles per window");
+  return UHLA_OK;
+}
+
+template <int D>
+void launch_dq(int nwaves, bool hi, const BwdArgs& a, hipStream_t s) {
+  if (!hi) hipLaunchKernelGGL((bwd_dq_kernel<D, 4, false>), dim3(a.total_blocks), dim3(256), 0, s, a);
+  else if (nwaves == 4) hipLaunchKernelGGL((bwd_dq_kernel<D, 4, true>), dim3(a.total_blocks), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((bwd_dq_kernel<D, 2, true>), dim3(a.total_blocks), dim3(128), 0, s, a);
+}
+
+template <int D>
+void launch_dkv(int nwaves, bool hi, const BwdArgs& a, hipStream_t s) {
+  if (!hi) hipLaunchKernelGGL((bwd_dkv_kernel<D, 4, false>), dim3(a.total_blocks), dim3(256), 0, s, a);
+  else if (nwaves == 4) hipLaunchKernelGGL((bwd_dkv_kernel<D, 4, true>), dim3(a.total_blocks), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((bwd_dkv_kernel<D, 2, true>), dim3(a.total_blocks), dim3(128), 0, s, a);
+}
+
+}  // namespace
+
+}  // namespace uhla
+
+extern "C" size_t uhla_backward_workspace_bytes(int B, int H, int W, int w, int H_lr, int W_lr,
+                                                int rho, int heads, int head_dim, int radius) {
+  if (B < 1 || H < 1 || W < 1 || w < 1 || heads < 1 || H_lr < 0 || W_lr < 0 || radius < 0) return 0;
+  if (H % w || W % w || (H_lr == 0) != (W_lr == 0)) return 0;
+  if (head_dim != 64 && head_dim != 128) return 0;
+  if (static_cast<int64_t>(H_lr) * W_lr > 0 && rho < 1) return 0;
+  return uhla::carve_bwd(uhla::make_bwd_geom(B, H, W, w, H_lr, W_lr, rho, heads, head_dim, radius),
+                         nullptr).bytes;
+}
+
+extern "C" int uhla_backward(const void* q, const void* k, const void* v, const void* o,
+                             const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                             int B, int H, int W, int w, int H_lr, int W_lr, int rho, int heads,
+                             int head_dim, float scale, float theta, int radius, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  using namespace uhla;
+  const void* ptrs[9] = {q, k, v, o, dout, lse, dq, dk, dv};
+  int st = validate_backward(ptrs, 9, B, H, W, w, H_lr, W_lr, rho, heads, head_dim, radius);
+  if (st) return st;
+  radius = std::min(radius, H / w + W / w);
+  const int D = head_dim;
+  const BwdGeom g = make_bwd_geom(B, H, W, w, H_lr, W_lr, rho, heads, D, radius);
+  const BwdWorkspace need = carve_bwd(g, nullptr);
+  if (!workspace || workspace_bytes < need.bytes)
+    return (set_detail("workspace too small"), UHLA_ERR_WORKSPACE);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail_arg("workspace must be 256-byte aligned");
+  const int64_t L = g.N + g.M;
+  const size_t tb = static_cast<size_t>(B) * L * heads * D * 2;
+  const void* ins[5] = {q, k, v, o, dout};
+  void* outs[3] = {dq, dk, dv};
+  for (void* x : outs) {
+    for (const void* y : ins)
+      if (ranges_overlap(x, tb, y, tb)) return fail_arg("a gradient overlaps an input");
+    if (ranges_overlap(x, tb, workspace, need.bytes) ||
+        ranges_overlap(x, tb, lse, static_cast<size_t>(B) * heads * L * 4))
+      return fail_arg("a gradient overlaps the workspace or lse");
+  }
+  if (ranges_overlap(dq, tb, dk, tb) || ranges_overlap(dq, tb, dv, tb) || ranges_overlap(dk, tb, dv, tb))
+    return fail_arg("gradients overlap each other");
+  const BwdWorkspace ws = carve_bwd(g, workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool rope_on = theta > 0.0f;
+  const float sc = scale > 0.0f ? scale : 1.0f / sqrtf(static_cast<float>(D));
+  const double l2t = rope_on ? log2(static_cast<double>(theta)) : 0.0;
+  const int64_t BH = static_cast<int64_t>(B) * heads;
+  const int n_wx = W / w;
+
+#define UHLA_BSTEP(call, name) \
+  do {                         \
+    call;                      \
+    st = check_launch(name);   \
+    if (st) return st;         \
+  } while (0)
+
+  if (rope_on) {
+    const int n = g.P * (D / 4);
+    UHLA_BSTEP(hipLaunchKernelGGL(bwd_cos_sin_kernel, dim3((n + 255) / 256), dim3(256), 0, s, ws.cs,
+                                  g.P, D, l2t),
+               "bwd_cos_sin_kernel");
+  }
+  {
+    const dim3 grid(static_cast<unsigned>((g.R + kBwdRowsPerBlock - 1) / kBwdRowsPerBlock), B);
+    const double qs = static_cast<double>(sc) * 1.4426950408889634;
+    const bf16_t* qp = static_cast<const bf16_t*>(q);
+    const bf16_t* kp = static_cast<const bf16_t*>(k);
+    const bf16_t* vp = static_cast<const bf16_t*>(v);
+    const bf16_t* gp = static_cast<const bf16_t*>(dout);
+    if (D == 128)
+      hipLaunchKernelGGL(bwd_rows_kernel<128>, grid, dim3(kBwdThreads), 0, s, qp, kp, vp, gp, ws.qb,
+                         ws.kb, ws.vb, ws.dob, ws.cs, g.P, l2t, g.N, g.M, g.R, W, w, n_wx, W_lr, rho,
+                         heads, rope_on ? 1 : 0, qs);
+    else
+      hipLaunchKernelGGL(bwd_rows_kernel<64>, grid, dim3(kBwdThreads), 0, s, qp, kp, vp, gp, ws.qb,
+                         ws.kb, ws.vb, ws.dob, ws.cs, g.P, l2t, g.N, g.M, g.R, W, w, n_wx, W_lr, rho,
+                         heads, rope_on ? 1 : 0, qs);
+    st = check_launch("bwd_rows_kernel");
+    if (st) return st;
+    const int64_t rows = BH * g.R;
+    UHLA_BSTEP(hipLaunchKernelGGL(bwd_aux_kernel, dim3(static_cast<unsigned>((rows + 255) / 256)), dim3(256), 0, s,
+                                  static_cast<const bf16_t*>(o), gp, lse, ws.aux, g.N, g.M, g.R, W, w,
+                                  n_wx, W_lr, rho, heads, D, BH),
+               "bwd_aux_kernel");
+    const dim3 tg(static_cast<unsigned>(g.R / kKeyTile), static_cast<unsigned>(BH));
+    UHLA_BSTEP(hipLaunchKernelGGL(bwd_transpose_kernel, tg, dim3(kBwdThreads), 0, s, ws.qb, ws.qt, g.R, D),
+               "bwd_transpose_kernel(q)");
+    UHLA_BSTEP(hipLaunchKernelGGL(bwd_transpose_kernel, tg, dim3(kBwdThreads), 0, s, ws.kb, ws.kt, g.R, D),
+               "bwd_transpose_kernel(k)");
+    UHLA_BSTEP(hipLaunchKernelGGL(bwd_transpose_kernel, tg, dim3(kBwdThreads), 0, s, ws.dob, ws.dot, g.R, D),
+               "bwd_transpose_kernel(do)");
+  }
+
+  BwdArgs a{};
+  a.qb = ws.qb; a.kb = ws.kb; a.vb = ws.vb; a.dob = ws.dob; a.qt = ws.qt; a.kt = ws.kt; a.dot = ws.dot;
+  a.aux = ws.aux; a.cs = ws.cs;
+  a.N = g.N; a.M = g.M; a.R = g.R;
+  a.heads = heads; a.w2 = w * w; a.W = W; a.w = w; a.n_wx = n_wx; a.n_wy = H / w;
+  a.radius = radius; a.rho = rho; a.W_lr = W_lr; a.P = g.P;
+  a.rope_on = rope_on ? 1 : 0; a.log2_theta = l2t;
+  const int nw_hi = std::min(4, w * w / 32);
+
+  // dQ: hi queries, then guide queries
+  a.out0 = static_cast<bf16_t*>(dq);
+  a.out_scale = sc;
+  a.blocks_per_bh = static_cast<int>(g.N / (nw_hi * 32));
+  a.total_blocks = static_cast<int>(BH * a.blocks_per_bh);
+  UHLA_BSTEP((D == 128 ? launch_dq<128>(nw_hi, true, a, s) : launch_dq<64>(nw_hi, true, a, s)),
+             "bwd_dq_kernel(hi)");
+  if (g.M > 0) {
+    a.blocks_per_bh = static_cast<int>((g.R - g.N) / 128);
+    a.total_blocks = static_cast<int>(BH * a.blocks_per_bh);
+    UHLA_BSTEP((D == 128 ? launch_dq<128>(4, false, a, s) : launch_dq<64>(4, false, a, s)),
+               "bwd_dq_kernel(guide)");
+  }
+  // dK, dV: hi keys, then guide keys
+  a.out0 = static_cast<bf16_t*>(dk);
+  a.out1 = static_cast<bf16_t*>(dv);
+  a.out_scale = 0.69314718055994531f;
+  a.blocks_per_bh = static_cast<int>(g.N / (nw_hi * 32));
+  a.total_blocks = static_cast<int>(BH * a.blocks_per_bh);
+  UHLA_BSTEP((D == 128 ? launch_dkv<128>(nw_hi, true, a, s) : launch_dkv<64>(nw_hi, true, a, s)),
+             "bwd_dkv_kernel(hi)");
+  if (g.M > 0) {
+    a.blocks_per_bh = static_cast<int>((g.R - g.N) / 128);
+    a.total_blocks = static_cast<int>(BH * a.blocks_per_bh);
+    UHLA_BSTEP((D == 128 ? launch_dkv<128>(4, false, a, s) : launch_dkv<64>(4, false, a, s)),
+               "bwd_dkv_kernel(guide)");
+  }
+#undef UHLA_BSTEP
+  return UHLA_OK;
+}

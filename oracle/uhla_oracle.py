@@ -329,3 +329,47 @@ def backward(q, k, v, do, geom):
             dq[b, :, h] = dqr
             dk[b, :, h] = dkr
     return dq, dk, dv
+
+
+def backward_rows(q, k, v, do, geom, b: int, h: int, q_rows, k_rows, block: int = 512):
+    """Rows of the backward of one (batch, head) without the full L x L matrices:
+    (dQ[q_rows], dK[k_rows], dV[k_rows]), fp64.  Same definitions as ``backward``: each
+    query row's probabilities come from its LSE, D_i = dO_i . O_i, and a key's gradients sum
+    over the query rows whose mask row allows it."""
+    q_rows = np.asarray(q_rows, dtype=np.int64)
+    k_rows = np.asarray(k_rows, dtype=np.int64)
+    L = q.shape[1]
+    py, px = token_positions(geom)
+    qr, kr = rotated_qk(q, k, geom, b, h)
+    vv = v[b, :, h].astype(np.float64)
+    g = do[b, :, h].astype(np.float64)
+    # queries that see any requested key
+    need = np.zeros(L, dtype=bool)
+    need[q_rows] = True
+    for s0 in range(0, L, block):
+        blk = np.arange(s0, min(L, s0 + block))
+        need[blk] |= mask_rows(geom, blk)[:, k_rows].any(axis=1)
+    rows = np.nonzero(need)[0]
+    lse = lse_rows(q, k, geom, b, h, rows, block, qk=(qr, kr))
+    o = attention_rows(q, k, v, geom, b, h, rows, block, qk=(qr, kr))
+    dd = (g[rows] * o).sum(axis=1)
+    where = {int(r): i for i, r in enumerate(rows)}
+    dq = np.zeros((len(q_rows), q.shape[-1]))
+    dk = np.zeros((len(k_rows), q.shape[-1]))
+    dv = np.zeros((len(k_rows), q.shape[-1]))
+    for s0 in range(0, len(rows), block):
+        blk = rows[s0:s0 + block]
+        m = mask_rows(geom, blk)
+        sc = np.where(m, (qr[blk] @ kr.T) * geom.scale, -np.inf)
+        p = np.exp(sc - lse[s0:s0 + len(blk), None])
+        ds = p * (g[blk] @ vv.T - dd[s0:s0 + len(blk), None])
+        dv += p[:, k_rows].T @ g[blk]
+        dk += geom.scale * (ds[:, k_rows].T @ qr[blk])
+        for i, r in enumerate(blk):
+            hit = np.nonzero(q_rows == r)[0]
+            if len(hit):
+                dq[hit] = geom.scale * (ds[i] @ kr)
+    if geom.theta > 0:
+        dq = rope_rotate_inverse(dq[:, None, :], py[q_rows], px[q_rows], geom.theta)[:, 0, :]
+        dk = rope_rotate_inverse(dk[:, None, :], py[k_rows], px[k_rows], geom.theta)[:, 0, :]
+    return dq, dk, dv

@@ -1,0 +1,104 @@
+"""uhla_forward_lse and uhla_backward on the GPU vs the fp64 oracle (gradients pinned
+against torch autograd and finite differences in the oracle tests).
+
+Tolerances.  LSE: max-abs <= 2e-2, mean-abs <= 2e-3 (natural-log units, from bf16 inputs).
+Gradients are compared relative to the oracle gradient's own scale: max-abs error <= 2e-2
+x max |ref| and mean-abs error <= 5e-3 x mean |ref|.  The kernels round Q (rotated and
+scaled), P and dS to bf16 for the MFMAs (relative 2^-9 each) and store bf16 (2^-9), and the
+sums they enter have random signs, so the errors stay a small multiple of 2^-9 of the
+gradient's scale.
+* every row / every key at small sizes: both head dims, window sizes 8 and 16, radius
+  0 / 1 / 2, ragged guide grids, no guide tokens, RoPE off;
+* sampled query and key rows at the 2K workload (oracle rows of the backward);
+* determinism.
+"""
+import numpy as np
+import pytest
+
+import oracle.uhla_oracle as orc
+from global_attention_image_amd import api
+from global_attention_image_amd.inputs import CONFIGS, Geometry, make_qkv_bits
+
+from gpu_util import bf16_f64, from_dev, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fwd_bwd(g, q, k, v, do):
+    import torch
+    qt, kt, vt, gt = to_dev(q), to_dev(k), to_dev(v), to_dev(do)
+    o, lse = api.forward_lse(qt, kt, vt, g.H, g.W, g.w, g.H_lr, g.W_lr, rho=g.rho, theta=g.theta,
+                             radius=g.radius)
+    dq, dk, dv = api.backward(qt, kt, vt, o, gt, lse, g.H, g.W, g.w, g.H_lr, g.W_lr, rho=g.rho,
+                              theta=g.theta, radius=g.radius)
+    torch.cuda.synchronize()
+    return lse.cpu().numpy().astype(np.float64), from_dev(dq), from_dev(dk), from_dev(dv)
+
+
+def check_rel(got, want, what):
+    err = np.abs(got - want)
+    scale_max, scale_mean = np.abs(want).max(), np.abs(want).mean()
+    say(f"{what}: max-abs {err.max():.3e} (ref max {scale_max:.3e}) mean-abs {err.mean():.3e} "
+        f"(ref mean {scale_mean:.3e})")
+    assert err.max() <= 2e-2 * scale_max, what
+    assert err.mean() <= 5e-3 * scale_mean, what
+
+
+CASES = {
+    "d64_w8_r1": Geometry(B=1, heads=2, head_dim=64, H=32, W=32, w=8, H_lr=8, W_lr=8),
+    "d128_w16_ragged": Geometry(B=2, heads=2, head_dim=128, H=48, W=32, w=16, H_lr=13, W_lr=9),
+    "d128_r0": Geometry(B=1, heads=1, head_dim=128, H=48, W=48, w=16, H_lr=12, W_lr=12, radius=0),
+    "d64_r2": Geometry(B=1, heads=2, head_dim=64, H=80, W=48, w=16, H_lr=20, W_lr=12, radius=2),
+    "d128_no_guide": Geometry(B=1, heads=2, head_dim=128, H=48, W=48, w=16, H_lr=0, W_lr=0),
+    "d128_rope_off": Geometry(B=1, heads=1, head_dim=128, H=32, W=48, w=16, H_lr=8, W_lr=12,
+                              theta=0.0),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_backward_every_row(name):
+    g = CASES[name]
+    say(f"backward every row: {name} {g}")
+    q, k, v = make_qkv_bits(g, 111)
+    do = make_qkv_bits(g, 112)[0]
+    lse, dq, dk, dv = run_fwd_bwd(g, q, k, v, do)
+    rq, rk, rv = orc.backward(bf16_f64(q), bf16_f64(k), bf16_f64(v), bf16_f64(do), g)
+    for b in range(g.B):
+        for h in range(g.heads):
+            want_lse = orc.lse_rows(bf16_f64(q), bf16_f64(k), g, b, h, np.arange(g.L))
+            err = np.abs(lse[b, h] - want_lse)
+            say(f"  lse b{b} h{h}: max-abs {err.max():.3e} mean-abs {err.mean():.3e}")
+            assert err.max() <= 2e-2 and err.mean() <= 2e-3
+            check_rel(bf16_f64(dq[b, :, h]), rq[b, :, h], f"{name} dq b{b} h{h}")
+            check_rel(bf16_f64(dk[b, :, h]), rk[b, :, h], f"{name} dk b{b} h{h}")
+            check_rel(bf16_f64(dv[b, :, h]), rv[b, :, h], f"{name} dv b{b} h{h}")
+
+
+def test_backward_sampled_rows_2k():
+    g = CONFIGS["2k"]
+    say("backward sampled rows 2k")
+    q, k, v = make_qkv_bits(g, 1)
+    do = make_qkv_bits(g, 2)[0]
+    _, dq, dk, dv = run_fwd_bwd(g, q, k, v, do)
+    rng = np.random.default_rng(5)
+    qf, kf, vf, gf = (bf16_f64(x) for x in (q, k, v, do))
+    for h in (0, 17):
+        q_rows = np.unique(np.concatenate([[0, g.W - 1, g.N - 1, g.N, g.L - 1],
+                                           rng.integers(0, g.L, 120)]))
+        k_rows = np.unique(np.concatenate([[0, g.N - 1, g.N, g.L - 1], rng.integers(0, g.N, 60),
+                                           g.N + rng.integers(0, g.M, 4)]))
+        rq, rk, rv = orc.backward_rows(qf, kf, vf, gf, g, 0, h, q_rows, k_rows)
+        check_rel(bf16_f64(dq[0, q_rows, h]), rq, f"2k dq h{h}")
+        check_rel(bf16_f64(dk[0, k_rows, h]), rk, f"2k dk h{h}")
+        check_rel(bf16_f64(dv[0, k_rows, h]), rv, f"2k dv h{h}")
+
+
+def test_backward_deterministic():
+    g = CASES["d128_w16_ragged"]
+    say("backward determinism")
+    q, k, v = make_qkv_bits(g, 3)
+    do = make_qkv_bits(g, 4)[0]
+    a = run_fwd_bwd(g, q, k, v, do)
+    b = run_fwd_bwd(g, q, k, v, do)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)

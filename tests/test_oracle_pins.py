@@ -697,6 +697,20 @@ def test_pins_catch_backward_mutants(mutant):
         check_backward(mutant)
 
 
+def test_backward_rows_match_full_backward():
+    for g in (small_geom(head_dim=8, H=8, W=12, H_lr=2, W_lr=3),
+              small_geom(head_dim=8, T=3, guide_mode=2, radius=0)):
+        q, k, v = rand_qkv(g, 41)
+        do = rand_qkv(g, 42)[0]
+        dq, dk, dv = orc.backward(q, k, v, do, g)
+        qrows = np.array([0, 5, g.L - 1, g.N // 2])
+        krows = np.array([1, g.L - 2, g.T + g.N, 7])
+        rq, rk, rv = orc.backward_rows(q, k, v, do, g, 0, 0, qrows, krows, block=7)
+        assert np.max(np.abs(rq - dq[0, qrows, 0])) < 1e-12
+        assert np.max(np.abs(rk - dk[0, krows, 0])) < 1e-12
+        assert np.max(np.abs(rv - dv[0, krows, 0])) < 1e-12
+
+
 # --------------------------------------------------------- planted mistakes must be caught
 
 def _mut_index_transposed(H, W, w):
