@@ -1,7 +1,7 @@
 """Benchmark: hierarchical local attention forward at the 8K workload on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 8k] [--cpu-seconds S]
-                    [--radius R] [--guide-mode M] [--text T]
+                    [--radius R] [--guide-mode M] [--text T] [--backward]
 
 A step is one full uhla_forward (neighbour/cos-sin tables -> permutation fused with RoPE
 -> hi-res block-sparse attention -> guide attention -> inverse permutation) over one
@@ -11,6 +11,8 @@ value       effective TFLOP/s of the whole step: algorithmic FLOPs (4 * head_dim
             unmasked (query, key) pair) / step time.  --radius / --guide-mode measure the
             mask variants of uhla_forward_masked instead (default: the pages' mask), and
             --text T a joint sequence with T text tokens (uhla_forward_text).
+            --backward times a training step instead: uhla_forward_lse then uhla_backward
+            (algorithmic FLOPs: 4*d per pair forward, 10*d per pair backward).
 roofline    the dominant kernel (hi-res attention pass) against the bf16 MFMA peak:
             its algorithmic FLOPs per launch / its mean launch duration, measured with
             HIP events recorded on the launch stream during the timed steps.
@@ -98,6 +100,70 @@ def cpu_baseline(geom, q, k, v, seconds):
             "seconds": dt}
 
 
+def bench_backward(args, g):
+    """Training step: uhla_forward_lse + uhla_backward on the workload, dO synthetic."""
+    import torch
+    from global_attention_image_amd import api
+    from global_attention_image_amd.inputs import CONFIG_SEEDS, algorithmic_pairs, make_qkv_bits
+    if g.guide_mode or g.T:
+        print("the backward covers guide mode 0 without text tokens", file=sys.stderr)
+        sys.exit(2)
+    log(f"[bench] backward: generating seeded inputs for {g}")
+    q, k, v = make_qkv_bits(g, CONFIG_SEEDS[g.name])
+    do = make_qkv_bits(g, CONFIG_SEEDS[g.name] + 100)[0]
+    dev = torch.device("cuda:0")
+    up = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+    qt, kt, vt, gt = up(q), up(k), up(v), up(do)
+    out = torch.empty_like(qt)
+    lse = torch.empty((g.B, g.heads, g.L), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(qt), torch.empty_like(qt), torch.empty_like(qt)
+    fws = api.alloc_workspace(g.B, g.H, g.W, g.w, g.H_lr, g.W_lr, g.heads, g.head_dim, dev,
+                              rho=g.rho, radius=g.radius)
+    nb = api.load().uhla_backward_workspace_bytes(g.B, g.H, g.W, g.w, g.H_lr, g.W_lr, g.rho,
+                                                  g.heads, g.head_dim, g.radius)
+    bws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    fwd = lambda: api.forward_lse(qt, kt, vt, g.H, g.W, g.w, g.H_lr, g.W_lr, rho=g.rho,
+                                  theta=g.theta, radius=g.radius, out=out, lse=lse, workspace=fws)
+    bwd = lambda: api.backward(qt, kt, vt, out, gt, lse, g.H, g.W, g.w, g.H_lr, g.W_lr, rho=g.rho,
+                               theta=g.theta, radius=g.radius, dq=dq, dk=dk, dv=dv, workspace=bws)
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1, e2 in ev:
+        e0.record()
+        fwd()
+        e1.record()
+        bwd()
+        e2.record()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    f_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / args.steps
+    b_ms = sum(b.elapsed_time(c) for _, b, c in ev) / args.steps
+    pairs = algorithmic_pairs(g)["total"] * g.B * g.heads
+    f_fl, b_fl = 4 * g.head_dim * pairs, 10 * g.head_dim * pairs
+    res = {
+        "metric": METRIC + " (training step: forward with LSE + backward)",
+        "value": round((f_fl + b_fl) / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": g.name, "B": g.B, "heads": g.heads, "head_dim": g.head_dim,
+                   "grid": f"{g.H}x{g.W}", "window": g.w, "guide_grid": f"{g.H_lr}x{g.W_lr}",
+                   "rho": g.rho, "neighbourhood_radius": g.radius, "parallelism": "single GPU"},
+        "forward_ms": round(f_ms, 4), "backward_ms": round(b_ms, 4),
+        "algorithmic_flops": {"forward": f_fl, "backward": b_fl},
+        "roofline": {"kernel": "uhla_backward (all its kernels)", "bound": "mfma",
+                     "achieved": round(b_fl / (b_ms * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(b_fl / (b_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -109,6 +175,7 @@ def main():
     ap.add_argument("--radius", type=int, default=1)
     ap.add_argument("--guide-mode", type=int, default=0, choices=(0, 1, 2))
     ap.add_argument("--text", type=int, default=0, help="text tokens in the joint sequence")
+    ap.add_argument("--backward", action="store_true", help="time forward (with LSE) + backward")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -121,6 +188,8 @@ def main():
                                                     algorithmic_pairs, make_qkv_bits)
 
     g = CONFIGS[args.config].with_(radius=args.radius, guide_mode=args.guide_mode, T=args.text)
+    if args.backward:
+        return bench_backward(args, g)
     variant = args.radius != 1 or args.guide_mode != 0 or args.text != 0
     log(f"[bench] generating seeded inputs for {g}")
     t0 = time.perf_counter()
