@@ -9,7 +9,7 @@
 // Pipeline (caller's stream, no allocation):
 //   1. fp64 cos/sin table (as the forward);
 //   2. bwd_rows_kernel: per (b, h) buffers with hi rows window-first then guide rows,
-//      padded to 128: Qb = rope(Q) * s * log2 e (the forward's base-2 query), Kb = rope(K),
+//      padded to 256: Qb = rope(Q) * s * log2 e (the forward's base-2 query), Kb = rope(K),
 //      Vb, dOb; bwd_aux_kernel: per 64-row tile, lse2 = lse * log2 e (pad rows +inf) and D;
 //      bwd_transpose_kernel: Q, K, dO as 64-row tiles transposed to [D][64];
 //   3. bwd_dq_kernel (query-outer, the forward's tile lists): per key tile S, dP (two
@@ -30,10 +30,12 @@ constexpr int kBwdRowsPerBlock = 4;
 constexpr int kBwdThreads = 256;
 constexpr int kBwdMaxTiles = 1024;  // neighbour-window tiles per window (table in LDS)
 constexpr int kAuxBytes = 2 * kKeyTile * 4;  // per tile: 64 lse2 then 64 D values
+constexpr int kBwdWaves = 8;                  // guide-row workgroups: 8 waves x 32 rows
+constexpr int kBwdGuideRows = kBwdWaves * 32;
 
 struct BwdGeom {
   int B, H, W, w, H_lr, W_lr, rho, heads, D, radius;
-  int64_t N, M, R;  // R: rows per (b, h) = N + guide rows padded to 128
+  int64_t N, M, R;  // R: rows per (b, h) = N + guide rows padded to kBwdGuideRows
   int n_wx, n_wy, P;
 };
 
@@ -44,7 +46,7 @@ BwdGeom make_bwd_geom(int B, int H, int W, int w, int H_lr, int W_lr, int rho, i
   g.heads = heads; g.D = D; g.radius = radius;
   g.N = static_cast<int64_t>(H) * W;
   g.M = static_cast<int64_t>(H_lr) * W_lr;
-  g.R = g.N + (g.M + 127) / 128 * 128;
+  g.R = g.N + (g.M + kBwdGuideRows - 1) / kBwdGuideRows * kBwdGuideRows;
   g.n_wx = W / w; g.n_wy = H / w;
   g.P = H > W ? H : W;
   return g;
@@ -179,34 +181,50 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_rows_kernel(
 }
 
 // Per buffer row: lse2 = lse * log2 e (+inf for padding, so those rows get P = 0) and
-// D = sum_d dO * O in fp32, stored per 64-row tile as [64 lse2][64 D].
-__global__ void bwd_aux_kernel(const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout,
-                               const float* __restrict__ lse, float* __restrict__ aux, int64_t N,
-                               int64_t M, int64_t R, int W, int w, int n_wx, int W_lr, int rho,
-                               int heads, int D, int64_t bh_total) {
+// D = sum_d dO * O in fp32, stored per 64-row tile as [64 lse2][64 D].  D / 8 lanes read
+// one (token, head) row of O and dO in raster memory order (coalesced) and reduce across
+// lanes; threads past the B * L * heads rows fill the padding rows.
+__global__ __launch_bounds__(kBwdThreads) void bwd_aux_kernel(
+    const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout, const float* __restrict__ lse,
+    float* __restrict__ aux, int64_t N, int64_t M, int64_t R, int W, int w, int n_wx, int heads,
+    int D, int64_t bh_total) {
+  const int cpr = D / 8;  // 16-byte chunks per row: 16 or 8, a power of two dividing 64
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= bh_total * R) return;
-  const int64_t bh = i / R, row = i - bh * R;
-  const int64_t b = bh / heads, h = bh - b * heads;
-  int py, px;
-  const int64_t src = bwd_source(row, N, M, W, w, n_wx, W_lr, rho, py, px);
-  float l2 = INFINITY, dd = 0.0f;
-  if (src >= 0) {
-    l2 = lse[bh * (N + M) + src] * 1.4426950408889634f;
-    const bf16_t* orow = o + ((b * (N + M) + src) * heads + h) * D;
-    const bf16_t* grow = dout + ((b * (N + M) + src) * heads + h) * D;
-    for (int d = 0; d < D; d += 8) {
-      const uint4 a = *reinterpret_cast<const uint4*>(orow + d);
-      const uint4 c = *reinterpret_cast<const uint4*>(grow + d);
-      const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, cw[4] = {c.x, c.y, c.z, c.w};
-      for (int e = 0; e < 4; ++e)
-        dd += __uint_as_float(aw[e] << 16) * __uint_as_float(cw[e] << 16) +
-              __uint_as_float(aw[e] & 0xffff0000u) * __uint_as_float(cw[e] & 0xffff0000u);
+  const int64_t rows = bh_total * (N + M);  // (b, token, head) rows, raster memory order
+  const int64_t gi = i / cpr;
+  const int c = static_cast<int>(i - gi * cpr);
+  if (gi < rows) {
+    const uint4 a = *reinterpret_cast<const uint4*>(o + gi * D + c * 8);
+    const uint4 g = *reinterpret_cast<const uint4*>(dout + gi * D + c * 8);
+    const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, gw[4] = {g.x, g.y, g.z, g.w};
+    float dd = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      dd += __uint_as_float(aw[e] << 16) * __uint_as_float(gw[e] << 16) +
+            __uint_as_float(aw[e] & 0xffff0000u) * __uint_as_float(gw[e] & 0xffff0000u);
+    for (int m = 1; m < cpr; m <<= 1) dd += __shfl_xor(dd, m, 64);
+    if (c) return;
+    const int64_t bt = gi / heads, h = gi - bt * heads;  // bt = b * (N + M) + token
+    const int64_t b = bt / (N + M), src = bt - b * (N + M);
+    int64_t row = src;
+    if (src < N) {  // raster -> window-first
+      const int y = static_cast<int>(src / W), x = static_cast<int>(src - static_cast<int64_t>(y) * W);
+      const int wy = y / w, wx = x / w;
+      row = (static_cast<int64_t>(wy) * n_wx + wx) * w * w + (y - wy * w) * w + (x - wx * w);
     }
+    const int64_t bh = b * heads + h;
+    float* t = aux + (bh * (R / kKeyTile) + row / kKeyTile) * (2 * kKeyTile);
+    t[row % kKeyTile] = lse[bh * (N + M) + src] * 1.4426950408889634f;
+    t[kKeyTile + row % kKeyTile] = dd;
+    return;
   }
+  const int64_t pad = R - N - M;
+  const int64_t j = i - rows * cpr;
+  if (j >= bh_total * pad) return;
+  const int64_t bh = j / pad, row = N + M + (j - bh * pad);
   float* t = aux + (bh * (R / kKeyTile) + row / kKeyTile) * (2 * kKeyTile);
-  t[row % kKeyTile] = l2;
-  t[kKeyTile + row % kKeyTile] = dd;
+  t[row % kKeyTile] = INFINITY;
+  t[kKeyTile + row % kKeyTile] = 0.0f;
 }
 
 // [bh][R][D] row-major -> [bh][R/64][D][64] tiles, rows within a tile in v_slot order.
@@ -637,15 +655,15 @@ int validate_backward(const void* const* ptrs, int n_ptrs, int B, int H, int W, 
 
 template <int D>
 void launch_dq(int nwaves, bool hi, const BwdArgs& a, hipStream_t s) {
-  if (!hi) hipLaunchKernelGGL((bwd_dq_kernel<D, 4, false>), dim3(a.total_blocks), dim3(256), 0, s, a);
-  else if (nwaves == 4) hipLaunchKernelGGL((bwd_dq_kernel<D, 4, true>), dim3(a.total_blocks), dim3(256), 0, s, a);
+  if (!hi) hipLaunchKernelGGL((bwd_dq_kernel<D, kBwdWaves, false>), dim3(a.total_blocks), dim3(kBwdWaves * 64), 0, s, a);
+  else if (nwaves == kBwdWaves) hipLaunchKernelGGL((bwd_dq_kernel<D, kBwdWaves, true>), dim3(a.total_blocks), dim3(kBwdWaves * 64), 0, s, a);
   else hipLaunchKernelGGL((bwd_dq_kernel<D, 2, true>), dim3(a.total_blocks), dim3(128), 0, s, a);
 }
 
 template <int D>
 void launch_dkv(int nwaves, bool hi, const BwdArgs& a, hipStream_t s) {
-  if (!hi) hipLaunchKernelGGL((bwd_dkv_kernel<D, 4, false>), dim3(a.total_blocks), dim3(256), 0, s, a);
-  else if (nwaves == 4) hipLaunchKernelGGL((bwd_dkv_kernel<D, 4, true>), dim3(a.total_blocks), dim3(256), 0, s, a);
+  if (!hi) hipLaunchKernelGGL((bwd_dkv_kernel<D, kBwdWaves, false>), dim3(a.total_blocks), dim3(kBwdWaves * 64), 0, s, a);
+  else if (nwaves == kBwdWaves) hipLaunchKernelGGL((bwd_dkv_kernel<D, kBwdWaves, true>), dim3(a.total_blocks), dim3(kBwdWaves * 64), 0, s, a);
   else hipLaunchKernelGGL((bwd_dkv_kernel<D, 2, true>), dim3(a.total_blocks), dim3(128), 0, s, a);
 }
 
@@ -730,10 +748,10 @@ extern "C" int uhla_backward(const void* q, const void* k, const void* v, const 
                          heads, rope_on ? 1 : 0, qs);
     st = check_launch("bwd_rows_kernel");
     if (st) return st;
-    const int64_t rows = BH * g.R;
-    UHLA_BSTEP(hipLaunchKernelGGL(bwd_aux_kernel, dim3(static_cast<unsigned>((rows + 255) / 256)), dim3(256), 0, s,
-                                  static_cast<const bf16_t*>(o), gp, lse, ws.aux, g.N, g.M, g.R, W, w,
-                                  n_wx, W_lr, rho, heads, D, BH),
+    const int64_t aux_threads = BH * (g.N + g.M) * (D / 8) + BH * (g.R - g.N - g.M);
+    UHLA_BSTEP(hipLaunchKernelGGL(bwd_aux_kernel, dim3(static_cast<unsigned>((aux_threads + kBwdThreads - 1) / kBwdThreads)),
+                                  dim3(kBwdThreads), 0, s, static_cast<const bf16_t*>(o), gp, lse,
+                                  ws.aux, g.N, g.M, g.R, W, w, n_wx, heads, D, BH),
                "bwd_aux_kernel");
     const dim3 tg(static_cast<unsigned>(g.R / kKeyTile), static_cast<unsigned>(BH));
     UHLA_BSTEP(hipLaunchKernelGGL(bwd_transpose_kernel, tg, dim3(kBwdThreads), 0, s, ws.qb, ws.qt, g.R, D),
@@ -751,7 +769,7 @@ extern "C" int uhla_backward(const void* q, const void* k, const void* v, const 
   a.heads = heads; a.w2 = w * w; a.W = W; a.w = w; a.n_wx = n_wx; a.n_wy = H / w;
   a.radius = radius; a.rho = rho; a.W_lr = W_lr; a.P = g.P;
   a.rope_on = rope_on ? 1 : 0; a.log2_theta = l2t;
-  const int nw_hi = std::min(4, w * w / 32);
+  const int nw_hi = std::min(kBwdWaves, w * w / 32);  // w * w is 64 or a multiple of 256
 
   // dQ: hi queries, then guide queries
   a.out0 = static_cast<bf16_t*>(dq);
@@ -761,9 +779,9 @@ extern "C" int uhla_backward(const void* q, const void* k, const void* v, const 
   UHLA_BSTEP((D == 128 ? launch_dq<128>(nw_hi, true, a, s) : launch_dq<64>(nw_hi, true, a, s)),
              "bwd_dq_kernel(hi)");
   if (g.M > 0) {
-    a.blocks_per_bh = static_cast<int>((g.R - g.N) / 128);
+    a.blocks_per_bh = static_cast<int>((g.R - g.N) / kBwdGuideRows);
     a.total_blocks = static_cast<int>(BH * a.blocks_per_bh);
-    UHLA_BSTEP((D == 128 ? launch_dq<128>(4, false, a, s) : launch_dq<64>(4, false, a, s)),
+    UHLA_BSTEP((D == 128 ? launch_dq<128>(kBwdWaves, false, a, s) : launch_dq<64>(kBwdWaves, false, a, s)),
                "bwd_dq_kernel(guide)");
   }
   // dK, dV: hi keys, then guide keys
@@ -775,9 +793,9 @@ extern "C" int uhla_backward(const void* q, const void* k, const void* v, const 
   UHLA_BSTEP((D == 128 ? launch_dkv<128>(nw_hi, true, a, s) : launch_dkv<64>(nw_hi, true, a, s)),
              "bwd_dkv_kernel(hi)");
   if (g.M > 0) {
-    a.blocks_per_bh = static_cast<int>((g.R - g.N) / 128);
+    a.blocks_per_bh = static_cast<int>((g.R - g.N) / kBwdGuideRows);
     a.total_blocks = static_cast<int>(BH * a.blocks_per_bh);
-    UHLA_BSTEP((D == 128 ? launch_dkv<128>(4, false, a, s) : launch_dkv<64>(4, false, a, s)),
+    UHLA_BSTEP((D == 128 ? launch_dkv<128>(kBwdWaves, false, a, s) : launch_dkv<64>(kBwdWaves, false, a, s)),
                "bwd_dkv_kernel(guide)");
   }
 #undef UHLA_BSTEP
