@@ -82,15 +82,12 @@ static Geom make_geom(int B, int H, int W, int w, int H_lr, int W_lr, int rho, i
 
 struct Workspace {
   double2* cs;    // [P][D/4]
-  bf16_t* q_hi;   // [B*heads][N][D]   window-first, rotated
   bf16_t* k_hi;   // [B*heads][N][D]   window-first, rotated
   bf16_t* v_hi;   // [B*heads][N/64][D][64]  window-first, transposed tiles
-  bf16_t* q_lr;   // [B*heads][Mq][D]  rotated, zero padded
   bf16_t* k_lr;   // [B*heads][Mg][D]  global keys: guide rows (Mk, zero padded), text rows (Tk)
   bf16_t* v_lr;   // [B*heads][Mg/64][D][64]
   bf16_t* k_gb;   // [B*heads][Mbg][D] guide K in 8x8 cell blocks, then text (guide modes 1, 2)
   bf16_t* v_gb;   // [B*heads][Mbg/64][D][64]
-  bf16_t* q_tx;   // [B*heads][Tq][D]  text queries (scaled, zero padded)
   float* o_part;  // [splits][B*heads][Tq][D]  text-query partial outputs (unnormalised)
   float2* ml_part;  // [splits][B*heads][Tq]   their (running max, sum)
   size_t bytes;
@@ -107,28 +104,22 @@ static Workspace carve(const Geom& g, void* base) {
   const size_t bh = static_cast<size_t>(g.B) * g.heads;
   const size_t e = sizeof(bf16_t);
   const size_t o_cs = take(sizeof(double2) * g.P * (g.D / 4));
-  const size_t o_qh = take(bh * g.N * g.D * e);
   const size_t o_kh = take(bh * g.N * g.D * e);
   const size_t o_vh = take(bh * g.N * g.D * e);
-  const size_t o_ql = take(bh * g.Mq * g.D * e);
   const size_t o_kl = take(bh * g.Mg * g.D * e);
   const size_t o_vl = take(bh * g.Mg * g.D * e);
   const size_t o_kb = take(bh * g.Mbg * g.D * e);
   const size_t o_vb = take(bh * g.Mbg * g.D * e);
-  const size_t o_qt = take(bh * g.Tq * g.D * e);
   const size_t o_op = take(static_cast<size_t>(g.splits) * bh * g.Tq * g.D * sizeof(float));
   const size_t o_ml = take(static_cast<size_t>(g.splits) * bh * g.Tq * sizeof(float2));
   char* b = static_cast<char*>(base);
   ws.cs = reinterpret_cast<double2*>(b + o_cs);
-  ws.q_hi = reinterpret_cast<bf16_t*>(b + o_qh);
   ws.k_hi = reinterpret_cast<bf16_t*>(b + o_kh);
   ws.v_hi = reinterpret_cast<bf16_t*>(b + o_vh);
-  ws.q_lr = reinterpret_cast<bf16_t*>(b + o_ql);
   ws.k_lr = reinterpret_cast<bf16_t*>(b + o_kl);
   ws.v_lr = reinterpret_cast<bf16_t*>(b + o_vl);
   ws.k_gb = reinterpret_cast<bf16_t*>(b + o_kb);
   ws.v_gb = reinterpret_cast<bf16_t*>(b + o_vb);
-  ws.q_tx = reinterpret_cast<bf16_t*>(b + o_qt);
   ws.o_part = reinterpret_cast<float*>(b + o_op);
   ws.ml_part = reinterpret_cast<float2*>(b + o_ml);
   ws.bytes = off;
@@ -159,35 +150,30 @@ __global__ void cos_sin_table_kernel(double2* cs, int P, int D, double log2_thet
 constexpr int kPrepThreads = 256;
 constexpr int kPrepRows = 4;
 
-// Q and K rows -> head-major, rotated.  The input rows are [text | hi | guide].  Prep rows
-// of a batch:
-//   [0, N)            hi-res rows in window-first order (source row T + r(p)) -> q_hi, k_hi;
-//   [N, N + Mq)       guide rows s (source T + N + s, zero beyond M) -> q_lr row s, and
-//                     k_lr row s for s < Mk;
+// K rows -> head-major, rotated.  The input rows are [text | hi | guide].  Prep rows of a
+// batch:
+//   [0, N)            hi-res rows in window-first order (source row T + r(p)) -> k_hi;
+//   [N, N + Mk)       guide rows s (source T + N + s, zero beyond M) -> k_lr row s;
 //   [.., + Mb)        guide cells in 8x8 block order (zero outside the grid) -> k_gb, used
 //                     by the guide-locality masks;
-//   [.., + Tq)        text rows x (source x, zero beyond T; position (0, 0), so RoPE is the
-//                     identity) -> q_tx row x, k_lr row Mk + x and, with cell blocks,
-//                     k_gb row Mb + x.
-// Q is also multiplied by q_scale (the softmax scale times log2 e) before its single
-// rounding to bf16, so the attention kernel's scores come out in base-2 logits.
+//   [.., + Tk)        text rows x (source x, zero beyond T; position (0, 0), so RoPE is the
+//                     identity) -> k_lr row Mk + x and, with cell blocks, k_gb row Mb + x.
+// Q is not prepared: the attention kernel rotates its query rows as it loads them.
 template <int D>
-__global__ __launch_bounds__(kPrepThreads) void prep_qk_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, bf16_t* __restrict__ q_hi,
-    bf16_t* __restrict__ k_hi, bf16_t* __restrict__ q_lr, bf16_t* __restrict__ k_lr,
-    bf16_t* __restrict__ k_gb, bf16_t* __restrict__ q_tx, const double2* __restrict__ cs,
-    int P, double log2_theta, int64_t T, int64_t N, int64_t M, int64_t Mq, int64_t Mk,
-    int64_t Mg, int64_t Mb, int64_t Mbg, int64_t Tk, int64_t Tq, int W, int w, int n_wx,
-    int H_lr, int W_lr, int nbj, int rho, int heads, int rope_on, double q_scale) {
+__global__ __launch_bounds__(kPrepThreads) void prep_k_kernel(
+    const bf16_t* __restrict__ k, bf16_t* __restrict__ k_hi, bf16_t* __restrict__ k_lr,
+    bf16_t* __restrict__ k_gb, const double2* __restrict__ cs, int P, double log2_theta,
+    int64_t T, int64_t N, int64_t M, int64_t Mk, int64_t Mg, int64_t Mb, int64_t Mbg,
+    int64_t Tk, int W, int w, int n_wx, int H_lr, int W_lr, int nbj, int rho, int heads,
+    int rope_on) {
   constexpr int CPH = D / 8;      // 16-byte chunks per head row
   constexpr int QUARTER = D / 4;  // rotation pairs per axis
   // Per row of this block: source row (-1: zero row), destinations (buffer row offsets in
-  // elements of one head row, -1: none), and the RoPE factors of its y and x positions.
+  // elements of one head row, null: none), and the RoPE factors of its y and x positions.
   __shared__ int64_t src_s[kPrepRows];
-  __shared__ bf16_t* dq_s[kPrepRows];
   __shared__ bf16_t* dk_s[kPrepRows];
   __shared__ bf16_t* dk2_s[kPrepRows];
-  __shared__ int64_t qst_s[kPrepRows], kst_s[kPrepRows], k2st_s[kPrepRows];  // per-head strides
+  __shared__ int64_t kst_s[kPrepRows], k2st_s[kPrepRows];  // per-head strides
   __shared__ int pos_s[kPrepRows][2];
   __shared__ double2 cs_s[kPrepRows][2][QUARTER];
   const int64_t L = T + N + M;
@@ -197,19 +183,17 @@ __global__ __launch_bounds__(kPrepThreads) void prep_qk_kernel(
     const int64_t row = static_cast<int64_t>(blockIdx.x) * kPrepRows + tid;
     const int64_t bh0 = b * heads;  // first (b, h) of this batch
     int64_t src = -1;
-    bf16_t* dq = nullptr;
     bf16_t* dk = nullptr;
     bf16_t* dk2 = nullptr;
-    int64_t qst = 0, kst = 0, k2st = 0;
+    int64_t kst = 0, k2st = 0;
     int py = 0, px = 0;
     if (row < N) {
       const int r = window_first_to_raster(static_cast<int>(row), W, w, n_wx);
       src = T + r;
       py = r / W;
       px = r - py * W;
-      dq = q_hi + (bh0 * N + row) * D;  qst = N * D;
       dk = k_hi + (bh0 * N + row) * D;  kst = N * D;
-    } else if (row < N + Mq) {
+    } else if (row < N + Mk) {
       const int64_t s = row - N;
       if (s < M) {
         src = T + N + s;
@@ -217,27 +201,22 @@ __global__ __launch_bounds__(kPrepThreads) void prep_qk_kernel(
         py = rho * sy;
         px = rho * static_cast<int>(s - static_cast<int64_t>(sy) * W_lr);
       }
-      dq = q_lr + (bh0 * Mq + s) * D;  qst = Mq * D;
-      if (s < Mk) { dk = k_lr + (bh0 * Mg + s) * D;  kst = Mg * D; }
-    } else if (row < N + Mq + Mb) {
-      const int64_t slot = row - N - Mq;
+      dk = k_lr + (bh0 * Mg + s) * D;  kst = Mg * D;
+    } else if (row < N + Mk + Mb) {
+      const int64_t slot = row - N - Mk;
       int ci, cj;
       block_cell(slot, nbj, ci, cj);
       if (ci < H_lr && cj < W_lr) src = T + N + static_cast<int64_t>(ci) * W_lr + cj;
       py = rho * ci;
       px = rho * cj;
       dk = k_gb + (bh0 * Mbg + slot) * D;  kst = Mbg * D;
-    } else if (row < N + Mq + Mb + Tq) {
-      const int64_t x = row - N - Mq - Mb;
+    } else if (row < N + Mk + Mb + Tk) {
+      const int64_t x = row - N - Mk - Mb;
       if (x < T) src = x;
-      dq = q_tx + (bh0 * Tq + x) * D;  qst = Tq * D;
-      if (x < Tk) {
-        dk = k_lr + (bh0 * Mg + Mk + x) * D;  kst = Mg * D;
-        if (Mb > 0) { dk2 = k_gb + (bh0 * Mbg + Mb + x) * D;  k2st = Mbg * D; }
-      }
+      dk = k_lr + (bh0 * Mg + Mk + x) * D;  kst = Mg * D;
+      if (Mb > 0) { dk2 = k_gb + (bh0 * Mbg + Mb + x) * D;  k2st = Mbg * D; }
     }
     src_s[tid] = src;
-    dq_s[tid] = dq;  qst_s[tid] = qst;
     dk_s[tid] = dk;  kst_s[tid] = kst;
     dk2_s[tid] = dk2;  k2st_s[tid] = k2st;
     pos_s[tid][0] = py;
@@ -259,29 +238,22 @@ __global__ __launch_bounds__(kPrepThreads) void prep_qk_kernel(
   for (; t < kPrepRows; ) {
     const int h = c / CPH, j = c % CPH;
     const int64_t src = src_s[t];
-    uint4 qo = make_uint4(0, 0, 0, 0), ko = make_uint4(0, 0, 0, 0);
+    uint4 ko = make_uint4(0, 0, 0, 0);
     if (src >= 0) {
       const int64_t so = ((b * L + src) * heads + h) * D + j * 8;
-      const uint4 qi = *reinterpret_cast<const uint4*>(q + so);
       const uint4 ki = *reinterpret_cast<const uint4*>(k + so);
       if (rope_on) {
         // pairs 4j .. 4j+3 lie on one axis (y for the first D/4 pairs)
         const int axis = (4 * j) / QUARTER, k0 = 4 * j - axis * QUARTER;
         const double2* f = &cs_s[t][axis][k0];
-        qo = make_uint4(rope_rotate_word(qi.x, f[0], q_scale), rope_rotate_word(qi.y, f[1], q_scale),
-                        rope_rotate_word(qi.z, f[2], q_scale), rope_rotate_word(qi.w, f[3], q_scale));
         ko = make_uint4(rope_rotate_word(ki.x, f[0]), rope_rotate_word(ki.y, f[1]),
                         rope_rotate_word(ki.z, f[2]), rope_rotate_word(ki.w, f[3]));
       } else {
-        qo = make_uint4(scale_word(qi.x, q_scale), scale_word(qi.y, q_scale),
-                        scale_word(qi.z, q_scale), scale_word(qi.w, q_scale));
         ko = ki;
       }
     }
-    bf16_t* dq = dq_s[t];
     bf16_t* dk = dk_s[t];
     bf16_t* dk2 = dk2_s[t];
-    if (dq) *reinterpret_cast<uint4*>(dq + h * qst_s[t] + j * 8) = qo;
     if (dk) *reinterpret_cast<uint4*>(dk + h * kst_s[t] + j * 8) = ko;
     if (dk2) *reinterpret_cast<uint4*>(dk2 + h * k2st_s[t] + j * 8) = ko;
     c += kPrepThreads;
@@ -362,8 +334,13 @@ __global__ __launch_bounds__(kPrepThreads) void prep_v_kernel(
 // ------------------------------------------------------------------ steps 3-4: attention
 
 struct AttnArgs {
-  const bf16_t* q;        // [B*heads][q_rows][D]
-  int64_t q_rows;         // rows per (b, h) of q
+  const bf16_t* q;        // the caller's token-major Q [B][out_rows][heads][D]; query row i of
+                          // the pass is token out_row0 + (hi pass: r(i), else i)
+  int64_t q_rows;         // query rows per (b, h) of the pass (a multiple of the block)
+  const double2* cs;      // fp64 RoPE factors [P][D/4]
+  double log2_theta;      // for positions >= P
+  double q_scale;         // softmax scale * log2 e, applied to Q before its rounding to bf16
+  int P, rope_on;
   const bf16_t* k_hi;     // [B*heads][N][D]
   const bf16_t* v_hi;     // [B*heads][N/64][D][64]
   const bf16_t* k_lr;     // [B*heads][Mg][D]        global keys: guide rows, then text rows
@@ -581,13 +558,55 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
     return 0xffffu;
   };
 
-  // Query fragment (B operand of S^T = K Q^T): lane holds query ql, dims 16kk + 8g .. +8.
+  // Query fragment (B operand of S^T = K Q^T): lane holds query ql, dims 16kk + 8g .. +8,
+  // read from the caller's Q row and rotated here (RoPE fused into the Q load): fp64
+  // rotation times the softmax scale * log2 e, one rounding to bf16, so the scores come out
+  // in base-2 logits.  Hi queries sit at their raster position, guide query s at
+  // (rho * (s / W_lr), rho * (s % W_lr)), text queries at (0, 0); rows past the pass's
+  // valid rows are zero.
   bf16x8 qf[D / 16];
   {
-    const bf16_t* qrow = a.q + (bh * a.q_rows + q0 + wave * 32 + ql) * D;
+    constexpr int QUARTER = D / 4;
+    const int qi = q0 + wave * 32 + ql;
+    uint4 raw[D / 16];
+    int py = 0, px = 0;
+    const bool qvalid = qi < a.q_valid;
+    if (qvalid) {
+      int tok = qi;
+      if (HI) {
+        tok = window_first_to_raster(qi, a.W, a.w, a.n_wx);
+        py = tok / a.W;
+        px = tok - py * a.W;
+      } else if (!TEXT) {
+        const int sy = qi / a.W_lr;
+        py = a.rho * sy;
+        px = a.rho * (qi - sy * a.W_lr);
+      }
+      const bf16_t* qrow = a.q + ((static_cast<int64_t>(b) * a.out_rows + a.out_row0 + tok) * a.heads + h) * D;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-      qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + 16 * kk + 8 * g);
+      for (int kk = 0; kk < D / 16; ++kk) raw[kk] = *reinterpret_cast<const uint4*>(qrow + 16 * kk + 8 * g);
+    }
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      uint4 qo = make_uint4(0, 0, 0, 0);
+      if (qvalid) {
+        // pairs 8kk + 4g .. +3 lie on one axis (y for the first D/4 pairs)
+        const int pr = 8 * kk + 4 * g, axis = pr / QUARTER, k0 = pr - axis * QUARTER;
+        if (a.rope_on) {
+          const int pos = axis ? px : py;
+          double2 f[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            f[e] = pos < a.P ? a.cs[pos * QUARTER + k0 + e] : rope_cos_sin(pos, k0 + e, D / 2, a.log2_theta);
+          qo = make_uint4(rope_rotate_word(raw[kk].x, f[0], a.q_scale), rope_rotate_word(raw[kk].y, f[1], a.q_scale),
+                          rope_rotate_word(raw[kk].z, f[2], a.q_scale), rope_rotate_word(raw[kk].w, f[3], a.q_scale));
+        } else {
+          qo = make_uint4(scale_word(raw[kk].x, a.q_scale), scale_word(raw[kk].y, a.q_scale),
+                          scale_word(raw[kk].z, a.q_scale), scale_word(raw[kk].w, a.q_scale));
+        }
+      }
+      qf[kk] = *reinterpret_cast<const bf16x8*>(&qo);
+    }
   }
   // Let the Q loads complete here, in a wait the compiler sees: it cannot see the
   // tile DMA below, and would otherwise wait for "the Q loads" inside the loop by
@@ -1035,27 +1054,24 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
   }
   if (timer) timer_end(timer, UHLA_STAGE_TABLES, s);
 
-  // 2. prep: permutation + RoPE (Q, K) and permutation + tile transpose (V)
-  const bf16_t* qb = static_cast<const bf16_t*>(q);
+  // 2. prep: permutation + RoPE (K) and permutation + tile transpose (V); Q is rotated
+  //    as the attention kernel loads it
+  const double l2t = rope_on ? log2(static_cast<double>(theta)) : 0.0;
   const bf16_t* kb = static_cast<const bf16_t*>(k);
   const bf16_t* vb = static_cast<const bf16_t*>(v);
   if (timer) timer_begin(timer, UHLA_STAGE_PREP_HI, s);
   {
-    const int64_t rows = g.N + g.Mq + g.Mb + g.Tq;
+    const int64_t rows = g.N + g.Mk + g.Mb + g.Tk;
     const dim3 grid(static_cast<unsigned>((rows + kPrepRows - 1) / kPrepRows), B);
-    const double l2t = rope_on ? log2(static_cast<double>(theta)) : 0.0;
-    const double qs = static_cast<double>(sc) * 1.4426950408889634;
     if (D == 128)
-      hipLaunchKernelGGL(prep_qk_kernel<128>, grid, dim3(kPrepThreads), 0, s, qb, kb, ws.q_hi,
-                         ws.k_hi, ws.q_lr, ws.k_lr, ws.k_gb, ws.q_tx, ws.cs, g.P, l2t, T, g.N,
-                         g.M, g.Mq, g.Mk, g.Mg, g.Mb, g.Mbg, g.Tk, g.Tq, W, w, g.n_wx, H_lr, W_lr,
-                         g.nbj, rho, heads, rope_on ? 1 : 0, qs);
+      hipLaunchKernelGGL(prep_k_kernel<128>, grid, dim3(kPrepThreads), 0, s, kb, ws.k_hi, ws.k_lr,
+                         ws.k_gb, ws.cs, g.P, l2t, T, g.N, g.M, g.Mk, g.Mg, g.Mb, g.Mbg, g.Tk, W,
+                         w, g.n_wx, H_lr, W_lr, g.nbj, rho, heads, rope_on ? 1 : 0);
     else
-      hipLaunchKernelGGL(prep_qk_kernel<64>, grid, dim3(kPrepThreads), 0, s, qb, kb, ws.q_hi,
-                         ws.k_hi, ws.q_lr, ws.k_lr, ws.k_gb, ws.q_tx, ws.cs, g.P, l2t, T, g.N,
-                         g.M, g.Mq, g.Mk, g.Mg, g.Mb, g.Mbg, g.Tk, g.Tq, W, w, g.n_wx, H_lr, W_lr,
-                         g.nbj, rho, heads, rope_on ? 1 : 0, qs);
-    st = check_launch("prep_qk_kernel");
+      hipLaunchKernelGGL(prep_k_kernel<64>, grid, dim3(kPrepThreads), 0, s, kb, ws.k_hi, ws.k_lr,
+                         ws.k_gb, ws.cs, g.P, l2t, T, g.N, g.M, g.Mk, g.Mg, g.Mb, g.Mbg, g.Tk, W,
+                         w, g.n_wx, H_lr, W_lr, g.nbj, rho, heads, rope_on ? 1 : 0);
+    st = check_launch("prep_k_kernel");
     if (st) return st;
     const int64_t tiles = (g.N + g.Mg + g.Mbg) / kKeyTile;
     UHLA_STEP(hipLaunchKernelGGL(prep_v_kernel, dim3(static_cast<unsigned>(tiles), B), dim3(kPrepThreads), 0, s,
@@ -1068,6 +1084,10 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
   if (timer) timer_end(timer, UHLA_STAGE_PREP_LR, s);
 
   AttnArgs a{};
+  a.q = static_cast<const bf16_t*>(q);
+  a.cs = ws.cs; a.log2_theta = l2t; a.P = g.P; a.rope_on = rope_on ? 1 : 0;
+  a.q_scale = static_cast<double>(sc) * 1.4426950408889634;
+  a.rho = rho; a.H_lr = H_lr; a.W_lr = W_lr; a.nbj = g.nbj;  // guide query positions
   a.k_hi = ws.k_hi; a.v_hi = ws.v_hi; a.k_lr = ws.k_lr; a.v_lr = ws.v_lr;
   a.N = g.N; a.M = g.M; a.Mk = g.Mk; a.Mg = g.Mg; a.T = T; a.Mb = g.Mb;
   a.heads = heads; a.w2 = w2;
@@ -1081,7 +1101,7 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
     const int nwaves = w2 >= kMaxQuery ? 8 : w2 / 32;
     const int qt = nwaves * 32;
     AttnArgs h = a;
-    h.q = ws.q_hi; h.q_rows = g.N;
+    h.q_rows = g.N;
     h.out_row0 = T;
     h.W = W; h.w = w; h.n_wx = g.n_wx; h.n_wy = g.n_wy;
     h.radius = radius;
@@ -1090,7 +1110,6 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
       h.k_lr = ws.k_gb; h.v_lr = ws.v_gb; h.Mg = g.Mbg;
     }
     h.reach = guide_mode == 1 ? 0 : radius;
-    h.rho = rho; h.H_lr = H_lr; h.W_lr = W_lr; h.nbj = g.nbj;
     h.q_valid = static_cast<int>(g.N);
     h.blocks_per_bh = static_cast<int>(g.N / qt);
     h.total_blocks = static_cast<int>(BH * h.blocks_per_bh);
@@ -1102,7 +1121,7 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
   if (timer) timer_begin(timer, UHLA_STAGE_ATTN_LR, s);
   if (g.M > 0) {
     AttnArgs l = a;
-    l.q = ws.q_lr; l.q_rows = g.Mq;
+    l.q_rows = g.Mq;
     l.out_row0 = T + g.N;
     l.q_valid = static_cast<int>(g.M);
     l.blocks_per_bh = static_cast<int>(g.Mq / kMaxQuery);
@@ -1119,7 +1138,7 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
   if (timer) timer_begin(timer, UHLA_STAGE_ATTN_TEXT, s);
   if (T > 0) {
     AttnArgs x = a;
-    x.q = ws.q_tx; x.q_rows = g.Tq;
+    x.q_rows = g.Tq;
     x.q_valid = static_cast<int>(T);
     x.splits = g.splits;
     x.blocks_per_bh = static_cast<int>(g.Tq / kMaxQuery) * g.splits;

@@ -172,16 +172,15 @@ def test_forward_masked_rejects(lib, radius, mode, kw, status):
 
 def expected_workspace(B, H, W, w, H_lr, W_lr, heads, d, guide_mode=0):
     """Independent restatement of the workspace layout (regions 256-byte aligned): cos/sin
-    table, Q/K/V hi rows, Q guide rows (256-padded), K/V guide rows (64-padded), and for
-    guide modes 1 and 2 a copy of the guide K/V in 8x8 cell blocks."""
+    table, K/V hi rows, K/V guide rows (64-padded), and for guide modes 1 and 2 a copy of
+    the guide K/V in 8x8 cell blocks (Q is rotated as the attention kernel loads it)."""
     al = lambda x: (x + 255) // 256 * 256
     N, M = H * W, H_lr * W_lr
-    Mk, Mq = (M + 63) // 64 * 64, (M + 255) // 256 * 256
+    Mk = (M + 63) // 64 * 64
     Mb = ((H_lr + 7) // 8) * ((W_lr + 7) // 8) * 64 if (guide_mode and M) else 0
     e, bh = 2, B * heads
     parts = [16 * max(H, W) * (d // 4), bh * N * d * e, bh * N * d * e,
-             bh * N * d * e, bh * Mq * d * e, bh * Mk * d * e, bh * Mk * d * e,
-             bh * Mb * d * e, bh * Mb * d * e]
+             bh * Mk * d * e, bh * Mk * d * e, bh * Mb * d * e, bh * Mb * d * e]
     return sum(al(p) for p in parts)
 
 
@@ -207,7 +206,7 @@ def test_masked_workspace_bytes(lib, g, mode):
 
 def expected_text_extra(B, T, H, W, w, H_lr, W_lr, heads, d, guide_mode):
     """Extra workspace bytes with T text tokens: text rows appended to the global-key
-    buffers (and to the cell-block buffers), text queries, and the split partial results
+    buffers (and to the cell-block buffers) and the split partial results
     (splits = min(ceil(1024 / query blocks), max(1, key tiles // 8)))."""
     al = lambda x: (x + 255) // 256 * 256
     N, M = H * W, H_lr * W_lr
@@ -219,7 +218,7 @@ def expected_text_extra(B, T, H, W, w, H_lr, W_lr, heads, d, guide_mode):
     grown = [(bh * (Mk + Tk) * d * e, bh * Mk * d * e)] * 2 + \
         [(bh * (Mb + (Tk if Mb else 0)) * d * e, bh * Mb * d * e)] * 2
     extra = sum(al(a) - al(b) for a, b in grown)
-    return extra + al(bh * Tq * d * e) + al(splits * bh * Tq * d * 4) + al(splits * bh * Tq * 8)
+    return extra + al(splits * bh * Tq * d * 4) + al(splits * bh * Tq * 8)
 
 
 @pytest.mark.parametrize("g", GEOMS)
