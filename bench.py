@@ -1,11 +1,12 @@
 """Benchmark: hierarchical local attention forward at the 8K workload on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 8k] [--cpu-seconds S]
-                    [--radius R] [--guide-mode M] [--text T] [--backward]
+                    [--radius R] [--guide-mode M] [--text T] [--backward] [--rope-at-load]
 
-A step is one full uhla_forward (neighbour/cos-sin tables -> permutation fused with RoPE
--> hi-res block-sparse attention -> guide attention -> inverse permutation) over one
-batch of synthetic inputs already resident in HBM.  Prints ONE JSON line.
+A step is one full uhla_forward (cos/sin table -> K, V permutation, K fused with RoPE ->
+hi-res block-sparse attention with Q rotated at load and the inverse permutation fused
+into its stores -> guide attention) over one batch of synthetic inputs already resident
+in HBM.  Prints ONE JSON line.
 
 value       effective TFLOP/s of the whole step: algorithmic FLOPs (4 * head_dim per
             unmasked (query, key) pair) / step time.  --radius / --guide-mode measure the
@@ -13,6 +14,8 @@ value       effective TFLOP/s of the whole step: algorithmic FLOPs (4 * head_dim
             --text T a joint sequence with T text tokens (uhla_forward_text).
             --backward times a training step instead: uhla_forward_lse then uhla_backward
             (algorithmic FLOPs: 4*d per pair forward, 10*d per pair backward).
+            --rope-at-load times uhla_forward_rope_at_load (K rotated at every K tile
+            load instead of once in the prep pass).
 roofline    the dominant kernel (hi-res attention pass) against the bf16 MFMA peak:
             its algorithmic FLOPs per launch / its mean launch duration, measured with
             HIP events recorded on the launch stream during the timed steps.
@@ -176,6 +179,8 @@ def main():
     ap.add_argument("--guide-mode", type=int, default=0, choices=(0, 1, 2))
     ap.add_argument("--text", type=int, default=0, help="text tokens in the joint sequence")
     ap.add_argument("--backward", action="store_true", help="time forward (with LSE) + backward")
+    ap.add_argument("--rope-at-load", action="store_true",
+                    help="uhla_forward_rope_at_load: K rotated at every K tile load")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -190,7 +195,7 @@ def main():
     g = CONFIGS[args.config].with_(radius=args.radius, guide_mode=args.guide_mode, T=args.text)
     if args.backward:
         return bench_backward(args, g)
-    variant = args.radius != 1 or args.guide_mode != 0 or args.text != 0
+    variant = args.radius != 1 or args.guide_mode != 0 or args.text != 0 or args.rope_at_load
     log(f"[bench] generating seeded inputs for {g}")
     t0 = time.perf_counter()
     q, k, v = make_qkv_bits(g, CONFIG_SEEDS[args.config])
@@ -203,7 +208,8 @@ def main():
                              rho=g.rho, radius=g.radius, guide_mode=g.guide_mode, T=g.T)
     fwd = lambda timer=None: api.forward(qt, kt, vt, g.H, g.W, g.w, g.H_lr, g.W_lr, rho=g.rho,
                                          theta=g.theta, out=out, workspace=ws, timer=timer,
-                                         radius=g.radius, guide_mode=g.guide_mode, T=g.T)
+                                         radius=g.radius, guide_mode=g.guide_mode, T=g.T,
+                                         rope_at_load=args.rope_at_load)
     for _ in range(args.warmup):
         fwd()
     torch.cuda.synchronize()
@@ -264,6 +270,7 @@ def main():
                    "rho": g.rho, "rope_theta": g.theta, "tokens": g.L,
                    "neighbourhood_radius": g.radius, "guide_mode": g.guide_mode,
                    "text_tokens": g.T,
+                   "k_rope": "at every K tile load" if args.rope_at_load else "once, in the K prep pass",
                    "parallelism": "single GPU"},
         "tokens_per_s": round(g.B * g.L / (ms_step * 1e-3), 1),
         "hi_tokens_per_s": round(g.B * g.N / (ms_step * 1e-3), 1),
@@ -271,7 +278,8 @@ def main():
         "unmasked_pairs_per_head": pairs,
         "frac_bf16_peak_step": round(tflops / PEAK_BF16_TFLOPS, 4),
         "stage_ms": {s: round(x, 4) for s, x in stage_avg.items()},
-        "roofline": {"kernel": "attn_fwd_kernel<128, 8, hi> (hi-res pass)", "bound": "mfma",
+        "roofline": {"kernel": "attn_fwd_kernel<128, 8, hi%s> (hi-res pass)"
+                               % (", K rotated at load" if args.rope_at_load else ""), "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},

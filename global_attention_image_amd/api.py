@@ -56,6 +56,9 @@ EXPORTS = {
     "uhla_forward_timed": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_int] * 9
                            + [ctypes.c_float, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t,
                               ctypes.c_void_p, ctypes.c_void_p]),
+    "uhla_forward_rope_at_load": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_int] * 9
+                                  + [ctypes.c_float, ctypes.c_float, ctypes.c_void_p,
+                                     ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
 }
 
 _lib = None
@@ -219,13 +222,15 @@ class Timer:
 
 
 def forward(q, k, v, H, W, w, H_lr, W_lr, rho=4, scale=0.0, theta=10000.0, out=None,
-            workspace=None, timer: Timer | None = None, radius=1, guide_mode=0, T=0):
+            workspace=None, timer: Timer | None = None, radius=1, guide_mode=0, T=0,
+            rope_at_load=False):
     """Hierarchical local attention forward on bf16 [B, T + H*W + H_lr*W_lr, heads, d] tensors.
 
     radius / guide_mode select the mask variants of uhla_forward_masked and T > 0 the text
     tokens of uhla_forward_text (rows 0..T-1); with the defaults uhla_forward is called.
-    A timer records per-stage durations (uhla_forward_timed / uhla_forward_masked_timed /
-    uhla_forward_text)."""
+    rope_at_load selects uhla_forward_rope_at_load (K rotated at every K tile load; default
+    mask only).  A timer records per-stage durations (uhla_forward_timed /
+    uhla_forward_masked_timed / uhla_forward_text / uhla_forward_rope_at_load)."""
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _require(t, n, torch.bfloat16)
@@ -244,6 +249,12 @@ def forward(q, k, v, H, W, w, H_lr, W_lr, rho=4, scale=0.0, theta=10000.0, out=N
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, W, w, H_lr, W_lr, rho, Hh, d,
             float(scale), float(theta))
     tail = (_ptr(workspace), workspace.numel(), _stream(q))
+    if rope_at_load:
+        if T or radius != 1 or guide_mode != 0:
+            raise ValueError("rope_at_load covers the default mask only")
+        st = lib.uhla_forward_rope_at_load(*args, *tail, timer.h if timer is not None else None)
+        _check(st, "uhla_forward_rope_at_load")
+        return out
     if T:
         st = lib.uhla_forward_text(*args[:5], int(T), *args[5:], int(radius), int(guide_mode),
                                    *tail, timer.h if timer is not None else None)

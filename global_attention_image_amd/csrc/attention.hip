@@ -378,7 +378,15 @@ constexpr int kPvAhead = 4;  // V fragment reads in flight ahead of the PV MFMAs
 // a load writes LDS bytes [16 l, 16 l + 16) above the wave's base), two iterations ahead of
 // their first use.  Each lane picks the global 16-byte chunk that belongs at its LDS slot
 // under the XOR swizzle, so the LDS layout is the one the fragment reads expect.
-template <int D, int NWAVES, bool HI, bool RECT, bool TEXT>
+//
+// ROTK (uhla_forward_rope_at_load): K arrives unrotated and every workgroup rotates each K
+// tile in LDS after it lands (RoPE fused into the K tile load), instead of K being rotated
+// once by the prep pass.  Each thread rotates its own DMA chunks of the tile: cos/sin of
+// the key's position times the chunk's four frequencies from the hardware sin/cos (angle
+// in revolutions, reduced with fract), the rotation in fp32, one rounding to bf16.  Tile
+// t+1 is rotated in iteration t before a mid-iteration barrier, ahead of its first reader
+// (wave B's QK^T_{t+1} in the second half of that iteration).
+template <int D, int NWAVES, bool HI, bool RECT, bool TEXT, bool ROTK = false>
 __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   constexpr int NT = NWAVES * 64;
   constexpr int TILE_BYTES = kKeyTile * D * 2;       // one K or V tile
@@ -556,6 +564,76 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   auto tile_mask = [&](int t) __attribute__((always_inline)) -> uint32_t {
     if (RECT && t >= n_local) return __builtin_amdgcn_readfirstlane(tile_mask_s[t]);
     return 0xffffu;
+  };
+
+  // ROTK: this thread's chunk slots of a K tile.  With 8 waves every thread's slots hold
+  // the same 16-byte dims chunk (rows 32 apart, same swizzle), so one set of four pair
+  // frequencies (in revolutions per position step) serves them all.
+  static_assert(!ROTK || (NWAVES == 8 && !RECT && !TEXT), "K rotation at load: 8 waves, default mask");
+  int rk_row[CPT];
+  float rk_fr[4];
+  int rk_axis = 0;
+  if constexpr (ROTK) {
+    int chunk = 0;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int slot = (i * NWAVES + wave) * 64 + lane;
+      rk_row[i] = slot / KCH;
+      chunk = (slot - rk_row[i] * KCH) ^ k_swizzle<D>(rk_row[i]);
+    }
+    const int pr = 4 * chunk;  // first of the chunk's four rotation pairs
+    rk_axis = pr / (D / 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int kq = pr + e - rk_axis * (D / 4);
+      rk_fr[e] = static_cast<float>(exp2(-(2.0 * kq / (D / 2)) * a.log2_theta) * 0.15915494309189535);
+    }
+  }
+  // Position (py, px) of key `kr` of tile t (hi tiles: window-first rows; global tiles:
+  // guide rows, padding rows at (0, 0)).
+  auto key_pos = [&](int t, int kr, int& py, int& px) __attribute__((always_inline)) {
+    py = 0;
+    px = 0;
+    if (HI && t < n_local) {
+      const int row = static_cast<int>(tile_off_s[t] / TILE_BYTES) * kKeyTile + kr;
+      const int r = window_first_to_raster(row, a.W, a.w, a.n_wx);
+      py = r / a.W;
+      px = r - py * a.W;
+    } else {
+      const int64_t srow = static_cast<int64_t>(t - n_local) * kKeyTile + kr;
+      if (srow < a.M) {
+        const int sr = static_cast<int>(srow), sy = sr / a.W_lr;
+        py = a.rho * sy;
+        px = a.rho * (sr - sy * a.W_lr);
+      }
+    }
+  };
+  // Rotate this thread's chunks of K tile t in the stage buffer kbuf (LDS, in place).
+  auto rotate_k = [&](char* kbuf, int t) __attribute__((always_inline)) {
+    if (!a.rope_on) return;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      int py, px;
+      key_pos(t, rk_row[i], py, px);
+      const float pos = static_cast<float>(rk_axis ? px : py);
+      const int slot = (i * NWAVES + wave) * 64 + lane;
+      uint4* cp = reinterpret_cast<uint4*>(kbuf + slot * 16);
+      const uint4 wv = *cp;
+      const uint32_t win[4] = {wv.x, wv.y, wv.z, wv.w};
+      uint32_t wout[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float rev = __builtin_amdgcn_fractf(pos * rk_fr[e]);
+        const float c = __builtin_amdgcn_cosf(rev), sn = __builtin_amdgcn_sinf(rev);
+        const float x = __uint_as_float(win[e] << 16), y = __uint_as_float(win[e] & 0xffff0000u);
+        wout[e] = pack_bf16x2(x * c - y * sn, x * sn + y * c);
+      }
+      *cp = make_uint4(wout[0], wout[1], wout[2], wout[3]);
+    }
+  };
+  // LDS writes done and visible to the workgroup (no wait on the in-flight tile copies)
+  auto lds_barrier = []() __attribute__((always_inline)) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
 
   // Query fragment (B operand of S^T = K Q^T): lane holds query ql, dims 16kk + 8g .. +8,
@@ -788,6 +866,10 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   if (n_tiles > 2) wait_vm_and_barrier<LOADS_PER_TILE>();
   else if (n_tiles > 1) wait_vm_and_barrier<LOADS_PER_TILE / 2>();
   else wait_vm_and_barrier<0>();
+  if constexpr (ROTK) {
+    rotate_k(stage0, 0);
+    lds_barrier();
+  }
   bf16x8 pa[4];  // wave A: P of the previous tile, consumed by the next iteration's PV
   // One copy of the loop per role (B = wave B), so that neither carries the other's state.
   auto run = [&]<bool B>() __attribute__((always_inline)) {
@@ -813,11 +895,19 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
         dma_slot(1);
         qk(cur);
         __builtin_amdgcn_s_setprio(0);
+        if constexpr (ROTK) {
+          if (t + 1 < n_tiles) rotate_k(stage((S + 1) & 3), t + 1);
+          lds_barrier();
+        }
         dma_slot(2);
         softmax(tile_valid(t), tile_mask(t), pa);
       } else {
         bf16x8 pf[4];
         softmax(tile_valid(t), tile_mask(t), pf);
+        if constexpr (ROTK) {
+          if (t + 1 < n_tiles) rotate_k(stage((S + 1) & 3), t + 1);
+          lds_barrier();
+        }
         __builtin_amdgcn_s_setprio(1);
         dma_slot(1);
         pv(cur + TILE_BYTES, pf);
@@ -918,19 +1008,22 @@ __global__ void text_combine_kernel(const float* __restrict__ o_part, const floa
   if (lse && d == 0) lse[bh * out_rows + x] = (mx + __log2f(l)) * 0.69314718055994531f;
 }
 
-template <int D, int NWAVES, bool HI, bool RECT, bool TEXT>
+template <int D, int NWAVES, bool HI, bool RECT, bool TEXT, bool ROTK = false>
 static void launch_attn(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, NWAVES, HI, RECT, TEXT>), dim3(a.total_blocks),
+  hipLaunchKernelGGL((attn_fwd_kernel<D, NWAVES, HI, RECT, TEXT, ROTK>), dim3(a.total_blocks),
                      dim3(NWAVES * 64), 0, s, a);
 }
 
-enum PassKind { kPassHi = 0, kPassHiRect = 1, kPassGuide = 2, kPassText = 3 };
+enum PassKind { kPassHi = 0, kPassHiRect = 1, kPassGuide = 2, kPassText = 3, kPassHiRotK = 4,
+                kPassGuideRotK = 5 };
 
 template <int D>
 static void dispatch_attn_d(int nwaves, PassKind kind, const AttnArgs& a, hipStream_t s) {
   switch (kind) {
     case kPassGuide: launch_attn<D, 8, false, false, false>(a, s); break;
     case kPassText: launch_attn<D, 8, false, false, true>(a, s); break;
+    case kPassHiRotK: launch_attn<D, 8, true, false, false, true>(a, s); break;
+    case kPassGuideRotK: launch_attn<D, 8, false, false, false, true>(a, s); break;
     case kPassHiRect:
       nwaves == 8 ? launch_attn<D, 8, true, true, false>(a, s) : launch_attn<D, 2, true, true, false>(a, s);
       break;
@@ -1010,9 +1103,11 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
                         int H, int W, int w, int H_lr, int W_lr, int rho, int heads, int D,
                         float scale, float theta, int radius, int guide_mode, void* workspace,
                         size_t workspace_bytes, void* stream, uhla_timer* timer,
-                        float* lse = nullptr) {
+                        float* lse = nullptr, bool rope_k_at_load = false) {
   int st = validate_forward(q, k, v, o, B, T, H, W, w, H_lr, W_lr, rho, heads, D, radius, guide_mode);
   if (st) return st;
+  if (rope_k_at_load && w * w < kMaxQuery)
+    return fail_unsupported("K rotation at tile load needs windows of at least 256 tokens");
   // a radius reaching past the grid is the whole grid
   radius = std::min(radius, H / w + W / w);
   const Geom g = make_geom(B, H, W, w, H_lr, W_lr, rho, heads, D, radius, guide_mode, T);
@@ -1066,11 +1161,11 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
     if (D == 128)
       hipLaunchKernelGGL(prep_k_kernel<128>, grid, dim3(kPrepThreads), 0, s, kb, ws.k_hi, ws.k_lr,
                          ws.k_gb, ws.cs, g.P, l2t, T, g.N, g.M, g.Mk, g.Mg, g.Mb, g.Mbg, g.Tk, W,
-                         w, g.n_wx, H_lr, W_lr, g.nbj, rho, heads, rope_on ? 1 : 0);
+                         w, g.n_wx, H_lr, W_lr, g.nbj, rho, heads, rope_on && !rope_k_at_load ? 1 : 0);
     else
       hipLaunchKernelGGL(prep_k_kernel<64>, grid, dim3(kPrepThreads), 0, s, kb, ws.k_hi, ws.k_lr,
                          ws.k_gb, ws.cs, g.P, l2t, T, g.N, g.M, g.Mk, g.Mg, g.Mb, g.Mbg, g.Tk, W,
-                         w, g.n_wx, H_lr, W_lr, g.nbj, rho, heads, rope_on ? 1 : 0);
+                         w, g.n_wx, H_lr, W_lr, g.nbj, rho, heads, rope_on && !rope_k_at_load ? 1 : 0);
     st = check_launch("prep_k_kernel");
     if (st) return st;
     const int64_t tiles = (g.N + g.Mg + g.Mbg) / kKeyTile;
@@ -1113,7 +1208,8 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
     h.q_valid = static_cast<int>(g.N);
     h.blocks_per_bh = static_cast<int>(g.N / qt);
     h.total_blocks = static_cast<int>(BH * h.blocks_per_bh);
-    UHLA_STEP(dispatch_attn(D, nwaves, rect ? kPassHiRect : kPassHi, h, s), "attn_fwd_kernel(hi)");
+    const PassKind kind = rope_k_at_load ? kPassHiRotK : rect ? kPassHiRect : kPassHi;
+    UHLA_STEP(dispatch_attn(D, nwaves, kind, h, s), "attn_fwd_kernel(hi)");
   }
   if (timer) timer_end(timer, UHLA_STAGE_ATTN_HI, s);
 
@@ -1126,7 +1222,7 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
     l.q_valid = static_cast<int>(g.M);
     l.blocks_per_bh = static_cast<int>(g.Mq / kMaxQuery);
     l.total_blocks = static_cast<int>(BH * l.blocks_per_bh);
-    UHLA_STEP(dispatch_attn(D, 8, kPassGuide, l, s), "attn_fwd_kernel(guide)");
+    UHLA_STEP(dispatch_attn(D, 8, rope_k_at_load ? kPassGuideRotK : kPassGuide, l, s), "attn_fwd_kernel(guide)");
   }
   if (timer) timer_end(timer, UHLA_STAGE_ATTN_LR, s);
 
@@ -1240,4 +1336,13 @@ extern "C" int uhla_forward_lse(const void* q, const void* k, const void* v, voi
   return uhla::forward_impl(q, k, v, o, B, T, H, W, w, H_lr, W_lr, rho, heads, head_dim, scale,
                             theta, radius, guide_mode, workspace, workspace_bytes, stream, nullptr,
                             lse);
+}
+
+extern "C" int uhla_forward_rope_at_load(const void* q, const void* k, const void* v, void* o,
+                                         int B, int H, int W, int w, int H_lr, int W_lr, int rho,
+                                         int heads, int head_dim, float scale, float theta,
+                                         void* workspace, size_t workspace_bytes, void* stream,
+                                         uhla_timer* timer) {
+  return uhla::forward_impl(q, k, v, o, B, 0, H, W, w, H_lr, W_lr, rho, heads, head_dim, scale,
+                            theta, 1, 0, workspace, workspace_bytes, stream, timer, nullptr, true);
 }

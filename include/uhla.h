@@ -109,10 +109,12 @@ size_t uhla_forward_workspace_bytes(int B, int H, int W, int w, int H_lr, int W_
  * with the mask of [UltraGen/ar §2.B] and [UltraGen/es §2]: a hi-res token attends to
  * every token of its own window and of the clipped 3x3 neighbourhood of windows, and to
  * all M guide tokens; a guide token attends to all guide tokens and to no hi-res token.
- * Steps: window-first permutation of the hi segment of Q, K, V fused with RoPE (guide rows rotated in place of permuting); block-sparse attention of
- * each window over its neighbour windows and the guide tokens (bf16 MFMA, fp32
- * accumulation and softmax) whose stores put each output row back at its raster
- * position (the inverse permutation, fused); guide-only attention.
+ * Steps: window-first permutation of the hi segment of K and V, fused with RoPE on K
+ * (guide rows rotated in place of permuting); block-sparse attention of each window over
+ * its neighbour windows and the guide tokens (bf16 MFMA, fp32 accumulation and softmax),
+ * which reads its query rows from Q in raster order and rotates them as it loads them,
+ * and whose stores put each output row back at its raster position (the inverse
+ * permutation, fused); guide-only attention.
  * scale <= 0 selects 1/sqrt(head_dim); theta <= 0 switches RoPE off; H_lr = W_lr = 0
  * means no guide tokens.  Deterministic: no atomics, fixed reduction order.
  * workspace: device memory of at least uhla_forward_workspace_bytes(...) bytes, 256-byte
@@ -234,7 +236,7 @@ const char* uhla_last_error_detail(void);
  */
 typedef enum {
   UHLA_STAGE_TABLES = 0,    /* RoPE cos/sin table */
-  UHLA_STAGE_PREP_HI = 1,   /* window-first permutation of Q, K, V fused with RoPE */
+  UHLA_STAGE_PREP_HI = 1,   /* window-first permutation of K, V fused with RoPE on K */
   UHLA_STAGE_PREP_LR = 2,   /* guide-token RoPE / V re-layout */
   UHLA_STAGE_ATTN_HI = 3,   /* hi-res block-sparse attention */
   UHLA_STAGE_ATTN_LR = 4,   /* guide-only attention */
@@ -257,6 +259,23 @@ int uhla_forward_masked_timed(const void* q, const void* k, const void* v, void*
                               int B, int H, int W, int w, int H_lr, int W_lr, int rho,
                               int heads, int head_dim, float scale, float theta,
                               int radius, int guide_mode,
+                              void* workspace, size_t workspace_bytes, void* stream,
+                              uhla_timer* timer);
+
+/*
+ * uhla_forward with RoPE on K fused into the K tile loads instead of applied once by the
+ * prep pass (the alternative design, kept to measure against): the prep pass only
+ * permutes K, and every attention workgroup rotates each K tile in LDS after it lands,
+ * in fp32 from the hardware sin/cos of the key's position (2D axial RoPE, guide positions
+ * scaled by rho, [UltraGen/ar §2.B]) with one rounding to bf16.  Same arguments,
+ * layouts, workspace (uhla_forward_workspace_bytes) and errors as uhla_forward, plus
+ * UHLA_ERR_UNSUPPORTED for windows of fewer than 256 tokens.  The result equals
+ * uhla_forward's up to the rounding of rotated K (not bit for bit).  timer may be NULL;
+ * otherwise stages are recorded as in uhla_forward_timed.
+ */
+int uhla_forward_rope_at_load(const void* q, const void* k, const void* v, void* o,
+                              int B, int H, int W, int w, int H_lr, int W_lr, int rho,
+                              int heads, int head_dim, float scale, float theta,
                               void* workspace, size_t workspace_bytes, void* stream,
                               uhla_timer* timer);
 
