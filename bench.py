@@ -59,7 +59,7 @@ def read_traffic():
     fields = {}
     for line in open(TRAFFIC_PROFILE):
         if ":" in line and line.strip().startswith("- "):
-            k, v = line.strip()[2:].split(":", 1)
+            k, v = line.strip()[2:].rsplit(":", 1)
             fields[k.strip()] = v.strip()
     if fields.get("attention.hip sha256[:16]") != source_hash(ATTN_SOURCE):
         return None
