@@ -11,13 +11,15 @@
 //   2. bwd_rows_kernel: per (b, h) buffers with hi rows window-first then guide rows,
 //      padded to 256: Qb = rope(Q) * s * log2 e (the forward's base-2 query), Kb = rope(K),
 //      Vb, dOb; bwd_aux_kernel: per 64-row tile, lse2 = lse * log2 e (pad rows +inf) and D;
-//      bwd_transpose_kernel: Q, K, dO as 64-row tiles transposed to [D][64];
 //   3. bwd_dq_kernel (query-outer, the forward's tile lists): per key tile S, dP (two
 //      32x32x16 MFMA chains from K and V tiles), dS, and dQ^T += K^T dS^T;
 //   4. bwd_dkv_kernel (key-outer, the transposed mask: a hi window's keys are seen by the
 //      queries of its neighbour windows, a guide key by every hi and guide query):
 //      per query tile S, dP, dS and dV^T += dO^T P, dK^T += Q^T dS.
-// Both write bf16 gradients in the caller's raster layout, undoing RoPE in the epilogue.
+// Tiles are row-major in LDS; the transposed operands (K^T, Q^T, dO^T) are read from the
+// same tiles with the gfx950 transposing LDS read, so each tile is copied once.  Both
+// kernels keep a 4-stage ring of tiles, copied three tiles ahead, and write bf16
+// gradients in the caller's raster layout, undoing RoPE in the epilogue.
 #include <algorithm>
 
 #include "tile_common.h"
@@ -30,6 +32,7 @@ constexpr int kBwdRowsPerBlock = 4;
 constexpr int kBwdThreads = 256;
 constexpr int kBwdMaxTiles = 1024;  // neighbour-window tiles per window (table in LDS)
 constexpr int kAuxBytes = 2 * kKeyTile * 4;  // per tile: 64 lse2 then 64 D values
+constexpr int kBwdStages = 4;                 // LDS ring of tiles; copies run 3 tiles ahead
 constexpr int kBwdWaves = 8;                  // guide-row workgroups: 8 waves x 32 rows
 constexpr int kBwdGuideRows = kBwdWaves * 32;
 
@@ -55,7 +58,6 @@ BwdGeom make_bwd_geom(int B, int H, int W, int w, int H_lr, int W_lr, int rho, i
 struct BwdWorkspace {
   double2* cs;
   bf16_t *qb, *kb, *vb, *dob;  // [B*heads][R][D]
-  bf16_t *qt, *kt, *dot;       // [B*heads][R/64][D][64]
   float* aux;                  // [B*heads][R/64][128]
   size_t bytes;
 };
@@ -71,13 +73,13 @@ BwdWorkspace carve_bwd(const BwdGeom& g, void* base) {
   const size_t rows = static_cast<size_t>(g.B) * g.heads * g.R;
   const size_t mat = rows * g.D * sizeof(bf16_t);
   const size_t o_cs = take(sizeof(double2) * g.P * (g.D / 4));
-  size_t o_m[7];
+  size_t o_m[4];
   for (auto& x : o_m) x = take(mat);
   const size_t o_aux = take(rows / kKeyTile * kAuxBytes);
   char* b = static_cast<char*>(base);
   ws.cs = reinterpret_cast<double2*>(b + o_cs);
-  bf16_t** mats[7] = {&ws.qb, &ws.kb, &ws.vb, &ws.dob, &ws.qt, &ws.kt, &ws.dot};
-  for (int i = 0; i < 7; ++i) *mats[i] = reinterpret_cast<bf16_t*>(b + o_m[i]);
+  bf16_t** mats[4] = {&ws.qb, &ws.kb, &ws.vb, &ws.dob};
+  for (int i = 0; i < 4; ++i) *mats[i] = reinterpret_cast<bf16_t*>(b + o_m[i]);
   ws.aux = reinterpret_cast<float*>(b + o_aux);
   ws.bytes = off;
   return ws;
@@ -227,38 +229,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_aux_kernel(
   t[kKeyTile + row % kKeyTile] = 0.0f;
 }
 
-// [bh][R][D] row-major -> [bh][R/64][D][64] tiles, rows within a tile in v_slot order.
-__global__ __launch_bounds__(kBwdThreads) void bwd_transpose_kernel(const bf16_t* __restrict__ src,
-                                                                    bf16_t* __restrict__ dst,
-                                                                    int64_t R, int D) {
-  __shared__ bf16_t tile[kKeyTile][128 + 2];
-  const int64_t bh = blockIdx.y, t = blockIdx.x;
-  const int cpr = D / 8;
-  const bf16_t* s = src + (bh * R + t * kKeyTile) * D;
-  for (int i = threadIdx.x; i < kKeyTile * cpr; i += kBwdThreads) {
-    const int r = i / cpr, j = i - r * cpr;
-    const uint4 x = *reinterpret_cast<const uint4*>(s + static_cast<int64_t>(r) * D + j * 8);
-    const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
-    for (int e = 0; e < 4; ++e) {
-      tile[r][j * 8 + 2 * e] = static_cast<bf16_t>(xw[e] & 0xffff);
-      tile[r][j * 8 + 2 * e + 1] = static_cast<bf16_t>(xw[e] >> 16);
-    }
-  }
-  __syncthreads();
-  bf16_t* d = dst + (bh * (R / kKeyTile) + t) * static_cast<int64_t>(D) * kKeyTile;
-  for (int i = threadIdx.x; i < D * (kKeyTile / 8); i += kBwdThreads) {
-    const int dd = i / (kKeyTile / 8), s8 = (i - dd * (kKeyTile / 8)) * 8;
-    uint32_t wv[4];
-    for (int e = 0; e < 4; ++e)
-      wv[e] = static_cast<uint32_t>(tile[v_slot(s8 + 2 * e)][dd]) |
-              (static_cast<uint32_t>(tile[v_slot(s8 + 2 * e + 1)][dd]) << 16);
-    *reinterpret_cast<uint4*>(d + static_cast<int64_t>(dd) * kKeyTile + s8) =
-        make_uint4(wv[0], wv[1], wv[2], wv[3]);
-  }
-}
-
 struct BwdArgs {
-  const bf16_t *qb, *kb, *vb, *dob, *qt, *kt, *dot;
+  const bf16_t *qb, *kb, *vb, *dob;
   const float* aux;
   const double2* cs;
   bf16_t* out0;  // dQ (dq kernel) or dK (dkv kernel), raster [B][N+M][heads][D]
@@ -319,20 +291,81 @@ __device__ int build_local_table(const BwdArgs& A, int r0, uint32_t* tab) {
   return n;
 }
 
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// Transposed MFMA operands from a row-major LDS tile (rows of D bf16, 16-byte chunks
+// XOR-swizzled by k_swizzle<D>(row)): A[i][k] = tile[row(k)][32 dt + i], i = lane % 32, for
+// the 16 rows of reduction step ks, in the order of an accumulator converted in place
+// (element jj of lane group g = lane / 32 is row 16 ks + 8 (jj / 4) + 4 g + jj % 4).  Two
+// ds_read_b64_tr_b16 per fragment: within each 16-lane group, lane i' receives element
+// i' % 4 of the 8 bytes addressed by lane 4 j + i' / 4 (j = 0..3), so the group's lanes
+// address 4 rows x 16 consecutive columns and each lane receives one column of those rows.
+// Lane l addresses row 16 ks + 8 b + R0 (R0 = 4 g + (l % 16) / 4) at byte 64 dt + C0
+// (C0 = 32 ((l / 16) % 2) + 8 (l % 4)).  Under the swizzle the byte offset splits into a
+// per-lane part and a compile-time part, so a fragment costs no address arithmetic:
+//   D = 128 (swizzle row % 16): 256 R0 + 16 ((C0 / 16) ^ (R0 % 4)) + C0 % 16 + 64 ((v ^ g))
+//     with v = dt ^ 2b, i.e. base +/- 64 g (sign by v's low bit) + 64 v + 2048 b + 4096 ks;
+//   D = 64 (swizzle (row / 2) % 8): 128 R0 + 16 ((C0 / 16) ^ (R0 / 2)) + C0 % 16
+//     + 64 (dt ^ b) + 1024 b + 2048 ks.
+template <int D>
+struct TrAddr {
+  int lo, hi;  // per-lane bases (D = 128: for v even / odd; D = 64: both the same)
+  __device__ __forceinline__ explicit TrAddr(int lane) {
+    const int g = lane >> 5, r0 = 4 * g + ((lane & 15) >> 2);
+    const int c0 = 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+    if (D == 128) {
+      const int base = 256 * r0 + (((c0 >> 4) ^ (r0 & 3)) << 4) + (c0 & 15);
+      lo = base + 64 * g;
+      hi = base - 64 * g;
+    } else {
+      lo = hi = 128 * r0 + (((c0 >> 4) ^ (r0 >> 1)) << 4) + (c0 & 15);
+    }
+  }
+  __device__ __forceinline__ bf16x8 frag(const char* tile, int ks, int dt) const {
+    bf16x8 out;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      int off;
+      if (D == 128) {
+        const int v = dt ^ (2 * b);
+        off = ((v & 1) ? hi : lo) + 64 * v + 2048 * b + 4096 * ks;
+      } else {
+        off = lo + 64 * (dt ^ b) + 1024 * b + 2048 * ks;
+      }
+      const bf16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (__attribute__((address_space(3))) bf16x4*)(tile + off));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[4 * b + e] = x[e];
+    }
+    return out;
+  }
+};
+
+// Wait until at most n tiles' copies (ops_per_tile DMA instructions each) of this wave are
+// in flight, then barrier: the older tiles are then complete and visible.
+template <int OPS>
+__device__ __forceinline__ void wait_tiles(int n) {
+  if (n >= 2) wait_vm_and_barrier<2 * OPS>();
+  else if (n == 1) wait_vm_and_barrier<OPS>();
+  else wait_vm_and_barrier<0>();
+}
+
 // ---------------------------------------------------------------- dQ (query-outer)
 //
 // Wave = 32 queries (lane & 31), as the forward: S^T = K Q^T and dP^T = V dO^T (A = K / V
 // tile rows from LDS, B = Q / dO held in registers), so each lane holds one query's
-// scores; dS^T converted to bf16 in place is the B operand of dQ^T += K~^T dS^T with
-// A = the transposed K tile.
+// scores; dS^T converted to bf16 in place is the B operand of dQ^T += K~^T dS^T with A read
+// transposed from the same K tile.
 template <int D, int NWAVES, bool HI>
 __global__ __launch_bounds__(NWAVES * 64) void bwd_dq_kernel(BwdArgs A) {
   constexpr int NT = NWAVES * 64;
   constexpr int TILE = kKeyTile * D * 2;
   constexpr int CPT = TILE / 16 / NT;
   constexpr int KCH = D / 8;
-  constexpr int STAGE = 3 * TILE;  // K, V, K^T
-  __shared__ __attribute__((aligned(16))) char ring[2 * STAGE];
+  constexpr int OPS = 2 * CPT;      // DMA instructions per wave per tile
+  constexpr int STAGE = 2 * TILE;   // K rows, V rows
+  constexpr int AH = kBwdStages - 1;
+  __shared__ __attribute__((aligned(16))) char ring[kBwdStages * STAGE];
   __shared__ uint32_t tab[HI ? kBwdMaxTiles : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -352,7 +385,6 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dq_kernel(BwdArgs A) {
   const int64_t mat = static_cast<int64_t>(bh) * A.R * D * 2;
   const char* kbase = reinterpret_cast<const char*>(A.kb) + mat;
   const char* vbase = reinterpret_cast<const char*>(A.vb) + mat;
-  const char* tbase = reinterpret_cast<const char*>(A.kt) + mat;
   auto tile_index = [&](int t) -> int {
     if (HI && t < n_local) return __builtin_amdgcn_readfirstlane(tab[t]);
     return n_hi_tiles + (t - n_local);
@@ -362,24 +394,21 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dq_kernel(BwdArgs A) {
     const int64_t rem = A.M - static_cast<int64_t>(t - n_local) * kKeyTile;
     return rem < kKeyTile ? static_cast<int>(rem) : kKeyTile;
   };
-  int k_src[CPT], t_src[CPT];
+  int k_src[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int slot = (i * NWAVES + wave) * 64 + lane;
     const int kr = slot / KCH, kp = slot - kr * KCH;
     k_src[i] = kr * (D * 2) + ((kp ^ k_swizzle<D>(kr)) << 4);
-    const int vr = slot >> 3, vp = slot & 7;
-    t_src[i] = vr * (kKeyTile * 2) + ((vp ^ v_swizzle(vr)) << 4);
   }
-  auto issue = [&](int t, int st) {
+  auto issue = [&](int t) {
     const int64_t off = static_cast<int64_t>(tile_index(t)) * TILE;
-    const uint32_t base = lds_addr(ring + st * STAGE);
+    const uint32_t base = lds_addr(ring + (t & (kBwdStages - 1)) * STAGE);
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const uint32_t o = __builtin_amdgcn_readfirstlane(base + (i * NWAVES + wave) * 64 * 16);
       dma_16b(kbase + off, k_src[i], o);
       dma_16b(vbase + off, k_src[i], o + TILE);
-      dma_16b(tbase + off, t_src[i], o + 2 * TILE);
     }
   };
 
@@ -405,23 +434,26 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dq_kernel(BwdArgs A) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[dt][r] = 0.0f;
 
+  // Row fragment for reduction step kk: rows ql (half 0) and 32 + ql (half 1).  The
+  // swizzled offset is row * 2D + (((2 kk + g) ^ swz(row)) << 4) = kfo ^ (kk << 5) (+ 64 D
+  // for half 1: swz(row) is the same for both halves); kfo is made opaque once per tile
+  // so that the XORs are recomputed there instead of held in registers across the loop.
+  const int kfo0 = ql * (D * 2) + ((g ^ k_swizzle<D>(ql)) << 4);
+  int kfo = kfo0;
   auto k_frag = [&](const char* tb, int kk, int half) -> bf16x8 {
-    const int row = half * 32 + ql;
-    return *reinterpret_cast<const bf16x8*>(tb + row * (D * 2) + (((2 * kk + g) ^ k_swizzle<D>(row)) << 4));
+    return *reinterpret_cast<const bf16x8*>(tb + (kfo ^ (kk << 5)) + half * 32 * (D * 2));
   };
-  auto t_frag = [&](const char* tb, int ks, int dt) -> bf16x8 {
-    const int vr = dt * 32 + ql;
-    return *reinterpret_cast<const bf16x8*>(tb + vr * (kKeyTile * 2) + (((2 * ks + g) ^ v_swizzle(vr)) << 4));
-  };
+  const TrAddr<D> tra(lane);
 
-  issue(0, 0);
-  wait_vm_and_barrier<0>();
+  for (int p = 0; p < AH; ++p)
+    if (p < n_tiles) issue(p);
+  wait_tiles<OPS>(std::min(n_tiles, AH) - 1);
   for (int t = 0; t < n_tiles; ++t) {
-    const int st = t & 1;
-    if (t + 1 < n_tiles) issue(t + 1, st ^ 1);
-    const char* kt_ = ring + st * STAGE;
+    if (t + AH < n_tiles) issue(t + AH);
+    kfo = kfo0;
+    asm volatile("" : "+v"(kfo));
+    const char* kt_ = ring + (t & (kBwdStages - 1)) * STAGE;
     const char* vt_ = kt_ + TILE;
-    const char* tt_ = kt_ + 2 * TILE;
     f32x16 s0 = {}, s1 = {}, p0 = {}, p1 = {};
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
@@ -444,8 +476,8 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dq_kernel(BwdArgs A) {
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t_frag(tt_, ks, dt), dsb[ks], acc[dt], 0, 0, 0);
-    wait_vm_and_barrier<0>();
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tra.frag(kt_, ks, dt), dsb[ks], acc[dt], 0, 0, 0);
+    wait_tiles<OPS>(std::min(n_tiles - 1, t + AH) - (t + 1));
   }
 
   // epilogue: dQ~ = scale * acc (lane: query ql, dims dt*32 + 8*(r/4) + 4g + r%4), unrotate
@@ -469,15 +501,19 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dq_kernel(BwdArgs A) {
 // Wave = 32 keys (lane & 31).  Per 64-query tile, in halves of 32 queries: S = Q K~^T and
 // dP = dO V^T (A = Q / dO tile rows from LDS, B = K / V held in registers), so a lane holds
 // one key's scores for 16 queries; P and dS converted to bf16 in place are the B operands
-// of dV^T += dO^T P and dK^T += Q^T dS with A = the transposed dO / Q tiles.
+// of dV^T += dO^T P and dK^T += Q^T dS with A read transposed from the same dO / Q tiles.
 template <int D, int NWAVES, bool HI>
 __global__ __launch_bounds__(NWAVES * 64) void bwd_dkv_kernel(BwdArgs A) {
   constexpr int NT = NWAVES * 64;
   constexpr int TILE = kKeyTile * D * 2;
   constexpr int CPT = TILE / 16 / NT;
   constexpr int KCH = D / 8;
-  constexpr int STAGE = 4 * TILE + kAuxBytes;  // Q, Q^T, dO, dO^T, aux
-  __shared__ __attribute__((aligned(16))) char ring[2 * STAGE];
+  constexpr int AUX_LANES = kAuxBytes / 16 / NWAVES;  // lanes per wave copying the aux block
+  constexpr int OPS = 2 * CPT + 1;                     // DMA instructions per wave per tile
+  constexpr int STAGE = 2 * TILE + kAuxBytes;          // Q rows, dO rows, lse2 / D
+  constexpr int AH = kBwdStages - 1;
+  static_assert(AUX_LANES >= 1 && AUX_LANES * 16 * NWAVES == kAuxBytes, "aux split");
+  __shared__ __attribute__((aligned(16))) char ring[kBwdStages * STAGE];
   __shared__ uint32_t tab[HI ? kBwdMaxTiles : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -497,37 +533,34 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dkv_kernel(BwdArgs A) {
   }
   const int64_t mat = static_cast<int64_t>(bh) * A.R * D * 2;
   const char* qbase = reinterpret_cast<const char*>(A.qb) + mat;
-  const char* qtbase = reinterpret_cast<const char*>(A.qt) + mat;
   const char* gbase = reinterpret_cast<const char*>(A.dob) + mat;
-  const char* gtbase = reinterpret_cast<const char*>(A.dot) + mat;
   const char* abase = reinterpret_cast<const char*>(A.aux) + static_cast<int64_t>(bh) * (A.R / kKeyTile) * kAuxBytes;
   auto tile_index = [&](int t) -> int {
     if (HI) return __builtin_amdgcn_readfirstlane(tab[t]);
     return t;
   };
-  int k_src[CPT], t_src[CPT];
+  int k_src[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int slot = (i * NWAVES + wave) * 64 + lane;
     const int kr = slot / KCH, kp = slot - kr * KCH;
     k_src[i] = kr * (D * 2) + ((kp ^ k_swizzle<D>(kr)) << 4);
-    const int vr = slot >> 3, vp = slot & 7;
-    t_src[i] = vr * (kKeyTile * 2) + ((vp ^ v_swizzle(vr)) << 4);
   }
-  auto issue = [&](int t, int st) {
+  // every wave issues the same number of copies per tile (its share of the aux block
+  // included), so the in-flight counts of wait_tiles hold for all waves
+  auto issue = [&](int t) {
     const int ti = tile_index(t);
     const int64_t off = static_cast<int64_t>(ti) * TILE;
-    const uint32_t base = lds_addr(ring + st * STAGE);
+    const uint32_t base = lds_addr(ring + (t & (kBwdStages - 1)) * STAGE);
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const uint32_t o = __builtin_amdgcn_readfirstlane(base + (i * NWAVES + wave) * 64 * 16);
       dma_16b(qbase + off, k_src[i], o);
-      dma_16b(qtbase + off, t_src[i], o + TILE);
-      dma_16b(gbase + off, k_src[i], o + 2 * TILE);
-      dma_16b(gtbase + off, t_src[i], o + 3 * TILE);
+      dma_16b(gbase + off, k_src[i], o + TILE);
     }
-    if (wave == 0 && lane < kAuxBytes / 16)
-      dma_16b(abase + static_cast<int64_t>(ti) * kAuxBytes, lane * 16, __builtin_amdgcn_readfirstlane(base + 4 * TILE));
+    if (lane < AUX_LANES)
+      dma_16b(abase + static_cast<int64_t>(ti) * kAuxBytes, (wave * AUX_LANES + lane) * 16,
+              __builtin_amdgcn_readfirstlane(base + 2 * TILE + wave * AUX_LANES * 16));
   };
 
   // key fragments (B operands): K~ and V rows of this lane's key
@@ -550,25 +583,27 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dkv_kernel(BwdArgs A) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dk[dt][r] = dv[dt][r] = 0.0f;
 
+  // Row fragment for reduction step kk: rows ql (half 0) and 32 + ql (half 1).  The
+  // swizzled offset is row * 2D + (((2 kk + g) ^ swz(row)) << 4) = kfo ^ (kk << 5) (+ 64 D
+  // for half 1: swz(row) is the same for both halves); kfo is made opaque once per tile
+  // so that the XORs are recomputed there instead of held in registers across the loop.
+  const int kfo0 = ql * (D * 2) + ((g ^ k_swizzle<D>(ql)) << 4);
+  int kfo = kfo0;
   auto k_frag = [&](const char* tb, int kk, int half) -> bf16x8 {
-    const int row = half * 32 + ql;
-    return *reinterpret_cast<const bf16x8*>(tb + row * (D * 2) + (((2 * kk + g) ^ k_swizzle<D>(row)) << 4));
+    return *reinterpret_cast<const bf16x8*>(tb + (kfo ^ (kk << 5)) + half * 32 * (D * 2));
   };
-  auto t_frag = [&](const char* tb, int ks, int dt) -> bf16x8 {
-    const int vr = dt * 32 + ql;
-    return *reinterpret_cast<const bf16x8*>(tb + vr * (kKeyTile * 2) + (((2 * ks + g) ^ v_swizzle(vr)) << 4));
-  };
+  const TrAddr<D> tra(lane);
 
-  issue(0, 0);
-  wait_vm_and_barrier<0>();
+  for (int p = 0; p < AH; ++p)
+    if (p < n_tiles) issue(p);
+  wait_tiles<OPS>(std::min(n_tiles, AH) - 1);
   for (int t = 0; t < n_tiles; ++t) {
-    const int st = t & 1;
-    if (t + 1 < n_tiles) issue(t + 1, st ^ 1);
-    const char* qt_ = ring + st * STAGE;
-    const char* qtt = qt_ + TILE;
-    const char* gt_ = qt_ + 2 * TILE;
-    const char* gtt = qt_ + 3 * TILE;
-    const float* aux = reinterpret_cast<const float*>(qt_ + 4 * TILE);
+    if (t + AH < n_tiles) issue(t + AH);
+    kfo = kfo0;
+    asm volatile("" : "+v"(kfo));
+    const char* qt_ = ring + (t & (kBwdStages - 1)) * STAGE;
+    const char* gt_ = qt_ + TILE;
+    const float* aux = reinterpret_cast<const float*>(qt_ + 2 * TILE);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       f32x16 s = {}, p = {};
@@ -596,11 +631,11 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dkv_kernel(BwdArgs A) {
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
-          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t_frag(gtt, 2 * half + j, dt), pb[j], dv[dt], 0, 0, 0);
-          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t_frag(qtt, 2 * half + j, dt), db[j], dk[dt], 0, 0, 0);
+          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tra.frag(gt_, 2 * half + j, dt), pb[j], dv[dt], 0, 0, 0);
+          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tra.frag(qt_, 2 * half + j, dt), db[j], dk[dt], 0, 0, 0);
         }
     }
-    wait_vm_and_barrier<0>();
+    wait_tiles<OPS>(std::min(n_tiles - 1, t + AH) - (t + 1));
   }
 
   // epilogue: dK~ = ln2 * dk (Q carried scale * log2 e), unrotated; dV = dv
@@ -753,17 +788,10 @@ extern "C" int uhla_backward(const void* q, const void* k, const void* v, const 
                                   dim3(kBwdThreads), 0, s, static_cast<const bf16_t*>(o), gp, lse,
                                   ws.aux, g.N, g.M, g.R, W, w, n_wx, heads, D, BH),
                "bwd_aux_kernel");
-    const dim3 tg(static_cast<unsigned>(g.R / kKeyTile), static_cast<unsigned>(BH));
-    UHLA_BSTEP(hipLaunchKernelGGL(bwd_transpose_kernel, tg, dim3(kBwdThreads), 0, s, ws.qb, ws.qt, g.R, D),
-               "bwd_transpose_kernel(q)");
-    UHLA_BSTEP(hipLaunchKernelGGL(bwd_transpose_kernel, tg, dim3(kBwdThreads), 0, s, ws.kb, ws.kt, g.R, D),
-               "bwd_transpose_kernel(k)");
-    UHLA_BSTEP(hipLaunchKernelGGL(bwd_transpose_kernel, tg, dim3(kBwdThreads), 0, s, ws.dob, ws.dot, g.R, D),
-               "bwd_transpose_kernel(do)");
   }
 
   BwdArgs a{};
-  a.qb = ws.qb; a.kb = ws.kb; a.vb = ws.vb; a.dob = ws.dob; a.qt = ws.qt; a.kt = ws.kt; a.dot = ws.dot;
+  a.qb = ws.qb; a.kb = ws.kb; a.vb = ws.vb; a.dob = ws.dob;
   a.aux = ws.aux; a.cs = ws.cs;
   a.N = g.N; a.M = g.M; a.R = g.R;
   a.heads = heads; a.w2 = w * w; a.W = W; a.w = w; a.n_wx = n_wx; a.n_wy = H / w;
