@@ -250,3 +250,84 @@ def test_workspace_bytes_invalid(lib):
     assert lib.uhla_forward_workspace_bytes(1, 30, 32, 8, 8, 8, 2, 64) == 0
     assert lib.uhla_forward_workspace_bytes(1, 32, 32, 8, 8, 0, 2, 64) == 0
     assert lib.uhla_forward_workspace_bytes(1, 32, 32, 8, 8, 8, 2, 96) == 0
+
+
+def lse_args(lse=ctypes.c_void_p(0x60000000), **kw):
+    a = fwd_args(**kw)
+    # uhla_forward_lse(q, k, v, o, lse, B, T, H, W, w, H_lr, W_lr, rho, heads, d, scale, theta,
+    #                  radius, guide_mode, ws, bytes, stream)
+    return (*a[:4], lse, a[4], 0, *a[5:15], 1, 0, *a[15:])
+
+
+def test_forward_lse_rejects(lib):
+    f = lib.uhla_forward_lse
+    assert f(*lse_args(lse=NULL)) == api.UHLA_ERR_ARG
+    assert f(*lse_args(lse=ctypes.c_void_p(0x60000002))) == api.UHLA_ERR_ARG  # misaligned
+    assert f(*lse_args(lse=ctypes.c_void_p(0x40000000 + 64))) == api.UHLA_ERR_ARG  # inside o
+    assert f(*lse_args(q=NULL)) == api.UHLA_ERR_ARG
+    assert f(*lse_args(d=96)) == api.UHLA_ERR_UNSUPPORTED
+
+
+def test_forward_rope_at_load_rejects(lib):
+    a = fwd_args()
+    f = lib.uhla_forward_rope_at_load
+    assert f(*a[:17], NULL, NULL) == api.UHLA_ERR_UNSUPPORTED  # w = 8: windows of 64 tokens
+    assert f(*fwd_args(q=NULL)[:17], NULL, NULL) == api.UHLA_ERR_ARG
+    assert f(*fwd_args(w=16, wsb=1000)[:17], NULL, NULL) == api.UHLA_ERR_WORKSPACE
+
+
+def bwd_args(**kw):
+    a = dict(q=P, k=P2, v=P3, o=P4, do=ctypes.c_void_p(0x70000000),
+             lse=ctypes.c_void_p(0x80000000), dq=ctypes.c_void_p(0x90000000),
+             dk=ctypes.c_void_p(0xa0000000), dv=ctypes.c_void_p(0xb0000000), B=1, H=32, W=32,
+             w=8, H_lr=8, W_lr=8, rho=4, heads=2, d=64, scale=0.0, theta=10000.0, radius=1,
+             ws=ctypes.c_void_p(0x50000000), wsb=1 << 40)
+    a.update(kw)
+    return tuple(a[n] for n in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "B", "H", "W",
+                                "w", "H_lr", "W_lr", "rho", "heads", "d", "scale", "theta",
+                                "radius", "ws", "wsb")) + (NULL,)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=NULL), api.UHLA_ERR_ARG),
+    (dict(lse=NULL), api.UHLA_ERR_ARG),
+    (dict(dv=NULL), api.UHLA_ERR_ARG),
+    (dict(dq=ctypes.c_void_p(0x90000008)), api.UHLA_ERR_ARG),  # not 16-byte aligned
+    (dict(B=0), api.UHLA_ERR_ARG),
+    (dict(w=12), api.UHLA_ERR_ARG),
+    (dict(W_lr=0), api.UHLA_ERR_ARG),
+    (dict(rho=0), api.UHLA_ERR_ARG),
+    (dict(radius=-1), api.UHLA_ERR_ARG),
+    (dict(d=96), api.UHLA_ERR_UNSUPPORTED),
+    (dict(H=36, W=36, w=4), api.UHLA_ERR_UNSUPPORTED),
+    (dict(H=384, W=384, w=96, H_lr=0, W_lr=0), api.UHLA_ERR_UNSUPPORTED),
+    (dict(ws=NULL), api.UHLA_ERR_WORKSPACE),
+    (dict(wsb=1000), api.UHLA_ERR_WORKSPACE),
+    (dict(ws=ctypes.c_void_p(0x50000010)), api.UHLA_ERR_ARG),  # misaligned workspace
+    (dict(dq=P), api.UHLA_ERR_ARG),  # gradient aliases q
+    (dict(dk=ctypes.c_void_p(0x90000000 + 4096)), api.UHLA_ERR_ARG),  # overlaps dq
+    (dict(dv=ctypes.c_void_p(0x80000000)), api.UHLA_ERR_ARG),  # overlaps lse
+    (dict(dq=ctypes.c_void_p(0x50000000 + 4096)), api.UHLA_ERR_ARG),  # inside the workspace
+])
+def test_backward_rejects(lib, kw, status):
+    assert lib.uhla_backward(*bwd_args(**kw)) == status
+
+
+def expected_backward_workspace(B, H, W, w, H_lr, W_lr, heads, d):
+    """Independent restatement: cos/sin table, then Q, K, V, dO rows per (b, h) with hi rows
+    then guide rows padded to 256 (bf16), then per 64-row tile 64 lse2 and 64 row dots (fp32);
+    regions 256-byte aligned."""
+    al = lambda x: (x + 255) // 256 * 256
+    N, M = H * W, H_lr * W_lr
+    R = N + (M + 255) // 256 * 256
+    bh = B * heads
+    return al(16 * max(H, W) * (d // 4)) + 4 * al(bh * R * d * 2) + al(bh * R // 64 * 512)
+
+
+@pytest.mark.parametrize("g", GEOMS)
+def test_backward_workspace_bytes(lib, g):
+    B, H, W, w, H_lr, W_lr, heads, d = g
+    got = lib.uhla_backward_workspace_bytes(B, H, W, w, H_lr, W_lr, 4, heads, d, 1)
+    assert got == expected_backward_workspace(*g)
+    assert lib.uhla_backward_workspace_bytes(B, H, W, w, H_lr, W_lr, 4, heads, d, -1) == 0
+    assert lib.uhla_backward_workspace_bytes(B, H, W, w, H_lr, W_lr, 4, heads, 96, 1) == 0
