@@ -346,7 +346,7 @@ def backward_rows(q, k, v, do, geom, b: int, h: int, q_rows, k_rows, block: int 
     # queries that see any requested key
     need = np.zeros(L, dtype=bool)
     need[q_rows] = True
-    for s0 in range(0, L, block):
+    for s0 in range(0, L, block) if len(k_rows) else ():
         blk = np.arange(s0, min(L, s0 + block))
         need[blk] |= mask_rows(geom, blk)[:, k_rows].any(axis=1)
     rows = np.nonzero(need)[0]

@@ -7,9 +7,10 @@ x max |ref| and mean-abs error <= 5e-3 x mean |ref|.  The kernels round Q (rotat
 scaled), P and dS to bf16 for the MFMAs (relative 2^-9 each) and store bf16 (2^-9), and the
 sums they enter have random signs, so the errors stay a small multiple of 2^-9 of the
 gradient's scale.
-* every row / every key at small sizes: both head dims, window sizes 8 and 16, radius
-  0 / 1 / 2, ragged guide grids, no guide tokens, RoPE off;
+* every row / every key at small sizes: both head dims, window sizes 8, 16 and 32, radius
+  0 / 1 / 2, ragged guide grids, guide positions past the hi grid, no guide tokens, RoPE off;
 * sampled query and key rows at the 2K workload (oracle rows of the backward);
+* the 8K workload: sampled dQ rows against the oracle and the dV sum rule over all keys;
 * determinism.
 """
 import numpy as np
@@ -52,6 +53,11 @@ CASES = {
     "d128_no_guide": Geometry(B=1, heads=2, head_dim=128, H=48, W=48, w=16, H_lr=0, W_lr=0),
     "d128_rope_off": Geometry(B=1, heads=1, head_dim=128, H=32, W=48, w=16, H_lr=8, W_lr=12,
                               theta=0.0),
+    "d128_w32": Geometry(B=1, heads=1, head_dim=128, H=64, W=96, w=32, H_lr=16, W_lr=24),
+    # guide positions (4i, 4j) up to (40, 32) lie past the 32x32 hi grid: RoPE factors beyond
+    # the cos/sin table are evaluated directly
+    "d64_guide_beyond_grid": Geometry(B=2, heads=1, head_dim=64, H=32, W=32, w=16, H_lr=11,
+                                      W_lr=9),
 }
 
 
@@ -91,6 +97,32 @@ def test_backward_sampled_rows_2k():
         check_rel(bf16_f64(dq[0, q_rows, h]), rq, f"2k dq h{h}")
         check_rel(bf16_f64(dk[0, k_rows, h]), rk, f"2k dk h{h}")
         check_rel(bf16_f64(dv[0, k_rows, h]), rv, f"2k dv h{h}")
+
+
+def test_backward_8k_sampled_dq_and_dv_sum():
+    """The 8K workload in the launch configuration bench.py --backward times: dQ of sampled
+    rows (corner / edge / interior windows, guide rows) against the oracle's rows, and the
+    sum rule at full size: every row of P sums to 1, so the sum of dV over all keys equals
+    the sum of dO over all queries (per batch, head and dim; bf16 storage of 278 528 dV rows
+    and fp32 accumulation keep the difference far below 1e-3 of the sum of |dO|)."""
+    from gpu_util import config_inputs
+    from test_gpu_forward import stratified_rows
+    g, q, k, v = config_inputs("8k")
+    say("backward 8k: sampled dQ rows, dV sum rule")
+    do = make_qkv_bits(g, 77)[0]
+    _, dq, _, dv = run_fwd_bwd(g, q, k, v, do)
+    rng = np.random.default_rng(8)
+    for h in (0, 23):
+        qf, kf, vf, gf = (bf16_f64(x[:, :, h:h + 1, :]) for x in (q, k, v, do))
+        rows = stratified_rows(g, rng, 45, 8)
+        rq, _, _ = orc.backward_rows(qf, kf, vf, gf, g, 0, 0, rows, [])
+        check_rel(bf16_f64(dq[0, rows, h]), rq, f"8k dq h{h} ({len(rows)} rows)")
+    for h in range(g.heads):
+        sum_dv = bf16_f64(dv[:, :, h, :]).sum(axis=1)   # [B, D]
+        gh = bf16_f64(do[:, :, h, :])
+        err = np.abs(sum_dv - gh.sum(axis=1)) / np.abs(gh).sum(axis=1)
+        assert err.max() <= 1e-3, (h, err.max())
+    say(f"8k dV sum rule holds for all {g.heads} heads (last max relative difference {err.max():.3e})")
 
 
 def test_backward_deterministic():
