@@ -42,9 +42,9 @@ EXPORTS = {
     "uhla_forward_lse": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int] * 10
                          + [ctypes.c_float, ctypes.c_float, ctypes.c_int, ctypes.c_int,
                             ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
-    "uhla_backward_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 10),
-    "uhla_backward": (ctypes.c_int, [ctypes.c_void_p] * 9 + [ctypes.c_int] * 9
-                      + [ctypes.c_float, ctypes.c_float, ctypes.c_int,
+    "uhla_backward_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 11),
+    "uhla_backward": (ctypes.c_int, [ctypes.c_void_p] * 9 + [ctypes.c_int] * 10
+                      + [ctypes.c_float, ctypes.c_float, ctypes.c_int, ctypes.c_int,
                          ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "uhla_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "uhla_last_error_detail": (ctypes.c_char_p, []),
@@ -300,27 +300,33 @@ def forward_lse(q, k, v, H, W, w, H_lr, W_lr, rho=4, scale=0.0, theta=10000.0, r
     return out, lse
 
 
+def backward_workspace_bytes(B, T, H, W, w, H_lr, W_lr, rho, heads, head_dim, radius) -> int:
+    return int(load().uhla_backward_workspace_bytes(B, T, H, W, w, H_lr, W_lr, rho, heads,
+                                                    head_dim, radius))
+
+
 def backward(q, k, v, o, do, lse, H, W, w, H_lr, W_lr, rho=4, scale=0.0, theta=10000.0,
-             radius=1, dq=None, dk=None, dv=None, workspace=None):
-    """uhla_backward: (dq, dk, dv) bf16 for the output gradient do (guide mode 0, no text)."""
+             radius=1, T=0, dq=None, dk=None, dv=None, workspace=None):
+    """uhla_backward: (dq, dk, dv) bf16 for the output gradient do (guide mode 0; T text
+    tokens in rows 0..T-1)."""
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
         _require(t, n, torch.bfloat16)
     _require(lse, "lse", torch.float32)
     B, L, Hh, d = q.shape
-    if L != H * W + H_lr * W_lr:
+    if L != T + H * W + H_lr * W_lr:
         raise ValueError("token count does not match the grids")
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
     if workspace is None:
-        n = int(load().uhla_backward_workspace_bytes(B, H, W, w, H_lr, W_lr, rho, Hh, d, radius))
+        n = backward_workspace_bytes(B, T, H, W, w, H_lr, W_lr, rho, Hh, d, radius)
         if n == 0:
             raise ValueError("invalid geometry")
         workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
     st = load().uhla_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
-                              _ptr(dk), _ptr(dv), B, H, W, w, H_lr, W_lr, rho, Hh, d, float(scale),
-                              float(theta), int(radius), _ptr(workspace), workspace.numel(),
-                              _stream(q))
+                              _ptr(dk), _ptr(dv), B, int(T), H, W, w, H_lr, W_lr, rho, Hh, d,
+                              float(scale), float(theta), int(radius), 0, _ptr(workspace),
+                              workspace.numel(), _stream(q))
     _check(st, "uhla_backward")
     return dq, dk, dv

@@ -1,6 +1,7 @@
 // Hierarchical local attention backward on gfx950: dQ, dK, dV for the mask of uhla_forward
 // with any neighbourhood radius (all guide tokens visible to hi-res queries, guide queries
-// seeing guide keys only), from Q, K, V, O, dO and the forward's per-row log-sum-exp.
+// seeing guide keys only) and optional text tokens (text queries see every key, every query
+// sees the text keys), from Q, K, V, O, dO and the forward's per-row log-sum-exp.
 //
 // Math per (batch, head), rotated Q~ K~, scale s: P = exp(s Q~ K~^T - lse) on the allowed
 // pairs, dV = P^T dO, dP = dO V^T, dS = P (dP - D) with D = rowsum(dO O), dQ~ = s dS K~,
@@ -8,8 +9,8 @@
 //
 // Pipeline (caller's stream, no allocation):
 //   1. fp64 cos/sin table (as the forward);
-//   2. bwd_rows_kernel: per (b, h) buffers with hi rows window-first then guide rows,
-//      padded to 256: Qb = rope(Q) * s * log2 e (the forward's base-2 query), Kb = rope(K),
+//   2. bwd_rows_kernel: per (b, h) buffers with hi rows window-first, then guide rows and
+//      then text rows, each of the last two padded to 256: Qb = rope(Q) * s * log2 e (the forward's base-2 query), Kb = rope(K),
 //      Vb, dOb; bwd_aux_kernel: per 64-row tile, lse2 = lse * log2 e (pad rows +inf) and D;
 //   3. bwd_dq_kernel (query-outer, the forward's tile lists): per key tile S, dP (two
 //      32x32x16 MFMA chains from K and V tiles), dS, and dQ^T += K^T dS^T;
@@ -38,18 +39,21 @@ constexpr int kBwdGuideRows = kBwdWaves * 32;
 
 struct BwdGeom {
   int B, H, W, w, H_lr, W_lr, rho, heads, D, radius;
-  int64_t N, M, R;  // R: rows per (b, h) = N + guide rows padded to kBwdGuideRows
+  int64_t T, N, M, Mp, Tp, R;  // R: rows per (b, h) = N + Mp + Tp (guide / text rows padded)
   int n_wx, n_wy, P;
 };
 
-BwdGeom make_bwd_geom(int B, int H, int W, int w, int H_lr, int W_lr, int rho, int heads, int D,
-                      int radius) {
+BwdGeom make_bwd_geom(int B, int64_t T, int H, int W, int w, int H_lr, int W_lr, int rho,
+                      int heads, int D, int radius) {
   BwdGeom g;
   g.B = B; g.H = H; g.W = W; g.w = w; g.H_lr = H_lr; g.W_lr = W_lr; g.rho = rho;
   g.heads = heads; g.D = D; g.radius = radius;
+  g.T = T;
   g.N = static_cast<int64_t>(H) * W;
   g.M = static_cast<int64_t>(H_lr) * W_lr;
-  g.R = g.N + (g.M + kBwdGuideRows - 1) / kBwdGuideRows * kBwdGuideRows;
+  g.Mp = (g.M + kBwdGuideRows - 1) / kBwdGuideRows * kBwdGuideRows;
+  g.Tp = (T + kBwdGuideRows - 1) / kBwdGuideRows * kBwdGuideRows;
+  g.R = g.N + g.Mp + g.Tp;
   g.n_wx = W / w; g.n_wy = H / w;
   g.P = H > W ? H : W;
   return g;
@@ -95,25 +99,29 @@ __global__ void bwd_cos_sin_kernel(double2* cs, int P, int D, double log2_theta)
   cs[i] = rope_cos_sin(pos, k, D / 2, log2_theta);
 }
 
-// Raster source row and RoPE position of buffer row `row` (hi rows window-first, then guide
-// rows); -1 for padding rows.
-__device__ __forceinline__ int64_t bwd_source(int64_t row, int64_t N, int64_t M, int W, int w,
-                                              int n_wx, int W_lr, int rho, int& py, int& px) {
+// Token (row of the caller's [text | hi | guide] tensors) and RoPE position of buffer row
+// `row`: hi rows window-first, then guide rows (padded to Mp), then text rows (padded, at
+// position (0, 0)); -1 for padding rows.
+__device__ __forceinline__ int64_t bwd_source(int64_t row, int64_t T, int64_t N, int64_t M,
+                                              int64_t Mp, int W, int w, int n_wx, int W_lr,
+                                              int rho, int& py, int& px) {
+  py = px = 0;
   if (row < N) {
     const int r = window_first_to_raster(static_cast<int>(row), W, w, n_wx);
     py = r / W;
     px = r - py * W;
-    return r;
+    return T + r;
   }
-  const int64_t s = row - N;
-  if (s >= M) {
-    py = px = 0;
-    return -1;
+  if (row < N + Mp) {
+    const int64_t s = row - N;
+    if (s >= M) return -1;
+    const int sy = static_cast<int>(s / W_lr);
+    py = rho * sy;
+    px = rho * static_cast<int>(s - static_cast<int64_t>(sy) * W_lr);
+    return T + N + s;
   }
-  const int sy = static_cast<int>(s / W_lr);
-  py = rho * sy;
-  px = rho * static_cast<int>(s - static_cast<int64_t>(sy) * W_lr);
-  return N + s;
+  const int64_t x = row - N - Mp;
+  return x < T ? x : -1;
 }
 
 // Q, K, V, dO rows -> per (b, h) buffers [R][D]: Q rotated and scaled by q_scale in fp64
@@ -123,18 +131,18 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_rows_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dout, bf16_t* __restrict__ qb, bf16_t* __restrict__ kb,
     bf16_t* __restrict__ vb, bf16_t* __restrict__ dob, const double2* __restrict__ cs, int P,
-    double log2_theta, int64_t N, int64_t M, int64_t R, int W, int w, int n_wx, int W_lr,
-    int rho, int heads, int rope_on, double q_scale) {
+    double log2_theta, int64_t T, int64_t N, int64_t M, int64_t Mp, int64_t R, int W, int w,
+    int n_wx, int W_lr, int rho, int heads, int rope_on, double q_scale) {
   constexpr int CPH = D / 8, QUARTER = D / 4;
   __shared__ int64_t src_s[kBwdRowsPerBlock];
   __shared__ int pos_s[kBwdRowsPerBlock][2];
   __shared__ double2 cs_s[kBwdRowsPerBlock][2][QUARTER];
-  const int64_t L = N + M, b = blockIdx.y;
+  const int64_t L = T + N + M, b = blockIdx.y;
   const int tid = threadIdx.x;
   if (tid < kBwdRowsPerBlock) {
     int py, px;
-    src_s[tid] = bwd_source(static_cast<int64_t>(blockIdx.x) * kBwdRowsPerBlock + tid, N, M, W, w,
-                            n_wx, W_lr, rho, py, px);
+    src_s[tid] = bwd_source(static_cast<int64_t>(blockIdx.x) * kBwdRowsPerBlock + tid, T, N, M, Mp,
+                            W, w, n_wx, W_lr, rho, py, px);
     pos_s[tid][0] = py;
     pos_s[tid][1] = px;
   }
@@ -188,11 +196,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_rows_kernel(
 // lanes; threads past the B * L * heads rows fill the padding rows.
 __global__ __launch_bounds__(kBwdThreads) void bwd_aux_kernel(
     const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout, const float* __restrict__ lse,
-    float* __restrict__ aux, int64_t N, int64_t M, int64_t R, int W, int w, int n_wx, int heads,
-    int D, int64_t bh_total) {
+    float* __restrict__ aux, int64_t T, int64_t N, int64_t M, int64_t Mp, int64_t R, int W,
+    int w, int n_wx, int heads, int D, int64_t bh_total) {
   const int cpr = D / 8;  // 16-byte chunks per row: 16 or 8, a power of two dividing 64
+  const int64_t L = T + N + M;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t rows = bh_total * (N + M);  // (b, token, head) rows, raster memory order
+  const int64_t rows = bh_total * L;  // (b, token, head) rows, raster memory order
   const int64_t gi = i / cpr;
   const int c = static_cast<int>(i - gi * cpr);
   if (gi < rows) {
@@ -206,24 +215,31 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_aux_kernel(
             __uint_as_float(aw[e] & 0xffff0000u) * __uint_as_float(gw[e] & 0xffff0000u);
     for (int m = 1; m < cpr; m <<= 1) dd += __shfl_xor(dd, m, 64);
     if (c) return;
-    const int64_t bt = gi / heads, h = gi - bt * heads;  // bt = b * (N + M) + token
-    const int64_t b = bt / (N + M), src = bt - b * (N + M);
-    int64_t row = src;
-    if (src < N) {  // raster -> window-first
-      const int y = static_cast<int>(src / W), x = static_cast<int>(src - static_cast<int64_t>(y) * W);
+    const int64_t bt = gi / heads, h = gi - bt * heads;  // bt = b * L + token
+    const int64_t b = bt / L, src = bt - b * L;
+    int64_t row;
+    if (src < T) {
+      row = N + Mp + src;
+    } else if (src < T + N) {  // raster -> window-first
+      const int64_t r = src - T;
+      const int y = static_cast<int>(r / W), x = static_cast<int>(r - static_cast<int64_t>(y) * W);
       const int wy = y / w, wx = x / w;
       row = (static_cast<int64_t>(wy) * n_wx + wx) * w * w + (y - wy * w) * w + (x - wx * w);
+    } else {
+      row = src - T;  // guide s = src - T - N sits at buffer row N + s
     }
     const int64_t bh = b * heads + h;
     float* t = aux + (bh * (R / kKeyTile) + row / kKeyTile) * (2 * kKeyTile);
-    t[row % kKeyTile] = lse[bh * (N + M) + src] * 1.4426950408889634f;
+    t[row % kKeyTile] = lse[bh * L + src] * 1.4426950408889634f;
     t[kKeyTile + row % kKeyTile] = dd;
     return;
   }
-  const int64_t pad = R - N - M;
+  // padding rows: guide rows [N + M, N + Mp) and text rows [N + Mp + T, R)
+  const int64_t pad_g = Mp - M, pad = pad_g + (R - N - Mp - T);
   const int64_t j = i - rows * cpr;
   if (j >= bh_total * pad) return;
-  const int64_t bh = j / pad, row = N + M + (j - bh * pad);
+  const int64_t bh = j / pad, jj = j - bh * pad;
+  const int64_t row = jj < pad_g ? N + M + jj : N + Mp + T + (jj - pad_g);
   float* t = aux + (bh * (R / kKeyTile) + row / kKeyTile) * (2 * kKeyTile);
   t[row % kKeyTile] = INFINITY;
   t[kKeyTile + row % kKeyTile] = 0.0f;
@@ -233,9 +249,9 @@ struct BwdArgs {
   const bf16_t *qb, *kb, *vb, *dob;
   const float* aux;
   const double2* cs;
-  bf16_t* out0;  // dQ (dq kernel) or dK (dkv kernel), raster [B][N+M][heads][D]
+  bf16_t* out0;  // dQ (dq kernel) or dK (dkv kernel), the caller's [B][L][heads][D]
   bf16_t* out1;  // dV (dkv kernel)
-  int64_t N, M, R;
+  int64_t T, N, M, Mp, R, L;  // L = T + N + M tokens per batch
   int heads, w2, W, w, n_wx, n_wy, radius, rho, W_lr, P;
   int rope_on;
   double log2_theta;
@@ -255,19 +271,68 @@ __device__ __forceinline__ uint32_t unrotate_pair(float a, float b, int pr, int 
   return pack_bf16x2(a * c + b * s, b * c - a * s);
 }
 
-// Raster row and position of buffer row `row` (hi rows window-first, then guide rows).
+// Token (row of the caller's tensors) and position of valid buffer row `row`.
 __device__ __forceinline__ int64_t raster_row(int64_t row, const BwdArgs& A, int& py, int& px) {
-  if (row < A.N) {
-    const int r = window_first_to_raster(static_cast<int>(row), A.W, A.w, A.n_wx);
-    py = r / A.W;
-    px = r - py * A.W;
-    return r;
+  return bwd_source(row, A.T, A.N, A.M, A.Mp, A.W, A.w, A.n_wx, A.W_lr, A.rho, py, px);
+}
+
+// Row blocks of the three kinds: hi rows (window-first), guide rows, text rows.
+enum { kRowsHi = 0, kRowsGuide = 1, kRowsText = 2 };
+
+// Tile list of a row block (key tiles for dQ, query tiles for dK/dV), in three segments:
+// first the tiles of the windows within `radius` of a hi block's window (an LDS table;
+// the mask is symmetric there) or every hi tile, then guide tiles, then text tiles.
+//   dQ:    hi rows: neighbours, guide, text; guide rows: guide, text; text rows: all.
+//   dK/dV: hi rows: neighbours, text; guide and text rows: all.
+struct TileSegs {
+  int n_first, n_g, n_t;  // tiles per segment
+  bool table;             // first segment from the table (else every hi tile)
+  int hi_tiles, g_base, t_base;
+  __device__ __forceinline__ int count() const { return n_first + n_g + n_t; }
+  __device__ __forceinline__ int index(int t, const uint32_t* tab) const {
+    if (t < n_first) return table ? static_cast<int>(__builtin_amdgcn_readfirstlane(tab[t])) : t;
+    if (t < n_first + n_g) return g_base + (t - n_first);
+    return t_base + (t - n_first - n_g);
   }
-  const int64_t s = row - A.N;
-  const int sy = static_cast<int>(s / A.W_lr);
-  py = A.rho * sy;
-  px = A.rho * static_cast<int>(s - static_cast<int64_t>(sy) * A.W_lr);
-  return A.N + s;
+  // rows of tile t that exist (guide and text segments end in partial tiles)
+  __device__ __forceinline__ int valid(int t, const BwdArgs& A) const {
+    if (t < n_first) return kKeyTile;
+    const int64_t rem = t < n_first + n_g ? A.M - static_cast<int64_t>(t - n_first) * kKeyTile
+                                          : A.T - static_cast<int64_t>(t - n_first - n_g) * kKeyTile;
+    return rem < kKeyTile ? static_cast<int>(rem) : kKeyTile;
+  }
+};
+
+__device__ __forceinline__ TileSegs make_segs(const BwdArgs& A, int kind, bool key_outer, int n_local) {
+  TileSegs s;
+  const int n_g = static_cast<int>((A.M + kKeyTile - 1) / kKeyTile);
+  const int n_t = static_cast<int>((A.T + kKeyTile - 1) / kKeyTile);
+  s.hi_tiles = static_cast<int>(A.N / kKeyTile);
+  s.g_base = s.hi_tiles;
+  s.t_base = static_cast<int>((A.N + A.Mp) / kKeyTile);
+  s.table = kind == kRowsHi;
+  if (kind == kRowsHi) {
+    s.n_first = n_local;
+    s.n_g = key_outer ? 0 : n_g;
+  } else {
+    s.n_first = (kind == kRowsText || key_outer) ? s.hi_tiles : 0;
+    s.n_g = n_g;
+  }
+  s.n_t = n_t;
+  return s;
+}
+
+// First buffer row of row block `blk` of a kind (hi blocks hold `rows` rows, the others 256)
+__device__ __forceinline__ int64_t block_row0(const BwdArgs& A, int kind, int blk, int rows) {
+  if (kind == kRowsHi) return static_cast<int64_t>(blk) * rows;
+  if (kind == kRowsGuide) return A.N + static_cast<int64_t>(blk) * rows;
+  return A.N + A.Mp + static_cast<int64_t>(blk) * rows;
+}
+// Whether buffer row `row` of a block of this kind holds a token (not padding)
+__device__ __forceinline__ bool row_exists(const BwdArgs& A, int kind, int64_t row) {
+  if (kind == kRowsHi) return true;
+  if (kind == kRowsGuide) return row - A.N < A.M;
+  return row - A.N - A.Mp < A.T;
 }
 
 // Tile list of a block of rows (queries for dQ, keys for dK/dV): for hi rows the tiles of
@@ -356,8 +421,9 @@ __device__ __forceinline__ void wait_tiles(int n) {
 // tile rows from LDS, B = Q / dO held in registers), so each lane holds one query's
 // scores; dS^T converted to bf16 in place is the B operand of dQ^T += K~^T dS^T with A read
 // transposed from the same K tile.
-template <int D, int NWAVES, bool HI>
+template <int D, int NWAVES, int KIND>
 __global__ __launch_bounds__(NWAVES * 64) void bwd_dq_kernel(BwdArgs A) {
+  constexpr bool HI = KIND == kRowsHi;
   constexpr int NT = NWAVES * 64;
   constexpr int TILE = kKeyTile * D * 2;
   constexpr int CPT = TILE / 16 / NT;
@@ -373,27 +439,19 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dq_kernel(BwdArgs A) {
   const int blk = xcd_remap(blockIdx.x, A.total_blocks);
   const int bh = blk / A.blocks_per_bh, qb = blk - bh * A.blocks_per_bh;
   const int b = bh / A.heads, h = bh - b * A.heads;
-  const int64_t r0 = HI ? static_cast<int64_t>(qb) * NWAVES * 32 : A.N + static_cast<int64_t>(qb) * NWAVES * 32;
-  const int n_guide = static_cast<int>((A.M + kKeyTile - 1) / kKeyTile);
+  const int64_t r0 = block_row0(A, KIND, qb, NWAVES * 32);
   int n_local = 0;
   if (HI) {
     n_local = build_local_table<NT>(A, static_cast<int>(r0), tab);
     __syncthreads();
   }
-  const int n_tiles = n_local + n_guide;
-  const int n_hi_tiles = static_cast<int>(A.N / kKeyTile);
+  const TileSegs segs = make_segs(A, KIND, false, n_local);
+  const int n_tiles = segs.count();
   const int64_t mat = static_cast<int64_t>(bh) * A.R * D * 2;
   const char* kbase = reinterpret_cast<const char*>(A.kb) + mat;
   const char* vbase = reinterpret_cast<const char*>(A.vb) + mat;
-  auto tile_index = [&](int t) -> int {
-    if (HI && t < n_local) return __builtin_amdgcn_readfirstlane(tab[t]);
-    return n_hi_tiles + (t - n_local);
-  };
-  auto tile_valid = [&](int t) -> int {
-    if (HI && t < n_local) return kKeyTile;
-    const int64_t rem = A.M - static_cast<int64_t>(t - n_local) * kKeyTile;
-    return rem < kKeyTile ? static_cast<int>(rem) : kKeyTile;
-  };
+  auto tile_index = [&](int t) -> int { return segs.index(t, tab); };
+  auto tile_valid = [&](int t) -> int { return segs.valid(t, A); };
   int k_src[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
@@ -481,10 +539,10 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dq_kernel(BwdArgs A) {
   }
 
   // epilogue: dQ~ = scale * acc (lane: query ql, dims dt*32 + 8*(r/4) + 4g + r%4), unrotate
-  if (!HI && qrow - A.N >= A.M) return;
+  if (!row_exists(A, KIND, qrow)) return;
   int py, px;
   const int64_t rr = raster_row(qrow, A, py, px);
-  bf16_t* orow = A.out0 + ((static_cast<int64_t>(b) * (A.N + A.M) + rr) * A.heads + h) * D;
+  bf16_t* orow = A.out0 + ((static_cast<int64_t>(b) * A.L + rr) * A.heads + h) * D;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -502,8 +560,9 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dq_kernel(BwdArgs A) {
 // dP = dO V^T (A = Q / dO tile rows from LDS, B = K / V held in registers), so a lane holds
 // one key's scores for 16 queries; P and dS converted to bf16 in place are the B operands
 // of dV^T += dO^T P and dK^T += Q^T dS with A read transposed from the same dO / Q tiles.
-template <int D, int NWAVES, bool HI>
+template <int D, int NWAVES, int KIND>
 __global__ __launch_bounds__(NWAVES * 64) void bwd_dkv_kernel(BwdArgs A) {
+  constexpr bool HI = KIND == kRowsHi;
   constexpr int NT = NWAVES * 64;
   constexpr int TILE = kKeyTile * D * 2;
   constexpr int CPT = TILE / 16 / NT;
@@ -521,24 +580,19 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dkv_kernel(BwdArgs A) {
   const int blk = xcd_remap(blockIdx.x, A.total_blocks);
   const int bh = blk / A.blocks_per_bh, kb_ = blk - bh * A.blocks_per_bh;
   const int b = bh / A.heads, h = bh - b * A.heads;
-  const int64_t r0 = HI ? static_cast<int64_t>(kb_) * NWAVES * 32 : A.N + static_cast<int64_t>(kb_) * NWAVES * 32;
-  const int n_hi_tiles = static_cast<int>(A.N / kKeyTile);
-  const int n_guide_q = static_cast<int>((A.M + kKeyTile - 1) / kKeyTile);
-  int n_tiles;
+  const int64_t r0 = block_row0(A, KIND, kb_, NWAVES * 32);
+  int n_local = 0;
   if (HI) {
-    n_tiles = build_local_table<NT>(A, static_cast<int>(r0), tab);
+    n_local = build_local_table<NT>(A, static_cast<int>(r0), tab);
     __syncthreads();
-  } else {
-    n_tiles = n_hi_tiles + n_guide_q;  // every query tile: hi, then guide
   }
+  const TileSegs segs = make_segs(A, KIND, true, n_local);
+  const int n_tiles = segs.count();
   const int64_t mat = static_cast<int64_t>(bh) * A.R * D * 2;
   const char* qbase = reinterpret_cast<const char*>(A.qb) + mat;
   const char* gbase = reinterpret_cast<const char*>(A.dob) + mat;
   const char* abase = reinterpret_cast<const char*>(A.aux) + static_cast<int64_t>(bh) * (A.R / kKeyTile) * kAuxBytes;
-  auto tile_index = [&](int t) -> int {
-    if (HI) return __builtin_amdgcn_readfirstlane(tab[t]);
-    return t;
-  };
+  auto tile_index = [&](int t) -> int { return segs.index(t, tab); };
   int k_src[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
@@ -639,10 +693,10 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dkv_kernel(BwdArgs A) {
   }
 
   // epilogue: dK~ = ln2 * dk (Q carried scale * log2 e), unrotated; dV = dv
-  if (!HI && krow - A.N >= A.M) return;
+  if (!row_exists(A, KIND, krow)) return;
   int py, px;
   const int64_t rr = raster_row(krow, A, py, px);
-  const int64_t ro = ((static_cast<int64_t>(b) * (A.N + A.M) + rr) * A.heads + h) * D;
+  const int64_t ro = ((static_cast<int64_t>(b) * A.L + rr) * A.heads + h) * D;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -662,24 +716,26 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dkv_kernel(BwdArgs A) {
 
 namespace {
 
-int validate_backward(const void* const* ptrs, int n_ptrs, int B, int H, int W, int w, int H_lr,
-                      int W_lr, int rho, int heads, int D, int radius) {
+int validate_backward(const void* const* ptrs, int n_ptrs, int B, int T, int H, int W, int w,
+                      int H_lr, int W_lr, int rho, int heads, int D, int radius, int guide_mode) {
   for (int i = 0; i < n_ptrs; ++i) {
     if (!ptrs[i]) return fail_arg("null pointer");
     if (reinterpret_cast<uintptr_t>(ptrs[i]) % 16) return fail_arg("tensors must be 16-byte aligned");
   }
-  if (B < 1 || H < 1 || W < 1 || w < 1 || heads < 1 || H_lr < 0 || W_lr < 0)
+  if (B < 1 || T < 0 || H < 1 || W < 1 || w < 1 || heads < 1 || H_lr < 0 || W_lr < 0)
     return fail_arg("sizes out of range");
   if (H % w || W % w) return fail_arg("w must divide H and W");
   if ((H_lr == 0) != (W_lr == 0)) return fail_arg("H_lr and W_lr must both be zero or not");
   if (static_cast<int64_t>(H_lr) * W_lr > 0 && rho < 1) return fail_arg("rho must be >= 1 with guide tokens");
   if (radius < 0) return fail_arg("radius must be >= 0");
+  if (guide_mode < 0 || guide_mode > 2) return fail_arg("guide_mode must be 0, 1 or 2");
+  if (guide_mode != 0) return fail_unsupported("the backward covers guide mode 0");
   if (D != 64 && D != 128) return fail_unsupported("head_dim must be 64 or 128");
   if (w % 8 || (w > 16 && w % 16)) return fail_unsupported("window size must be 8, 16 or a multiple of 16");
   if (B > 65535) return fail_unsupported("batch too large");
   const int64_t N = static_cast<int64_t>(H) * W, M = static_cast<int64_t>(H_lr) * W_lr;
-  if (N > (int64_t(1) << 26) || M > (int64_t(1) << 26) ||
-      static_cast<int64_t>(B) * heads * ((N + M) / 64 + 2) > 0x7fffffff)
+  if (N > (int64_t(1) << 26) || M > (int64_t(1) << 26) || T > (int64_t(1) << 24) ||
+      static_cast<int64_t>(B) * heads * ((N + M + T) / 64 + 10) > 0x7fffffff)
     return fail_unsupported("problem too large");
   const int r = std::min(radius, H / w + W / w);
   const int64_t tiles = static_cast<int64_t>(std::min(2 * r + 1, H / w)) * std::min(2 * r + 1, W / w) *
@@ -688,51 +744,63 @@ int validate_backward(const void* const* ptrs, int n_ptrs, int B, int H, int W, 
   return UHLA_OK;
 }
 
-template <int D>
-void launch_dq(int nwaves, bool hi, const BwdArgs& a, hipStream_t s) {
-  if (!hi) hipLaunchKernelGGL((bwd_dq_kernel<D, kBwdWaves, false>), dim3(a.total_blocks), dim3(kBwdWaves * 64), 0, s, a);
-  else if (nwaves == kBwdWaves) hipLaunchKernelGGL((bwd_dq_kernel<D, kBwdWaves, true>), dim3(a.total_blocks), dim3(kBwdWaves * 64), 0, s, a);
-  else hipLaunchKernelGGL((bwd_dq_kernel<D, 2, true>), dim3(a.total_blocks), dim3(128), 0, s, a);
+template <int D, int KIND>
+void launch_dq(int nwaves, const BwdArgs& a, hipStream_t s) {
+  if (KIND != kRowsHi || nwaves == kBwdWaves)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, kBwdWaves, KIND>), dim3(a.total_blocks), dim3(kBwdWaves * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<D, 2, kRowsHi>), dim3(a.total_blocks), dim3(128), 0, s, a);
 }
 
-template <int D>
-void launch_dkv(int nwaves, bool hi, const BwdArgs& a, hipStream_t s) {
-  if (!hi) hipLaunchKernelGGL((bwd_dkv_kernel<D, kBwdWaves, false>), dim3(a.total_blocks), dim3(kBwdWaves * 64), 0, s, a);
-  else if (nwaves == kBwdWaves) hipLaunchKernelGGL((bwd_dkv_kernel<D, kBwdWaves, true>), dim3(a.total_blocks), dim3(kBwdWaves * 64), 0, s, a);
-  else hipLaunchKernelGGL((bwd_dkv_kernel<D, 2, true>), dim3(a.total_blocks), dim3(128), 0, s, a);
+template <int D, int KIND>
+void launch_dkv(int nwaves, const BwdArgs& a, hipStream_t s) {
+  if (KIND != kRowsHi || nwaves == kBwdWaves)
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, kBwdWaves, KIND>), dim3(a.total_blocks), dim3(kBwdWaves * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, 2, kRowsHi>), dim3(a.total_blocks), dim3(128), 0, s, a);
+}
+
+template <int KIND>
+void launch_both(bool dkv, int D, int nwaves, const BwdArgs& a, hipStream_t s) {
+  if (dkv) D == 128 ? launch_dkv<128, KIND>(nwaves, a, s) : launch_dkv<64, KIND>(nwaves, a, s);
+  else D == 128 ? launch_dq<128, KIND>(nwaves, a, s) : launch_dq<64, KIND>(nwaves, a, s);
 }
 
 }  // namespace
 
 }  // namespace uhla
 
-extern "C" size_t uhla_backward_workspace_bytes(int B, int H, int W, int w, int H_lr, int W_lr,
-                                                int rho, int heads, int head_dim, int radius) {
-  if (B < 1 || H < 1 || W < 1 || w < 1 || heads < 1 || H_lr < 0 || W_lr < 0 || radius < 0) return 0;
+extern "C" size_t uhla_backward_workspace_bytes(int B, int T, int H, int W, int w, int H_lr,
+                                                int W_lr, int rho, int heads, int head_dim,
+                                                int radius) {
+  if (B < 1 || T < 0 || H < 1 || W < 1 || w < 1 || heads < 1 || H_lr < 0 || W_lr < 0 || radius < 0)
+    return 0;
   if (H % w || W % w || (H_lr == 0) != (W_lr == 0)) return 0;
   if (head_dim != 64 && head_dim != 128) return 0;
   if (static_cast<int64_t>(H_lr) * W_lr > 0 && rho < 1) return 0;
-  return uhla::carve_bwd(uhla::make_bwd_geom(B, H, W, w, H_lr, W_lr, rho, heads, head_dim, radius),
+  return uhla::carve_bwd(uhla::make_bwd_geom(B, T, H, W, w, H_lr, W_lr, rho, heads, head_dim, radius),
                          nullptr).bytes;
 }
 
 extern "C" int uhla_backward(const void* q, const void* k, const void* v, const void* o,
                              const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                             int B, int H, int W, int w, int H_lr, int W_lr, int rho, int heads,
-                             int head_dim, float scale, float theta, int radius, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+                             int B, int T, int H, int W, int w, int H_lr, int W_lr, int rho,
+                             int heads, int head_dim, float scale, float theta, int radius,
+                             int guide_mode, void* workspace, size_t workspace_bytes,
+                             void* stream) {
   using namespace uhla;
   const void* ptrs[9] = {q, k, v, o, dout, lse, dq, dk, dv};
-  int st = validate_backward(ptrs, 9, B, H, W, w, H_lr, W_lr, rho, heads, head_dim, radius);
+  int st = validate_backward(ptrs, 9, B, T, H, W, w, H_lr, W_lr, rho, heads, head_dim, radius,
+                             guide_mode);
   if (st) return st;
   radius = std::min(radius, H / w + W / w);
   const int D = head_dim;
-  const BwdGeom g = make_bwd_geom(B, H, W, w, H_lr, W_lr, rho, heads, D, radius);
+  const BwdGeom g = make_bwd_geom(B, T, H, W, w, H_lr, W_lr, rho, heads, D, radius);
   const BwdWorkspace need = carve_bwd(g, nullptr);
   if (!workspace || workspace_bytes < need.bytes)
     return (set_detail("workspace too small"), UHLA_ERR_WORKSPACE);
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail_arg("workspace must be 256-byte aligned");
-  const int64_t L = g.N + g.M;
+  const int64_t L = g.T + g.N + g.M;
   const size_t tb = static_cast<size_t>(B) * L * heads * D * 2;
   const void* ins[5] = {q, k, v, o, dout};
   void* outs[3] = {dq, dk, dv};
@@ -775,56 +843,51 @@ extern "C" int uhla_backward(const void* q, const void* k, const void* v, const 
     const bf16_t* gp = static_cast<const bf16_t*>(dout);
     if (D == 128)
       hipLaunchKernelGGL(bwd_rows_kernel<128>, grid, dim3(kBwdThreads), 0, s, qp, kp, vp, gp, ws.qb,
-                         ws.kb, ws.vb, ws.dob, ws.cs, g.P, l2t, g.N, g.M, g.R, W, w, n_wx, W_lr, rho,
-                         heads, rope_on ? 1 : 0, qs);
+                         ws.kb, ws.vb, ws.dob, ws.cs, g.P, l2t, g.T, g.N, g.M, g.Mp, g.R, W, w, n_wx,
+                         W_lr, rho, heads, rope_on ? 1 : 0, qs);
     else
       hipLaunchKernelGGL(bwd_rows_kernel<64>, grid, dim3(kBwdThreads), 0, s, qp, kp, vp, gp, ws.qb,
-                         ws.kb, ws.vb, ws.dob, ws.cs, g.P, l2t, g.N, g.M, g.R, W, w, n_wx, W_lr, rho,
-                         heads, rope_on ? 1 : 0, qs);
+                         ws.kb, ws.vb, ws.dob, ws.cs, g.P, l2t, g.T, g.N, g.M, g.Mp, g.R, W, w, n_wx,
+                         W_lr, rho, heads, rope_on ? 1 : 0, qs);
     st = check_launch("bwd_rows_kernel");
     if (st) return st;
-    const int64_t aux_threads = BH * (g.N + g.M) * (D / 8) + BH * (g.R - g.N - g.M);
+    const int64_t aux_threads = BH * L * (D / 8) + BH * (g.R - L);  // rows, then padding rows
     UHLA_BSTEP(hipLaunchKernelGGL(bwd_aux_kernel, dim3(static_cast<unsigned>((aux_threads + kBwdThreads - 1) / kBwdThreads)),
                                   dim3(kBwdThreads), 0, s, static_cast<const bf16_t*>(o), gp, lse,
-                                  ws.aux, g.N, g.M, g.R, W, w, n_wx, heads, D, BH),
+                                  ws.aux, g.T, g.N, g.M, g.Mp, g.R, W, w, n_wx, heads, D, BH),
                "bwd_aux_kernel");
   }
 
   BwdArgs a{};
   a.qb = ws.qb; a.kb = ws.kb; a.vb = ws.vb; a.dob = ws.dob;
   a.aux = ws.aux; a.cs = ws.cs;
-  a.N = g.N; a.M = g.M; a.R = g.R;
+  a.T = g.T; a.N = g.N; a.M = g.M; a.Mp = g.Mp; a.R = g.R; a.L = L;
   a.heads = heads; a.w2 = w * w; a.W = W; a.w = w; a.n_wx = n_wx; a.n_wy = H / w;
   a.radius = radius; a.rho = rho; a.W_lr = W_lr; a.P = g.P;
   a.rope_on = rope_on ? 1 : 0; a.log2_theta = l2t;
   const int nw_hi = std::min(kBwdWaves, w * w / 32);  // w * w is 64 or a multiple of 256
 
-  // dQ: hi queries, then guide queries
-  a.out0 = static_cast<bf16_t*>(dq);
-  a.out_scale = sc;
-  a.blocks_per_bh = static_cast<int>(g.N / (nw_hi * 32));
-  a.total_blocks = static_cast<int>(BH * a.blocks_per_bh);
-  UHLA_BSTEP((D == 128 ? launch_dq<128>(nw_hi, true, a, s) : launch_dq<64>(nw_hi, true, a, s)),
-             "bwd_dq_kernel(hi)");
-  if (g.M > 0) {
-    a.blocks_per_bh = static_cast<int>((g.R - g.N) / kBwdGuideRows);
+  // dQ, then dK / dV, each over hi rows, guide rows and text rows
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool dkv = pass == 1;
+    a.out0 = static_cast<bf16_t*>(dkv ? dk : dq);
+    a.out1 = static_cast<bf16_t*>(dv);
+    a.out_scale = dkv ? 0.69314718055994531f : sc;
+    a.blocks_per_bh = static_cast<int>(g.N / (nw_hi * 32));
     a.total_blocks = static_cast<int>(BH * a.blocks_per_bh);
-    UHLA_BSTEP((D == 128 ? launch_dq<128>(kBwdWaves, false, a, s) : launch_dq<64>(kBwdWaves, false, a, s)),
-               "bwd_dq_kernel(guide)");
-  }
-  // dK, dV: hi keys, then guide keys
-  a.out0 = static_cast<bf16_t*>(dk);
-  a.out1 = static_cast<bf16_t*>(dv);
-  a.out_scale = 0.69314718055994531f;
-  a.blocks_per_bh = static_cast<int>(g.N / (nw_hi * 32));
-  a.total_blocks = static_cast<int>(BH * a.blocks_per_bh);
-  UHLA_BSTEP((D == 128 ? launch_dkv<128>(nw_hi, true, a, s) : launch_dkv<64>(nw_hi, true, a, s)),
-             "bwd_dkv_kernel(hi)");
-  if (g.M > 0) {
-    a.blocks_per_bh = static_cast<int>((g.R - g.N) / kBwdGuideRows);
-    a.total_blocks = static_cast<int>(BH * a.blocks_per_bh);
-    UHLA_BSTEP((D == 128 ? launch_dkv<128>(kBwdWaves, false, a, s) : launch_dkv<64>(kBwdWaves, false, a, s)),
-               "bwd_dkv_kernel(guide)");
+    UHLA_BSTEP(launch_both<kRowsHi>(dkv, D, nw_hi, a, s), dkv ? "bwd_dkv_kernel(hi)" : "bwd_dq_kernel(hi)");
+    if (g.M > 0) {
+      a.blocks_per_bh = static_cast<int>(g.Mp / kBwdGuideRows);
+      a.total_blocks = static_cast<int>(BH * a.blocks_per_bh);
+      UHLA_BSTEP(launch_both<kRowsGuide>(dkv, D, kBwdWaves, a, s),
+                 dkv ? "bwd_dkv_kernel(guide)" : "bwd_dq_kernel(guide)");
+    }
+    if (g.T > 0) {
+      a.blocks_per_bh = static_cast<int>(g.Tp / kBwdGuideRows);
+      a.total_blocks = static_cast<int>(BH * a.blocks_per_bh);
+      UHLA_BSTEP(launch_both<kRowsText>(dkv, D, kBwdWaves, a, s),
+                 dkv ? "bwd_dkv_kernel(text)" : "bwd_dq_kernel(text)");
+    }
   }
 #undef UHLA_BSTEP
   return UHLA_OK;

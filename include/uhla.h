@@ -192,29 +192,32 @@ int uhla_forward_text(const void* q, const void* k, const void* v, void* o,
  *   sum of exp(scale * q.k) over the keys the row sees.  Errors: as uhla_forward_text, plus
  *   UHLA_ERR_ARG for a null or misaligned lse or one overlapping O or the workspace.
  *
- * uhla_backward: gradients dQ, dK, dV (bf16, layout of Q) of O = uhla_forward_masked(Q, K,
- *   V; radius, guide_mode 0) for the output gradient dO, given O and the lse written by
- *   uhla_forward_lse for the same inputs.  Per (batch, head), with rotated Q~, K~ and
- *   P = exp(scale Q~ K~^T - lse) on the allowed pairs: dV = P^T dO, dS = P (dO V^T - D),
- *   D = rowsum(dO O), dQ~ = scale dS K~, dK~ = scale dS^T Q~, and dQ, dK rotate dQ~, dK~
- *   back (the transpose of RoPE).  Computed as the forward: bf16 MFMA, fp32 accumulation,
- *   P and dS rounded to bf16 for their products.  Deterministic (no atomics).
+ * uhla_backward: gradients dQ, dK, dV (bf16, layout of Q) of O = uhla_forward_text(Q, K,
+ *   V; T, radius, guide_mode 0) (T = 0: uhla_forward_masked) for the output gradient dO,
+ *   given O and the lse written by uhla_forward_lse for the same inputs.  Q, K, V, O, dO:
+ *   bf16 [B, T + N + M, heads, head_dim], text rows first.  Per (batch, head), with rotated
+ *   Q~, K~ and P = exp(scale Q~ K~^T - lse) on the allowed pairs: dV = P^T dO,
+ *   dS = P (dO V^T - D), D = rowsum(dO O), dQ~ = scale dS K~, dK~ = scale dS^T Q~, and dQ,
+ *   dK rotate dQ~, dK~ back (the transpose of RoPE).  Computed as the forward: bf16 MFMA,
+ *   fp32 accumulation, P and dS rounded to bf16 for their products.  Deterministic (no
+ *   atomics).
  *   workspace: at least uhla_backward_workspace_bytes(...) bytes, 256-byte aligned.
- *   Errors: UHLA_ERR_ARG (null or misaligned pointers, sizes < 1, w not dividing H or W,
- *   radius < 0, gradients overlapping an input, lse, the workspace or each other);
- *   UHLA_ERR_UNSUPPORTED (head_dim not in {64, 128}, w as in uhla_forward, more than 1024
- *   key tiles per window); UHLA_ERR_WORKSPACE; UHLA_ERR_HIP.
+ *   Errors: UHLA_ERR_ARG (null or misaligned pointers, sizes < 1, T < 0, w not dividing H
+ *   or W, radius < 0, guide_mode outside 0..2, gradients overlapping an input, lse, the
+ *   workspace or each other); UHLA_ERR_UNSUPPORTED (guide_mode 1 or 2, head_dim not in
+ *   {64, 128}, w as in uhla_forward, more than 1024 key tiles per window, T > 2^24);
+ *   UHLA_ERR_WORKSPACE; UHLA_ERR_HIP.
  */
 int uhla_forward_lse(const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int T, int H, int W, int w, int H_lr, int W_lr, int rho,
                      int heads, int head_dim, float scale, float theta, int radius,
                      int guide_mode, void* workspace, size_t workspace_bytes, void* stream);
-size_t uhla_backward_workspace_bytes(int B, int H, int W, int w, int H_lr, int W_lr, int rho,
-                                     int heads, int head_dim, int radius);
+size_t uhla_backward_workspace_bytes(int B, int T, int H, int W, int w, int H_lr, int W_lr,
+                                     int rho, int heads, int head_dim, int radius);
 int uhla_backward(const void* q, const void* k, const void* v, const void* o,
                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                  int B, int H, int W, int w, int H_lr, int W_lr, int rho, int heads,
-                  int head_dim, float scale, float theta, int radius,
+                  int B, int T, int H, int W, int w, int H_lr, int W_lr, int rho, int heads,
+                  int head_dim, float scale, float theta, int radius, int guide_mode,
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status code (static storage). */

@@ -279,13 +279,13 @@ def test_forward_rope_at_load_rejects(lib):
 def bwd_args(**kw):
     a = dict(q=P, k=P2, v=P3, o=P4, do=ctypes.c_void_p(0x70000000),
              lse=ctypes.c_void_p(0x80000000), dq=ctypes.c_void_p(0x90000000),
-             dk=ctypes.c_void_p(0xa0000000), dv=ctypes.c_void_p(0xb0000000), B=1, H=32, W=32,
-             w=8, H_lr=8, W_lr=8, rho=4, heads=2, d=64, scale=0.0, theta=10000.0, radius=1,
-             ws=ctypes.c_void_p(0x50000000), wsb=1 << 40)
+             dk=ctypes.c_void_p(0xa0000000), dv=ctypes.c_void_p(0xb0000000), B=1, T=0, H=32,
+             W=32, w=8, H_lr=8, W_lr=8, rho=4, heads=2, d=64, scale=0.0, theta=10000.0,
+             radius=1, mode=0, ws=ctypes.c_void_p(0x50000000), wsb=1 << 40)
     a.update(kw)
-    return tuple(a[n] for n in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "B", "H", "W",
-                                "w", "H_lr", "W_lr", "rho", "heads", "d", "scale", "theta",
-                                "radius", "ws", "wsb")) + (NULL,)
+    return tuple(a[n] for n in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "B", "T", "H",
+                                "W", "w", "H_lr", "W_lr", "rho", "heads", "d", "scale", "theta",
+                                "radius", "mode", "ws", "wsb")) + (NULL,)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -298,6 +298,10 @@ def bwd_args(**kw):
     (dict(W_lr=0), api.UHLA_ERR_ARG),
     (dict(rho=0), api.UHLA_ERR_ARG),
     (dict(radius=-1), api.UHLA_ERR_ARG),
+    (dict(T=-1), api.UHLA_ERR_ARG),
+    (dict(mode=3), api.UHLA_ERR_ARG),
+    (dict(mode=1), api.UHLA_ERR_UNSUPPORTED),
+    (dict(T=1 << 25), api.UHLA_ERR_UNSUPPORTED),
     (dict(d=96), api.UHLA_ERR_UNSUPPORTED),
     (dict(H=36, W=36, w=4), api.UHLA_ERR_UNSUPPORTED),
     (dict(H=384, W=384, w=96, H_lr=0, W_lr=0), api.UHLA_ERR_UNSUPPORTED),
@@ -313,21 +317,23 @@ def test_backward_rejects(lib, kw, status):
     assert lib.uhla_backward(*bwd_args(**kw)) == status
 
 
-def expected_backward_workspace(B, H, W, w, H_lr, W_lr, heads, d):
-    """Independent restatement: cos/sin table, then Q, K, V, dO rows per (b, h) with hi rows
-    then guide rows padded to 256 (bf16), then per 64-row tile 64 lse2 and 64 row dots (fp32);
-    regions 256-byte aligned."""
+def expected_backward_workspace(B, H, W, w, H_lr, W_lr, heads, d, T=0):
+    """Independent restatement: cos/sin table, then Q, K, V, dO rows per (b, h) with hi rows,
+    then guide rows and text rows each padded to 256 (bf16), then per 64-row tile 64 lse2 and
+    64 row dots (fp32); regions 256-byte aligned."""
     al = lambda x: (x + 255) // 256 * 256
     N, M = H * W, H_lr * W_lr
-    R = N + (M + 255) // 256 * 256
+    R = N + (M + 255) // 256 * 256 + (T + 255) // 256 * 256
     bh = B * heads
     return al(16 * max(H, W) * (d // 4)) + 4 * al(bh * R * d * 2) + al(bh * R // 64 * 512)
 
 
 @pytest.mark.parametrize("g", GEOMS)
-def test_backward_workspace_bytes(lib, g):
+@pytest.mark.parametrize("T", [0, 1, 300])
+def test_backward_workspace_bytes(lib, g, T):
     B, H, W, w, H_lr, W_lr, heads, d = g
-    got = lib.uhla_backward_workspace_bytes(B, H, W, w, H_lr, W_lr, 4, heads, d, 1)
-    assert got == expected_backward_workspace(*g)
-    assert lib.uhla_backward_workspace_bytes(B, H, W, w, H_lr, W_lr, 4, heads, d, -1) == 0
-    assert lib.uhla_backward_workspace_bytes(B, H, W, w, H_lr, W_lr, 4, heads, 96, 1) == 0
+    got = lib.uhla_backward_workspace_bytes(B, T, H, W, w, H_lr, W_lr, 4, heads, d, 1)
+    assert got == expected_backward_workspace(*g, T=T)
+    assert lib.uhla_backward_workspace_bytes(B, T, H, W, w, H_lr, W_lr, 4, heads, d, -1) == 0
+    assert lib.uhla_backward_workspace_bytes(B, T, H, W, w, H_lr, W_lr, 4, heads, 96, 1) == 0
+    assert lib.uhla_backward_workspace_bytes(B, -1, H, W, w, H_lr, W_lr, 4, heads, d, 1) == 0

@@ -8,8 +8,10 @@ scaled), P and dS to bf16 for the MFMAs (relative 2^-9 each) and store bf16 (2^-
 sums they enter have random signs, so the errors stay a small multiple of 2^-9 of the
 gradient's scale.
 * every row / every key at small sizes: both head dims, window sizes 8, 16 and 32, radius
-  0 / 1 / 2, ragged guide grids, guide positions past the hi grid, no guide tokens, RoPE off;
-* sampled query and key rows at the 2K workload (oracle rows of the backward);
+  0 / 1 / 2, ragged guide grids, guide positions past the hi grid, no guide tokens, RoPE off,
+  text tokens (ragged, several tiles, without guide tokens);
+* sampled query and key rows at the 2K workload, without and with 512 text tokens (oracle
+  rows of the backward);
 * the 8K workload: sampled dQ rows against the oracle and the dV sum rule over all keys;
 * determinism.
 """
@@ -29,9 +31,9 @@ def run_fwd_bwd(g, q, k, v, do):
     import torch
     qt, kt, vt, gt = to_dev(q), to_dev(k), to_dev(v), to_dev(do)
     o, lse = api.forward_lse(qt, kt, vt, g.H, g.W, g.w, g.H_lr, g.W_lr, rho=g.rho, theta=g.theta,
-                             radius=g.radius)
+                             radius=g.radius, T=g.T)
     dq, dk, dv = api.backward(qt, kt, vt, o, gt, lse, g.H, g.W, g.w, g.H_lr, g.W_lr, rho=g.rho,
-                              theta=g.theta, radius=g.radius)
+                              theta=g.theta, radius=g.radius, T=g.T)
     torch.cuda.synchronize()
     return lse.cpu().numpy().astype(np.float64), from_dev(dq), from_dev(dk), from_dev(dv)
 
@@ -58,6 +60,14 @@ CASES = {
     # the cos/sin table are evaluated directly
     "d64_guide_beyond_grid": Geometry(B=2, heads=1, head_dim=64, H=32, W=32, w=16, H_lr=11,
                                       W_lr=9),
+    # text tokens (rows 0..T-1): a ragged text tile, several text tiles with radius 0, text
+    # without guide tokens and with windows of 8
+    "d128_text77": Geometry(B=1, heads=2, head_dim=128, H=48, W=32, w=16, H_lr=12, W_lr=8,
+                            T=77),
+    "d128_text300_r0": Geometry(B=1, heads=1, head_dim=128, H=32, W=48, w=16, H_lr=8, W_lr=12,
+                                radius=0, T=300),
+    "d64_text_w8_no_guide": Geometry(B=2, heads=1, head_dim=64, H=32, W=32, w=8, H_lr=0, W_lr=0,
+                                     T=64),
 }
 
 
@@ -97,6 +107,26 @@ def test_backward_sampled_rows_2k():
         check_rel(bf16_f64(dq[0, q_rows, h]), rq, f"2k dq h{h}")
         check_rel(bf16_f64(dk[0, k_rows, h]), rk, f"2k dk h{h}")
         check_rel(bf16_f64(dv[0, k_rows, h]), rv, f"2k dv h{h}")
+
+
+def test_backward_sampled_rows_2k_text():
+    g = CONFIGS["2k"].with_(T=512)
+    say("backward sampled rows 2k with 512 text tokens")
+    q, k, v = make_qkv_bits(g, 11)
+    do = make_qkv_bits(g, 12)[0]
+    _, dq, dk, dv = run_fwd_bwd(g, q, k, v, do)
+    rng = np.random.default_rng(6)
+    qf, kf, vf, gf = (bf16_f64(x[:, :, 5:6, :]) for x in (q, k, v, do))
+    T, N = g.T, g.N
+    q_rows = np.unique(np.concatenate([[0, T - 1, T, T + N - 1, T + N, g.L - 1],
+                                       rng.integers(0, T, 10), T + rng.integers(0, N, 40),
+                                       T + N + rng.integers(0, g.M, 10)]))
+    k_rows = np.unique(np.concatenate([[0, T - 1, T, T + N, g.L - 1], rng.integers(0, T, 6),
+                                       T + rng.integers(0, N, 20)]))
+    rq, rk, rv = orc.backward_rows(qf, kf, vf, gf, g, 0, 0, q_rows, k_rows)
+    check_rel(bf16_f64(dq[0, q_rows, 5]), rq, "2k+text dq h5")
+    check_rel(bf16_f64(dk[0, k_rows, 5]), rk, "2k+text dk h5")
+    check_rel(bf16_f64(dv[0, k_rows, 5]), rv, "2k+text dv h5")
 
 
 def test_backward_8k_sampled_dq_and_dv_sum():
