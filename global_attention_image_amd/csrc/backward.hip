@@ -41,6 +41,7 @@ struct BwdGeom {
   int B, H, W, w, H_lr, W_lr, rho, heads, D, radius;
   int64_t T, N, M, Mp, Tp, R;  // R: rows per (b, h) = N + Mp + Tp (guide / text rows padded)
   int n_wx, n_wy, P;
+  int splits;  // text row blocks: tile-range splits (0 without text tokens)
 };
 
 BwdGeom make_bwd_geom(int B, int64_t T, int H, int W, int w, int H_lr, int W_lr, int rho,
@@ -54,6 +55,16 @@ BwdGeom make_bwd_geom(int B, int64_t T, int H, int W, int w, int H_lr, int W_lr,
   g.Mp = (g.M + kBwdGuideRows - 1) / kBwdGuideRows * kBwdGuideRows;
   g.Tp = (T + kBwdGuideRows - 1) / kBwdGuideRows * kBwdGuideRows;
   g.R = g.N + g.Mp + g.Tp;
+  // Text row blocks walk every tile of the other side: few blocks, long lists.  Split each
+  // list so that the GPU gets about 1024 workgroups, each split at least 8 tiles long.
+  g.splits = 0;
+  if (T > 0) {
+    const int64_t blocks = static_cast<int64_t>(B) * heads * (g.Tp / kBwdGuideRows);
+    const int64_t tiles = g.R / kKeyTile;
+    int64_t sp = (1024 + blocks - 1) / blocks;
+    sp = std::min(sp, std::max<int64_t>(1, tiles / 8));
+    g.splits = static_cast<int>(std::max<int64_t>(1, sp));
+  }
   g.n_wx = W / w; g.n_wy = H / w;
   g.P = H > W ? H : W;
   return g;
@@ -63,6 +74,7 @@ struct BwdWorkspace {
   double2* cs;
   bf16_t *qb, *kb, *vb, *dob;  // [B*heads][R][D]
   float* aux;                  // [B*heads][R/64][128]
+  float *part0, *part1;        // [splits][B*heads][Tp][D] text row blocks' partial sums
   size_t bytes;
 };
 
@@ -80,11 +92,15 @@ BwdWorkspace carve_bwd(const BwdGeom& g, void* base) {
   size_t o_m[4];
   for (auto& x : o_m) x = take(mat);
   const size_t o_aux = take(rows / kKeyTile * kAuxBytes);
+  const size_t part = static_cast<size_t>(g.splits) * g.B * g.heads * g.Tp * g.D * sizeof(float);
+  const size_t o_p0 = take(part), o_p1 = take(part);
   char* b = static_cast<char*>(base);
   ws.cs = reinterpret_cast<double2*>(b + o_cs);
   bf16_t** mats[4] = {&ws.qb, &ws.kb, &ws.vb, &ws.dob};
   for (int i = 0; i < 4; ++i) *mats[i] = reinterpret_cast<bf16_t*>(b + o_m[i]);
   ws.aux = reinterpret_cast<float*>(b + o_aux);
+  ws.part0 = reinterpret_cast<float*>(b + o_p0);
+  ws.part1 = reinterpret_cast<float*>(b + o_p1);
   ws.bytes = off;
   return ws;
 }
@@ -257,7 +273,43 @@ struct BwdArgs {
   double log2_theta;
   float out_scale;  // scale (dQ) or ln 2 (dK)
   int blocks_per_bh, total_blocks;
+  int splits;             // text row blocks: tile-range splits per block
+  float *part0, *part1;   // text row blocks: fp32 partial sums [splits][B*heads][Tp][D]
+  int64_t Tp;
 };
+
+// Tile range [t0, t1) of split `split` of a list of n tiles (splits of equal length)
+__device__ __forceinline__ void split_range(int n, int splits, int split, int& t0, int& t1) {
+  const int per = (n + splits - 1) / splits;
+  t0 = min(n, split * per);
+  t1 = min(n, t0 + per);
+}
+
+// Sum of the text row blocks' split partials in a fixed order, scaled and stored as bf16
+// in the caller's layout (text rows sit at position (0, 0), where RoPE is the identity).
+// One thread per pair of dims of one (b, h, text row); part1 / out1 are optional.
+__global__ void bwd_text_combine_kernel(const float* __restrict__ part0, const float* __restrict__ part1,
+                                        bf16_t* out0, bf16_t* out1, float scale0, int splits,
+                                        int64_t bh_total, int64_t Tp, int64_t T, int64_t L,
+                                        int heads, int D) {
+  const int64_t x = blockIdx.x, bh = blockIdx.y;
+  const int d = 2 * threadIdx.x;
+  if (x >= T || d >= D) return;
+  float a0 = 0.0f, a1 = 0.0f, c0 = 0.0f, c1 = 0.0f;
+  for (int sp = 0; sp < splits; ++sp) {
+    const int64_t o = ((sp * bh_total + bh) * Tp + x) * D + d;
+    a0 += part0[o];
+    a1 += part0[o + 1];
+    if (part1) {
+      c0 += part1[o];
+      c1 += part1[o + 1];
+    }
+  }
+  const int64_t b = bh / heads, h = bh - b * heads;
+  const int64_t ro = ((b * L + x) * heads + h) * D + d;
+  *reinterpret_cast<uint32_t*>(out0 + ro) = pack_bf16x2(scale0 * a0, scale0 * a1);
+  if (part1) *reinterpret_cast<uint32_t*>(out1 + ro) = pack_bf16x2(c0, c1);
+}
 
 // Inverse RoPE of the pair (a, b) at pair index pr of a row at position (py, px), in fp32
 // from the fp64 factors, then bf16.
@@ -437,7 +489,9 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dq_kernel(BwdArgs A) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ql = lane & 31, g = lane >> 5;
   const int blk = xcd_remap(blockIdx.x, A.total_blocks);
-  const int bh = blk / A.blocks_per_bh, qb = blk - bh * A.blocks_per_bh;
+  const int bh = blk / A.blocks_per_bh, rem_blk = blk - bh * A.blocks_per_bh;
+  const int qb = KIND == kRowsText ? rem_blk / A.splits : rem_blk;
+  const int split = KIND == kRowsText ? rem_blk - qb * A.splits : 0;
   const int b = bh / A.heads, h = bh - b * A.heads;
   const int64_t r0 = block_row0(A, KIND, qb, NWAVES * 32);
   int n_local = 0;
@@ -446,12 +500,14 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dq_kernel(BwdArgs A) {
     __syncthreads();
   }
   const TileSegs segs = make_segs(A, KIND, false, n_local);
-  const int n_tiles = segs.count();
+  int t_first = 0, t_end = segs.count();
+  if (KIND == kRowsText) split_range(segs.count(), A.splits, split, t_first, t_end);
+  const int n_tiles = t_end - t_first;  // this workgroup's tiles t_first + [0, n_tiles)
   const int64_t mat = static_cast<int64_t>(bh) * A.R * D * 2;
   const char* kbase = reinterpret_cast<const char*>(A.kb) + mat;
   const char* vbase = reinterpret_cast<const char*>(A.vb) + mat;
-  auto tile_index = [&](int t) -> int { return segs.index(t, tab); };
-  auto tile_valid = [&](int t) -> int { return segs.valid(t, A); };
+  auto tile_index = [&](int t) -> int { return segs.index(t_first + t, tab); };
+  auto tile_valid = [&](int t) -> int { return segs.valid(t_first + t, A); };
   int k_src[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
@@ -538,7 +594,21 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dq_kernel(BwdArgs A) {
     wait_tiles<OPS>(std::min(n_tiles - 1, t + AH) - (t + 1));
   }
 
-  // epilogue: dQ~ = scale * acc (lane: query ql, dims dt*32 + 8*(r/4) + 4g + r%4), unrotate
+  // epilogue: dQ~ = scale * acc (lane: query ql, dims dt*32 + 8*(r/4) + 4g + r%4), unrotate;
+  // text row blocks store their split's unscaled partial sums for bwd_text_combine_kernel
+  if (KIND == kRowsText) {
+    float* pp = A.part0 + ((static_cast<int64_t>(split) * A.total_blocks / A.blocks_per_bh + bh) * A.Tp +
+                           (qrow - A.N - A.Mp)) * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d0 = dt * 32 + 8 * rg + 4 * g;
+        *reinterpret_cast<f32x4*>(pp + d0) =
+            f32x4{acc[dt][4 * rg], acc[dt][4 * rg + 1], acc[dt][4 * rg + 2], acc[dt][4 * rg + 3]};
+      }
+    return;
+  }
   if (!row_exists(A, KIND, qrow)) return;
   int py, px;
   const int64_t rr = raster_row(qrow, A, py, px);
@@ -578,7 +648,9 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dkv_kernel(BwdArgs A) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ql = lane & 31, g = lane >> 5;
   const int blk = xcd_remap(blockIdx.x, A.total_blocks);
-  const int bh = blk / A.blocks_per_bh, kb_ = blk - bh * A.blocks_per_bh;
+  const int bh = blk / A.blocks_per_bh, rem_blk = blk - bh * A.blocks_per_bh;
+  const int kb_ = KIND == kRowsText ? rem_blk / A.splits : rem_blk;
+  const int split = KIND == kRowsText ? rem_blk - kb_ * A.splits : 0;
   const int b = bh / A.heads, h = bh - b * A.heads;
   const int64_t r0 = block_row0(A, KIND, kb_, NWAVES * 32);
   int n_local = 0;
@@ -587,12 +659,14 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dkv_kernel(BwdArgs A) {
     __syncthreads();
   }
   const TileSegs segs = make_segs(A, KIND, true, n_local);
-  const int n_tiles = segs.count();
+  int t_first = 0, t_end = segs.count();
+  if (KIND == kRowsText) split_range(segs.count(), A.splits, split, t_first, t_end);
+  const int n_tiles = t_end - t_first;  // this workgroup's tiles t_first + [0, n_tiles)
   const int64_t mat = static_cast<int64_t>(bh) * A.R * D * 2;
   const char* qbase = reinterpret_cast<const char*>(A.qb) + mat;
   const char* gbase = reinterpret_cast<const char*>(A.dob) + mat;
   const char* abase = reinterpret_cast<const char*>(A.aux) + static_cast<int64_t>(bh) * (A.R / kKeyTile) * kAuxBytes;
-  auto tile_index = [&](int t) -> int { return segs.index(t, tab); };
+  auto tile_index = [&](int t) -> int { return segs.index(t_first + t, tab); };
   int k_src[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
@@ -692,7 +766,23 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dkv_kernel(BwdArgs A) {
     wait_tiles<OPS>(std::min(n_tiles - 1, t + AH) - (t + 1));
   }
 
-  // epilogue: dK~ = ln2 * dk (Q carried scale * log2 e), unrotated; dV = dv
+  // epilogue: dK~ = ln2 * dk (Q carried scale * log2 e), unrotated; dV = dv; text row
+  // blocks store their split's unscaled partial sums for bwd_text_combine_kernel
+  if (KIND == kRowsText) {
+    const int64_t po = ((static_cast<int64_t>(split) * A.total_blocks / A.blocks_per_bh + bh) * A.Tp +
+                        (krow - A.N - A.Mp)) * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d0 = dt * 32 + 8 * rg + 4 * g;
+        *reinterpret_cast<f32x4*>(A.part0 + po + d0) =
+            f32x4{dk[dt][4 * rg], dk[dt][4 * rg + 1], dk[dt][4 * rg + 2], dk[dt][4 * rg + 3]};
+        *reinterpret_cast<f32x4*>(A.part1 + po + d0) =
+            f32x4{dv[dt][4 * rg], dv[dt][4 * rg + 1], dv[dt][4 * rg + 2], dv[dt][4 * rg + 3]};
+      }
+    return;
+  }
   if (!row_exists(A, KIND, krow)) return;
   int py, px;
   const int64_t rr = raster_row(krow, A, py, px);
@@ -865,6 +955,7 @@ extern "C" int uhla_backward(const void* q, const void* k, const void* v, const 
   a.heads = heads; a.w2 = w * w; a.W = W; a.w = w; a.n_wx = n_wx; a.n_wy = H / w;
   a.radius = radius; a.rho = rho; a.W_lr = W_lr; a.P = g.P;
   a.rope_on = rope_on ? 1 : 0; a.log2_theta = l2t;
+  a.splits = g.splits; a.part0 = ws.part0; a.part1 = ws.part1; a.Tp = g.Tp;
   const int nw_hi = std::min(kBwdWaves, w * w / 32);  // w * w is 64 or a multiple of 256
 
   // dQ, then dK / dV, each over hi rows, guide rows and text rows
@@ -883,10 +974,15 @@ extern "C" int uhla_backward(const void* q, const void* k, const void* v, const 
                  dkv ? "bwd_dkv_kernel(guide)" : "bwd_dq_kernel(guide)");
     }
     if (g.T > 0) {
-      a.blocks_per_bh = static_cast<int>(g.Tp / kBwdGuideRows);
+      a.blocks_per_bh = static_cast<int>(g.Tp / kBwdGuideRows) * g.splits;
       a.total_blocks = static_cast<int>(BH * a.blocks_per_bh);
       UHLA_BSTEP(launch_both<kRowsText>(dkv, D, kBwdWaves, a, s),
                  dkv ? "bwd_dkv_kernel(text)" : "bwd_dq_kernel(text)");
+      UHLA_BSTEP(hipLaunchKernelGGL(bwd_text_combine_kernel, dim3(static_cast<unsigned>(g.T), static_cast<unsigned>(BH)),
+                                    dim3(D / 2), 0, s, ws.part0, dkv ? ws.part1 : nullptr, a.out0,
+                                    dkv ? a.out1 : nullptr, a.out_scale, g.splits, BH, g.Tp, g.T, L,
+                                    heads, D),
+                 "bwd_text_combine_kernel");
     }
   }
 #undef UHLA_BSTEP

@@ -320,12 +320,18 @@ def test_backward_rejects(lib, kw, status):
 def expected_backward_workspace(B, H, W, w, H_lr, W_lr, heads, d, T=0):
     """Independent restatement: cos/sin table, then Q, K, V, dO rows per (b, h) with hi rows,
     then guide rows and text rows each padded to 256 (bf16), then per 64-row tile 64 lse2 and
-    64 row dots (fp32); regions 256-byte aligned."""
+    64 row dots (fp32), then the text blocks' partial sums; regions 256-byte aligned."""
     al = lambda x: (x + 255) // 256 * 256
     N, M = H * W, H_lr * W_lr
     R = N + (M + 255) // 256 * 256 + (T + 255) // 256 * 256
     bh = B * heads
-    return al(16 * max(H, W) * (d // 4)) + 4 * al(bh * R * d * 2) + al(bh * R // 64 * 512)
+    # text row blocks split their tile lists: about 1024 workgroups, each >= 8 tiles long;
+    # two fp32 partial buffers [splits][B*heads][Tp][d]
+    Tp = (T + 255) // 256 * 256
+    splits = min(-(-1024 // (bh * (Tp // 256))), max(1, R // 64 // 8)) if T else 0
+    part = al(splits * bh * Tp * d * 4)
+    return (al(16 * max(H, W) * (d // 4)) + 4 * al(bh * R * d * 2) + al(bh * R // 64 * 512)
+            + 2 * part)
 
 
 @pytest.mark.parametrize("g", GEOMS)
