@@ -108,9 +108,6 @@ def bench_backward(args, g):
     import torch
     from global_attention_image_amd import api
     from global_attention_image_amd.inputs import CONFIG_SEEDS, algorithmic_pairs, make_qkv_bits
-    if g.guide_mode:
-        print("the backward covers guide mode 0", file=sys.stderr)
-        sys.exit(2)
     log(f"[bench] backward: generating seeded inputs for {g}")
     q, k, v = make_qkv_bits(g, CONFIG_SEEDS[g.name])
     do = make_qkv_bits(g, CONFIG_SEEDS[g.name] + 100)[0]
@@ -121,16 +118,16 @@ def bench_backward(args, g):
     lse = torch.empty((g.B, g.heads, g.L), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(qt), torch.empty_like(qt), torch.empty_like(qt)
     fws = api.alloc_workspace(g.B, g.H, g.W, g.w, g.H_lr, g.W_lr, g.heads, g.head_dim, dev,
-                              rho=g.rho, radius=g.radius, T=g.T)
+                              rho=g.rho, radius=g.radius, guide_mode=g.guide_mode, T=g.T)
     nb = api.backward_workspace_bytes(g.B, g.T, g.H, g.W, g.w, g.H_lr, g.W_lr, g.rho, g.heads,
-                                      g.head_dim, g.radius)
+                                      g.head_dim, g.radius, g.guide_mode)
     bws = torch.empty(nb, dtype=torch.uint8, device=dev)
     fwd = lambda: api.forward_lse(qt, kt, vt, g.H, g.W, g.w, g.H_lr, g.W_lr, rho=g.rho,
-                                  theta=g.theta, radius=g.radius, T=g.T, out=out, lse=lse,
-                                  workspace=fws)
+                                  theta=g.theta, radius=g.radius, guide_mode=g.guide_mode,
+                                  T=g.T, out=out, lse=lse, workspace=fws)
     bwd = lambda: api.backward(qt, kt, vt, out, gt, lse, g.H, g.W, g.w, g.H_lr, g.W_lr, rho=g.rho,
-                               theta=g.theta, radius=g.radius, T=g.T, dq=dq, dk=dk, dv=dv,
-                               workspace=bws)
+                               theta=g.theta, radius=g.radius, T=g.T, guide_mode=g.guide_mode,
+                               dq=dq, dk=dk, dv=dv, workspace=bws)
     for _ in range(args.warmup):
         fwd()
         bwd()
@@ -158,8 +155,8 @@ def bench_backward(args, g):
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": g.name, "B": g.B, "heads": g.heads, "head_dim": g.head_dim,
                    "grid": f"{g.H}x{g.W}", "window": g.w, "guide_grid": f"{g.H_lr}x{g.W_lr}",
-                   "rho": g.rho, "neighbourhood_radius": g.radius, "text_tokens": g.T,
-                   "parallelism": "single GPU"},
+                   "rho": g.rho, "neighbourhood_radius": g.radius, "guide_mode": g.guide_mode,
+                   "text_tokens": g.T, "parallelism": "single GPU"},
         "forward_ms": round(f_ms, 4), "backward_ms": round(b_ms, 4),
         "algorithmic_flops": {"forward": f_fl, "backward": b_fl},
         "roofline": {"kernel": "uhla_backward (all its kernels)", "bound": "mfma",

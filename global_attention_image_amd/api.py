@@ -42,7 +42,7 @@ EXPORTS = {
     "uhla_forward_lse": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int] * 10
                          + [ctypes.c_float, ctypes.c_float, ctypes.c_int, ctypes.c_int,
                             ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
-    "uhla_backward_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 11),
+    "uhla_backward_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 12),
     "uhla_backward": (ctypes.c_int, [ctypes.c_void_p] * 9 + [ctypes.c_int] * 10
                       + [ctypes.c_float, ctypes.c_float, ctypes.c_int, ctypes.c_int,
                          ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
@@ -300,15 +300,16 @@ def forward_lse(q, k, v, H, W, w, H_lr, W_lr, rho=4, scale=0.0, theta=10000.0, r
     return out, lse
 
 
-def backward_workspace_bytes(B, T, H, W, w, H_lr, W_lr, rho, heads, head_dim, radius) -> int:
+def backward_workspace_bytes(B, T, H, W, w, H_lr, W_lr, rho, heads, head_dim, radius,
+                             guide_mode=0) -> int:
     return int(load().uhla_backward_workspace_bytes(B, T, H, W, w, H_lr, W_lr, rho, heads,
-                                                    head_dim, radius))
+                                                    head_dim, radius, guide_mode))
 
 
 def backward(q, k, v, o, do, lse, H, W, w, H_lr, W_lr, rho=4, scale=0.0, theta=10000.0,
-             radius=1, T=0, dq=None, dk=None, dv=None, workspace=None):
-    """uhla_backward: (dq, dk, dv) bf16 for the output gradient do (guide mode 0; T text
-    tokens in rows 0..T-1)."""
+             radius=1, T=0, guide_mode=0, dq=None, dk=None, dv=None, workspace=None):
+    """uhla_backward: (dq, dk, dv) bf16 for the output gradient do (T text tokens in rows
+    0..T-1; radius and guide_mode as in the forward)."""
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
         _require(t, n, torch.bfloat16)
@@ -320,13 +321,14 @@ def backward(q, k, v, o, do, lse, H, W, w, H_lr, W_lr, rho=4, scale=0.0, theta=1
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
     if workspace is None:
-        n = backward_workspace_bytes(B, T, H, W, w, H_lr, W_lr, rho, Hh, d, radius)
+        n = backward_workspace_bytes(B, T, H, W, w, H_lr, W_lr, rho, Hh, d, radius, guide_mode)
         if n == 0:
             raise ValueError("invalid geometry")
         workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
     st = load().uhla_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
                               _ptr(dk), _ptr(dv), B, int(T), H, W, w, H_lr, W_lr, rho, Hh, d,
-                              float(scale), float(theta), int(radius), 0, _ptr(workspace),
+                              float(scale), float(theta), int(radius), int(guide_mode),
+                              _ptr(workspace),
                               workspace.numel(), _stream(q))
     _check(st, "uhla_backward")
     return dq, dk, dv

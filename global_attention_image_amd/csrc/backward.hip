@@ -38,17 +38,23 @@ constexpr int kBwdWaves = 8;                  // guide-row workgroups: 8 waves x
 constexpr int kBwdGuideRows = kBwdWaves * 32;
 
 struct BwdGeom {
-  int B, H, W, w, H_lr, W_lr, rho, heads, D, radius;
+  int B, H, W, w, H_lr, W_lr, rho, heads, D, radius, guide_mode;
+  int nbi, nbjp;  // guide modes 1, 2: blocks of 8x8 guide cells, block rows padded to 4 blocks
+  int64_t Mb;     // cell-block rows (nbi * nbjp * 64), 0 in guide mode 0
   int64_t T, N, M, Mp, Tp, R;  // R: rows per (b, h) = N + Mp + Tp (guide / text rows padded)
   int n_wx, n_wy, P;
   int splits;  // text row blocks: tile-range splits (0 without text tokens)
 };
 
 BwdGeom make_bwd_geom(int B, int64_t T, int H, int W, int w, int H_lr, int W_lr, int rho,
-                      int heads, int D, int radius) {
+                      int heads, int D, int radius, int guide_mode) {
   BwdGeom g;
   g.B = B; g.H = H; g.W = W; g.w = w; g.H_lr = H_lr; g.W_lr = W_lr; g.rho = rho;
-  g.heads = heads; g.D = D; g.radius = radius;
+  g.heads = heads; g.D = D; g.radius = radius; g.guide_mode = guide_mode;
+  g.nbi = (H_lr + 7) / 8;
+  g.nbjp = ((W_lr + 7) / 8 + 3) / 4 * 4;
+  g.Mb = (guide_mode != 0 && static_cast<int64_t>(H_lr) * W_lr > 0)
+             ? static_cast<int64_t>(g.nbi) * g.nbjp * kKeyTile : 0;
   g.T = T;
   g.N = static_cast<int64_t>(H) * W;
   g.M = static_cast<int64_t>(H_lr) * W_lr;
@@ -75,6 +81,7 @@ struct BwdWorkspace {
   bf16_t *qb, *kb, *vb, *dob;  // [B*heads][R][D]
   float* aux;                  // [B*heads][R/64][128]
   float *part0, *part1;        // [splits][B*heads][Tp][D] text row blocks' partial sums
+  bf16_t *kgb, *vgb;           // [B*heads][Mb][D] guide K~, V in 8x8 cell blocks (modes 1, 2)
   size_t bytes;
 };
 
@@ -94,6 +101,8 @@ BwdWorkspace carve_bwd(const BwdGeom& g, void* base) {
   const size_t o_aux = take(rows / kKeyTile * kAuxBytes);
   const size_t part = static_cast<size_t>(g.splits) * g.B * g.heads * g.Tp * g.D * sizeof(float);
   const size_t o_p0 = take(part), o_p1 = take(part);
+  const size_t cells = static_cast<size_t>(g.B) * g.heads * g.Mb * g.D * sizeof(bf16_t);
+  const size_t o_kg = take(cells), o_vg = take(cells);
   char* b = static_cast<char*>(base);
   ws.cs = reinterpret_cast<double2*>(b + o_cs);
   bf16_t** mats[4] = {&ws.qb, &ws.kb, &ws.vb, &ws.dob};
@@ -101,6 +110,8 @@ BwdWorkspace carve_bwd(const BwdGeom& g, void* base) {
   ws.aux = reinterpret_cast<float*>(b + o_aux);
   ws.part0 = reinterpret_cast<float*>(b + o_p0);
   ws.part1 = reinterpret_cast<float*>(b + o_p1);
+  ws.kgb = reinterpret_cast<bf16_t*>(b + o_kg);
+  ws.vgb = reinterpret_cast<bf16_t*>(b + o_vg);
   ws.bytes = off;
   return ws;
 }
@@ -261,8 +272,35 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_aux_kernel(
   t[kKeyTile + row % kKeyTile] = 0.0f;
 }
 
+// Guide modes 1 and 2: guide K~ and V rows copied into 8x8 cell blocks (slot s: block s/64
+// = (bi, bj) over an nbjp-wide block grid, cell (8 bi + (s%64)/8, 8 bj + s%8)), zero for
+// cells outside the guide grid.  One thread per 16-byte chunk.
+__global__ __launch_bounds__(kBwdThreads) void bwd_cellblock_kernel(
+    const bf16_t* __restrict__ kb, const bf16_t* __restrict__ vb, bf16_t* __restrict__ kgb,
+    bf16_t* __restrict__ vgb, int64_t N, int64_t R, int64_t Mb, int H_lr, int W_lr, int nbjp,
+    int D, int64_t bh_total) {
+  const int cpr = D / 8;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= bh_total * Mb * cpr) return;
+  const int64_t row = i / cpr, bh = row / Mb, slot = row - bh * Mb;
+  const int c = static_cast<int>(i - row * cpr);
+  const int blk = static_cast<int>(slot / kKeyTile), k = static_cast<int>(slot % kKeyTile);
+  const int bi = blk / nbjp, bj = blk - bi * nbjp;
+  const int ci = 8 * bi + (k >> 3), cj = 8 * bj + (k & 7);
+  uint4 kx = make_uint4(0, 0, 0, 0), vx = kx;
+  if (ci < H_lr && cj < W_lr) {
+    const int64_t src = (bh * R + N + static_cast<int64_t>(ci) * W_lr + cj) * D + c * 8;
+    kx = *reinterpret_cast<const uint4*>(kb + src);
+    vx = *reinterpret_cast<const uint4*>(vb + src);
+  }
+  const int64_t dst = (bh * Mb + slot) * D + c * 8;
+  *reinterpret_cast<uint4*>(kgb + dst) = kx;
+  *reinterpret_cast<uint4*>(vgb + dst) = vx;
+}
+
 struct BwdArgs {
   const bf16_t *qb, *kb, *vb, *dob;
+  const bf16_t *kgb, *vgb;  // guide modes 1, 2: guide K~, V in cell blocks [B*heads][Mb][D]
   const float* aux;
   const double2* cs;
   bf16_t* out0;  // dQ (dq kernel) or dK (dkv kernel), the caller's [B][L][heads][D]
@@ -276,7 +314,21 @@ struct BwdArgs {
   int splits;             // text row blocks: tile-range splits per block
   float *part0, *part1;   // text row blocks: fp32 partial sums [splits][B*heads][Tp][D]
   int64_t Tp;
+  int reach, H_lr, nbjp;  // guide modes 1, 2: a hi query sees the guide cells whose scaled
+  int64_t Mb;             // position lies in a window within `reach` of its own window
 };
+
+// Guide cells [i0, i1) x [j0, j1) visible to the queries of window (wy, wx) in guide modes
+// 1 and 2: cell (i, j) is visible when (rho i, rho j) lies in a window within `reach`.
+__device__ __forceinline__ void window_cells(const BwdArgs& A, int wy, int wx, int& i0, int& i1,
+                                             int& j0, int& j1) {
+  const int gy0 = max(0, wy - A.reach), gy1 = min(A.n_wy - 1, wy + A.reach);
+  const int gx0 = max(0, wx - A.reach), gx1 = min(A.n_wx - 1, wx + A.reach);
+  i0 = (gy0 * A.w + A.rho - 1) / A.rho;
+  i1 = min(A.H_lr, ((gy1 + 1) * A.w + A.rho - 1) / A.rho);
+  j0 = (gx0 * A.w + A.rho - 1) / A.rho;
+  j1 = min(A.W_lr, ((gx1 + 1) * A.w + A.rho - 1) / A.rho);
+}
 
 // Tile range [t0, t1) of split `split` of a list of n tiles (splits of equal length)
 __device__ __forceinline__ void split_range(int n, int splits, int split, int& t0, int& t1) {
@@ -339,16 +391,20 @@ enum { kRowsHi = 0, kRowsGuide = 1, kRowsText = 2 };
 struct TileSegs {
   int n_first, n_g, n_t;  // tiles per segment
   bool table;             // first segment from the table (else every hi tile)
+  bool g_table;           // guide segment from the table too: cell blocks (guide modes 1, 2)
   int hi_tiles, g_base, t_base;
   __device__ __forceinline__ int count() const { return n_first + n_g + n_t; }
+  __device__ __forceinline__ bool in_cells(int t) const { return g_table && t >= n_first && t < n_first + n_g; }
   __device__ __forceinline__ int index(int t, const uint32_t* tab) const {
     if (t < n_first) return table ? static_cast<int>(__builtin_amdgcn_readfirstlane(tab[t])) : t;
-    if (t < n_first + n_g) return g_base + (t - n_first);
+    if (t < n_first + n_g)
+      return g_table ? static_cast<int>(__builtin_amdgcn_readfirstlane(tab[t])) : g_base + (t - n_first);
     return t_base + (t - n_first - n_g);
   }
-  // rows of tile t that exist (guide and text segments end in partial tiles)
+  // rows of tile t that exist (guide and text segments end in partial tiles; cell blocks
+  // are masked by their cell masks)
   __device__ __forceinline__ int valid(int t, const BwdArgs& A) const {
-    if (t < n_first) return kKeyTile;
+    if (t < n_first || in_cells(t)) return kKeyTile;
     const int64_t rem = t < n_first + n_g ? A.M - static_cast<int64_t>(t - n_first) * kKeyTile
                                           : A.T - static_cast<int64_t>(t - n_first - n_g) * kKeyTile;
     return rem < kKeyTile ? static_cast<int>(rem) : kKeyTile;
@@ -363,6 +419,7 @@ __device__ __forceinline__ TileSegs make_segs(const BwdArgs& A, int kind, bool k
   s.g_base = s.hi_tiles;
   s.t_base = static_cast<int>((A.N + A.Mp) / kKeyTile);
   s.table = kind == kRowsHi;
+  s.g_table = false;
   if (kind == kRowsHi) {
     s.n_first = n_local;
     s.n_g = key_outer ? 0 : n_g;
@@ -473,9 +530,10 @@ __device__ __forceinline__ void wait_tiles(int n) {
 // tile rows from LDS, B = Q / dO held in registers), so each lane holds one query's
 // scores; dS^T converted to bf16 in place is the B operand of dQ^T += K~^T dS^T with A read
 // transposed from the same K tile.
-template <int D, int NWAVES, int KIND>
+template <int D, int NWAVES, int KIND, bool RECT>
 __global__ __launch_bounds__(NWAVES * 64) void bwd_dq_kernel(BwdArgs A) {
   constexpr bool HI = KIND == kRowsHi;
+  static_assert(!RECT || HI, "cell blocks serve hi-res queries");
   constexpr int NT = NWAVES * 64;
   constexpr int TILE = kKeyTile * D * 2;
   constexpr int CPT = TILE / 16 / NT;
@@ -485,6 +543,7 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dq_kernel(BwdArgs A) {
   constexpr int AH = kBwdStages - 1;
   __shared__ __attribute__((aligned(16))) char ring[kBwdStages * STAGE];
   __shared__ uint32_t tab[HI ? kBwdMaxTiles : 1];
+  __shared__ uint32_t tmask[RECT ? kBwdMaxTiles : 1];  // cell-block tiles: row / column masks
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ql = lane & 31, g = lane >> 5;
@@ -494,20 +553,51 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dq_kernel(BwdArgs A) {
   const int split = KIND == kRowsText ? rem_blk - qb * A.splits : 0;
   const int b = bh / A.heads, h = bh - b * A.heads;
   const int64_t r0 = block_row0(A, KIND, qb, NWAVES * 32);
-  int n_local = 0;
+  int n_local = 0, n_rect = 0;
   if (HI) {
     n_local = build_local_table<NT>(A, static_cast<int>(r0), tab);
+    if (RECT) {
+      // the 8x8 cell blocks that meet the window's visible guide cells, with row / column
+      // masks (bits 0-7 the block's cell rows, bits 8-15 its columns)
+      const int win = static_cast<int>(r0 / A.w2), wy = win / A.n_wx, wx = win - wy * A.n_wx;
+      int i0, i1, j0, j1;
+      window_cells(A, wy, wx, i0, i1, j0, j1);
+      if (i0 < i1 && j0 < j1) {
+        const int bi0 = i0 >> 3, bj0 = j0 >> 3, nbx = ((j1 - 1) >> 3) - bj0 + 1;
+        n_rect = (((i1 - 1) >> 3) - bi0 + 1) * nbx;
+        for (int k = threadIdx.x; k < n_rect; k += NT) {
+          const int ky = k / nbx, bi = bi0 + ky, bj = bj0 + (k - ky * nbx);
+          uint32_t rows = 0, cols = 0;
+          for (int e = 0; e < 8; ++e) {
+            rows |= static_cast<uint32_t>(8 * bi + e >= i0 && 8 * bi + e < i1) << e;
+            cols |= static_cast<uint32_t>(8 * bj + e >= j0 && 8 * bj + e < j1) << e;
+          }
+          tab[n_local + k] = static_cast<uint32_t>(bi * A.nbjp + bj);
+          tmask[n_local + k] = rows | (cols << 8);
+        }
+      }
+    }
     __syncthreads();
   }
-  const TileSegs segs = make_segs(A, KIND, false, n_local);
+  TileSegs segs = make_segs(A, KIND, false, n_local);
+  if (RECT) {
+    segs.n_g = n_rect;
+    segs.g_table = true;
+  }
   int t_first = 0, t_end = segs.count();
   if (KIND == kRowsText) split_range(segs.count(), A.splits, split, t_first, t_end);
   const int n_tiles = t_end - t_first;  // this workgroup's tiles t_first + [0, n_tiles)
   const int64_t mat = static_cast<int64_t>(bh) * A.R * D * 2;
   const char* kbase = reinterpret_cast<const char*>(A.kb) + mat;
   const char* vbase = reinterpret_cast<const char*>(A.vb) + mat;
+  const int64_t cmat = static_cast<int64_t>(bh) * A.Mb * D * 2;
+  const char* kgbase = reinterpret_cast<const char*>(A.kgb) + cmat;
+  const char* vgbase = reinterpret_cast<const char*>(A.vgb) + cmat;
   auto tile_index = [&](int t) -> int { return segs.index(t_first + t, tab); };
   auto tile_valid = [&](int t) -> int { return segs.valid(t_first + t, A); };
+  auto tile_cells = [&](int t) -> uint32_t {
+    return RECT && segs.in_cells(t_first + t) ? __builtin_amdgcn_readfirstlane(tmask[t_first + t]) : 0xffffu;
+  };
   int k_src[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
@@ -517,12 +607,15 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dq_kernel(BwdArgs A) {
   }
   auto issue = [&](int t) {
     const int64_t off = static_cast<int64_t>(tile_index(t)) * TILE;
+    const bool cellt = RECT && segs.in_cells(t_first + t);
+    const char* ks = (cellt ? kgbase : kbase) + off;
+    const char* vs = (cellt ? vgbase : vbase) + off;
     const uint32_t base = lds_addr(ring + (t & (kBwdStages - 1)) * STAGE);
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const uint32_t o = __builtin_amdgcn_readfirstlane(base + (i * NWAVES + wave) * 64 * 16);
-      dma_16b(kbase + off, k_src[i], o);
-      dma_16b(vbase + off, k_src[i], o + TILE);
+      dma_16b(ks, k_src[i], o);
+      dma_16b(vs, k_src[i], o + TILE);
     }
   };
 
@@ -577,12 +670,19 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dq_kernel(BwdArgs A) {
       p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(vt_, kk, 1), gf[kk], p1, 0, 0, 0);
     }
     const int valid = tile_valid(t);
+    // cell-block tiles: key k is cell (k / 8, k % 8) of the block, i.e. row r/4 (+4 in the
+    // second half) and column 4g + r%4
+    const uint32_t cells = tile_cells(t);
+    const uint32_t colm = (cells >> (8 + 4 * g)) & 15u;
     bf16x8 dsb[4];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = 8 * (r >> 2) + 4 * g + (r & 3);
-      const float a0 = key < valid ? __builtin_amdgcn_exp2f(s0[r] - lse2) : 0.0f;
-      const float a1 = key + 32 < valid ? __builtin_amdgcn_exp2f(s1[r] - lse2) : 0.0f;
+      const bool c_ok = (colm >> (r & 3)) & 1u;
+      const bool v0 = key < valid && c_ok && ((cells >> (r >> 2)) & 1u);
+      const bool v1 = key + 32 < valid && c_ok && ((cells >> (4 + (r >> 2))) & 1u);
+      const float a0 = v0 ? __builtin_amdgcn_exp2f(s0[r] - lse2) : 0.0f;
+      const float a1 = v1 ? __builtin_amdgcn_exp2f(s1[r] - lse2) : 0.0f;
       dsb[r >> 3][r & 7] = static_cast<__bf16>(a0 * (p0[r] - dd));
       dsb[2 + (r >> 3)][r & 7] = static_cast<__bf16>(a1 * (p1[r] - dd));
     }
@@ -630,9 +730,11 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dq_kernel(BwdArgs A) {
 // dP = dO V^T (A = Q / dO tile rows from LDS, B = K / V held in registers), so a lane holds
 // one key's scores for 16 queries; P and dS converted to bf16 in place are the B operands
 // of dV^T += dO^T P and dK^T += Q^T dS with A read transposed from the same dO / Q tiles.
-template <int D, int NWAVES, int KIND>
+template <int D, int NWAVES, int KIND, bool RECT>
 __global__ __launch_bounds__(NWAVES * 64) void bwd_dkv_kernel(BwdArgs A) {
   constexpr bool HI = KIND == kRowsHi;
+  // RECT: guide keys of guide modes 1 and 2, in cell-block order (slot = block * 64 + cell)
+  static_assert(!RECT || KIND == kRowsGuide, "cell blocks order guide keys");
   constexpr int NT = NWAVES * 64;
   constexpr int TILE = kKeyTile * D * 2;
   constexpr int CPT = TILE / 16 / NT;
@@ -643,7 +745,7 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dkv_kernel(BwdArgs A) {
   constexpr int AH = kBwdStages - 1;
   static_assert(AUX_LANES >= 1 && AUX_LANES * 16 * NWAVES == kAuxBytes, "aux split");
   __shared__ __attribute__((aligned(16))) char ring[kBwdStages * STAGE];
-  __shared__ uint32_t tab[HI ? kBwdMaxTiles : 1];
+  __shared__ uint32_t tab[HI || RECT ? kBwdMaxTiles : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ql = lane & 31, g = lane >> 5;
@@ -652,13 +754,39 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dkv_kernel(BwdArgs A) {
   const int kb_ = KIND == kRowsText ? rem_blk / A.splits : rem_blk;
   const int split = KIND == kRowsText ? rem_blk - kb_ * A.splits : 0;
   const int b = bh / A.heads, h = bh - b * A.heads;
-  const int64_t r0 = block_row0(A, KIND, kb_, NWAVES * 32);
+  // RECT: r0 is the first cell-block slot of the workgroup (4 blocks of one block row)
+  const int64_t r0 = RECT ? static_cast<int64_t>(kb_) * NWAVES * 32 : block_row0(A, KIND, kb_, NWAVES * 32);
   int n_local = 0;
   if (HI) {
     n_local = build_local_table<NT>(A, static_cast<int>(r0), tab);
     __syncthreads();
   }
-  const TileSegs segs = make_segs(A, KIND, true, n_local);
+  if (RECT) {
+    // query tiles of the windows that see any cell of the workgroup's blocks: the window
+    // holding a visible cell's scaled position, widened by `reach` (a bounding box; the
+    // per-key masks below drop the pairs it over-covers)
+    const int blk0 = static_cast<int>(r0 / kKeyTile), bi = blk0 / A.nbjp, bj0 = blk0 - bi * A.nbjp;
+    const int ci0 = 8 * bi, cj0 = 8 * bj0;
+    const int ci1 = min(min(8 * bi + 7, A.H_lr - 1), (A.n_wy * A.w - 1) / A.rho);
+    const int cj1 = min(min(8 * bj0 + 31, A.W_lr - 1), (A.n_wx * A.w - 1) / A.rho);
+    if (ci0 <= ci1 && cj0 <= cj1) {
+      const int y0 = max(0, A.rho * ci0 / A.w - A.reach), y1 = min(A.n_wy - 1, A.rho * ci1 / A.w + A.reach);
+      const int x0 = max(0, A.rho * cj0 / A.w - A.reach), x1 = min(A.n_wx - 1, A.rho * cj1 / A.w + A.reach);
+      const int tpw = A.w2 / kKeyTile, nx = x1 - x0 + 1;
+      n_local = (y1 - y0 + 1) * nx * tpw;
+      for (int i = threadIdx.x; i < n_local; i += NT) {
+        const int j = i / tpw, sub = i - j * tpw;
+        const int jy = j / nx, nw = (y0 + jy) * A.n_wx + x0 + (j - jy * nx);
+        tab[i] = static_cast<uint32_t>(nw * tpw + sub);
+      }
+    }
+    __syncthreads();
+  }
+  TileSegs segs = make_segs(A, KIND, true, n_local);
+  if (RECT) {
+    segs.n_first = n_local;
+    segs.table = true;
+  }
   int t_first = 0, t_end = segs.count();
   if (KIND == kRowsText) split_range(segs.count(), A.splits, split, t_first, t_end);
   const int n_tiles = t_end - t_first;  // this workgroup's tiles t_first + [0, n_tiles)
@@ -692,11 +820,20 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dkv_kernel(BwdArgs A) {
   };
 
   // key fragments (B operands): K~ and V rows of this lane's key
-  const int64_t krow = r0 + wave * 32 + ql;
+  const int64_t krow = r0 + wave * 32 + ql;  // RECT: cell-block slot
+  int kci = 0, kcj = 0;                        // RECT: the key's guide cell
+  if (RECT) {
+    const int cb = static_cast<int>(krow / kKeyTile), cc = static_cast<int>(krow % kKeyTile);
+    const int bi = cb / A.nbjp;
+    kci = 8 * bi + (cc >> 3);
+    kcj = 8 * (cb - bi * A.nbjp) + (cc & 7);
+  }
   bf16x8 kf[D / 16], vf[D / 16];
   {
-    const bf16_t* kp = A.kb + (static_cast<int64_t>(bh) * A.R + krow) * D;
-    const bf16_t* vp = A.vb + (static_cast<int64_t>(bh) * A.R + krow) * D;
+    const bf16_t* kp = RECT ? A.kgb + (static_cast<int64_t>(bh) * A.Mb + krow) * D
+                            : A.kb + (static_cast<int64_t>(bh) * A.R + krow) * D;
+    const bf16_t* vp = RECT ? A.vgb + (static_cast<int64_t>(bh) * A.Mb + krow) * D
+                            : A.vb + (static_cast<int64_t>(bh) * A.R + krow) * D;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       kf[kk] = *reinterpret_cast<const bf16x8*>(kp + 16 * kk + 8 * g);
@@ -732,6 +869,15 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dkv_kernel(BwdArgs A) {
     const char* qt_ = ring + (t & (kBwdStages - 1)) * STAGE;
     const char* gt_ = qt_ + TILE;
     const float* aux = reinterpret_cast<const float*>(qt_ + 2 * TILE);
+    // RECT: hi query tiles (first segment) see this lane's key only if the tile's window
+    // sees its cell; guide and text queries see every guide key
+    bool kvis = true;
+    if (RECT && t_first + t < segs.n_first) {
+      const int win = tile_index(t) / (A.w2 / kKeyTile), wy = win / A.n_wx, wx = win - wy * A.n_wx;
+      int i0, i1, j0, j1;
+      window_cells(A, wy, wx, i0, i1, j0, j1);
+      kvis = kci >= i0 && kci < i1 && kcj >= j0 && kcj < j1;
+    }
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       f32x16 s = {}, p = {};
@@ -750,7 +896,7 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dkv_kernel(BwdArgs A) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * rq + e;
-          const float pr = __builtin_amdgcn_exp2f(s[r] - l4[e]);
+          const float pr = kvis ? __builtin_amdgcn_exp2f(s[r] - l4[e]) : 0.0f;
           pb[r >> 3][r & 7] = static_cast<__bf16>(pr);
           db[r >> 3][r & 7] = static_cast<__bf16>(pr * (p[r] - d4[e]));
         }
@@ -783,9 +929,17 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dkv_kernel(BwdArgs A) {
       }
     return;
   }
-  if (!row_exists(A, KIND, krow)) return;
   int py, px;
-  const int64_t rr = raster_row(krow, A, py, px);
+  int64_t rr;
+  if (RECT) {
+    if (kci >= A.H_lr || kcj >= A.W_lr) return;
+    py = A.rho * kci;
+    px = A.rho * kcj;
+    rr = A.T + A.N + static_cast<int64_t>(kci) * A.W_lr + kcj;
+  } else {
+    if (!row_exists(A, KIND, krow)) return;
+    rr = raster_row(krow, A, py, px);
+  }
   const int64_t ro = ((static_cast<int64_t>(b) * A.L + rr) * A.heads + h) * D;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
@@ -806,6 +960,39 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dkv_kernel(BwdArgs A) {
 
 namespace {
 
+// Largest LDS tile tables of guide modes 1 and 2 (mirrors the kernels' constructions): per
+// window its neighbour tiles plus the cell blocks of its visible cells (dQ), and per
+// workgroup of 4 cell blocks the tiles of the windows that can see them (dK/dV).
+int64_t max_rect_tables(const BwdGeom& g) {
+  const int tpw = g.w * g.w / kKeyTile, n_wy = g.H / g.w, n_wx = g.W / g.w;
+  const int reach = g.guide_mode == 1 ? 0 : g.radius;
+  auto span = [](int c, int r, int n) { return std::min(n - 1, c + r) - std::max(0, c - r) + 1; };
+  int64_t best = 0;
+  for (int wy = 0; wy < n_wy; ++wy)
+    for (int wx = 0; wx < n_wx; ++wx) {
+      int64_t n = static_cast<int64_t>(span(wy, g.radius, n_wy)) * span(wx, g.radius, n_wx) * tpw;
+      const int gy0 = std::max(0, wy - reach), gy1 = std::min(n_wy - 1, wy + reach);
+      const int gx0 = std::max(0, wx - reach), gx1 = std::min(n_wx - 1, wx + reach);
+      const int i0 = (gy0 * g.w + g.rho - 1) / g.rho, i1 = std::min(g.H_lr, ((gy1 + 1) * g.w + g.rho - 1) / g.rho);
+      const int j0 = (gx0 * g.w + g.rho - 1) / g.rho, j1 = std::min(g.W_lr, ((gx1 + 1) * g.w + g.rho - 1) / g.rho);
+      if (i0 < i1 && j0 < j1)
+        n += static_cast<int64_t>(((i1 - 1) >> 3) - (i0 >> 3) + 1) * (((j1 - 1) >> 3) - (j0 >> 3) + 1);
+      best = std::max(best, n);
+    }
+  for (int bi = 0; bi < g.nbi; ++bi)
+    for (int bj0 = 0; bj0 < g.nbjp; bj0 += 4) {
+      const int ci0 = 8 * bi, cj0 = 8 * bj0;
+      const int ci1 = std::min(std::min(8 * bi + 7, g.H_lr - 1), (n_wy * g.w - 1) / g.rho);
+      const int cj1 = std::min(std::min(8 * bj0 + 31, g.W_lr - 1), (n_wx * g.w - 1) / g.rho);
+      if (ci0 > ci1 || cj0 > cj1) continue;
+      const int y0 = std::max(0, g.rho * ci0 / g.w - reach), y1 = std::min(n_wy - 1, g.rho * ci1 / g.w + reach);
+      const int x0 = std::max(0, g.rho * cj0 / g.w - reach), x1 = std::min(n_wx - 1, g.rho * cj1 / g.w + reach);
+      best = std::max<int64_t>(best, static_cast<int64_t>(y1 - y0 + 1) * (x1 - x0 + 1) * tpw);
+    }
+  return best;
+}
+
+
 int validate_backward(const void* const* ptrs, int n_ptrs, int B, int T, int H, int W, int w,
                       int H_lr, int W_lr, int rho, int heads, int D, int radius, int guide_mode) {
   for (int i = 0; i < n_ptrs; ++i) {
@@ -819,7 +1006,6 @@ int validate_backward(const void* const* ptrs, int n_ptrs, int B, int T, int H, 
   if (static_cast<int64_t>(H_lr) * W_lr > 0 && rho < 1) return fail_arg("rho must be >= 1 with guide tokens");
   if (radius < 0) return fail_arg("radius must be >= 0");
   if (guide_mode < 0 || guide_mode > 2) return fail_arg("guide_mode must be 0, 1 or 2");
-  if (guide_mode != 0) return fail_unsupported("the backward covers guide mode 0");
   if (D != 64 && D != 128) return fail_unsupported("head_dim must be 64 or 128");
   if (w % 8 || (w > 16 && w % 16)) return fail_unsupported("window size must be 8, 16 or a multiple of 16");
   if (B > 65535) return fail_unsupported("batch too large");
@@ -831,29 +1017,40 @@ int validate_backward(const void* const* ptrs, int n_ptrs, int B, int T, int H, 
   const int64_t tiles = static_cast<int64_t>(std::min(2 * r + 1, H / w)) * std::min(2 * r + 1, W / w) *
                         (w * w / kKeyTile);
   if (tiles > kBwdMaxTiles) return fail_unsupported("too many key tiles per window");
+  if (guide_mode != 0 && M > 0 &&
+      max_rect_tables(make_bwd_geom(B, T, H, W, w, H_lr, W_lr, rho, heads, D, r, guide_mode)) > kBwdMaxTiles)
+    return fail_unsupported("too many tiles per window or cell-block group");
   return UHLA_OK;
 }
 
-template <int D, int KIND>
+// RECT (guide modes 1, 2) selects the cell-block variants: dQ of hi rows, dK/dV of guide rows
+template <int D, int KIND, bool RECT>
 void launch_dq(int nwaves, const BwdArgs& a, hipStream_t s) {
+  constexpr bool R = RECT && KIND == kRowsHi;
   if (KIND != kRowsHi || nwaves == kBwdWaves)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, kBwdWaves, KIND>), dim3(a.total_blocks), dim3(kBwdWaves * 64), 0, s, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, kBwdWaves, KIND, R>), dim3(a.total_blocks), dim3(kBwdWaves * 64), 0, s, a);
   else
-    hipLaunchKernelGGL((bwd_dq_kernel<D, 2, kRowsHi>), dim3(a.total_blocks), dim3(128), 0, s, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, 2, kRowsHi, R>), dim3(a.total_blocks), dim3(128), 0, s, a);
 }
 
-template <int D, int KIND>
+template <int D, int KIND, bool RECT>
 void launch_dkv(int nwaves, const BwdArgs& a, hipStream_t s) {
+  constexpr bool R = RECT && KIND == kRowsGuide;
   if (KIND != kRowsHi || nwaves == kBwdWaves)
-    hipLaunchKernelGGL((bwd_dkv_kernel<D, kBwdWaves, KIND>), dim3(a.total_blocks), dim3(kBwdWaves * 64), 0, s, a);
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, kBwdWaves, KIND, R>), dim3(a.total_blocks), dim3(kBwdWaves * 64), 0, s, a);
   else
-    hipLaunchKernelGGL((bwd_dkv_kernel<D, 2, kRowsHi>), dim3(a.total_blocks), dim3(128), 0, s, a);
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, 2, kRowsHi, false>), dim3(a.total_blocks), dim3(128), 0, s, a);
 }
 
 template <int KIND>
-void launch_both(bool dkv, int D, int nwaves, const BwdArgs& a, hipStream_t s) {
-  if (dkv) D == 128 ? launch_dkv<128, KIND>(nwaves, a, s) : launch_dkv<64, KIND>(nwaves, a, s);
-  else D == 128 ? launch_dq<128, KIND>(nwaves, a, s) : launch_dq<64, KIND>(nwaves, a, s);
+void launch_both(bool dkv, bool rect, int D, int nwaves, const BwdArgs& a, hipStream_t s) {
+  if (rect) {
+    if (dkv) D == 128 ? launch_dkv<128, KIND, true>(nwaves, a, s) : launch_dkv<64, KIND, true>(nwaves, a, s);
+    else D == 128 ? launch_dq<128, KIND, true>(nwaves, a, s) : launch_dq<64, KIND, true>(nwaves, a, s);
+  } else {
+    if (dkv) D == 128 ? launch_dkv<128, KIND, false>(nwaves, a, s) : launch_dkv<64, KIND, false>(nwaves, a, s);
+    else D == 128 ? launch_dq<128, KIND, false>(nwaves, a, s) : launch_dq<64, KIND, false>(nwaves, a, s);
+  }
 }
 
 }  // namespace
@@ -862,13 +1059,15 @@ void launch_both(bool dkv, int D, int nwaves, const BwdArgs& a, hipStream_t s) {
 
 extern "C" size_t uhla_backward_workspace_bytes(int B, int T, int H, int W, int w, int H_lr,
                                                 int W_lr, int rho, int heads, int head_dim,
-                                                int radius) {
-  if (B < 1 || T < 0 || H < 1 || W < 1 || w < 1 || heads < 1 || H_lr < 0 || W_lr < 0 || radius < 0)
+                                                int radius, int guide_mode) {
+  if (B < 1 || T < 0 || H < 1 || W < 1 || w < 1 || heads < 1 || H_lr < 0 || W_lr < 0 || radius < 0 ||
+      guide_mode < 0 || guide_mode > 2)
     return 0;
   if (H % w || W % w || (H_lr == 0) != (W_lr == 0)) return 0;
   if (head_dim != 64 && head_dim != 128) return 0;
   if (static_cast<int64_t>(H_lr) * W_lr > 0 && rho < 1) return 0;
-  return uhla::carve_bwd(uhla::make_bwd_geom(B, T, H, W, w, H_lr, W_lr, rho, heads, head_dim, radius),
+  return uhla::carve_bwd(uhla::make_bwd_geom(B, T, H, W, w, H_lr, W_lr, rho, heads, head_dim, radius,
+                                             guide_mode),
                          nullptr).bytes;
 }
 
@@ -885,7 +1084,8 @@ extern "C" int uhla_backward(const void* q, const void* k, const void* v, const 
   if (st) return st;
   radius = std::min(radius, H / w + W / w);
   const int D = head_dim;
-  const BwdGeom g = make_bwd_geom(B, T, H, W, w, H_lr, W_lr, rho, heads, D, radius);
+  const BwdGeom g = make_bwd_geom(B, T, H, W, w, H_lr, W_lr, rho, heads, D, radius, guide_mode);
+  const bool rect = g.Mb > 0;
   const BwdWorkspace need = carve_bwd(g, nullptr);
   if (!workspace || workspace_bytes < need.bytes)
     return (set_detail("workspace too small"), UHLA_ERR_WORKSPACE);
@@ -946,6 +1146,13 @@ extern "C" int uhla_backward(const void* q, const void* k, const void* v, const 
                                   dim3(kBwdThreads), 0, s, static_cast<const bf16_t*>(o), gp, lse,
                                   ws.aux, g.T, g.N, g.M, g.Mp, g.R, W, w, n_wx, heads, D, BH),
                "bwd_aux_kernel");
+    if (rect) {
+      const int64_t n = BH * g.Mb * (D / 8);
+      UHLA_BSTEP(hipLaunchKernelGGL(bwd_cellblock_kernel, dim3(static_cast<unsigned>((n + kBwdThreads - 1) / kBwdThreads)),
+                                    dim3(kBwdThreads), 0, s, ws.kb, ws.vb, ws.kgb, ws.vgb, g.N, g.R, g.Mb,
+                                    H_lr, W_lr, g.nbjp, D, BH),
+                 "bwd_cellblock_kernel");
+    }
   }
 
   BwdArgs a{};
@@ -956,6 +1163,8 @@ extern "C" int uhla_backward(const void* q, const void* k, const void* v, const 
   a.radius = radius; a.rho = rho; a.W_lr = W_lr; a.P = g.P;
   a.rope_on = rope_on ? 1 : 0; a.log2_theta = l2t;
   a.splits = g.splits; a.part0 = ws.part0; a.part1 = ws.part1; a.Tp = g.Tp;
+  a.kgb = ws.kgb; a.vgb = ws.vgb; a.Mb = g.Mb; a.nbjp = g.nbjp; a.H_lr = H_lr;
+  a.reach = guide_mode == 1 ? 0 : radius;
   const int nw_hi = std::min(kBwdWaves, w * w / 32);  // w * w is 64 or a multiple of 256
 
   // dQ, then dK / dV, each over hi rows, guide rows and text rows
@@ -966,17 +1175,18 @@ extern "C" int uhla_backward(const void* q, const void* k, const void* v, const 
     a.out_scale = dkv ? 0.69314718055994531f : sc;
     a.blocks_per_bh = static_cast<int>(g.N / (nw_hi * 32));
     a.total_blocks = static_cast<int>(BH * a.blocks_per_bh);
-    UHLA_BSTEP(launch_both<kRowsHi>(dkv, D, nw_hi, a, s), dkv ? "bwd_dkv_kernel(hi)" : "bwd_dq_kernel(hi)");
+    UHLA_BSTEP(launch_both<kRowsHi>(dkv, rect, D, nw_hi, a, s), dkv ? "bwd_dkv_kernel(hi)" : "bwd_dq_kernel(hi)");
     if (g.M > 0) {
-      a.blocks_per_bh = static_cast<int>(g.Mp / kBwdGuideRows);
+      // guide keys of modes 1, 2 are processed in cell-block order
+      a.blocks_per_bh = static_cast<int>((dkv && rect ? g.Mb : g.Mp) / kBwdGuideRows);
       a.total_blocks = static_cast<int>(BH * a.blocks_per_bh);
-      UHLA_BSTEP(launch_both<kRowsGuide>(dkv, D, kBwdWaves, a, s),
+      UHLA_BSTEP(launch_both<kRowsGuide>(dkv, rect, D, kBwdWaves, a, s),
                  dkv ? "bwd_dkv_kernel(guide)" : "bwd_dq_kernel(guide)");
     }
     if (g.T > 0) {
       a.blocks_per_bh = static_cast<int>(g.Tp / kBwdGuideRows) * g.splits;
       a.total_blocks = static_cast<int>(BH * a.blocks_per_bh);
-      UHLA_BSTEP(launch_both<kRowsText>(dkv, D, kBwdWaves, a, s),
+      UHLA_BSTEP(launch_both<kRowsText>(dkv, rect, D, kBwdWaves, a, s),
                  dkv ? "bwd_dkv_kernel(text)" : "bwd_dq_kernel(text)");
       UHLA_BSTEP(hipLaunchKernelGGL(bwd_text_combine_kernel, dim3(static_cast<unsigned>(g.T), static_cast<unsigned>(BH)),
                                     dim3(D / 2), 0, s, ws.part0, dkv ? ws.part1 : nullptr, a.out0,

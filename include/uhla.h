@@ -193,7 +193,7 @@ int uhla_forward_text(const void* q, const void* k, const void* v, void* o,
  *   UHLA_ERR_ARG for a null or misaligned lse or one overlapping O or the workspace.
  *
  * uhla_backward: gradients dQ, dK, dV (bf16, layout of Q) of O = uhla_forward_text(Q, K,
- *   V; T, radius, guide_mode 0) (T = 0: uhla_forward_masked) for the output gradient dO,
+ *   V; T, radius, guide_mode) (T = 0: uhla_forward_masked) for the output gradient dO,
  *   given O and the lse written by uhla_forward_lse for the same inputs.  Q, K, V, O, dO:
  *   bf16 [B, T + N + M, heads, head_dim], text rows first.  Per (batch, head), with rotated
  *   Q~, K~ and P = exp(scale Q~ K~^T - lse) on the allowed pairs: dV = P^T dO,
@@ -204,8 +204,9 @@ int uhla_forward_text(const void* q, const void* k, const void* v, void* o,
  *   workspace: at least uhla_backward_workspace_bytes(...) bytes, 256-byte aligned.
  *   Errors: UHLA_ERR_ARG (null or misaligned pointers, sizes < 1, T < 0, w not dividing H
  *   or W, radius < 0, guide_mode outside 0..2, gradients overlapping an input, lse, the
- *   workspace or each other); UHLA_ERR_UNSUPPORTED (guide_mode 1 or 2, head_dim not in
- *   {64, 128}, w as in uhla_forward, more than 1024 key tiles per window, T > 2^24);
+ *   workspace or each other); UHLA_ERR_UNSUPPORTED (head_dim not in {64, 128}, w as in
+ *   uhla_forward, more than 1024 key tiles per window or, in guide modes 1 and 2, more
+ *   than 1024 tiles in a window's or a cell-block group's tile list, T > 2^24);
  *   UHLA_ERR_WORKSPACE; UHLA_ERR_HIP.
  */
 int uhla_forward_lse(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -213,7 +214,8 @@ int uhla_forward_lse(const void* q, const void* k, const void* v, void* o, float
                      int heads, int head_dim, float scale, float theta, int radius,
                      int guide_mode, void* workspace, size_t workspace_bytes, void* stream);
 size_t uhla_backward_workspace_bytes(int B, int T, int H, int W, int w, int H_lr, int W_lr,
-                                     int rho, int heads, int head_dim, int radius);
+                                     int rho, int heads, int head_dim, int radius,
+                                     int guide_mode);
 int uhla_backward(const void* q, const void* k, const void* v, const void* o,
                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
                   int B, int T, int H, int W, int w, int H_lr, int W_lr, int rho, int heads,

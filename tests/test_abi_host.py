@@ -300,7 +300,8 @@ def bwd_args(**kw):
     (dict(radius=-1), api.UHLA_ERR_ARG),
     (dict(T=-1), api.UHLA_ERR_ARG),
     (dict(mode=3), api.UHLA_ERR_ARG),
-    (dict(mode=1), api.UHLA_ERR_UNSUPPORTED),
+    # modes 1 / 2: 3x3 windows of 96x96 tokens exceed the tile tables here too
+    (dict(mode=2, H=384, W=384, w=96, H_lr=96, W_lr=96), api.UHLA_ERR_UNSUPPORTED),
     (dict(T=1 << 25), api.UHLA_ERR_UNSUPPORTED),
     (dict(d=96), api.UHLA_ERR_UNSUPPORTED),
     (dict(H=36, W=36, w=4), api.UHLA_ERR_UNSUPPORTED),
@@ -317,7 +318,7 @@ def test_backward_rejects(lib, kw, status):
     assert lib.uhla_backward(*bwd_args(**kw)) == status
 
 
-def expected_backward_workspace(B, H, W, w, H_lr, W_lr, heads, d, T=0):
+def expected_backward_workspace(B, H, W, w, H_lr, W_lr, heads, d, T=0, guide_mode=0):
     """Independent restatement: cos/sin table, then Q, K, V, dO rows per (b, h) with hi rows,
     then guide rows and text rows each padded to 256 (bf16), then per 64-row tile 64 lse2 and
     64 row dots (fp32), then the text blocks' partial sums; regions 256-byte aligned."""
@@ -330,16 +331,22 @@ def expected_backward_workspace(B, H, W, w, H_lr, W_lr, heads, d, T=0):
     Tp = (T + 255) // 256 * 256
     splits = min(-(-1024 // (bh * (Tp // 256))), max(1, R // 64 // 8)) if T else 0
     part = al(splits * bh * Tp * d * 4)
+    # guide modes 1 / 2: guide K and V again in 8x8 cell blocks, block rows padded to 4 blocks
+    nbjp = -(-(-(-W_lr // 8)) // 4) * 4
+    mb = (-(-H_lr // 8)) * nbjp * 64 if (guide_mode and M) else 0
+    cells = al(bh * mb * d * 2)
     return (al(16 * max(H, W) * (d // 4)) + 4 * al(bh * R * d * 2) + al(bh * R // 64 * 512)
-            + 2 * part)
+            + 2 * part + 2 * cells)
 
 
 @pytest.mark.parametrize("g", GEOMS)
-@pytest.mark.parametrize("T", [0, 1, 300])
-def test_backward_workspace_bytes(lib, g, T):
+@pytest.mark.parametrize("T,mode", [(0, 0), (1, 0), (300, 0), (0, 1), (77, 2)])
+def test_backward_workspace_bytes(lib, g, T, mode):
     B, H, W, w, H_lr, W_lr, heads, d = g
-    got = lib.uhla_backward_workspace_bytes(B, T, H, W, w, H_lr, W_lr, 4, heads, d, 1)
-    assert got == expected_backward_workspace(*g, T=T)
-    assert lib.uhla_backward_workspace_bytes(B, T, H, W, w, H_lr, W_lr, 4, heads, d, -1) == 0
-    assert lib.uhla_backward_workspace_bytes(B, T, H, W, w, H_lr, W_lr, 4, heads, 96, 1) == 0
-    assert lib.uhla_backward_workspace_bytes(B, -1, H, W, w, H_lr, W_lr, 4, heads, d, 1) == 0
+    f = lib.uhla_backward_workspace_bytes
+    assert f(B, T, H, W, w, H_lr, W_lr, 4, heads, d, 1, mode) == \
+        expected_backward_workspace(*g, T=T, guide_mode=mode)
+    assert f(B, T, H, W, w, H_lr, W_lr, 4, heads, d, -1, mode) == 0
+    assert f(B, T, H, W, w, H_lr, W_lr, 4, heads, 96, 1, mode) == 0
+    assert f(B, -1, H, W, w, H_lr, W_lr, 4, heads, d, 1, mode) == 0
+    assert f(B, T, H, W, w, H_lr, W_lr, 4, heads, d, 1, 3) == 0

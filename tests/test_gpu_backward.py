@@ -9,9 +9,10 @@ sums they enter have random signs, so the errors stay a small multiple of 2^-9 o
 gradient's scale.
 * every row / every key at small sizes: both head dims, window sizes 8, 16 and 32, radius
   0 / 1 / 2, ragged guide grids, guide positions past the hi grid, no guide tokens, RoPE off,
-  text tokens (ragged, several tiles, without guide tokens);
-* sampled query and key rows at the 2K workload, without and with 512 text tokens (oracle
-  rows of the backward);
+  text tokens (ragged, several tiles, without guide tokens), guide modes 1 and 2 (rho not
+  dividing w, guide cells past the hi grid, radius 2, windows of 8, with text);
+* sampled query and key rows at the 2K workload, without and with 512 text tokens and in
+  guide modes 1 and 2 (oracle rows of the backward);
 * the 8K workload: sampled dQ rows against the oracle and the dV sum rule over all keys;
 * determinism.
 """
@@ -31,9 +32,9 @@ def run_fwd_bwd(g, q, k, v, do):
     import torch
     qt, kt, vt, gt = to_dev(q), to_dev(k), to_dev(v), to_dev(do)
     o, lse = api.forward_lse(qt, kt, vt, g.H, g.W, g.w, g.H_lr, g.W_lr, rho=g.rho, theta=g.theta,
-                             radius=g.radius, T=g.T)
+                             radius=g.radius, guide_mode=g.guide_mode, T=g.T)
     dq, dk, dv = api.backward(qt, kt, vt, o, gt, lse, g.H, g.W, g.w, g.H_lr, g.W_lr, rho=g.rho,
-                              theta=g.theta, radius=g.radius, T=g.T)
+                              theta=g.theta, radius=g.radius, T=g.T, guide_mode=g.guide_mode)
     torch.cuda.synchronize()
     return lse.cpu().numpy().astype(np.float64), from_dev(dq), from_dev(dk), from_dev(dv)
 
@@ -68,6 +69,16 @@ CASES = {
                                 radius=0, T=300),
     "d64_text_w8_no_guide": Geometry(B=2, heads=1, head_dim=64, H=32, W=32, w=8, H_lr=0, W_lr=0,
                                      T=64),
+    # guide modes 1 / 2 (a hi query sees the guide cells of its window / neighbourhood):
+    # rho not dividing w, guide cells past the hi grid, radius 2, windows of 8, text
+    "d128_mode1": Geometry(B=1, heads=2, head_dim=128, H=48, W=64, w=16, H_lr=12, W_lr=16,
+                           guide_mode=1),
+    "d64_mode2_rho3": Geometry(B=1, heads=1, head_dim=64, H=48, W=48, w=16, H_lr=14, W_lr=13,
+                               rho=3, guide_mode=2),
+    "d128_mode2_r2_beyond_grid": Geometry(B=1, heads=1, head_dim=128, H=32, W=64, w=16, H_lr=11,
+                                          W_lr=20, radius=2, guide_mode=2),
+    "d64_mode1_w8_text": Geometry(B=1, heads=2, head_dim=64, H=32, W=32, w=8, H_lr=8, W_lr=8,
+                                  guide_mode=1, T=40),
 }
 
 
@@ -127,6 +138,26 @@ def test_backward_sampled_rows_2k_text():
     check_rel(bf16_f64(dq[0, q_rows, 5]), rq, "2k+text dq h5")
     check_rel(bf16_f64(dk[0, k_rows, 5]), rk, "2k+text dk h5")
     check_rel(bf16_f64(dv[0, k_rows, 5]), rv, "2k+text dv h5")
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_backward_sampled_rows_2k_guide_modes(mode):
+    g = CONFIGS["2k"].with_(guide_mode=mode)
+    say(f"backward sampled rows 2k, guide mode {mode}")
+    q, k, v = make_qkv_bits(g, 21 + mode)
+    do = make_qkv_bits(g, 31 + mode)[0]
+    _, dq, dk, dv = run_fwd_bwd(g, q, k, v, do)
+    rng = np.random.default_rng(mode)
+    h = 3 * mode
+    qf, kf, vf, gf = (bf16_f64(x[:, :, h:h + 1, :]) for x in (q, k, v, do))
+    q_rows = np.unique(np.concatenate([[0, g.N - 1, g.N, g.L - 1], rng.integers(0, g.N, 40),
+                                       g.N + rng.integers(0, g.M, 10)]))
+    k_rows = np.unique(np.concatenate([[0, g.N, g.L - 1, g.N + 33], rng.integers(0, g.N, 10),
+                                       g.N + rng.integers(0, g.M, 12)]))
+    rq, rk, rv = orc.backward_rows(qf, kf, vf, gf, g, 0, 0, q_rows, k_rows)
+    check_rel(bf16_f64(dq[0, q_rows, h]), rq, f"2k mode {mode} dq h{h}")
+    check_rel(bf16_f64(dk[0, k_rows, h]), rk, f"2k mode {mode} dk h{h}")
+    check_rel(bf16_f64(dv[0, k_rows, h]), rv, f"2k mode {mode} dv h{h}")
 
 
 def test_backward_8k_sampled_dq_and_dv_sum():
