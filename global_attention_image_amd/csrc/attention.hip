@@ -6,14 +6,16 @@
 // [UltraGen/fr §2.A]).
 //
 // Pipeline (all on the caller's stream, no allocation):
-//   1. neighbour table [nW][9] + count, and the fp64 RoPE cos/sin table [P][head_dim/4]
-//   2. prep: window-first permutation of the hi rows of Q, K, V fused with RoPE on Q, K;
-//      Q, K land head-major [B*heads][rows][D]; V lands in 64-key tiles transposed to
+//   1. the fp64 RoPE cos/sin table [P][head_dim/4]
+//   2. prep: window-first permutation of the hi rows of K and V, fused with RoPE on K;
+//      K lands head-major [B*heads][rows][D]; V lands in 64-key tiles transposed to
 //      [D][64] so the P.V contraction reads it with one 16-byte LDS load per operand.
-//      Guide rows are rotated / re-laid out the same way (no permutation).
-//   3. hi pass: one workgroup per (b, h, window, 256-query chunk); it streams the K/V
-//      tiles of its neighbour windows, then of all guide tokens, through LDS, and stores
-//      each output row at its raster position (the inverse permutation, fused).
+//      Guide rows are rotated / re-laid out the same way (no permutation).  Q is not
+//      prepared: each wave reads its query rows from the caller's Q and rotates them.
+//   3. hi pass: one workgroup per (b, h, window, 256-query chunk); it computes its
+//      window's neighbour tiles, streams the K/V tiles of its neighbour windows, then of
+//      all guide tokens, through LDS, and stores each output row at its raster position
+//      (the inverse permutation, fused).
 //   4. guide pass: one workgroup per (b, h, 256 guide queries) over all guide keys.
 //
 // MFMA formulation (v_mfma_f32_32x32x16_bf16, wave64).  Each wave owns 32 queries.
