@@ -92,6 +92,8 @@ struct Workspace {
   bf16_t* v_gb;   // [B*heads][Mbg/64][D][64]
   float* o_part;  // [splits][B*heads][Tq][D]  text-query partial outputs (unnormalised)
   float2* ml_part;  // [splits][B*heads][Tq]   their (running max, sum)
+  bf16_t* q_hi;   // guide modes 1, 2: [B*heads][N][D] window-first Q, rotated and scaled
+  bf16_t* q_lr;   // guide modes 1, 2: [B*heads][M][D] guide Q, rotated and scaled
   size_t bytes;
 };
 
@@ -114,6 +116,12 @@ static Workspace carve(const Geom& g, void* base) {
   const size_t o_vb = take(bh * g.Mbg * g.D * e);
   const size_t o_op = take(static_cast<size_t>(g.splits) * bh * g.Tq * g.D * sizeof(float));
   const size_t o_ml = take(static_cast<size_t>(g.splits) * bh * g.Tq * sizeof(float2));
+  // With the guide-locality masks a workgroup has few key tiles (5 at radius 0), so the
+  // latency of gathering its query rows from the raster layout (one workgroup per CU) is
+  // not hidden by its loop: there Q is prepared like K.
+  const bool q_pre = g.guide_mode != 0 && g.M > 0;
+  const size_t o_qh = take(q_pre ? bh * g.N * g.D * e : 0);
+  const size_t o_ql = take(q_pre ? bh * g.M * g.D * e : 0);
   char* b = static_cast<char*>(base);
   ws.cs = reinterpret_cast<double2*>(b + o_cs);
   ws.k_hi = reinterpret_cast<bf16_t*>(b + o_kh);
@@ -124,6 +132,8 @@ static Workspace carve(const Geom& g, void* base) {
   ws.v_gb = reinterpret_cast<bf16_t*>(b + o_vb);
   ws.o_part = reinterpret_cast<float*>(b + o_op);
   ws.ml_part = reinterpret_cast<float2*>(b + o_ml);
+  ws.q_hi = q_pre ? reinterpret_cast<bf16_t*>(b + o_qh) : nullptr;
+  ws.q_lr = q_pre ? reinterpret_cast<bf16_t*>(b + o_ql) : nullptr;
   ws.bytes = off;
   return ws;
 }
@@ -160,14 +170,17 @@ constexpr int kPrepRows = 4;
 //                     by the guide-locality masks;
 //   [.., + Tk)        text rows x (source x, zero beyond T; position (0, 0), so RoPE is the
 //                     identity) -> k_lr row Mk + x and, with cell blocks, k_gb row Mb + x.
-// Q is not prepared: the attention kernel rotates its query rows as it loads them.
+// Q is normally not prepared (the attention kernel rotates its query rows as it loads
+// them); with q_hi non-null (guide modes 1, 2) the hi and guide rows of Q are also written,
+// rotated and multiplied by q_scale in fp64 and rounded once, to q_hi / q_lr.
 template <int D>
 __global__ __launch_bounds__(kPrepThreads) void prep_k_kernel(
     const bf16_t* __restrict__ k, bf16_t* __restrict__ k_hi, bf16_t* __restrict__ k_lr,
     bf16_t* __restrict__ k_gb, const double2* __restrict__ cs, int P, double log2_theta,
     int64_t T, int64_t N, int64_t M, int64_t Mk, int64_t Mg, int64_t Mb, int64_t Mbg,
     int64_t Tk, int W, int w, int n_wx, int H_lr, int W_lr, int nbj, int rho, int heads,
-    int rope_on) {
+    int rope_on, const bf16_t* __restrict__ q, bf16_t* __restrict__ q_hi,
+    bf16_t* __restrict__ q_lr, double q_scale) {
   constexpr int CPH = D / 8;      // 16-byte chunks per head row
   constexpr int QUARTER = D / 4;  // rotation pairs per axis
   // Per row of this block: source row (-1: zero row), destinations (buffer row offsets in
@@ -175,7 +188,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_k_kernel(
   __shared__ int64_t src_s[kPrepRows];
   __shared__ bf16_t* dk_s[kPrepRows];
   __shared__ bf16_t* dk2_s[kPrepRows];
-  __shared__ int64_t kst_s[kPrepRows], k2st_s[kPrepRows];  // per-head strides
+  __shared__ bf16_t* dq_s[kPrepRows];
+  __shared__ int64_t kst_s[kPrepRows], k2st_s[kPrepRows], qst_s[kPrepRows];  // per-head strides
   __shared__ int pos_s[kPrepRows][2];
   __shared__ double2 cs_s[kPrepRows][2][QUARTER];
   const int64_t L = T + N + M;
@@ -187,7 +201,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_k_kernel(
     int64_t src = -1;
     bf16_t* dk = nullptr;
     bf16_t* dk2 = nullptr;
-    int64_t kst = 0, k2st = 0;
+    bf16_t* dq = nullptr;
+    int64_t kst = 0, k2st = 0, qst = 0;
     int py = 0, px = 0;
     if (row < N) {
       const int r = window_first_to_raster(static_cast<int>(row), W, w, n_wx);
@@ -195,6 +210,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_k_kernel(
       py = r / W;
       px = r - py * W;
       dk = k_hi + (bh0 * N + row) * D;  kst = N * D;
+      if (q_hi) { dq = q_hi + (bh0 * N + row) * D;  qst = N * D; }
     } else if (row < N + Mk) {
       const int64_t s = row - N;
       if (s < M) {
@@ -202,6 +218,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_k_kernel(
         const int sy = static_cast<int>(s / W_lr);
         py = rho * sy;
         px = rho * static_cast<int>(s - static_cast<int64_t>(sy) * W_lr);
+        if (q_lr) { dq = q_lr + (bh0 * M + s) * D;  qst = M * D; }
       }
       dk = k_lr + (bh0 * Mg + s) * D;  kst = Mg * D;
     } else if (row < N + Mk + Mb) {
@@ -221,6 +238,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_k_kernel(
     src_s[tid] = src;
     dk_s[tid] = dk;  kst_s[tid] = kst;
     dk2_s[tid] = dk2;  k2st_s[tid] = k2st;
+    dq_s[tid] = dq;  qst_s[tid] = qst;
     pos_s[tid][0] = py;
     pos_s[tid][1] = px;
   }
@@ -240,7 +258,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_k_kernel(
   for (; t < kPrepRows; ) {
     const int h = c / CPH, j = c % CPH;
     const int64_t src = src_s[t];
-    uint4 ko = make_uint4(0, 0, 0, 0);
+    uint4 ko = make_uint4(0, 0, 0, 0), qo = ko;
+    bf16_t* dq = dq_s[t];
     if (src >= 0) {
       const int64_t so = ((b * L + src) * heads + h) * D + j * 8;
       const uint4 ki = *reinterpret_cast<const uint4*>(k + so);
@@ -250,10 +269,21 @@ __global__ __launch_bounds__(kPrepThreads) void prep_k_kernel(
         const double2* f = &cs_s[t][axis][k0];
         ko = make_uint4(rope_rotate_word(ki.x, f[0]), rope_rotate_word(ki.y, f[1]),
                         rope_rotate_word(ki.z, f[2]), rope_rotate_word(ki.w, f[3]));
+        if (dq) {
+          const uint4 qi = *reinterpret_cast<const uint4*>(q + so);
+          qo = make_uint4(rope_rotate_word(qi.x, f[0], q_scale), rope_rotate_word(qi.y, f[1], q_scale),
+                          rope_rotate_word(qi.z, f[2], q_scale), rope_rotate_word(qi.w, f[3], q_scale));
+        }
       } else {
         ko = ki;
+        if (dq) {
+          const uint4 qi = *reinterpret_cast<const uint4*>(q + so);
+          qo = make_uint4(scale_word(qi.x, q_scale), scale_word(qi.y, q_scale),
+                          scale_word(qi.z, q_scale), scale_word(qi.w, q_scale));
+        }
       }
     }
+    if (dq) *reinterpret_cast<uint4*>(dq + h * qst_s[t] + j * 8) = qo;
     bf16_t* dk = dk_s[t];
     bf16_t* dk2 = dk2_s[t];
     if (dk) *reinterpret_cast<uint4*>(dk + h * kst_s[t] + j * 8) = ko;
@@ -339,6 +369,7 @@ struct AttnArgs {
   const bf16_t* q;        // the caller's token-major Q [B][out_rows][heads][D]; query row i of
                           // the pass is token out_row0 + (hi pass: r(i), else i)
   int64_t q_rows;         // query rows per (b, h) of the pass (a multiple of the block)
+  const bf16_t* q_pre;    // or, when non-null, Q rows prepared (rotated, scaled) [B*heads][q_valid][D]
   const double2* cs;      // fp64 RoPE factors [P][D/4]
   double log2_theta;      // for positions >= P
   double q_scale;         // softmax scale * log2 e, applied to Q before its rounding to bf16
@@ -643,7 +674,8 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   // rotation times the softmax scale * log2 e, one rounding to bf16, so the scores come out
   // in base-2 logits.  Hi queries sit at their raster position, guide query s at
   // (rho * (s / W_lr), rho * (s % W_lr)), text queries at (0, 0); rows past the pass's
-  // valid rows are zero.
+  // valid rows are zero.  With q_pre (guide modes 1, 2, whose workgroups have few tiles)
+  // the rows come prepared by the prep pass instead, with the same rotation and rounding.
   bf16x8 qf[D / 16];
   {
     constexpr int QUARTER = D / 4;
@@ -651,7 +683,12 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
     uint4 raw[D / 16];
     int py = 0, px = 0;
     const bool qvalid = qi < a.q_valid;
-    if (qvalid) {
+    if (a.q_pre) {
+      const bf16_t* qrow = a.q_pre + (static_cast<int64_t>(bh) * a.q_valid + (qvalid ? qi : 0)) * D;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk)
+        qf[kk] = qvalid ? *reinterpret_cast<const bf16x8*>(qrow + 16 * kk + 8 * g) : bf16x8{};
+    } else if (qvalid) {
       int tok = qi;
       if (HI) {
         tok = window_first_to_raster(qi, a.W, a.w, a.n_wx);
@@ -666,26 +703,28 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) raw[kk] = *reinterpret_cast<const uint4*>(qrow + 16 * kk + 8 * g);
     }
+    if (!a.q_pre) {
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      uint4 qo = make_uint4(0, 0, 0, 0);
-      if (qvalid) {
-        // pairs 8kk + 4g .. +3 lie on one axis (y for the first D/4 pairs)
-        const int pr = 8 * kk + 4 * g, axis = pr / QUARTER, k0 = pr - axis * QUARTER;
-        if (a.rope_on) {
-          const int pos = axis ? px : py;
-          double2 f[4];
+      for (int kk = 0; kk < D / 16; ++kk) {
+        uint4 qo = make_uint4(0, 0, 0, 0);
+        if (qvalid) {
+          // pairs 8kk + 4g .. +3 lie on one axis (y for the first D/4 pairs)
+          const int pr = 8 * kk + 4 * g, axis = pr / QUARTER, k0 = pr - axis * QUARTER;
+          if (a.rope_on) {
+            const int pos = axis ? px : py;
+            double2 f[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            f[e] = pos < a.P ? a.cs[pos * QUARTER + k0 + e] : rope_cos_sin(pos, k0 + e, D / 2, a.log2_theta);
-          qo = make_uint4(rope_rotate_word(raw[kk].x, f[0], a.q_scale), rope_rotate_word(raw[kk].y, f[1], a.q_scale),
-                          rope_rotate_word(raw[kk].z, f[2], a.q_scale), rope_rotate_word(raw[kk].w, f[3], a.q_scale));
-        } else {
-          qo = make_uint4(scale_word(raw[kk].x, a.q_scale), scale_word(raw[kk].y, a.q_scale),
-                          scale_word(raw[kk].z, a.q_scale), scale_word(raw[kk].w, a.q_scale));
+            for (int e = 0; e < 4; ++e)
+              f[e] = pos < a.P ? a.cs[pos * QUARTER + k0 + e] : rope_cos_sin(pos, k0 + e, D / 2, a.log2_theta);
+            qo = make_uint4(rope_rotate_word(raw[kk].x, f[0], a.q_scale), rope_rotate_word(raw[kk].y, f[1], a.q_scale),
+                            rope_rotate_word(raw[kk].z, f[2], a.q_scale), rope_rotate_word(raw[kk].w, f[3], a.q_scale));
+          } else {
+            qo = make_uint4(scale_word(raw[kk].x, a.q_scale), scale_word(raw[kk].y, a.q_scale),
+                            scale_word(raw[kk].z, a.q_scale), scale_word(raw[kk].w, a.q_scale));
+          }
         }
+        qf[kk] = *reinterpret_cast<const bf16x8*>(&qo);
       }
-      qf[kk] = *reinterpret_cast<const bf16x8*>(&qo);
     }
   }
   // Let the Q loads complete here, in a wait the compiler sees: it cannot see the
@@ -1156,6 +1195,7 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
   const double l2t = rope_on ? log2(static_cast<double>(theta)) : 0.0;
   const bf16_t* kb = static_cast<const bf16_t*>(k);
   const bf16_t* vb = static_cast<const bf16_t*>(v);
+  const double qs = static_cast<double>(sc) * 1.4426950408889634;  // scale * log2 e
   if (timer) timer_begin(timer, UHLA_STAGE_PREP_HI, s);
   {
     const int64_t rows = g.N + g.Mk + g.Mb + g.Tk;
@@ -1163,11 +1203,13 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
     if (D == 128)
       hipLaunchKernelGGL(prep_k_kernel<128>, grid, dim3(kPrepThreads), 0, s, kb, ws.k_hi, ws.k_lr,
                          ws.k_gb, ws.cs, g.P, l2t, T, g.N, g.M, g.Mk, g.Mg, g.Mb, g.Mbg, g.Tk, W,
-                         w, g.n_wx, H_lr, W_lr, g.nbj, rho, heads, rope_on && !rope_k_at_load ? 1 : 0);
+                         w, g.n_wx, H_lr, W_lr, g.nbj, rho, heads, rope_on && !rope_k_at_load ? 1 : 0,
+                         static_cast<const bf16_t*>(q), ws.q_hi, ws.q_lr, qs);
     else
       hipLaunchKernelGGL(prep_k_kernel<64>, grid, dim3(kPrepThreads), 0, s, kb, ws.k_hi, ws.k_lr,
                          ws.k_gb, ws.cs, g.P, l2t, T, g.N, g.M, g.Mk, g.Mg, g.Mb, g.Mbg, g.Tk, W,
-                         w, g.n_wx, H_lr, W_lr, g.nbj, rho, heads, rope_on && !rope_k_at_load ? 1 : 0);
+                         w, g.n_wx, H_lr, W_lr, g.nbj, rho, heads, rope_on && !rope_k_at_load ? 1 : 0,
+                         static_cast<const bf16_t*>(q), ws.q_hi, ws.q_lr, qs);
     st = check_launch("prep_k_kernel");
     if (st) return st;
     const int64_t tiles = (g.N + g.Mg + g.Mbg) / kKeyTile;
@@ -1183,7 +1225,7 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
   AttnArgs a{};
   a.q = static_cast<const bf16_t*>(q);
   a.cs = ws.cs; a.log2_theta = l2t; a.P = g.P; a.rope_on = rope_on ? 1 : 0;
-  a.q_scale = static_cast<double>(sc) * 1.4426950408889634;
+  a.q_scale = qs;
   a.rho = rho; a.H_lr = H_lr; a.W_lr = W_lr; a.nbj = g.nbj;  // guide query positions
   a.k_hi = ws.k_hi; a.v_hi = ws.v_hi; a.k_lr = ws.k_lr; a.v_lr = ws.v_lr;
   a.N = g.N; a.M = g.M; a.Mk = g.Mk; a.Mg = g.Mg; a.T = T; a.Mb = g.Mb;
@@ -1199,6 +1241,7 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
     const int qt = nwaves * 32;
     AttnArgs h = a;
     h.q_rows = g.N;
+    h.q_pre = ws.q_hi;  // non-null in guide modes 1, 2
     h.out_row0 = T;
     h.W = W; h.w = w; h.n_wx = g.n_wx; h.n_wy = g.n_wy;
     h.radius = radius;
@@ -1220,6 +1263,7 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
   if (g.M > 0) {
     AttnArgs l = a;
     l.q_rows = g.Mq;
+    l.q_pre = ws.q_lr;
     l.out_row0 = T + g.N;
     l.q_valid = static_cast<int>(g.M);
     l.blocks_per_bh = static_cast<int>(g.Mq / kMaxQuery);

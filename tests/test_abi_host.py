@@ -173,7 +173,8 @@ def test_forward_masked_rejects(lib, radius, mode, kw, status):
 def expected_workspace(B, H, W, w, H_lr, W_lr, heads, d, guide_mode=0):
     """Independent restatement of the workspace layout (regions 256-byte aligned): cos/sin
     table, K/V hi rows, K/V guide rows (64-padded), and for guide modes 1 and 2 a copy of
-    the guide K/V in 8x8 cell blocks (Q is rotated as the attention kernel loads it)."""
+    the guide K/V in 8x8 cell blocks and prepared Q rows (otherwise Q is rotated as the
+    attention kernel loads it)."""
     al = lambda x: (x + 255) // 256 * 256
     N, M = H * W, H_lr * W_lr
     Mk = (M + 63) // 64 * 64
@@ -181,6 +182,8 @@ def expected_workspace(B, H, W, w, H_lr, W_lr, heads, d, guide_mode=0):
     e, bh = 2, B * heads
     parts = [16 * max(H, W) * (d // 4), bh * N * d * e, bh * N * d * e,
              bh * Mk * d * e, bh * Mk * d * e, bh * Mb * d * e, bh * Mb * d * e]
+    if guide_mode and M:  # prepared Q rows (hi, guide) for the guide-locality masks
+        parts += [bh * N * d * e, bh * M * d * e]
     return sum(al(p) for p in parts)
 
 
