@@ -15,7 +15,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests need the device; skip them loudly when none is present so that the
-    # CPU suite stays green here, while "-m gpu" on a GPU machine runs them for real.
+    # CPU suite stays green on a machine without one, while "-m gpu" on an MI355X runs them.
     try:
         import torch
         have_gpu = torch.cuda.is_available()
