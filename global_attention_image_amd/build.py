@@ -26,7 +26,7 @@ def hipcc() -> str:
 
 def flags() -> list:
     return [
-        f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-shared",
+        f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC",
         "-Wall", "-Wno-unused-function",
         # packed fp32 VALU ops stay disabled for all device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -34,17 +34,30 @@ def flags() -> list:
     ]
 
 
-def build(verbose: bool = True) -> str:
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + flags() + srcs + ["-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed with status {res.returncode}")
-    os.replace(tmp, LIB)
+
+
+def build(verbose: bool = True) -> str:
+    """Compile every csrc/*.hip to an object (in parallel, in a scratch directory), then
+    link libuhla.so in place."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    with tempfile.TemporaryDirectory(prefix="uhla_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, os.path.basename(s) + ".o") for s in srcs]
+        jobs = [[hipcc()] + flags() + ["-c", s, "-o", o] for s, o in zip(srcs, objs)]
+        workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(lambda c: _run(c, verbose), jobs))
+        tmp = LIB + ".tmp"
+        _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
+        os.replace(tmp, LIB)
     return LIB
 
 
