@@ -467,49 +467,51 @@ __device__ int build_local_table(const BwdArgs& A, int r0, uint32_t* tab) {
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-// Transposed MFMA operands from a row-major LDS tile (rows of D bf16, 16-byte chunks
-// XOR-swizzled by k_swizzle<D>(row)): A[i][k] = tile[row(k)][32 dt + i], i = lane % 32, for
-// the 16 rows of reduction step ks, in the order of an accumulator converted in place
-// (element jj of lane group g = lane / 32 is row 16 ks + 8 (jj / 4) + 4 g + jj % 4).  Two
+// 16-byte chunk swizzle of the backward's LDS row tiles: physical chunk = logical chunk ^
+// bwd_swizzle<D>(row).  The tiles are read two ways: 16 lanes reading one chunk of 16
+// consecutive rows (the row fragments) need 16 distinct values over any 16 consecutive
+// rows, and the transposed reads below, where each 32-lane half addresses 4 rows x 4
+// consecutive chunks, need those 16 (row, chunk) pairs in 16 distinct bank groups.  The
+// swizzle puts row bits 0-1 into chunk bits 2-3 and row bits 2-3 into chunk bits 0-1
+// (D = 64: the same on row / 2, two rows sharing a 256-byte bank line), which meets both;
+// XOR with the plain row % 16 would leave chunk bits 2-3 fixed within a half, 4 bank
+// groups for 16 pairs.
+template <int D>
+__device__ __forceinline__ int bwd_swizzle(int row) {
+  const int e = D == 128 ? (row & 15) : ((row >> 1) & 7);
+  return D == 128 ? (((e & 3) << 2) | (e >> 2)) : (((e & 1) << 2) | (e >> 1));
+}
+
+// Transposed MFMA operands from a row-major LDS tile (rows of D bf16, chunks swizzled by
+// bwd_swizzle<D>): A[i][k] = tile[row(k)][32 dt + i], i = lane % 32, for the 16 rows of
+// reduction step ks, in the order of an accumulator converted in place (element jj of
+// lane group g = lane / 32 is row 16 ks + 8 (jj / 4) + 4 g + jj % 4).  Two
 // ds_read_b64_tr_b16 per fragment: within each 16-lane group, lane i' receives element
 // i' % 4 of the 8 bytes addressed by lane 4 j + i' / 4 (j = 0..3), so the group's lanes
 // address 4 rows x 16 consecutive columns and each lane receives one column of those rows.
-// Lane l addresses row 16 ks + 8 b + R0 (R0 = 4 g + (l % 16) / 4) at byte 64 dt + C0
-// (C0 = 32 ((l / 16) % 2) + 8 (l % 4)).  Under the swizzle the byte offset splits into a
-// per-lane part and a compile-time part, so a fragment costs no address arithmetic:
-//   D = 128 (swizzle row % 16): 256 R0 + 16 ((C0 / 16) ^ (R0 % 4)) + C0 % 16 + 64 ((v ^ g))
-//     with v = dt ^ 2b, i.e. base +/- 64 g (sign by v's low bit) + 64 v + 2048 b + 4096 ks;
-//   D = 64 (swizzle (row / 2) % 8): 128 R0 + 16 ((C0 / 16) ^ (R0 / 2)) + C0 % 16
-//     + 64 (dt ^ b) + 1024 b + 2048 ks.
+// Lane l addresses row 16 ks + 8 b + R0 (R0 = 4 g + r, r = (l % 16) / 4) at logical chunk
+// 4 dt + c (D = 128; D = 64: 4 dt + c as well, chunks of a 128-byte row) with
+// c = 2 ((l / 16) % 2) + (l % 4) / 2, byte 8 (l % 2) of it.  Under the swizzle the byte
+// offset is x ^ (64 dt + 32 b) plus 2048 b + 4096 ks (D = 64: 1024 b + 2048 ks) for a
+// per-lane x: the XOR touches only bits 5-7 of x, so it costs one VALU op per (dt, b).
 template <int D>
 struct TrAddr {
-  int lo, hi;  // per-lane bases (D = 128: for v even / odd; D = 64: both the same)
+  int x;  // per-lane byte offset of (ks, dt, b) = (0, 0, 0)
   __device__ __forceinline__ explicit TrAddr(int lane) {
-    const int g = lane >> 5, r0 = 4 * g + ((lane & 15) >> 2);
-    const int c0 = 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
-    if (D == 128) {
-      const int base = 256 * r0 + (((c0 >> 4) ^ (r0 & 3)) << 4) + (c0 & 15);
-      lo = base + 64 * g;
-      hi = base - 64 * g;
-    } else {
-      lo = hi = 128 * r0 + (((c0 >> 4) ^ (r0 >> 1)) << 4) + (c0 & 15);
-    }
+    const int g = lane >> 5, r = (lane & 15) >> 2, r0 = 4 * g + r;
+    const int c = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    x = (D == 128 ? 256 * r0 + 64 * r : 128 * r0 + 64 * (r >> 1)) + 16 * (c ^ g) + 8 * (lane & 1);
   }
-  __device__ __forceinline__ bf16x8 frag(const char* tile, int ks, int dt) const {
+  // `xb` is x, made opaque by the caller where the XORs are to be recomputed
+  __device__ __forceinline__ static bf16x8 frag(const char* tile, int xb, int ks, int dt) {
     bf16x8 out;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      int off;
-      if (D == 128) {
-        const int v = dt ^ (2 * b);
-        off = ((v & 1) ? hi : lo) + 64 * v + 2048 * b + 4096 * ks;
-      } else {
-        off = lo + 64 * (dt ^ b) + 1024 * b + 2048 * ks;
-      }
-      const bf16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      const int off = (xb ^ (64 * dt + 32 * b)) + (D == 128 ? 2048 : 1024) * (b + 2 * ks);
+      const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
           (__attribute__((address_space(3))) bf16x4*)(tile + off));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) out[4 * b + e] = x[e];
+      for (int e = 0; e < 4; ++e) out[4 * b + e] = v[e];
     }
     return out;
   }
@@ -603,7 +605,7 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dq_kernel(BwdArgs A) {
   for (int i = 0; i < CPT; ++i) {
     const int slot = (i * NWAVES + wave) * 64 + lane;
     const int kr = slot / KCH, kp = slot - kr * KCH;
-    k_src[i] = kr * (D * 2) + ((kp ^ k_swizzle<D>(kr)) << 4);
+    k_src[i] = kr * (D * 2) + ((kp ^ bwd_swizzle<D>(kr)) << 4);
   }
   auto issue = [&](int t) {
     const int64_t off = static_cast<int64_t>(tile_index(t)) * TILE;
@@ -645,7 +647,7 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dq_kernel(BwdArgs A) {
   // swizzled offset is row * 2D + (((2 kk + g) ^ swz(row)) << 4) = kfo ^ (kk << 5) (+ 64 D
   // for half 1: swz(row) is the same for both halves); kfo is made opaque once per tile
   // so that the XORs are recomputed there instead of held in registers across the loop.
-  const int kfo0 = ql * (D * 2) + ((g ^ k_swizzle<D>(ql)) << 4);
+  const int kfo0 = ql * (D * 2) + ((g ^ bwd_swizzle<D>(ql)) << 4);
   int kfo = kfo0;
   auto k_frag = [&](const char* tb, int kk, int half) -> bf16x8 {
     return *reinterpret_cast<const bf16x8*>(tb + (kfo ^ (kk << 5)) + half * 32 * (D * 2));
@@ -686,11 +688,13 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dq_kernel(BwdArgs A) {
       dsb[r >> 3][r & 7] = static_cast<__bf16>(a0 * (p0[r] - dd));
       dsb[2 + (r >> 3)][r & 7] = static_cast<__bf16>(a1 * (p1[r] - dd));
     }
+    int xb = tra.x;
+    asm volatile("" : "+v"(xb));
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tra.frag(kt_, ks, dt), dsb[ks], acc[dt], 0, 0, 0);
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(TrAddr<D>::frag(kt_, xb, ks, dt), dsb[ks], acc[dt], 0, 0, 0);
     wait_tiles<OPS>(std::min(n_tiles - 1, t + AH) - (t + 1));
   }
 
@@ -800,7 +804,7 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dkv_kernel(BwdArgs A) {
   for (int i = 0; i < CPT; ++i) {
     const int slot = (i * NWAVES + wave) * 64 + lane;
     const int kr = slot / KCH, kp = slot - kr * KCH;
-    k_src[i] = kr * (D * 2) + ((kp ^ k_swizzle<D>(kr)) << 4);
+    k_src[i] = kr * (D * 2) + ((kp ^ bwd_swizzle<D>(kr)) << 4);
   }
   // every wave issues the same number of copies per tile (its share of the aux block
   // included), so the in-flight counts of wait_tiles hold for all waves
@@ -852,7 +856,7 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dkv_kernel(BwdArgs A) {
   // swizzled offset is row * 2D + (((2 kk + g) ^ swz(row)) << 4) = kfo ^ (kk << 5) (+ 64 D
   // for half 1: swz(row) is the same for both halves); kfo is made opaque once per tile
   // so that the XORs are recomputed there instead of held in registers across the loop.
-  const int kfo0 = ql * (D * 2) + ((g ^ k_swizzle<D>(ql)) << 4);
+  const int kfo0 = ql * (D * 2) + ((g ^ bwd_swizzle<D>(ql)) << 4);
   int kfo = kfo0;
   auto k_frag = [&](const char* tb, int kk, int half) -> bf16x8 {
     return *reinterpret_cast<const bf16x8*>(tb + (kfo ^ (kk << 5)) + half * 32 * (D * 2));
@@ -901,12 +905,14 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dkv_kernel(BwdArgs A) {
           db[r >> 3][r & 7] = static_cast<__bf16>(pr * (p[r] - d4[e]));
         }
       }
+      int xb = tra.x;
+      asm volatile("" : "+v"(xb));
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
-          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tra.frag(gt_, 2 * half + j, dt), pb[j], dv[dt], 0, 0, 0);
-          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tra.frag(qt_, 2 * half + j, dt), db[j], dk[dt], 0, 0, 0);
+          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(TrAddr<D>::frag(gt_, xb, 2 * half + j, dt), pb[j], dv[dt], 0, 0, 0);
+          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(TrAddr<D>::frag(qt_, xb, 2 * half + j, dt), db[j], dk[dt], 0, 0, 0);
         }
     }
     wait_tiles<OPS>(std::min(n_tiles - 1, t + AH) - (t + 1));
