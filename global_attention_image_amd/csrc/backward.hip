@@ -11,7 +11,7 @@
 //   1. fp64 cos/sin table (as the forward);
 //   2. bwd_rows_kernel: per (b, h) buffers with hi rows window-first, then guide rows and
 //      then text rows, each of the last two padded to 256: Qb = rope(Q) * s * log2 e (the forward's base-2 query), Kb = rope(K),
-//      Vb, dOb; bwd_aux_kernel: per 64-row tile, lse2 = lse * log2 e (pad rows +inf) and D;
+//      Vb, dOb; bwd_aux_kernel: per 64-row tile, -lse2 = -lse * log2 e (pad rows -inf) and -D;
 //   3. bwd_dq_kernel (query-outer, the forward's tile lists): per key tile S, dP (two
 //      32x32x16 MFMA chains from K and V tiles), dS, and dQ^T += K^T dS^T;
 //   4. bwd_dkv_kernel (key-outer, the transposed mask: a hi window's keys are seen by the
@@ -32,7 +32,7 @@ namespace {
 constexpr int kBwdRowsPerBlock = 4;
 constexpr int kBwdThreads = 256;
 constexpr int kBwdMaxTiles = 1024;  // neighbour-window tiles per window (table in LDS)
-constexpr int kAuxBytes = 2 * kKeyTile * 4;  // per tile: 64 lse2 then 64 D values
+constexpr int kAuxBytes = 2 * kKeyTile * 4;  // per tile: 64 -lse2 then 64 -D values
 constexpr int kBwdStages = 4;                 // LDS ring of tiles; copies run 3 tiles ahead
 constexpr int kBwdWaves = 8;                  // guide-row workgroups: 8 waves x 32 rows
 constexpr int kBwdGuideRows = kBwdWaves * 32;
@@ -218,7 +218,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_rows_kernel(
 }
 
 // Per buffer row: lse2 = lse * log2 e (+inf for padding, so those rows get P = 0) and
-// D = sum_d dO * O in fp32, stored per 64-row tile as [64 lse2][64 D].  D / 8 lanes read
+// D = sum_d dO * O in fp32, stored negated per 64-row tile as [64 -lse2][64 -D] (the
+// dK/dV kernel starts its S and dP accumulators from them).  D / 8 lanes read
 // one (token, head) row of O and dO in raster memory order (coalesced) and reduce across
 // lanes; threads past the B * L * heads rows fill the padding rows.
 __global__ __launch_bounds__(kBwdThreads) void bwd_aux_kernel(
@@ -257,8 +258,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_aux_kernel(
     }
     const int64_t bh = b * heads + h;
     float* t = aux + (bh * (R / kKeyTile) + row / kKeyTile) * (2 * kKeyTile);
-    t[row % kKeyTile] = lse[bh * L + src] * 1.4426950408889634f;
-    t[kKeyTile + row % kKeyTile] = dd;
+    t[row % kKeyTile] = -(lse[bh * L + src] * 1.4426950408889634f);
+    t[kKeyTile + row % kKeyTile] = -dd;
     return;
   }
   // padding rows: guide rows [N + M, N + Mp) and text rows [N + Mp + T, R)
@@ -268,7 +269,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_aux_kernel(
   const int64_t bh = j / pad, jj = j - bh * pad;
   const int64_t row = jj < pad_g ? N + M + jj : N + Mp + T + (jj - pad_g);
   float* t = aux + (bh * (R / kKeyTile) + row / kKeyTile) * (2 * kKeyTile);
-  t[row % kKeyTile] = INFINITY;
+  t[row % kKeyTile] = -INFINITY;
   t[kKeyTile + row % kKeyTile] = 0.0f;
 }
 
@@ -621,7 +622,7 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dq_kernel(BwdArgs A) {
     }
   };
 
-  // query fragments (B operands): Q (base-2 scaled) and dO; per-lane lse2 and D
+  // query fragments (B operands): Q (base-2 scaled) and dO; per-lane -lse2 and -D
   const int64_t qrow = r0 + wave * 32 + ql;
   bf16x8 qf[D / 16], gf[D / 16];
   {
@@ -634,7 +635,7 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dq_kernel(BwdArgs A) {
     }
   }
   const float* at = A.aux + (static_cast<int64_t>(bh) * (A.R / kKeyTile) + qrow / kKeyTile) * (2 * kKeyTile);
-  const float lse2 = at[qrow % kKeyTile], dd = at[kKeyTile + qrow % kKeyTile];
+  const float nl2 = at[qrow % kKeyTile], nd = at[kKeyTile + qrow % kKeyTile];
   __builtin_amdgcn_s_waitcnt(0);
 
   f32x16 acc[D / 32];
@@ -683,10 +684,10 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dq_kernel(BwdArgs A) {
       const bool c_ok = (colm >> (r & 3)) & 1u;
       const bool v0 = key < valid && c_ok && ((cells >> (r >> 2)) & 1u);
       const bool v1 = key + 32 < valid && c_ok && ((cells >> (4 + (r >> 2))) & 1u);
-      const float a0 = v0 ? __builtin_amdgcn_exp2f(s0[r] - lse2) : 0.0f;
-      const float a1 = v1 ? __builtin_amdgcn_exp2f(s1[r] - lse2) : 0.0f;
-      dsb[r >> 3][r & 7] = static_cast<__bf16>(a0 * (p0[r] - dd));
-      dsb[2 + (r >> 3)][r & 7] = static_cast<__bf16>(a1 * (p1[r] - dd));
+      const float a0 = v0 ? __builtin_amdgcn_exp2f(s0[r] + nl2) : 0.0f;
+      const float a1 = v1 ? __builtin_amdgcn_exp2f(s1[r] + nl2) : 0.0f;
+      dsb[r >> 3][r & 7] = static_cast<__bf16>(a0 * (p0[r] + nd));
+      dsb[2 + (r >> 3)][r & 7] = static_cast<__bf16>(a1 * (p1[r] + nd));
     }
     int xb = tra.x;
     asm volatile("" : "+v"(xb));
@@ -745,7 +746,7 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dkv_kernel(BwdArgs A) {
   constexpr int KCH = D / 8;
   constexpr int AUX_LANES = kAuxBytes / 16 / NWAVES;  // lanes per wave copying the aux block
   constexpr int OPS = 2 * CPT + 1;                     // DMA instructions per wave per tile
-  constexpr int STAGE = 2 * TILE + kAuxBytes;          // Q rows, dO rows, lse2 / D
+  constexpr int STAGE = 2 * TILE + kAuxBytes;          // Q rows, dO rows, -lse2 / -D
   constexpr int AH = kBwdStages - 1;
   static_assert(AUX_LANES >= 1 && AUX_LANES * 16 * NWAVES == kAuxBytes, "aux split");
   __shared__ __attribute__((aligned(16))) char ring[kBwdStages * STAGE];
@@ -884,14 +885,10 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dkv_kernel(BwdArgs A) {
     }
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      f32x16 s = {}, p = {};
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(qt_, kk, half), kf[kk], s, 0, 0, 0);
-        p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(gt_, kk, half), vf[kk], p, 0, 0, 0);
-      }
-      // rows are queries 32 half + 8(r/4) + 4g + r%4 of the tile; lanes are keys
-      bf16x8 pb[2], db[2];
+      // S and dP start from -lse2 and -D of their query rows (rows are queries
+      // 32 half + 8(r/4) + 4g + r%4 of the tile; lanes are keys), so P = exp2(S) and
+      // dS = P dP come out of the accumulators directly
+      f32x16 s, p;
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
         const int q0 = 32 * half + 8 * rq + 4 * g;
@@ -899,11 +896,21 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dkv_kernel(BwdArgs A) {
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(aux + kKeyTile + q0);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = 4 * rq + e;
-          const float pr = kvis ? __builtin_amdgcn_exp2f(s[r] - l4[e]) : 0.0f;
-          pb[r >> 3][r & 7] = static_cast<__bf16>(pr);
-          db[r >> 3][r & 7] = static_cast<__bf16>(pr * (p[r] - d4[e]));
+          s[4 * rq + e] = l4[e];
+          p[4 * rq + e] = d4[e];
         }
+      }
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(qt_, kk, half), kf[kk], s, 0, 0, 0);
+        p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(gt_, kk, half), vf[kk], p, 0, 0, 0);
+      }
+      bf16x8 pb[2], db[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pr = kvis ? __builtin_amdgcn_exp2f(s[r]) : 0.0f;
+        pb[r >> 3][r & 7] = static_cast<__bf16>(pr);
+        db[r >> 3][r & 7] = static_cast<__bf16>(pr * p[r]);
       }
       int xb = tra.x;
       asm volatile("" : "+v"(xb));
