@@ -676,16 +676,22 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dq_kernel(BwdArgs A) {
     // cell-block tiles: key k is cell (k / 8, k % 8) of the block, i.e. row r/4 (+4 in the
     // second half) and column 4g + r%4
     const uint32_t cells = tile_cells(t);
-    const uint32_t colm = (cells >> (8 + 4 * g)) & 15u;
+    if (valid < kKeyTile || cells != 0xffffu) {
+      // partial or cell-block tile: scores of keys past the end or outside the cells -> -inf
+      const uint32_t colm = (cells >> (8 + 4 * g)) & 15u;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 8 * (r >> 2) + 4 * g + (r & 3);
+        const bool c_ok = (colm >> (r & 3)) & 1u;
+        if (!(key < valid && c_ok && ((cells >> (r >> 2)) & 1u))) s0[r] = -INFINITY;
+        if (!(key + 32 < valid && c_ok && ((cells >> (4 + (r >> 2))) & 1u))) s1[r] = -INFINITY;
+      }
+    }
     bf16x8 dsb[4];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = 8 * (r >> 2) + 4 * g + (r & 3);
-      const bool c_ok = (colm >> (r & 3)) & 1u;
-      const bool v0 = key < valid && c_ok && ((cells >> (r >> 2)) & 1u);
-      const bool v1 = key + 32 < valid && c_ok && ((cells >> (4 + (r >> 2))) & 1u);
-      const float a0 = v0 ? __builtin_amdgcn_exp2f(s0[r] + nl2) : 0.0f;
-      const float a1 = v1 ? __builtin_amdgcn_exp2f(s1[r] + nl2) : 0.0f;
+      const float a0 = __builtin_amdgcn_exp2f(s0[r] + nl2);
+      const float a1 = __builtin_amdgcn_exp2f(s1[r] + nl2);
       dsb[r >> 3][r & 7] = static_cast<__bf16>(a0 * (p0[r] + nd));
       dsb[2 + (r >> 3)][r & 7] = static_cast<__bf16>(a1 * (p1[r] + nd));
     }
