@@ -697,11 +697,21 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dq_kernel(BwdArgs A) {
     }
     int xb = tra.x;
     asm volatile("" : "+v"(xb));
+    {
+      // dQ^T += K~^T dS^T: MFMA i takes key-step i / DT and dims i % DT; its transposed
+      // fragment is read two MFMAs ahead (S and dP are dead here)
+      constexpr int DT = D / 32, NI = 4 * DT, AHD = 2;
+      bf16x8 f[NI];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+      for (int i = 0; i < AHD; ++i) f[i] = TrAddr<D>::frag(kt_, xb, i / DT, i % DT);
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(TrAddr<D>::frag(kt_, xb, ks, dt), dsb[ks], acc[dt], 0, 0, 0);
+      for (int i = 0; i < NI; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        acc[i % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[i], dsb[i / DT], acc[i % DT], 0, 0, 0);
+        if (i + AHD < NI) f[i + AHD] = TrAddr<D>::frag(kt_, xb, (i + AHD) / DT, (i + AHD) % DT);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     wait_tiles<OPS>(std::min(n_tiles - 1, t + AH) - (t + 1));
   }
 
@@ -920,13 +930,28 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dkv_kernel(BwdArgs A) {
       }
       int xb = tra.x;
       asm volatile("" : "+v"(xb));
+      {
+        // dV^T += dO^T P and dK^T += Q^T dS: MFMA i takes key-step j = i / (2 DT) and dims
+        // dt = (i / 2) % DT, dV for even i, dK for odd i.  Its transposed fragment is read two
+        // MFMAs ahead (the scheduling barriers keep the reads there; S and dP are dead by
+        // now, so the registers are free)
+        constexpr int DT = D / 32, NI = 4 * DT, AHD = 2;
+        auto frag = [&](int i) __attribute__((always_inline)) {
+          return TrAddr<D>::frag((i & 1) ? qt_ : gt_, xb, 2 * half + i / (2 * DT), (i / 2) % DT);
+        };
+        bf16x8 f[NI];
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+        for (int i = 0; i < AHD; ++i) f[i] = frag(i);
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(TrAddr<D>::frag(gt_, xb, 2 * half + j, dt), pb[j], dv[dt], 0, 0, 0);
-          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(TrAddr<D>::frag(qt_, xb, 2 * half + j, dt), db[j], dk[dt], 0, 0, 0);
+        for (int i = 0; i < NI; ++i) {
+          __builtin_amdgcn_sched_barrier(0);
+          const int j = i / (2 * DT), dt = (i / 2) % DT;
+          if (i & 1) dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[i], db[j], dk[dt], 0, 0, 0);
+          else dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[i], pb[j], dv[dt], 0, 0, 0);
+          if (i + AHD < NI) f[i + AHD] = frag(i + AHD);
         }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     wait_tiles<OPS>(std::min(n_tiles - 1, t + AH) - (t + 1));
   }
