@@ -296,7 +296,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_k_kernel(
   }
 }
 
-// V rows -> 64-key tiles transposed to [D][64] (key order by v_slot).  Tiles of a batch:
+// V rows -> 64-key tiles transposed to [D][64] (key order by v_slot); one (tile, head, batch)
+// per workgroup (grid: tiles x heads x B).  Tiles of a batch:
 // [0, N/64) window-first hi rows -> v_hi; the next Mg/64 the global keys -> v_lr (guide
 // rows in raster order, zero padded to Mk, then text rows); the last Mbg/64 the cell-block
 // buffer -> v_gb (guide cells in 8x8 block order, then text rows).  Input rows are
@@ -305,9 +306,10 @@ __global__ __launch_bounds__(kPrepThreads) void prep_v_kernel(
     const bf16_t* __restrict__ v, bf16_t* v_hi, bf16_t* v_lr, bf16_t* v_gb, int64_t T,
     int64_t N, int64_t M, int64_t Mk, int64_t Mg, int64_t Mb, int64_t Mbg, int W, int w,
     int n_wx, int H_lr, int W_lr, int nbj, int heads, int D) {
-  __shared__ bf16_t tile[kKeyTile][128 + 2];
+  __shared__ __attribute__((aligned(16))) bf16_t tile[kKeyTile][128 + 2];
   const int64_t L = T + N + M;
-  const int64_t b = blockIdx.y;
+  const int64_t b = blockIdx.z;
+  const int h = blockIdx.y;
   const int64_t tile_id = blockIdx.x;
   const int64_t n_hi = N / kKeyTile, n_g = Mg / kKeyTile;
   const int chunks_per_row = D / 8;
@@ -325,41 +327,51 @@ __global__ __launch_bounds__(kPrepThreads) void prep_v_kernel(
     block_cell(r, nbj, ci, cj);
     return (ci < H_lr && cj < W_lr) ? T + N + static_cast<int64_t>(ci) * W_lr + cj : -1;
   };
-  for (int h = 0; h < heads; ++h) {
-    // load 64 rows x D of head h (each row 16-byte chunks)
-    for (int i = threadIdx.x; i < kKeyTile * chunks_per_row; i += kPrepThreads) {
+  // load 64 rows x D of head h (16-byte chunks; all of a thread's loads before its stores)
+  constexpr int kLoads = kKeyTile * 16 / kPrepThreads;  // chunks per thread for D = 128
+  uint4 x[kLoads];
+#pragma unroll
+  for (int u = 0; u < kLoads; ++u) {
+    const int i = threadIdx.x + u * kPrepThreads;
+    x[u] = make_uint4(0, 0, 0, 0);
+    if (i < kKeyTile * chunks_per_row) {
       const int kr = i / chunks_per_row, j = i - kr * chunks_per_row;
       const int64_t src_row = source(kr);
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (src_row >= 0) x = *reinterpret_cast<const uint4*>(v + ((b * L + src_row) * heads + h) * D + j * 8);
-      const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        tile[kr][j * 8 + 2 * e] = static_cast<bf16_t>(xw[e] & 0xffff);
-        tile[kr][j * 8 + 2 * e + 1] = static_cast<bf16_t>(xw[e] >> 16);
-      }
+      if (src_row >= 0) x[u] = *reinterpret_cast<const uint4*>(v + ((b * L + src_row) * heads + h) * D + j * 8);
     }
-    __syncthreads();
-    // write D rows x 64 keys; each thread writes 8 consecutive slots of one d-row
-    const int64_t bh = b * heads + h, tsz = static_cast<int64_t>(D) * kKeyTile;
-    bf16_t* dst;
-    if (tile_id < n_hi) dst = v_hi + (bh * n_hi + tile_id) * tsz;
-    else if (tile_id < n_hi + n_g) dst = v_lr + (bh * n_g + (tile_id - n_hi)) * tsz;
-    else dst = v_gb + (bh * (Mbg / kKeyTile) + (tile_id - n_hi - n_g)) * tsz;
-    for (int i = threadIdx.x; i < D * (kKeyTile / 8); i += kPrepThreads) {
-      const int d = i / (kKeyTile / 8), s8 = (i - d * (kKeyTile / 8)) * 8;
-      uint32_t wv[4];
+  }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // slot s holds key v_slot(s) (the mapping is its own inverse)
-        const uint32_t lo = tile[v_slot(s8 + 2 * e)][d];
-        const uint32_t hi = tile[v_slot(s8 + 2 * e + 1)][d];
-        wv[e] = lo | (hi << 16);
-      }
-      *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(d) * kKeyTile + s8) =
-          make_uint4(wv[0], wv[1], wv[2], wv[3]);
+  for (int u = 0; u < kLoads; ++u) {
+    const int i = threadIdx.x + u * kPrepThreads;
+    if (i < kKeyTile * chunks_per_row) {
+      const int kr = i / chunks_per_row, j = i - kr * chunks_per_row;
+      // row stride 260 bytes: the four words of a chunk are 4-byte aligned
+      uint32_t* tw = reinterpret_cast<uint32_t*>(&tile[kr][j * 8]);
+      tw[0] = x[u].x;
+      tw[1] = x[u].y;
+      tw[2] = x[u].z;
+      tw[3] = x[u].w;
     }
-    __syncthreads();
+  }
+  __syncthreads();
+  // write D rows x 64 keys; each thread writes 8 consecutive slots of one d-row
+  const int64_t bh = b * heads + h, tsz = static_cast<int64_t>(D) * kKeyTile;
+  bf16_t* dst;
+  if (tile_id < n_hi) dst = v_hi + (bh * n_hi + tile_id) * tsz;
+  else if (tile_id < n_hi + n_g) dst = v_lr + (bh * n_g + (tile_id - n_hi)) * tsz;
+  else dst = v_gb + (bh * (Mbg / kKeyTile) + (tile_id - n_hi - n_g)) * tsz;
+  for (int i = threadIdx.x; i < D * (kKeyTile / 8); i += kPrepThreads) {
+    const int d = i / (kKeyTile / 8), s8 = (i - d * (kKeyTile / 8)) * 8;
+    uint32_t wv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      // slot s holds key v_slot(s) (the mapping is its own inverse)
+      const uint32_t lo = tile[v_slot(s8 + 2 * e)][d];
+      const uint32_t hi = tile[v_slot(s8 + 2 * e + 1)][d];
+      wv[e] = lo | (hi << 16);
+    }
+    *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(d) * kKeyTile + s8) =
+        make_uint4(wv[0], wv[1], wv[2], wv[3]);
   }
 }
 
@@ -1127,6 +1139,7 @@ static int validate_forward(const void* q, const void* k, const void* v, void* o
        reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o)) % 16)
     return fail_arg("tensors must be 16-byte aligned");
   if (B > 65535) return fail_unsupported("batch too large");
+  if (heads > 65535) return fail_unsupported("too many heads");
   const int64_t N = static_cast<int64_t>(H) * W, M = static_cast<int64_t>(H_lr) * W_lr;
   const int64_t bh = static_cast<int64_t>(B) * heads;
   // 32-bit row indices and tile byte offsets inside the kernels; 32-bit workgroup counts
@@ -1213,7 +1226,7 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
     st = check_launch("prep_k_kernel");
     if (st) return st;
     const int64_t tiles = (g.N + g.Mg + g.Mbg) / kKeyTile;
-    UHLA_STEP(hipLaunchKernelGGL(prep_v_kernel, dim3(static_cast<unsigned>(tiles), B), dim3(kPrepThreads), 0, s,
+    UHLA_STEP(hipLaunchKernelGGL(prep_v_kernel, dim3(static_cast<unsigned>(tiles), heads, B), dim3(kPrepThreads), 0, s,
                                  vb, ws.v_hi, ws.v_lr, ws.v_gb, T, g.N, g.M, g.Mk, g.Mg, g.Mb, g.Mbg,
                                  W, w, g.n_wx, H_lr, W_lr, g.nbj, heads, D),
               "prep_v_kernel");

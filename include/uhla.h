@@ -123,8 +123,9 @@ size_t uhla_forward_workspace_bytes(int B, int H, int W, int w, int H_lr, int W_
  * guide tokens, exactly one of H_lr/W_lr zero, O overlapping Q, K, V or the workspace);
  * UHLA_ERR_UNSUPPORTED (head_dim not in {64, 128}; w not a multiple of 8, or w > 16
  * and not a multiple of 16; more than 1024 key tiles of 64 keys per window, counting
- * the neighbour windows' tiles and, in the masked variant, the guide cell blocks);
- * UHLA_ERR_WORKSPACE; UHLA_ERR_HIP.
+ * the neighbour windows' tiles and, in the masked variant, the guide cell blocks; B or
+ * heads above 65535; grids, guide grids or text too large for 32-bit row and workgroup
+ * indices); UHLA_ERR_WORKSPACE; UHLA_ERR_HIP.
  */
 int uhla_forward(const void* q, const void* k, const void* v, void* o,
                  int B, int H, int W, int w, int H_lr, int W_lr, int rho,
