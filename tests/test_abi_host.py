@@ -133,6 +133,8 @@ def fwd_args(**kw):
     (dict(H=36, W=36, w=4), api.UHLA_ERR_UNSUPPORTED),
     # 3x3 windows of 96x96 tokens: 9 * 144 key tiles per window, above the 1024-tile table
     (dict(H=384, W=384, w=96, H_lr=0, W_lr=0), api.UHLA_ERR_UNSUPPORTED),
+    (dict(B=65536), api.UHLA_ERR_UNSUPPORTED),  # grid dimension limits
+    (dict(heads=65536), api.UHLA_ERR_UNSUPPORTED),
     (dict(ws=NULL), api.UHLA_ERR_WORKSPACE),
     (dict(wsb=1000), api.UHLA_ERR_WORKSPACE),
     (dict(o=P), api.UHLA_ERR_ARG),  # aliases q
