@@ -1,7 +1,8 @@
-// Hierarchical local attention backward on gfx950: dQ, dK, dV for the mask of uhla_forward
-// with any neighbourhood radius (all guide tokens visible to hi-res queries, guide queries
-// seeing guide keys only) and optional text tokens (text queries see every key, every query
-// sees the text keys), from Q, K, V, O, dO and the forward's per-row log-sum-exp.
+// Hierarchical local attention backward on gfx950: dQ, dK, dV for every mask of the
+// forward (any neighbourhood radius; all guide tokens visible to hi-res queries, or in
+// guide modes 1 and 2 only those of the query's window or neighbourhood; guide queries
+// seeing guide keys only) and optional text tokens (text queries see every key, every
+// query sees the text keys), from Q, K, V, O, dO and the forward's per-row log-sum-exp.
 //
 // Math per (batch, head), rotated Q~ K~, scale s: P = exp(s Q~ K~^T - lse) on the allowed
 // pairs, dV = P^T dO, dP = dO V^T, dS = P (dP - D) with D = rowsum(dO O), dQ~ = s dS K~,
@@ -10,13 +11,15 @@
 // Pipeline (caller's stream, no allocation):
 //   1. fp64 cos/sin table (as the forward);
 //   2. bwd_rows_kernel: per (b, h) buffers with hi rows window-first, then guide rows and
-//      then text rows, each of the last two padded to 256: Qb = rope(Q) * s * log2 e (the forward's base-2 query), Kb = rope(K),
-//      Vb, dOb; bwd_aux_kernel: per 64-row tile, -lse2 = -lse * log2 e (pad rows -inf) and -D;
+//      then text rows, each of the last two padded to 256: Qb = rope(Q) * s * log2 e (the
+//      forward's base-2 query), Kb = rope(K), Vb, dOb; bwd_aux_kernel: per 64-row tile,
+//      -lse2 = -lse * log2 e (pad rows -inf) and -D; in guide modes 1 and 2
+//      bwd_cellblock_kernel copies the guide K~ and V rows into 8x8 cell blocks;
 //   3. bwd_dq_kernel (query-outer, the forward's tile lists): per key tile S, dP (two
 //      32x32x16 MFMA chains from K and V tiles), dS, and dQ^T += K^T dS^T;
 //   4. bwd_dkv_kernel (key-outer, the transposed mask: a hi window's keys are seen by the
-//      queries of its neighbour windows, a guide key by every hi and guide query):
-//      per query tile S, dP, dS and dV^T += dO^T P, dK^T += Q^T dS.
+//      queries of its neighbour windows, a guide key by every hi and guide query that
+//      sees it): per query tile S, dP, dS and dV^T += dO^T P, dK^T += Q^T dS.
 // Tiles are row-major in LDS; the transposed operands (K^T, Q^T, dO^T) are read from the
 // same tiles with the gfx950 transposing LDS read, so each tile is copied once.  Both
 // kernels keep a 4-stage ring of tiles, copied three tiles ahead, and write bf16
