@@ -229,6 +229,8 @@ def main():
     pairs = algorithmic_pairs(g)
     tflops = flops["total"] / (ms_step * 1e-3) / 1e12
     attn_hi_ms = stage_avg["attn_hi"]
+    attn_ms = stage_avg["attn_hi"] + stage_avg["attn_lr"] + stage_avg["attn_text"]
+    attn_tflops = flops["total"] / (attn_ms * 1e-3) / 1e12
     achieved = flops["hi"] / (attn_hi_ms * 1e-3) / 1e12
     log(f"[bench] {ms_step:.3f} ms/step; stages (ms/call): "
         + ", ".join(f"{s}={stage_avg[s]:.3f}" for s in stage_avg))
@@ -277,6 +279,9 @@ def main():
         "algorithmic_flops": flops,
         "unmasked_pairs_per_head": pairs,
         "frac_bf16_peak_step": round(tflops / PEAK_BF16_TFLOPS, 4),
+        # the same algorithmic FLOPs over the attention passes alone (hi, guide, text)
+        "attention_passes": {"ms": round(attn_ms, 4), "TFLOP/s": round(attn_tflops, 2),
+                             "frac_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4)},
         "stage_ms": {s: round(x, 4) for s, x in stage_avg.items()},
         "roofline": {"kernel": "attn_fwd_kernel<128, 8, hi%s> (hi-res pass)"
                                % (", K rotated at load" if args.rope_at_load else ""), "bound": "mfma",
