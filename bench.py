@@ -251,7 +251,17 @@ def main():
     perm_ms = e0.elapsed_time(e1) / reps
     perm_bytes = 2 * g.B * g.N * g.heads * g.head_dim * 2
     perm_gbs = perm_bytes / (perm_ms * 1e-3) / 1e9
-    del pdst
+    # a plain device-to-device copy of the same bytes, as a measured bandwidth ceiling
+    psrc = torch.empty_like(pdst)
+    for _ in range(3):
+        pdst.copy_(psrc)
+    e0.record()
+    for _ in range(reps):
+        pdst.copy_(psrc)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = perm_bytes / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+    del pdst, psrc
 
     traffic = None if variant else read_traffic()
     res = {
@@ -290,7 +300,8 @@ def main():
                      "traffic": traffic},
         "permute": {"entry_point": "uhla_window_permute (Q hi segment, bf16)",
                     "ms": round(perm_ms, 4), "GB/s": round(perm_gbs, 1),
-                    "frac_hbm_peak": round(perm_gbs / PEAK_HBM_GBS, 4)},
+                    "frac_hbm_peak": round(perm_gbs / PEAK_HBM_GBS, 4),
+                    "device_copy_GB/s": round(copy_gbs, 1)},
     }
     if not args.no_cpu_baseline:
         log(f"[bench] CPU baseline: oracle for ~{args.cpu_seconds:.0f} s")
