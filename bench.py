@@ -21,6 +21,9 @@ roofline    the dominant kernel (hi-res attention pass) against the bf16 MFMA pe
             HIP events recorded on the launch stream during the timed steps.
 cpu_baseline  the fp64 oracle on a time-bounded sample of query rows of the same
             workload, on this host's cores, in the same unit.
+attention_passes  the same FLOPs over the attention passes alone (prep excluded).
+permute     the standalone uhla_window_permute of the Q hi segment in GB/s, beside a plain
+            device-to-device copy of the same bytes.
 """
 from __future__ import annotations
 
