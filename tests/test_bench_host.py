@@ -21,3 +21,20 @@ def test_world_size_above_one_is_refused():
                        text=True, timeout=120, env=env)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_traffic_summary_is_used_only_for_the_source_it_was_taken_on(tmp_path, monkeypatch):
+    sys.path.insert(0, ROOT)
+    import bench
+    src = tmp_path / "kernel.hip"
+    src.write_text("// kernel source\n")
+    prof = tmp_path / "traffic.md"
+    good = bench.source_hash(str(src))
+    prof.write_text(f"# summary\n\n- hbm_bytes_per_launch: 1.25e+10\n- attention.hip sha256[:16]: {good}\n")
+    monkeypatch.setattr(bench, "ATTN_SOURCE", str(src))
+    monkeypatch.setattr(bench, "TRAFFIC_PROFILE", str(prof))
+    assert bench.read_traffic() == 1.25e10
+    src.write_text("// kernel source, changed\n")
+    assert bench.read_traffic() is None
+    monkeypatch.setattr(bench, "TRAFFIC_PROFILE", str(tmp_path / "missing.md"))
+    assert bench.read_traffic() is None
