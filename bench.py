@@ -72,8 +72,26 @@ def read_traffic():
         return None
 
 
+def stratified_rows(geom, rng, n):
+    """n query rows of one (batch, head), drawn class by class in proportion to each class's
+    share of the L rows (at least one each): hi rows of corner, edge and interior windows,
+    and guide rows."""
+    nwy, nwx, w = geom.H // geom.w, geom.W // geom.w, geom.w
+    r = np.arange(geom.N)
+    wy, wx = (r // geom.W) // w, (r % geom.W) // w
+    on_y, on_x = (wy == 0) | (wy == nwy - 1), (wx == 0) | (wx == nwx - 1)
+    classes = [r[on_y & on_x], r[on_y ^ on_x], r[~on_y & ~on_x],
+               np.arange(geom.N, geom.N + geom.M)]
+    classes = [c for c in classes if len(c)]
+    sizes = np.array([len(c) for c in classes], dtype=np.float64)
+    take = np.maximum(1, np.round(n * sizes / sizes.sum()).astype(int))
+    rows = [rng.choice(c, min(t, len(c)), replace=False) for c, t in zip(classes, take)]
+    return np.sort(np.concatenate(rows))
+
+
 def cpu_baseline(geom, q, k, v, seconds):
-    """Time the oracle on query rows of (b=0, h=0) in blocks until `seconds` elapse."""
+    """Time the oracle on stratified query rows of a few heads spread over the head range
+    (batch 0), a share of the time budget per head, and extrapolate the full oracle time."""
     import oracle.uhla_oracle as orc
     from global_attention_image_amd.inputs import bf16_bits_to_f64
     try:
@@ -82,28 +100,41 @@ def cpu_baseline(geom, q, k, v, seconds):
     except Exception:
         cores = len(os.sched_getaffinity(0))
     rng = np.random.default_rng(0)
-    t0 = time.perf_counter()
-    qs = bf16_bits_to_f64(q[0:1, :, 0:1, :])
-    ks = bf16_bits_to_f64(k[0:1, :, 0:1, :])
-    vs = bf16_bits_to_f64(v[0:1, :, 0:1, :])
-    qk = orc.rotated_qk(qs, ks, geom, 0, 0)
-    rows_done, pairs = 0, 0
+    heads = sorted({0, geom.heads // 3, (2 * geom.heads) // 3, geom.heads - 1})
+    t_start = time.perf_counter()
+    rows_done, pairs, t_rot, t_rows = 0, 0, 0.0, 0.0
     block = 64
-    while True:
-        rows = np.sort(rng.choice(geom.L, block, replace=False))
-        orc.attention_rows(qs, ks, vs, geom, 0, 0, rows, block=block, qk=qk)
-        rows_done += block
-        pairs += int(orc.allowed_key_count(geom, rows).sum())
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
+    for i, h in enumerate(heads):
+        t0 = time.perf_counter()
+        qs = bf16_bits_to_f64(q[0:1, :, h:h + 1, :])
+        ks = bf16_bits_to_f64(k[0:1, :, h:h + 1, :])
+        vs = bf16_bits_to_f64(v[0:1, :, h:h + 1, :])
+        qk = orc.rotated_qk(qs, ks, geom, 0, 0)
+        t1 = time.perf_counter()
+        t_rot += t1 - t0
+        budget = (seconds - (t1 - t_start)) / (len(heads) - i)
+        while True:
+            rows = stratified_rows(geom, rng, block)
+            orc.attention_rows(qs, ks, vs, geom, 0, 0, rows, block=block, qk=qk)
+            rows_done += len(rows)
+            pairs += int(orc.allowed_key_count(geom, rows).sum())
+            if time.perf_counter() - t1 >= budget:
+                break
+        t_rows += time.perf_counter() - t1
+    dt = time.perf_counter() - t_start
     flops = 4 * geom.head_dim * pairs
+    bh = geom.B * geom.heads
+    full_s = bh * t_rot / len(heads) + t_rows / rows_done * bh * geom.L
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{rows_done} uniformly sampled query rows of batch 0 / head 0 of the "
-                      f"{geom.name} workload (RoPE of that head, explicit mask rows, dense fp64 "
-                      f"softmax over all {geom.L} keys); {dt:.1f} s wall; FLOPs counted as 4*d "
-                      f"per unmasked pair",
-            "seconds": dt}
+            "sample": f"{rows_done} query rows of batch 0, heads {heads} of the {geom.name} "
+                      f"workload, stratified by class in proportion to its share of the rows "
+                      f"(corner / edge / interior windows, guide rows); per head the RoPE of "
+                      f"that head, then explicit mask rows and a dense fp64 softmax over all "
+                      f"{geom.L} keys; {dt:.1f} s wall; FLOPs counted as 4*d per unmasked pair",
+            "seconds": round(dt, 3),
+            "extrapolated_full_oracle_s": round(full_s, 1),
+            "extrapolation": "extrapolated, not measured: mean RoPE time per head x B*heads + "
+                             "mean time per query row x B*heads*L"}
 
 
 def bench_backward(args, g):
@@ -219,11 +250,16 @@ def main():
     timer = api.Timer(args.steps)
     log(f"[bench] warmup done; timing {args.steps} steps")
     torch.cuda.synchronize()
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for e_a, e_b in step_ev:
+        e_a.record()
         fwd(timer)
+        e_b.record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    step_list = sorted(a.elapsed_time(b) for a, b in step_ev)
     stage_ms, calls = timer.read()
     timer.close()
     ms_step = elapsed * 1e3 / args.steps
@@ -280,6 +316,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
+        # per-step device time (HIP events around each step on the launch stream)
+        "step_ms": {"median": round(float(np.median(step_list)), 4),
+                    "min": round(step_list[0], 4), "max": round(step_list[-1], 4)},
         "config": {"workload": g.name, "B": g.B, "heads": g.heads, "head_dim": g.head_dim,
                    "grid": f"{g.H}x{g.W}", "window": g.w, "guide_grid": f"{g.H_lr}x{g.W_lr}",
                    "rho": g.rho, "rope_theta": g.theta, "tokens": g.L,

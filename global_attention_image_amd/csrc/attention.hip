@@ -1146,6 +1146,15 @@ static int validate_forward(const void* q, const void* k, const void* v, void* o
   if (N > (int64_t(1) << 26) || M > (int64_t(1) << 26) || T > (int64_t(1) << 24) ||
       bh * ((N + M + T) / 64 + 1) > 0x7fffffff)
     return fail_unsupported("problem too large");
+  {
+    // The attention kernels address a K or V tile by its 32-bit byte offset inside the
+    // (batch, head) region of its buffer: hi rows (N), global keys (guide rows padded to
+    // the key tile, then text rows) and, in guide modes 1 and 2, the cell-block copy.
+    const Geom g = make_geom(B, H, W, w, H_lr, W_lr, rho > 0 ? rho : 1, heads, D, 1, guide_mode, T);
+    const int64_t row_bytes = static_cast<int64_t>(D) * 2, lim = int64_t(1) << 32;
+    if (g.N * row_bytes > lim || g.Mg * row_bytes > lim || g.Mbg * row_bytes > lim)
+      return fail_unsupported("a (batch, head) K or V region exceeds 4 GiB");
+  }
   // radius capped so that the neighbourhood span stays far inside int range
   if (max_table_tiles(make_geom(B, H, W, w, H_lr, W_lr, rho, heads, D,
                                 std::min(radius, H / w + W / w), guide_mode, T)) > kMaxTableTiles)

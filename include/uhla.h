@@ -85,8 +85,8 @@ int uhla_window_unpermute(const void* src, void* dst, int B, int H, int W, int w
  * Rotation: d_axis = head_dim / 2; dims [0, d_axis) rotate by y, dims [d_axis, head_dim)
  * by x; inside an axis block the pair (2k, 2k+1) = (a, b) becomes
  * (a cos phi - b sin phi, a sin phi + b cos phi), phi = pos * theta^(-2k / d_axis).
- * cos/sin are evaluated in fp64 and rounded to fp32; the rotation runs in fp32 and the
- * result is rounded to bf16.  theta <= 0 copies src to dst unchanged.
+ * cos/sin and the rotation are evaluated in fp64 and each result is rounded once to bf16
+ * (round to nearest even).  theta <= 0 copies src to dst unchanged.
  * Errors: UHLA_ERR_ARG (null pointers, sizes < 1, w not dividing H or W when
  * hi_order = 1, exactly one of H_lr/W_lr zero, rho < 1 with guide tokens, hi_order not
  * 0/1, partial overlap); UHLA_ERR_UNSUPPORTED when head_dim % 8 != 0.
@@ -125,7 +125,9 @@ size_t uhla_forward_workspace_bytes(int B, int H, int W, int w, int H_lr, int W_
  * and not a multiple of 16; more than 1024 key tiles of 64 keys per window, counting
  * the neighbour windows' tiles and, in the masked variant, the guide cell blocks; B or
  * heads above 65535; grids, guide grids or text too large for 32-bit row and workgroup
- * indices); UHLA_ERR_WORKSPACE; UHLA_ERR_HIP.
+ * indices; a (batch, head) region of K or V rows above 4 GiB, i.e. H*W rows, or the guide
+ * rows rounded up to 64 plus the text rows rounded up to 64, times head_dim * 2 bytes,
+ * above 2^32); UHLA_ERR_WORKSPACE; UHLA_ERR_HIP.
  */
 int uhla_forward(const void* q, const void* k, const void* v, void* o,
                  int B, int H, int W, int w, int H_lr, int W_lr, int rho,

@@ -150,9 +150,9 @@ def rope_joint(x: np.ndarray, geom) -> np.ndarray:
 # Mask  ([UltraGen/ar §2.B] attention-mask bullets; [UltraGen/es §2])
 # ---------------------------------------------------------------------------------
 
-def mask_rows(geom, rows: np.ndarray) -> np.ndarray:
-    """Explicit boolean mask rows (over all L keys of the [text | hi | lr] sequence) for
-    query rows ``rows``.
+def mask_block(geom, rows: np.ndarray, cols: np.ndarray) -> np.ndarray:
+    """Explicit boolean mask entries for query rows ``rows`` and key columns ``cols`` of the
+    [text | hi | lr] sequence (both raster indices into the L tokens).
 
     hi q -> hi k : allowed iff the windows differ by at most ``radius`` in both axes
                    (radius 1: the clipped 3x3 neighbourhood of the pages);
@@ -164,11 +164,11 @@ def mask_rows(geom, rows: np.ndarray) -> np.ndarray:
     text q -> any k, and any q -> text k : always.
     """
     rows = np.asarray(rows, dtype=np.int64)
+    key = np.asarray(cols, dtype=np.int64)
     T = getattr(geom, "T", 0)
-    N, L, w = geom.N, geom.L, geom.w
+    N, w = geom.N, geom.w
     r = getattr(geom, "radius", 1)
     mode = getattr(geom, "guide_mode", 0)
-    key = np.arange(L, dtype=np.int64)
     key_is_text = key < T
     key_is_hi = (key >= T) & (key < T + N)
     key_is_lr = key >= T + N
@@ -196,6 +196,12 @@ def mask_rows(geom, rows: np.ndarray) -> np.ndarray:
     lr_lr = q_is_lr[:, None] & key_is_lr[None, :]
     text = q_is_text[:, None] | key_is_text[None, :]
     return hi_hi | hi_lr | lr_lr | text
+
+
+def mask_rows(geom, rows: np.ndarray) -> np.ndarray:
+    """Explicit boolean mask rows over all L keys for query rows ``rows`` (the rules of
+    ``mask_block``)."""
+    return mask_block(geom, rows, np.arange(geom.L, dtype=np.int64))
 
 
 # ---------------------------------------------------------------------------------
@@ -333,9 +339,14 @@ def backward(q, k, v, do, geom):
 
 def backward_rows(q, k, v, do, geom, b: int, h: int, q_rows, k_rows, block: int = 512):
     """Rows of the backward of one (batch, head) without the full L x L matrices:
-    (dQ[q_rows], dK[k_rows], dV[k_rows]), fp64.  Same definitions as ``backward``: each
-    query row's probabilities come from its LSE, D_i = dO_i . O_i, and a key's gradients sum
-    over the query rows whose mask row allows it."""
+    (dQ[q_rows], dK[k_rows], dV[k_rows]), fp64.
+
+    The arithmetic of ``backward`` restricted to the query rows that matter: the rows in
+    ``q_rows`` and every query row whose mask row allows one of ``k_rows`` (a key's
+    gradients sum over those rows only; every other entry of its column of P and dS is
+    zero).  For each block of those rows: P = masked softmax of the row block over all L
+    keys, dP = dO V^T, dS = P * (dP - rowsum(dP * P)); dV[k] and dK~[k] sum P[:, k] dO and
+    s dS[:, k] Q~ over the block, dQ~ = s dS K~; dQ, dK rotate back."""
     q_rows = np.asarray(q_rows, dtype=np.int64)
     k_rows = np.asarray(k_rows, dtype=np.int64)
     L = q.shape[1]
@@ -343,26 +354,22 @@ def backward_rows(q, k, v, do, geom, b: int, h: int, q_rows, k_rows, block: int 
     qr, kr = rotated_qk(q, k, geom, b, h)
     vv = v[b, :, h].astype(np.float64)
     g = do[b, :, h].astype(np.float64)
-    # queries that see any requested key
     need = np.zeros(L, dtype=bool)
     need[q_rows] = True
-    for s0 in range(0, L, block) if len(k_rows) else ():
-        blk = np.arange(s0, min(L, s0 + block))
-        need[blk] |= mask_rows(geom, blk)[:, k_rows].any(axis=1)
+    if len(k_rows):
+        for s0 in range(0, L, 8 * block):
+            blk = np.arange(s0, min(L, s0 + 8 * block))
+            need[blk] |= mask_block(geom, blk, k_rows).any(axis=1)
     rows = np.nonzero(need)[0]
-    lse = lse_rows(q, k, geom, b, h, rows, block, qk=(qr, kr))
-    o = attention_rows(q, k, v, geom, b, h, rows, block, qk=(qr, kr))
-    dd = (g[rows] * o).sum(axis=1)
-    where = {int(r): i for i, r in enumerate(rows)}
     dq = np.zeros((len(q_rows), q.shape[-1]))
     dk = np.zeros((len(k_rows), q.shape[-1]))
     dv = np.zeros((len(k_rows), q.shape[-1]))
     for s0 in range(0, len(rows), block):
         blk = rows[s0:s0 + block]
-        m = mask_rows(geom, blk)
-        sc = np.where(m, (qr[blk] @ kr.T) * geom.scale, -np.inf)
-        p = np.exp(sc - lse[s0:s0 + len(blk), None])
-        ds = p * (g[blk] @ vv.T - dd[s0:s0 + len(blk), None])
+        _, p = masked_softmax_attention(qr[blk], kr, vv, mask_rows(geom, blk), geom.scale,
+                                        return_probs=True)
+        dp = g[blk] @ vv.T
+        ds = p * (dp - (dp * p).sum(axis=1, keepdims=True))
         dv += p[:, k_rows].T @ g[blk]
         dk += geom.scale * (ds[:, k_rows].T @ qr[blk])
         for i, r in enumerate(blk):

@@ -135,6 +135,15 @@ def fwd_args(**kw):
     (dict(H=384, W=384, w=96, H_lr=0, W_lr=0), api.UHLA_ERR_UNSUPPORTED),
     (dict(B=65536), api.UHLA_ERR_UNSUPPORTED),  # grid dimension limits
     (dict(heads=65536), api.UHLA_ERR_UNSUPPORTED),
+    # one head of a 4096 x 8192 grid at head_dim 128: 8 GiB of K (or V) rows per (batch,
+    # head), past the kernels' 32-bit tile byte offsets
+    (dict(heads=1, H=4096, W=8192, w=16, H_lr=0, W_lr=0, d=128), api.UHLA_ERR_UNSUPPORTED),
+    # the same for the guide rows: 2^25 guide tokens of head_dim 128
+    (dict(heads=1, H=64, W=64, w=16, H_lr=4096, W_lr=8192, d=128), api.UHLA_ERR_UNSUPPORTED),
+    # exactly 4 GiB per (batch, head) region is still addressable: it passes validation
+    # and stops at the (too small) workspace
+    (dict(heads=1, H=4096, W=4096, w=16, H_lr=0, W_lr=0, d=128, wsb=1000),
+     api.UHLA_ERR_WORKSPACE),
     (dict(ws=NULL), api.UHLA_ERR_WORKSPACE),
     (dict(wsb=1000), api.UHLA_ERR_WORKSPACE),
     (dict(o=P), api.UHLA_ERR_ARG),  # aliases q

@@ -711,6 +711,117 @@ def test_backward_rows_match_full_backward():
         assert np.max(np.abs(rv - dv[0, krows, 0])) < 1e-12
 
 
+def test_backward_rows_rich_geometry_vs_autograd():
+    """backward_rows against torch autograd of the rotation-matrix forward (independent of
+    the oracle's own backward) and against the oracle's full backward, on a geometry with
+    text tokens, guide mode 2, radius 2, rho not dividing w, a ragged guide tile (35 guide
+    tokens) and guide cells past the hi grid, at (batch 1, head 1) of a 2 x 2 problem;
+    key rows from every segment (text, corner / border / interior hi windows, guide)."""
+    import torch
+    g = small_geom(B=2, heads=2, head_dim=8, H=12, W=16, w=4, H_lr=5, W_lr=7, rho=3,
+                   radius=2, guide_mode=2, T=5)
+    q, k, v = rand_qkv(g, 51)
+    do = rand_qkv(g, 52)[0]
+    T, N = g.T, g.N
+    qrows = np.array([0, T - 1, T, T + 5, T + N - 1, T + N, g.L - 1, T + 77])
+    krows = np.array([1, T, T + 3, T + 4 * g.W + 4, T + N - 1, T + N, T + N + 13, g.L - 1])
+    rq, rk, rv = orc.backward_rows(q, k, v, do, g, 1, 1, qrows, krows, block=5)
+    f = torch_attention_fn(g)
+    tq, tk, tv = (torch.from_numpy(x[1, :, 1].copy()).requires_grad_(True) for x in (q, k, v))
+    o, _ = f(tq, tk, tv)
+    o.backward(torch.from_numpy(do[1, :, 1].copy()))
+    assert np.max(np.abs(rq - tq.grad.numpy()[qrows])) < 1e-10
+    assert np.max(np.abs(rk - tk.grad.numpy()[krows])) < 1e-10
+    assert np.max(np.abs(rv - tv.grad.numpy()[krows])) < 1e-10
+    dq, dk, dv = orc.backward(q, k, v, do, g)
+    assert np.max(np.abs(rq - dq[1, qrows, 1])) < 1e-12
+    assert np.max(np.abs(rk - dk[1, krows, 1])) < 1e-12
+    assert np.max(np.abs(rv - dv[1, krows, 1])) < 1e-12
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(T=3), dict(guide_mode=1, rho=3, H_lr=5, W_lr=5),
+                                dict(guide_mode=2, radius=2, T=2), dict(radius=0, H_lr=0, W_lr=0)])
+def test_mask_block_is_a_submatrix_of_the_brute_mask(kw):
+    """mask_block(rows, cols) equals the enumerated mask restricted to those rows and
+    columns, for arbitrary (unsorted, repeated) index lists."""
+    g = small_geom(**kw)
+    full = brute_mask(g)
+    rng = np.random.default_rng(3)
+    rows = rng.integers(0, g.L, 40)
+    cols = rng.integers(0, g.L, 33)
+    assert np.array_equal(orc.mask_block(g, rows, cols), full[np.ix_(rows, cols)])
+    assert np.array_equal(orc.mask_rows(g, rows), full[rows])
+
+
+def test_uniform_probe_backward_closed_form():
+    """Q = 0: the oracle's backward gives dV[j] = sum of dO[i] / c_i over the queries that
+    see key j (tests/probes.py, used at full size on the GPU) and dK = 0 exactly."""
+    from probes import uniform_probe_dv
+    for g in (small_geom(H=12, W=16, H_lr=3, W_lr=4), small_geom(H=8, W=8, H_lr=2, W_lr=2),
+              small_geom(H=20, W=8, w=4, H_lr=5, W_lr=2, heads=2)):
+        _, k, v = rand_qkv(g, 61)
+        do = rand_qkv(g, 62)[0]
+        q = np.zeros_like(k)
+        _, dk, dv = orc.backward(q, k, v, do, g)
+        for h in range(g.heads):
+            assert np.max(np.abs(dv[0, :, h] - uniform_probe_dv(g, do[0, :, h]))) < 1e-12
+        assert np.all(dk == 0.0)
+
+
+def test_uniform_probe_dv_catches_a_dropped_neighbour():
+    """The closed form must differ from the backward of a mask without diagonal
+    neighbours (so the full-size probe catches such a mask error)."""
+    from probes import uniform_probe_dv
+    g = small_geom(H=12, W=16, H_lr=3, W_lr=4)
+    _, k, v = rand_qkv(g, 61)
+    do = rand_qkv(g, 62)[0]
+    real = orc.mask_block
+
+    def no_diagonal(geom, rows, cols):
+        m = real(geom, rows, cols)
+        rows_ = np.asarray(rows)
+        cols_ = np.asarray(cols)
+        qy, qx = (rows_ // geom.W) // geom.w, (rows_ % geom.W) // geom.w
+        ky, kx = (cols_ // geom.W) // geom.w, (cols_ % geom.W) // geom.w
+        diag = (np.abs(qy[:, None] - ky[None, :]) == 1) & (np.abs(qx[:, None] - kx[None, :]) == 1)
+        hi = (rows_[:, None] < geom.N) & (cols_[None, :] < geom.N)
+        return m & ~(diag & hi)
+    orc.mask_block = no_diagonal
+    try:
+        _, _, dv = orc.backward(np.zeros_like(k), k, v, do, g)
+    finally:
+        orc.mask_block = real
+    assert np.max(np.abs(dv[0, :, 0] - uniform_probe_dv(g, do[0, :, 0]))) > 1e-3
+
+
+def test_sharp_gate_catches_a_dropped_neighbour():
+    """With Q scaled by 4 each row's softmax concentrates on a few keys, so a mask that
+    drops the diagonal neighbour windows moves the output far beyond the sharp gate's
+    tolerance (2e-2 of the output's max, 1e-2 of its mean; tests/test_gpu_parity_full.py),
+    while the unscaled case shows why the plain tolerance alone is weak."""
+    g = small_geom(head_dim=64, H=48, W=48, w=16, H_lr=12, W_lr=12)
+    q, k, v = rand_qkv(g, 71)
+    real = orc.mask_block
+
+    def no_diagonal(geom, rows, cols):
+        m = real(geom, rows, cols)
+        rows_, cols_ = np.asarray(rows), np.asarray(cols)
+        qy, qx = (rows_ // geom.W) // geom.w, (rows_ % geom.W) // geom.w
+        ky, kx = (cols_ // geom.W) // geom.w, (cols_ % geom.W) // geom.w
+        diag = (np.abs(qy[:, None] - ky[None, :]) == 1) & (np.abs(qx[:, None] - kx[None, :]) == 1)
+        hi = (rows_[:, None] < geom.N) & (cols_[None, :] < geom.N)
+        return m & ~(diag & hi)
+    good = orc.forward(4 * q, k, v, g)
+    orc.mask_block = no_diagonal
+    try:
+        bad = orc.forward(4 * q, k, v, g)
+    finally:
+        orc.mask_block = real
+    d = np.abs(good - bad)
+    assert d.max() > 10 * 2e-2 * np.abs(good).max()
+    assert d.mean() > 5 * 1e-2 * np.abs(good).mean()
+
+
 # --------------------------------------------------------- planted mistakes must be caught
 
 def _mut_index_transposed(H, W, w):
