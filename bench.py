@@ -19,11 +19,13 @@ value       effective TFLOP/s of the whole step: algorithmic FLOPs (4 * head_dim
 roofline    the dominant kernel (hi-res attention pass) against the bf16 MFMA peak:
             its algorithmic FLOPs per launch / its mean launch duration, measured with
             HIP events recorded on the launch stream during the timed steps.
-cpu_baseline  the fp64 oracle on a time-bounded sample of query rows of the same
-            workload, on this host's cores, in the same unit.
+cpu_baseline  the fp64 oracle on a time-bounded, stratified sample of query rows of four
+            heads of the same workload, on this host's cores, in the same unit, with the
+            full oracle time extrapolated from it (labelled as such).
 attention_passes  the same FLOPs over the attention passes alone (prep excluded).
 permute     the standalone uhla_window_permute of the Q hi segment in GB/s, beside a plain
-            device-to-device copy of the same bytes.
+            device-to-device copy of the same bytes and uhla_copy_probe of the same bytes
+            through each load path (plain, nontemporal, direct-to-LDS).
 """
 from __future__ import annotations
 
@@ -300,6 +302,17 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     copy_gbs = perm_bytes / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+    # uhla_copy_probe of the same bytes through each load path the kernels use: the
+    # known-size copies the HBM traffic counters are calibrated against
+    copy_paths = {}
+    for mode, name in ((0, "plain"), (1, "nontemporal"), (2, "direct_to_lds")):
+        api.copy_probe(psrc, pdst, mode)
+        e0.record()
+        for _ in range(3):
+            api.copy_probe(psrc, pdst, mode)
+        e1.record()
+        torch.cuda.synchronize()
+        copy_paths[name] = round(perm_bytes / (e0.elapsed_time(e1) / 3 * 1e-3) / 1e9, 1)
     del pdst, psrc
 
     traffic = None if variant else read_traffic()
@@ -343,7 +356,8 @@ def main():
         "permute": {"entry_point": "uhla_window_permute (Q hi segment, bf16)",
                     "ms": round(perm_ms, 4), "GB/s": round(perm_gbs, 1),
                     "frac_hbm_peak": round(perm_gbs / PEAK_HBM_GBS, 4),
-                    "device_copy_GB/s": round(copy_gbs, 1)},
+                    "device_copy_GB/s": round(copy_gbs, 1),
+                    "copy_probe_GB/s": copy_paths},
     }
     if not args.no_cpu_baseline:
         log(f"[bench] CPU baseline: oracle for ~{args.cpu_seconds:.0f} s")

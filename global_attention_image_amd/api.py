@@ -46,6 +46,8 @@ EXPORTS = {
     "uhla_backward": (ctypes.c_int, [ctypes.c_void_p] * 9 + [ctypes.c_int] * 10
                       + [ctypes.c_float, ctypes.c_float, ctypes.c_int, ctypes.c_int,
                          ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "uhla_copy_probe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                       ctypes.c_int, ctypes.c_void_p]),
     "uhla_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "uhla_last_error_detail": (ctypes.c_char_p, []),
     "uhla_timer_create": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_void_p)]),
@@ -157,6 +159,19 @@ def rope_apply(src, dst, H, W, H_lr, W_lr, rho=4, theta=10000.0, w=0, hi_order=0
     st = load().uhla_rope_apply(_ptr(src), _ptr(dst), B, H, W, w, hi_order, H_lr, W_lr, rho,
                                 Hh, d, float(theta), _stream(src))
     _check(st, "uhla_rope_apply")
+    return dst
+
+
+def copy_probe(src, dst, mode):
+    """Copy all bytes of ``src`` into ``dst`` (same byte size, a multiple of 16384) through
+    load path ``mode`` (0 plain, 1 nontemporal, 2 direct-to-LDS); a measurement aid."""
+    _require(src, "src")
+    _require(dst, "dst")
+    nb = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nb:
+        raise ValueError("src and dst must hold the same number of bytes")
+    _check(load().uhla_copy_probe(_ptr(src), _ptr(dst), nb, int(mode), _stream(src)),
+           "uhla_copy_probe")
     return dst
 
 

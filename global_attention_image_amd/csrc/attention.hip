@@ -253,7 +253,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_k_kernel(
   }
 
   const int cpr = heads * CPH;  // chunks per row
-  // task i = (row t, chunk c); t and c advance without divisions
+  // task i = (row t, chunk c); t and c advance without divisions.  K is read and written
+  // with nontemporal loads and stores: each byte is touched once here.
   int t = tid / cpr, c = tid - (tid / cpr) * cpr;
   for (; t < kPrepRows; ) {
     const int h = c / CPH, j = c % CPH;
@@ -262,7 +263,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_k_kernel(
     bf16_t* dq = dq_s[t];
     if (src >= 0) {
       const int64_t so = ((b * L + src) * heads + h) * D + j * 8;
-      const uint4 ki = *reinterpret_cast<const uint4*>(k + so);
+      const u32x4 kv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k + so));
+      const uint4 ki = make_uint4(kv[0], kv[1], kv[2], kv[3]);
       if (rope_on) {
         // pairs 4j .. 4j+3 lie on one axis (y for the first D/4 pairs)
         const int axis = (4 * j) / QUARTER, k0 = 4 * j - axis * QUARTER;
@@ -286,7 +288,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_k_kernel(
     if (dq) *reinterpret_cast<uint4*>(dq + h * qst_s[t] + j * 8) = qo;
     bf16_t* dk = dk_s[t];
     bf16_t* dk2 = dk2_s[t];
-    if (dk) *reinterpret_cast<uint4*>(dk + h * kst_s[t] + j * 8) = ko;
+    if (dk) __builtin_nontemporal_store(u32x4{ko.x, ko.y, ko.z, ko.w}, reinterpret_cast<u32x4*>(dk + h * kst_s[t] + j * 8));
     if (dk2) *reinterpret_cast<uint4*>(dk2 + h * k2st_s[t] + j * 8) = ko;
     c += kPrepThreads;
     while (c >= cpr) {
@@ -297,7 +299,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_k_kernel(
 }
 
 // V rows -> 64-key tiles transposed to [D][64] (key order by v_slot); one (tile, head, batch)
-// per workgroup (grid: tiles x heads x B).  Tiles of a batch:
+// per workgroup (grid: tiles * heads, B).  Tiles of a batch:
 // [0, N/64) window-first hi rows -> v_hi; the next Mg/64 the global keys -> v_lr (guide
 // rows in raster order, zero padded to Mk, then text rows); the last Mbg/64 the cell-block
 // buffer -> v_gb (guide cells in 8x8 block order, then text rows).  Input rows are
@@ -308,9 +310,11 @@ __global__ __launch_bounds__(kPrepThreads) void prep_v_kernel(
     int n_wx, int H_lr, int W_lr, int nbj, int heads, int D) {
   __shared__ __attribute__((aligned(16))) bf16_t tile[kKeyTile][128 + 2];
   const int64_t L = T + N + M;
-  const int64_t b = blockIdx.z;
-  const int h = blockIdx.y;
-  const int64_t tile_id = blockIdx.x;
+  const int64_t b = blockIdx.y;
+  // heads vary fastest over the grid, so the workgroups reading the same raster rows
+  // (one head's 256-byte slice each) run together
+  const int h = static_cast<int>(blockIdx.x % heads);
+  const int64_t tile_id = blockIdx.x / heads;
   const int64_t n_hi = N / kKeyTile, n_g = Mg / kKeyTile;
   const int chunks_per_row = D / 8;
   // source row (or -1) of key kr of this tile
@@ -327,7 +331,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_v_kernel(
     block_cell(r, nbj, ci, cj);
     return (ci < H_lr && cj < W_lr) ? T + N + static_cast<int64_t>(ci) * W_lr + cj : -1;
   };
-  // load 64 rows x D of head h (16-byte chunks; all of a thread's loads before its stores)
+  // load 64 rows x D of head h (16-byte chunks; all of a thread's loads before its stores;
+  // nontemporal, as every byte is read and written once here)
   constexpr int kLoads = kKeyTile * 16 / kPrepThreads;  // chunks per thread for D = 128
   uint4 x[kLoads];
 #pragma unroll
@@ -337,7 +342,10 @@ __global__ __launch_bounds__(kPrepThreads) void prep_v_kernel(
     if (i < kKeyTile * chunks_per_row) {
       const int kr = i / chunks_per_row, j = i - kr * chunks_per_row;
       const int64_t src_row = source(kr);
-      if (src_row >= 0) x[u] = *reinterpret_cast<const uint4*>(v + ((b * L + src_row) * heads + h) * D + j * 8);
+      if (src_row >= 0) {
+        const u32x4 xv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v + ((b * L + src_row) * heads + h) * D + j * 8));
+        x[u] = make_uint4(xv[0], xv[1], xv[2], xv[3]);
+      }
     }
   }
 #pragma unroll
@@ -370,8 +378,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_v_kernel(
       const uint32_t hi = tile[v_slot(s8 + 2 * e + 1)][d];
       wv[e] = lo | (hi << 16);
     }
-    *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(d) * kKeyTile + s8) =
-        make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    __builtin_nontemporal_store(u32x4{wv[0], wv[1], wv[2], wv[3]},
+                                reinterpret_cast<u32x4*>(dst + static_cast<int64_t>(d) * kKeyTile + s8));
   }
 }
 
@@ -1121,7 +1129,7 @@ static int64_t max_table_tiles(const Geom& g) {
   return best;
 }
 
-static int validate_forward(const void* q, const void* k, const void* v, void* o, int B,
+int validate_forward(const void* q, const void* k, const void* v, void* o, int B,
                             int64_t T, int H, int W, int w, int H_lr, int W_lr, int rho,
                             int heads, int D, int radius, int guide_mode) {
   if (!q || !k || !v || !o) return fail_arg("null pointer");
@@ -1162,11 +1170,11 @@ static int validate_forward(const void* q, const void* k, const void* v, void* o
   return UHLA_OK;
 }
 
-static int forward_impl(const void* q, const void* k, const void* v, void* o, int B, int64_t T,
+int forward_impl(const void* q, const void* k, const void* v, void* o, int B, int64_t T,
                         int H, int W, int w, int H_lr, int W_lr, int rho, int heads, int D,
                         float scale, float theta, int radius, int guide_mode, void* workspace,
                         size_t workspace_bytes, void* stream, uhla_timer* timer,
-                        float* lse = nullptr, bool rope_k_at_load = false) {
+                        float* lse, bool rope_k_at_load) {
   int st = validate_forward(q, k, v, o, B, T, H, W, w, H_lr, W_lr, rho, heads, D, radius, guide_mode);
   if (st) return st;
   if (rope_k_at_load && w * w < kMaxQuery)
@@ -1235,7 +1243,8 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
     st = check_launch("prep_k_kernel");
     if (st) return st;
     const int64_t tiles = (g.N + g.Mg + g.Mbg) / kKeyTile;
-    UHLA_STEP(hipLaunchKernelGGL(prep_v_kernel, dim3(static_cast<unsigned>(tiles), heads, B), dim3(kPrepThreads), 0, s,
+    if (tiles * heads > 0x7fffffff) return fail_unsupported("problem too large");
+    UHLA_STEP(hipLaunchKernelGGL(prep_v_kernel, dim3(static_cast<unsigned>(tiles * heads), B), dim3(kPrepThreads), 0, s,
                                  vb, ws.v_hi, ws.v_lr, ws.v_gb, T, g.N, g.M, g.Mk, g.Mg, g.Mb, g.Mbg,
                                  W, w, g.n_wx, H_lr, W_lr, g.nbj, heads, D),
               "prep_v_kernel");
@@ -1320,7 +1329,7 @@ static int forward_impl(const void* q, const void* k, const void* v, void* o, in
   return UHLA_OK;
 }
 
-static size_t workspace_bytes(int B, int64_t T, int H, int W, int w, int H_lr, int W_lr, int rho,
+size_t workspace_bytes(int B, int64_t T, int H, int W, int w, int H_lr, int W_lr, int rho,
                               int heads, int head_dim, int radius, int guide_mode) {
   if (B < 1 || H < 1 || W < 1 || w < 1 || heads < 1 || H_lr < 0 || W_lr < 0 || T < 0) return 0;
   if (H % w || W % w || (H_lr == 0) != (W_lr == 0)) return 0;
@@ -1414,3 +1423,4 @@ extern "C" int uhla_forward_rope_at_load(const void* q, const void* k, const voi
   return uhla::forward_impl(q, k, v, o, B, 0, H, W, w, H_lr, W_lr, rho, heads, head_dim, scale,
                             theta, 1, 0, workspace, workspace_bytes, stream, timer, nullptr, true);
 }
+

@@ -101,4 +101,20 @@ inline bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// ---------------------------------------------------------------- the forward (attention.hip)
+
+// Host-side argument checks of the forward entry points (no device call).
+int validate_forward(const void* q, const void* k, const void* v, void* o, int B, int64_t T,
+                     int H, int W, int w, int H_lr, int W_lr, int rho, int heads, int D,
+                     int radius, int guide_mode);
+// Workspace bytes of the forward for this geometry (0 on invalid geometry).
+size_t workspace_bytes(int B, int64_t T, int H, int W, int w, int H_lr, int W_lr, int rho,
+                       int heads, int head_dim, int radius, int guide_mode);
+// The forward: validation, then every launch on `stream`, scratch in `workspace`.
+int forward_impl(const void* q, const void* k, const void* v, void* o, int B, int64_t T, int H,
+                 int W, int w, int H_lr, int W_lr, int rho, int heads, int D, float scale,
+                 float theta, int radius, int guide_mode, void* workspace,
+                 size_t workspace_bytes, void* stream, uhla_timer* timer,
+                 float* lse = nullptr, bool rope_k_at_load = false);
+
 }  // namespace uhla

@@ -287,6 +287,21 @@ int uhla_forward_rope_at_load(const void* q, const void* k, const void* v, void*
                               void* workspace, size_t workspace_bytes, void* stream,
                               uhla_timer* timer);
 
+/*
+ * Measurement aid: copies `bytes` bytes from src to dst (device memory, 16-byte aligned,
+ * not overlapping) through one of the global-memory load paths the library's kernels use,
+ * so that memory-traffic counters can be read against a known byte count per path:
+ *   mode 0: plain 16-byte vector loads and stores;
+ *   mode 1: nontemporal 16-byte loads and stores (the path of uhla_window_permute);
+ *   mode 2: 16-byte loads straight into LDS (global_load_lds_dwordx4, the path the
+ *           attention kernels stage their K and V tiles with), then LDS reads and plain
+ *           stores.
+ * The copy is bit-exact.  Errors: UHLA_ERR_ARG for null or misaligned pointers, bytes not a
+ * positive multiple of 16384, mode outside 0..2, overlapping buffers;
+ * UHLA_ERR_UNSUPPORTED above 2^31 blocks of 16384 bytes; UHLA_ERR_HIP.
+ */
+int uhla_copy_probe(const void* src, void* dst, int64_t bytes, int mode, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

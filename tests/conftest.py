@@ -27,3 +27,25 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+# Error figures that passing GPU parity tests print (their "max-abs ..." lines) are
+# collected and listed at the end of the run, so the errors are on record even when
+# pytest captures a passing test's output.
+_PARITY_LINES = []
+
+
+def pytest_runtest_logreport(report):
+    if report.when != "call" or not report.passed or "gpu" not in report.keywords:
+        return
+    name = report.nodeid.split("::")[-1]
+    for line in report.capstdout.splitlines():
+        if "max-abs" in line or "bit-identical" in line or "sum rule" in line:
+            _PARITY_LINES.append(f"{name}: {line.strip()}")
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    if _PARITY_LINES:
+        terminalreporter.section("errors against the oracle (passing GPU tests)")
+        for line in _PARITY_LINES:
+            terminalreporter.write_line(line)

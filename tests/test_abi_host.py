@@ -364,3 +364,17 @@ def test_backward_workspace_bytes(lib, g, T, mode):
     assert f(B, T, H, W, w, H_lr, W_lr, 4, heads, 96, 1, mode) == 0
     assert f(B, -1, H, W, w, H_lr, W_lr, 4, heads, d, 1, mode) == 0
     assert f(B, T, H, W, w, H_lr, W_lr, 4, heads, d, 1, 3) == 0
+
+
+@pytest.mark.parametrize("args,status", [
+    ((NULL, P2, 16384, 0), api.UHLA_ERR_ARG),
+    ((P, NULL, 16384, 0), api.UHLA_ERR_ARG),
+    ((P, P2, 0, 0), api.UHLA_ERR_ARG),
+    ((P, P2, 16000, 1), api.UHLA_ERR_ARG),   # not a multiple of 16384
+    ((P, P2, 16384, 3), api.UHLA_ERR_ARG),
+    ((P, P2, 16384, -1), api.UHLA_ERR_ARG),
+    ((ctypes.c_void_p(0x10000008), P2, 16384, 0), api.UHLA_ERR_ARG),  # misaligned
+    ((P, ctypes.c_void_p(0x10000000 + 8192), 16384, 2), api.UHLA_ERR_ARG),  # overlap
+])
+def test_copy_probe_rejects(lib, args, status):
+    assert lib.uhla_copy_probe(*args, NULL) == status
