@@ -46,6 +46,8 @@ EXPORTS = {
     "uhla_backward": (ctypes.c_int, [ctypes.c_void_p] * 9 + [ctypes.c_int] * 10
                       + [ctypes.c_float, ctypes.c_float, ctypes.c_int, ctypes.c_int,
                          ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "uhla_forward_noalloc": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_int] * 9
+                             + [ctypes.c_float, ctypes.c_float, ctypes.c_void_p]),
     "uhla_copy_probe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                        ctypes.c_int, ctypes.c_void_p]),
     "uhla_strerror": (ctypes.c_char_p, [ctypes.c_int]),
@@ -160,6 +162,26 @@ def rope_apply(src, dst, H, W, H_lr, W_lr, rho=4, theta=10000.0, w=0, hi_order=0
                                 Hh, d, float(theta), _stream(src))
     _check(st, "uhla_rope_apply")
     return dst
+
+
+def forward_noalloc(q, k, v, H, W, w, H_lr, W_lr, rho=4, scale=0.0, theta=10000.0, out=None):
+    """uhla_forward with the library's static scratch instead of a workspace (no device
+    allocation inside the call; ``out`` must be given to avoid allocating it here)."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, n, torch.bfloat16)
+    if not (q.shape == k.shape == v.shape) or q.dim() != 4:
+        raise ValueError("q, k, v must share one [B, L, heads, head_dim] shape")
+    B, L, Hh, d = q.shape
+    if L != H * W + H_lr * W_lr:
+        raise ValueError("token count does not match the grids")
+    if out is None:
+        out = torch.empty_like(q)
+    _require(out, "out", torch.bfloat16)
+    st = load().uhla_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, W, w, H_lr,
+                                     W_lr, rho, Hh, d, float(scale), float(theta), _stream(q))
+    _check(st, "uhla_forward_noalloc")
+    return out
 
 
 def copy_probe(src, dst, mode):

@@ -14,7 +14,8 @@
  *   joint [hi | guide] part of the text | image | guide sequence of [UltraGen/it §2].
  * - Device pointers are HIP device memory owned by the caller.  The library never
  *   allocates, frees or synchronises (except uhla_timer_read), keeps no global mutable
- *   state and may be called from several host threads on different streams.
+ *   state (except the static scratch of uhla_forward_noalloc) and may be called from
+ *   several host threads on different streams.
  * - `stream` is a hipStream_t (NULL = the legacy default stream).  All work is enqueued
  *   asynchronously on it.
  * - Every function returns a uhla_status; nothing throws across the ABI.  Argument
@@ -286,6 +287,23 @@ int uhla_forward_rope_at_load(const void* q, const void* k, const void* v, void*
                               int heads, int head_dim, float scale, float theta,
                               void* workspace, size_t workspace_bytes, void* stream,
                               uhla_timer* timer);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): uhla_forward without a workspace
+ * argument.  Its scratch memory is a 64 MiB (67108864-byte) array in the library's device
+ * code, one per GPU, held until the process ends; the call allocates nothing and calls no
+ * allocating routine.  The first call on a device looks up that device's array with the
+ * device current (the stream must belong to the current device).  Every call on one GPU
+ * shares its array and rewrites what it reads of it, so calls in stream order are
+ * independent, but calls that overlap on one GPU (other streams or host threads) race.
+ * Same arguments (without workspace), result (bit for bit) and errors as uhla_forward,
+ * plus UHLA_ERR_WORKSPACE when uhla_forward_workspace_bytes(...) of the problem exceeds
+ * 64 MiB.
+ */
+int uhla_forward_noalloc(const void* q, const void* k, const void* v, void* o,
+                         int B, int H, int W, int w, int H_lr, int W_lr, int rho,
+                         int heads, int head_dim, float scale, float theta, void* stream);
 
 /*
  * Measurement aid: copies `bytes` bytes from src to dst (device memory, 16-byte aligned,
