@@ -430,7 +430,13 @@ constexpr int kPvAhead = 4;  // V fragment reads in flight ahead of the PV MFMAs
 // K/V tiles are copied global -> LDS by the DMA path of global_load_lds_dwordx4 (lane l of
 // a load writes LDS bytes [16 l, 16 l + 16) above the wave's base), two iterations ahead of
 // their first use.  Each lane picks the global 16-byte chunk that belongs at its LDS slot
-// under the XOR swizzle, so the LDS layout is the one the fragment reads expect.
+// under the XOR swizzle, so the LDS layout is the one the fragment reads expect.  Every
+// iteration issues the same copies (past the last tile it copies a tile again into a stage
+// nobody reads any more), so the loop has no per-copy branches and one fixed wait.  The
+// first V fragments of each PV block are read ahead of it (wave A before the barrier that
+// ends the previous iteration, wave B right after its softmax), and the first K fragments
+// of each QK^T block before the PV block that precedes it, so neither block's first MFMA
+// waits for LDS.
 //
 // ROTK (uhla_forward_rope_at_load): K arrives unrotated and every workgroup rotates each K
 // tile in LDS after it lands (RoPE fused into the K tile load), instead of K being rotated
@@ -596,21 +602,28 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
     tile_src(t, kp, vp);
     issue_parts(nullptr, vp, dst, dst, 0, LOADS_PER_TILE);
   };
-  // Keys of tile t that exist (a prefix: the guide rows and the text rows of the global
-  // buffer each end in a partial tile) ...
-  auto global_valid = [&](int64_t r) __attribute__((always_inline)) -> int {
-    const int64_t rem = r < a.Mk ? a.M - r : a.T - (r - a.Mk);
-    return rem < kKeyTile ? static_cast<int>(rem) : kKeyTile;
-  };
-  auto tile_valid = [&](int t) __attribute__((always_inline)) -> int {
-    if (HI && t < n_local) return kKeyTile;
-    if (RECT) {
-      if (t < n_local + n_rect) return kKeyTile;  // cell blocks: the cell mask decides
-      const int64_t rem = a.T - static_cast<int64_t>(t - n_local - n_rect) * kKeyTile;
-      return rem < kKeyTile ? static_cast<int>(rem) : kKeyTile;
+  // Keys of tile t that exist (a prefix): only the last guide tile and the last text tile
+  // of the global buffer can be partial, so their tile indices (-1: none) and key counts
+  // are found once and the loop tests two scalars per tile ...
+  int part_t0 = -1, part_v0 = kKeyTile, part_t1 = -1, part_v1 = kKeyTile;
+  if (RECT) {
+    if (a.T % kKeyTile) {
+      part_t1 = n_local + n_rect + static_cast<int>(a.T / kKeyTile);
+      part_v1 = static_cast<int>(a.T % kKeyTile);
     }
-    if (TEXT && t + t_base < n_hi_tiles) return kKeyTile;
-    return global_valid(static_cast<int64_t>(t + t_base - (TEXT ? n_hi_tiles : n_local)) * kKeyTile);
+  } else {
+    const int goff = TEXT ? n_hi_tiles - t_base : n_local;  // tile t = global tile t - goff
+    if (a.M % kKeyTile) {
+      part_t0 = static_cast<int>(a.M / kKeyTile) + goff;
+      part_v0 = static_cast<int>(a.M % kKeyTile);
+    }
+    if (a.T % kKeyTile) {
+      part_t1 = static_cast<int>(a.Mk / kKeyTile + a.T / kKeyTile) + goff;
+      part_v1 = static_cast<int>(a.T % kKeyTile);
+    }
+  }
+  auto tile_valid = [&](int t) __attribute__((always_inline)) -> int {
+    return t == part_t0 ? part_v0 : t == part_t1 ? part_v1 : kKeyTile;
   };
   // ... and, for a cell-block guide tile, which of its 8x8 cells are visible: bits 0-7 the
   // rows, bits 8-15 the columns (0xffff: all).
@@ -690,12 +703,15 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   };
 
   // Query fragment (B operand of S^T = K Q^T): lane holds query ql, dims 16kk + 8g .. +8,
-  // read from the caller's Q row and rotated here (RoPE fused into the Q load): fp64
-  // rotation times the softmax scale * log2 e, one rounding to bf16, so the scores come out
-  // in base-2 logits.  Hi queries sit at their raster position, guide query s at
-  // (rho * (s / W_lr), rho * (s % W_lr)), text queries at (0, 0); rows past the pass's
-  // valid rows are zero.  With q_pre (guide modes 1, 2, whose workgroups have few tiles)
-  // the rows come prepared by the prep pass instead, with the same rotation and rounding.
+  // read from the caller's Q row and rotated here (RoPE fused into the Q load): the fp64
+  // cos/sin factors rounded to fp32 and multiplied by the softmax scale * log2 e, the
+  // rotation in fp32 and one rounding to bf16, so the scores come out in base-2 logits
+  // (fp32 instead of fp64 arithmetic here cuts the exposed work before a workgroup's first
+  // tile; the result differs from a correctly rounded fp64 rotation in rare last-bit cases).
+  // Hi queries sit at their raster position, guide query s at (rho * (s / W_lr),
+  // rho * (s % W_lr)), text queries at (0, 0); rows past the pass's valid rows are zero.
+  // With q_pre (guide modes 1, 2, whose workgroups have few tiles) the rows come prepared
+  // by the prep pass instead (rotated and scaled in fp64, one rounding).
   bf16x8 qf[D / 16];
   {
     constexpr int QUARTER = D / 4;
@@ -736,8 +752,16 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               f[e] = pos < a.P ? a.cs[pos * QUARTER + k0 + e] : rope_cos_sin(pos, k0 + e, D / 2, a.log2_theta);
-            qo = make_uint4(rope_rotate_word(raw[kk].x, f[0], a.q_scale), rope_rotate_word(raw[kk].y, f[1], a.q_scale),
-                            rope_rotate_word(raw[kk].z, f[2], a.q_scale), rope_rotate_word(raw[kk].w, f[3], a.q_scale));
+            const float qs = static_cast<float>(a.q_scale);
+            const uint32_t wi[4] = {raw[kk].x, raw[kk].y, raw[kk].z, raw[kk].w};
+            uint32_t wo[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float c = static_cast<float>(f[e].x) * qs, sn = static_cast<float>(f[e].y) * qs;
+              const float x0 = lo_bf16(wi[e]), y0 = hi_bf16(wi[e]);
+              wo[e] = pack_bf16x2(x0 * c - y0 * sn, x0 * sn + y0 * c);
+            }
+            qo = make_uint4(wo[0], wo[1], wo[2], wo[3]);
           } else {
             qo = make_uint4(scale_word(raw[kk].x, a.q_scale), scale_word(raw[kk].y, a.q_scale),
                             scale_word(raw[kk].z, a.q_scale), scale_word(raw[kk].w, a.q_scale));
@@ -775,24 +799,32 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   // S^T = K Q^T - m.  K fragments are read kQkAhead reduction steps ahead of their MFMAs;
   // the scheduling barriers keep the compiler from sinking each read next to its use,
   // which would expose the full LDS latency at every step.
-  auto qk = [&](const char* kb) __attribute__((always_inline)) {
-    constexpr int KS = D / 16, AH = kQkAhead < KS ? kQkAhead : KS;
-    bf16x8 f0[KS], f1[KS];
+  constexpr int QKS = D / 16, QAH = kQkAhead < QKS ? kQkAhead : QKS;
+  // the first QAH K fragment pairs of a QK^T block, read ahead of the block
+  auto qk_pre = [&](const char* kb, bf16x8 (&a0)[QAH], bf16x8 (&a1)[QAH]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kk = 0; kk < AH; ++kk) {
-      f0[kk] = k_frag(kb, kk, 0);
-      f1[kk] = k_frag(kb, kk, 1);
+    for (int kk = 0; kk < QAH; ++kk) {
+      a0[kk] = k_frag(kb, kk, 0);
+      a1[kk] = k_frag(kb, kk, 1);
+    }
+  };
+  auto qk_run = [&](const char* kb, const bf16x8 (&a0)[QAH], const bf16x8 (&a1)[QAH]) __attribute__((always_inline)) {
+    bf16x8 f0[QKS], f1[QKS];
+#pragma unroll
+    for (int kk = 0; kk < QAH; ++kk) {
+      f0[kk] = a0[kk];
+      f1[kk] = a1[kk];
     }
     s0 = neg_m;
     s1 = neg_m;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
+    for (int kk = 0; kk < QKS; ++kk) {
       __builtin_amdgcn_sched_barrier(0);
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0[kk], qf[kk], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1[kk], qf[kk], s1, 0, 0, 0);
-      if (kk + AH < KS) {
-        f0[kk + AH] = k_frag(kb, kk + AH, 0);
-        f1[kk + AH] = k_frag(kb, kk + AH, 1);
+      if (kk + QAH < QKS) {
+        f0[kk + QAH] = k_frag(kb, kk + QAH, 0);
+        f1[kk + QAH] = k_frag(kb, kk + QAH, 1);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -891,17 +923,24 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
     const int vr = dt * 32 + ql;
     return *reinterpret_cast<const bf16x8*>(vb + vr * (kKeyTile * 2) + (((2 * ks + g) ^ v_swizzle(vr)) << 4));
   };
+  constexpr int PDT = D / 32, PNI = 4 * PDT, PAH = kPvAhead < PNI ? kPvAhead : PNI;
+  // the first PAH V fragments of a PV block, read ahead of the block
+  auto pv_pre = [&](const char* vb, bf16x8 (&a)[PAH]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < PAH; ++i) a[i] = v_frag(vb, i / PDT, i % PDT);
+  };
   // O^T += V^T P^T over 4 key-steps of 16 keys; V fragments are read kPvAhead MFMAs ahead
-  auto pv = [&](const char* vb, const bf16x8 (&pf)[4]) __attribute__((always_inline)) {
-    constexpr int DT = D / 32, NI = 4 * DT, AH = kPvAhead < NI ? kPvAhead : NI;
-    bf16x8 f[NI];
+  auto pv_run = [&](const char* vb, const bf16x8 (&pf)[4], const bf16x8 (&a)[PAH]) __attribute__((always_inline)) {
+    bf16x8 f[PNI];
 #pragma unroll
-    for (int i = 0; i < AH; ++i) f[i] = v_frag(vb, i / DT, i % DT);
+    for (int i = 0; i < PAH; ++i) f[i] = a[i];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
+    for (int i = 0; i < PNI; ++i) {
       __builtin_amdgcn_sched_barrier(0);
-      o[i % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[i], pf[i / DT], o[i % DT], 0, 0, 0);
-      if (i + AH < NI) f[i + AH] = v_frag(vb, (i + AH) / DT, (i + AH) % DT);
+      o[i % PDT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[i], pf[i / PDT], o[i % PDT], 0, 0, 0);
+      if (i + PAH < PNI) {
+        f[i + PAH] = v_frag(vb, (i + PAH) / PDT, (i + PAH) % PDT);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -932,29 +971,47 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
     lds_barrier();
   }
   bf16x8 pa[4];  // wave A: P of the previous tile, consumed by the next iteration's PV
+  bf16x8 va[PAH];  // V fragments read ahead of the next PV block
+  bf16x8 ka0[QAH], ka1[QAH];  // K fragments read ahead of the next QK^T block
   // One copy of the loop per role (B = wave B), so that neither carries the other's state.
   auto run = [&]<bool B>() __attribute__((always_inline)) {
-    if (B) qk(stage0);
+    if (B) {
+      qk_pre(stage0, ka0, ka1);
+      qk_run(stage0, ka0, ka1);
+    }
     // Tile t lives in stage t % 4; S is the (compile-time) stage of tile t.
     auto step = [&]<int S>(int t) __attribute__((always_inline)) {
       char* cur = stage(S);
-      const bool k3 = t + 3 < n_tiles, v2 = t + 2 < n_tiles;
-      const char* kp = nullptr;
-      const char* vp = nullptr;
+      // K_{t+3} and V_{t+2}; past the last tile, tile t is copied again instead: the
+      // stages written then hold K_{t-1} and V_{t-2}, which are never read again, so every
+      // iteration issues the same copies and waits the same way
+      const char* kp;
+      const char* vp;
       const char* unused;
-      if (k3) tile_src(t + 3, kp, unused);
-      if (v2) tile_src(t + 2, unused, vp);
+      tile_src(t + 3 < n_tiles ? t + 3 : t, kp, unused);
+      tile_src(t + 2 < n_tiles ? t + 2 : t, unused, vp);
       char* kdst = stage((S + 3) & 3);
       char* vdst = stage((S + 2) & 3);
       auto dma_slot = [&](int slot) __attribute__((always_inline)) {
-        issue_parts(kp, vp, kdst, vdst, slot * LOADS_PER_TILE / 4, (slot + 1) * LOADS_PER_TILE / 4);
+        const uint32_t klds = lds_addr(kdst), vlds = lds_addr(vdst) + TILE_BYTES;
+#pragma unroll
+        for (int p = slot * LOADS_PER_TILE / 4; p < (slot + 1) * LOADS_PER_TILE / 4; ++p) {
+          const int i = p >> 1;
+          const uint32_t off = (i * NWAVES + wave) * 64 * 16;
+          if (p & 1) dma_16b(vp, v_src[i], __builtin_amdgcn_readfirstlane(vlds + off));
+          else dma_16b(kp, k_src[i], __builtin_amdgcn_readfirstlane(klds + off));
+        }
       };
       dma_slot(0);
       if constexpr (!B) {
+        // PV_{t-1} (its first V fragments were read at the end of the previous iteration),
+        // with K_t's first fragments read before it so that they land during it; K_t and V_t
+        // are visible in iteration t
         __builtin_amdgcn_s_setprio(1);
-        if (t > 0) pv(stage((S + 3) & 3) + TILE_BYTES, pa);
+        qk_pre(cur, ka0, ka1);
+        if (t > 0) pv_run(stage((S + 3) & 3) + TILE_BYTES, pa, va);
         dma_slot(1);
-        qk(cur);
+        qk_run(cur, ka0, ka1);
         __builtin_amdgcn_s_setprio(0);
         if constexpr (ROTK) {
           if (t + 1 < n_tiles) rotate_k(stage((S + 1) & 3), t + 1);
@@ -962,24 +1019,28 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
         }
         dma_slot(2);
         softmax(tile_valid(t), tile_mask(t), pa);
+        pv_pre(cur + TILE_BYTES, va);  // V_t, for PV_t in the next iteration
       } else {
+        // V_t's first fragments are read right after the softmax and K_{t+1}'s before PV_t
+        // (both tiles are visible in iteration t; past the last tile the K reads fetch a stale
+        // stage and go unused)
         bf16x8 pf[4];
         softmax(tile_valid(t), tile_mask(t), pf);
+        pv_pre(cur + TILE_BYTES, va);
         if constexpr (ROTK) {
           if (t + 1 < n_tiles) rotate_k(stage((S + 1) & 3), t + 1);
           lds_barrier();
         }
         __builtin_amdgcn_s_setprio(1);
         dma_slot(1);
-        pv(cur + TILE_BYTES, pf);
+        qk_pre(stage((S + 1) & 3), ka0, ka1);
+        pv_run(cur + TILE_BYTES, pf, va);
         dma_slot(2);
-        if (t + 1 < n_tiles) qk(stage((S + 1) & 3));
+        if (t + 1 < n_tiles) qk_run(stage((S + 1) & 3), ka0, ka1);
         __builtin_amdgcn_s_setprio(0);
       }
       dma_slot(3);
-      if (k3) wait_vm_and_barrier<LOADS_PER_TILE>();
-      else if (v2) wait_vm_and_barrier<LOADS_PER_TILE / 2>();
-      else wait_vm_and_barrier<0>();
+      wait_vm_and_barrier<LOADS_PER_TILE>();
     };
     int t = 0;
     for (; t + 4 <= n_tiles; t += 4) {
@@ -991,12 +1052,15 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
     if (t < n_tiles) step.template operator()<0>(t);
     if (t + 1 < n_tiles) step.template operator()<1>(t + 1);
     if (t + 2 < n_tiles) step.template operator()<2>(t + 2);
+    // the last iteration's copies (of tiles never read) land before the workgroup ends
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (!B) {
+      // PV of the last tile (its V fragments were read at the end of the last iteration)
       switch ((n_tiles - 1) & 3) {
-        case 0: pv(stage0 + TILE_BYTES, pa); break;
-        case 1: pv(stage1 + TILE_BYTES, pa); break;
-        case 2: pv(stage2 + TILE_BYTES, pa); break;
-        default: pv(stage3 + TILE_BYTES, pa); break;
+        case 0: pv_run(stage0 + TILE_BYTES, pa, va); break;
+        case 1: pv_run(stage1 + TILE_BYTES, pa, va); break;
+        case 2: pv_run(stage2 + TILE_BYTES, pa, va); break;
+        default: pv_run(stage3 + TILE_BYTES, pa, va); break;
       }
     }
   };
