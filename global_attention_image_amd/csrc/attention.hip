@@ -740,24 +740,43 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
       for (int kk = 0; kk < D / 16; ++kk) raw[kk] = *reinterpret_cast<const uint4*>(qrow + 16 * kk + 8 * g);
     }
     if (!a.q_pre) {
+      // All factor loads are issued before any is used (one wait for the Q row and the
+      // table).  Hi and text positions always lie inside the table; a guide position past
+      // it (a guide grid reaching beyond the hi-res extent) reads a clamped entry first
+      // and is then evaluated directly, with the same function that fills the table.
+      double2 f[D / 16][4];
+      if (qvalid && a.rope_on) {
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+          const int pr = 8 * kk + 4 * g, axis = pr / QUARTER, k0 = pr - axis * QUARTER;
+          const int pos = axis ? px : py, pc = pos < a.P ? pos : a.P - 1;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) f[kk][e] = a.cs[pc * QUARTER + k0 + e];
+        }
+        if (!HI && !TEXT) {
+#pragma unroll
+          for (int kk = 0; kk < D / 16; ++kk) {
+            const int pr = 8 * kk + 4 * g, axis = pr / QUARTER, k0 = pr - axis * QUARTER;
+            const int pos = axis ? px : py;
+            if (pos >= a.P) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) f[kk][e] = rope_cos_sin(pos, k0 + e, D / 2, a.log2_theta);
+            }
+          }
+        }
+      }
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
         uint4 qo = make_uint4(0, 0, 0, 0);
         if (qvalid) {
           // pairs 8kk + 4g .. +3 lie on one axis (y for the first D/4 pairs)
-          const int pr = 8 * kk + 4 * g, axis = pr / QUARTER, k0 = pr - axis * QUARTER;
           if (a.rope_on) {
-            const int pos = axis ? px : py;
-            double2 f[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              f[e] = pos < a.P ? a.cs[pos * QUARTER + k0 + e] : rope_cos_sin(pos, k0 + e, D / 2, a.log2_theta);
             const float qs = static_cast<float>(a.q_scale);
             const uint32_t wi[4] = {raw[kk].x, raw[kk].y, raw[kk].z, raw[kk].w};
             uint32_t wo[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float c = static_cast<float>(f[e].x) * qs, sn = static_cast<float>(f[e].y) * qs;
+              const float c = static_cast<float>(f[kk][e].x) * qs, sn = static_cast<float>(f[kk][e].y) * qs;
               const float x0 = lo_bf16(wi[e]), y0 = hi_bf16(wi[e]);
               wo[e] = pack_bf16x2(x0 * c - y0 * sn, x0 * sn + y0 * c);
             }
@@ -1088,23 +1107,42 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
     return;
   }
   const float inv = 1.0f / lt;
-  if (qrow < a.q_valid) {
-    // The hi pass undoes the window-first permutation here: window-first row qrow goes to
-    // its raster row, so O needs no separate inverse-permutation pass.
-    const int orow_idx = HI ? window_first_to_raster(qrow, a.W, a.w, a.n_wx) : qrow;
-    if (a.lse && g == 0)  // scores are base-2 logits: ln(sum e^s) = ln 2 (m + log2 l)
-      a.lse[static_cast<int64_t>(bh) * a.out_rows + a.out_row0 + orow_idx] =
-          (m_run + __log2f(lt)) * 0.69314718055994531f;
-    bf16_t* orow = a.out + ((static_cast<int64_t>(b) * a.out_rows + a.out_row0 + orow_idx) * a.heads + h) * D;
+  // The hi pass undoes the window-first permutation here: window-first row qrow goes to
+  // its raster row, so O needs no separate inverse-permutation pass.
+  auto out_row = [&](int qr) __attribute__((always_inline)) {
+    return HI ? window_first_to_raster(qr, a.W, a.w, a.n_wx) : qr;
+  };
+  const int my_orow = qrow < a.q_valid ? out_row(qrow) : -1;  // -1: padding row
+  if (a.lse && g == 0 && my_orow >= 0)  // scores are base-2 logits: ln(sum e^s) = ln 2 (m + log2 l)
+    a.lse[static_cast<int64_t>(bh) * a.out_rows + a.out_row0 + my_orow] =
+        (m_run + __log2f(lt)) * 0.69314718055994531f;
+  // O goes out through LDS so that the stores are whole rows: each wave writes its 32 rows
+  // (bf16, 16-byte chunks XOR-swizzled by row) into its own slice of the stage buffers,
+  // then every store instruction covers 64 / (D / 8) complete rows.  The barrier makes sure
+  // no wave still reads a stage or has a tile copy landing in one.
+  constexpr int OCH = D / 8;  // 16-byte chunks per row
+  static_assert(NWAVES <= 16, "O staging: four waves per stage buffer");
+  __syncthreads();
+  char* obuf = stage(wave >> 2) + (wave & 3) * (32 * D * 2);
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+  for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int d0 = dt * 32 + 8 * rg + 4 * g;
-        const uint32_t w0 = pack_bf16x2(o[dt][4 * rg] * inv, o[dt][4 * rg + 1] * inv);
-        const uint32_t w1 = pack_bf16x2(o[dt][4 * rg + 2] * inv, o[dt][4 * rg + 3] * inv);
-        *reinterpret_cast<uint2*>(orow + d0) = make_uint2(w0, w1);
-      }
+    for (int rg = 0; rg < 4; ++rg) {
+      const int c = 4 * dt + rg;  // chunk of dims dt*32 + 8rg .. +8; this lane holds half g
+      const uint32_t w0 = pack_bf16x2(o[dt][4 * rg] * inv, o[dt][4 * rg + 1] * inv);
+      const uint32_t w1 = pack_bf16x2(o[dt][4 * rg + 2] * inv, o[dt][4 * rg + 3] * inv);
+      *reinterpret_cast<uint2*>(obuf + ql * (D * 2) + ((c ^ (ql & (OCH - 1))) << 4) + 8 * g) = make_uint2(w0, w1);
+    }
+  constexpr int RPI = 64 / OCH;  // rows per store instruction
+#pragma unroll
+  for (int u = 0; u < 32 / RPI; ++u) {
+    const int r = u * RPI + lane / OCH, c = lane % OCH;
+    const uint4 val = *reinterpret_cast<const uint4*>(obuf + r * (D * 2) + ((c ^ (r & (OCH - 1))) << 4));
+    const int orr = __shfl(my_orow, r);  // the output row of query r, from lane r
+    if (orr >= 0) {
+      bf16_t* orow = a.out + ((static_cast<int64_t>(b) * a.out_rows + a.out_row0 + orr) * a.heads + h) * D;
+      *reinterpret_cast<uint4*>(orow + 8 * c) = val;
+    }
   }
 }
 
