@@ -490,10 +490,65 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
     t_base = static_cast<int>(static_cast<int64_t>(split) * total / a.splits);
     n_guide = static_cast<int>(static_cast<int64_t>(split + 1) * total / a.splits) - t_base;
   }
+  // Query rows: loaded first, so that their latency overlaps the table set-up below.
+  // Lane (ql, g) holds query ql's dims 16kk + 8g .. +8 (the B operand layout of S^T = K Q^T).
+  // Hi queries sit at their raster position, guide query s at (rho * (s / W_lr),
+  // rho * (s % W_lr)), text queries at (0, 0); rows past the pass's valid rows are zero.
+  constexpr int QUARTER = D / 4;
+  const int qi = q0 + wave * 32 + ql;
+  const bool qvalid = qi < a.q_valid;
+  bf16x8 qf[D / 16];
+  uint4 raw[D / 16];
+  int py = 0, px = 0;
+  if (a.q_pre) {
+    const bf16_t* qrow = a.q_pre + (static_cast<int64_t>(bh) * a.q_valid + (qvalid ? qi : 0)) * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      qf[kk] = qvalid ? *reinterpret_cast<const bf16x8*>(qrow + 16 * kk + 8 * g) : bf16x8{};
+  } else if (qvalid) {
+    int tok = qi;
+    if (HI) {
+      tok = window_first_to_raster(qi, a.W, a.w, a.n_wx);
+      py = tok / a.W;
+      px = tok - py * a.W;
+    } else if (!TEXT) {
+      const int sy = qi / a.W_lr;
+      py = a.rho * sy;
+      px = a.rho * (qi - sy * a.W_lr);
+    }
+    const bf16_t* qrow = a.q + ((static_cast<int64_t>(b) * a.out_rows + a.out_row0 + tok) * a.heads + h) * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) raw[kk] = *reinterpret_cast<const uint4*>(qrow + 16 * kk + 8 * g);
+  }
+  // Hi pass: the RoPE factors of the workgroup's query positions (ny window rows from
+  // ry0, and every column of the window), rounded to fp32 and multiplied by the Q scale,
+  // are staged once in LDS (stage 3, which the tile ring first writes in iteration 0), so
+  // that each lane reads its 2 x D/4 factors from LDS instead of the fp64 table.  Rows are
+  // FRS bytes apart (16 bytes of padding spread the column rows over the banks).  A window
+  // too wide for the stage falls back to the table reads.
+  constexpr int FRS = QUARTER * 8 + 16;
+  int ry0 = 0, ny = 0;
+  bool lds_rope = false;
   if (HI) {
     const int tiles_per_win = a.w2 / kKeyTile;
     const int win = q0 / a.w2;
     const int wy = win / a.n_wx, wx = win - wy * a.n_wx;
+    {
+      const int p0 = q0 - win * a.w2;
+      ry0 = p0 / a.w;
+      ny = (p0 + NWAVES * 32 - 1) / a.w - ry0 + 1;
+      lds_rope = a.rope_on && !a.q_pre && (ny + a.w) * FRS <= 2 * TILE_BYTES;
+      if (lds_rope) {
+        const float qs = static_cast<float>(a.q_scale);
+        for (int i = tid; i < (ny + a.w) * QUARTER; i += NT) {
+          const int row = i / QUARTER, k = i - row * QUARTER;
+          const int pos = row < ny ? wy * a.w + ry0 + row : wx * a.w + (row - ny);
+          const double2 f = a.cs[pos * QUARTER + k];
+          *reinterpret_cast<float2*>(stage3 + row * FRS + k * 8) =
+              make_float2(static_cast<float>(f.x) * qs, static_cast<float>(f.y) * qs);
+        }
+      }
+    }
     const int y0 = max(0, wy - a.radius), y1 = min(a.n_wy - 1, wy + a.radius);
     const int x0 = max(0, wx - a.radius), x1 = min(a.n_wx - 1, wx + a.radius);
     const int nx = x1 - x0 + 1;
@@ -702,91 +757,80 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
 
-  // Query fragment (B operand of S^T = K Q^T): lane holds query ql, dims 16kk + 8g .. +8,
-  // read from the caller's Q row and rotated here (RoPE fused into the Q load): the fp64
-  // cos/sin factors rounded to fp32 and multiplied by the softmax scale * log2 e, the
-  // rotation in fp32 and one rounding to bf16, so the scores come out in base-2 logits
-  // (fp32 instead of fp64 arithmetic here cuts the exposed work before a workgroup's first
-  // tile; the result differs from a correctly rounded fp64 rotation in rare last-bit cases).
-  // Hi queries sit at their raster position, guide query s at (rho * (s / W_lr),
-  // rho * (s % W_lr)), text queries at (0, 0); rows past the pass's valid rows are zero.
-  // With q_pre (guide modes 1, 2, whose workgroups have few tiles) the rows come prepared
-  // by the prep pass instead (rotated and scaled in fp64, one rounding).
-  bf16x8 qf[D / 16];
-  {
-    constexpr int QUARTER = D / 4;
-    const int qi = q0 + wave * 32 + ql;
-    uint4 raw[D / 16];
-    int py = 0, px = 0;
-    const bool qvalid = qi < a.q_valid;
-    if (a.q_pre) {
-      const bf16_t* qrow = a.q_pre + (static_cast<int64_t>(bh) * a.q_valid + (qvalid ? qi : 0)) * D;
+  // Q rotation (RoPE fused into the Q load): the fp64 cos/sin factors rounded to fp32 and
+  // multiplied by the softmax scale * log2 e, the rotation in fp32 and one rounding to
+  // bf16, so the scores come out in base-2 logits (the result differs from a correctly
+  // rounded fp64 rotation in rare last-bit cases).  With q_pre (guide modes 1, 2, whose
+  // workgroups have few tiles) the rows come prepared by the prep pass instead (rotated
+  // and scaled in fp64, one rounding).
+  if (!a.q_pre) {
+    // pairs 8kk + 4g .. +3 lie on one axis (y for the first D/4 pairs)
+    auto rotate = [&](int kk, const float (&c)[4], const float (&sn)[4]) __attribute__((always_inline)) {
+      const uint32_t wi[4] = {raw[kk].x, raw[kk].y, raw[kk].z, raw[kk].w};
+      uint32_t wo[4];
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk)
-        qf[kk] = qvalid ? *reinterpret_cast<const bf16x8*>(qrow + 16 * kk + 8 * g) : bf16x8{};
-    } else if (qvalid) {
-      int tok = qi;
-      if (HI) {
-        tok = window_first_to_raster(qi, a.W, a.w, a.n_wx);
-        py = tok / a.W;
-        px = tok - py * a.W;
-      } else if (!TEXT) {
-        const int sy = qi / a.W_lr;
-        py = a.rho * sy;
-        px = a.rho * (qi - sy * a.W_lr);
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = lo_bf16(wi[e]), y0 = hi_bf16(wi[e]);
+        wo[e] = pack_bf16x2(x0 * c[e] - y0 * sn[e], x0 * sn[e] + y0 * c[e]);
       }
-      const bf16_t* qrow = a.q + ((static_cast<int64_t>(b) * a.out_rows + a.out_row0 + tok) * a.heads + h) * D;
+      const uint4 qo = make_uint4(wo[0], wo[1], wo[2], wo[3]);
+      qf[kk] = *reinterpret_cast<const bf16x8*>(&qo);
+    };
+    if (!qvalid) {
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) raw[kk] = *reinterpret_cast<const uint4*>(qrow + 16 * kk + 8 * g);
-    }
-    if (!a.q_pre) {
-      // All factor loads are issued before any is used (one wait for the Q row and the
-      // table).  Hi and text positions always lie inside the table; a guide position past
-      // it (a guide grid reaching beyond the hi-res extent) reads a clamped entry first
-      // and is then evaluated directly, with the same function that fills the table.
+      for (int kk = 0; kk < D / 16; ++kk) qf[kk] = bf16x8{};
+    } else if (!a.rope_on) {
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const uint4 qo = make_uint4(scale_word(raw[kk].x, a.q_scale), scale_word(raw[kk].y, a.q_scale),
+                                    scale_word(raw[kk].z, a.q_scale), scale_word(raw[kk].w, a.q_scale));
+        qf[kk] = *reinterpret_cast<const bf16x8*>(&qo);
+      }
+    } else if (HI && lds_rope) {
+      const int p = qi % a.w2, ry = p / a.w - ry0, cx = p % a.w;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const int pr = 8 * kk + 4 * g, axis = pr / QUARTER, k0 = pr - axis * QUARTER;
+        const char* fp = stage3 + (axis ? ny + cx : ry) * FRS + k0 * 8;
+        const float4 f01 = *reinterpret_cast<const float4*>(fp);
+        const float4 f23 = *reinterpret_cast<const float4*>(fp + 16);
+        const float c[4] = {f01.x, f01.z, f23.x, f23.z}, sn[4] = {f01.y, f01.w, f23.y, f23.w};
+        rotate(kk, c, sn);
+      }
+    } else {
+      // All factor loads are issued before any is used.  Hi and text positions always lie
+      // inside the table; a guide position past it (a guide grid reaching beyond the
+      // hi-res extent) reads a clamped entry first and is then evaluated directly, with
+      // the same function that fills the table.
       double2 f[D / 16][4];
-      if (qvalid && a.rope_on) {
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const int pr = 8 * kk + 4 * g, axis = pr / QUARTER, k0 = pr - axis * QUARTER;
+        const int pos = axis ? px : py, pc = pos < a.P ? pos : a.P - 1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[kk][e] = a.cs[pc * QUARTER + k0 + e];
+      }
+      if (!HI && !TEXT) {
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
           const int pr = 8 * kk + 4 * g, axis = pr / QUARTER, k0 = pr - axis * QUARTER;
-          const int pos = axis ? px : py, pc = pos < a.P ? pos : a.P - 1;
+          const int pos = axis ? px : py;
+          if (pos >= a.P) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) f[kk][e] = a.cs[pc * QUARTER + k0 + e];
-        }
-        if (!HI && !TEXT) {
-#pragma unroll
-          for (int kk = 0; kk < D / 16; ++kk) {
-            const int pr = 8 * kk + 4 * g, axis = pr / QUARTER, k0 = pr - axis * QUARTER;
-            const int pos = axis ? px : py;
-            if (pos >= a.P) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) f[kk][e] = rope_cos_sin(pos, k0 + e, D / 2, a.log2_theta);
-            }
+            for (int e = 0; e < 4; ++e) f[kk][e] = rope_cos_sin(pos, k0 + e, D / 2, a.log2_theta);
           }
         }
       }
+      const float qs = static_cast<float>(a.q_scale);
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        uint4 qo = make_uint4(0, 0, 0, 0);
-        if (qvalid) {
-          // pairs 8kk + 4g .. +3 lie on one axis (y for the first D/4 pairs)
-          if (a.rope_on) {
-            const float qs = static_cast<float>(a.q_scale);
-            const uint32_t wi[4] = {raw[kk].x, raw[kk].y, raw[kk].z, raw[kk].w};
-            uint32_t wo[4];
+        float c[4], sn[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float c = static_cast<float>(f[kk][e].x) * qs, sn = static_cast<float>(f[kk][e].y) * qs;
-              const float x0 = lo_bf16(wi[e]), y0 = hi_bf16(wi[e]);
-              wo[e] = pack_bf16x2(x0 * c - y0 * sn, x0 * sn + y0 * c);
-            }
-            qo = make_uint4(wo[0], wo[1], wo[2], wo[3]);
-          } else {
-            qo = make_uint4(scale_word(raw[kk].x, a.q_scale), scale_word(raw[kk].y, a.q_scale),
-                            scale_word(raw[kk].z, a.q_scale), scale_word(raw[kk].w, a.q_scale));
-          }
+        for (int e = 0; e < 4; ++e) {
+          c[e] = static_cast<float>(f[kk][e].x) * qs;
+          sn[e] = static_cast<float>(f[kk][e].y) * qs;
         }
-        qf[kk] = *reinterpret_cast<const bf16x8*>(&qo);
+        rotate(kk, c, sn);
       }
     }
   }
