@@ -367,16 +367,57 @@ __global__ void bwd_text_combine_kernel(const float* __restrict__ part0, const f
   if (part1) *reinterpret_cast<uint32_t*>(out1 + ro) = pack_bf16x2(c0, c1);
 }
 
-// Inverse RoPE of the pair (a, b) at pair index pr of a row at position (py, px), in fp32
-// from the fp64 factors, then bf16.
-__device__ __forceinline__ uint32_t unrotate_pair(float a, float b, int pr, int py, int px,
-                                                  const BwdArgs& A, int D) {
-  if (!A.rope_on) return pack_bf16x2(a, b);
-  const int quarter = D / 4, axis = pr / quarter, kk = pr - axis * quarter;
-  const int pos = axis ? px : py;
-  const double2 f = pos < A.P ? A.cs[pos * quarter + kk] : rope_cos_sin(pos, kk, D / 2, A.log2_theta);
-  const float c = static_cast<float>(f.x), s = static_cast<float>(f.y);
-  return pack_bf16x2(a * c + b * s, b * c - a * s);
+// Inverse-RoPE factors of the D/4 pairs one lane stores: pairs d0/2 and d0/2 + 1 of each
+// d0 = dt*32 + 8 rg + 4 g, factor i = 2 (4 dt + rg) + e, for a row at position (py, px):
+// the fp64 factors rounded to fp32.  All table loads are issued before the first use (one
+// wait); a position past the table (a guide row of a guide grid reaching beyond the
+// hi-res extent) reads a clamped entry first and is then evaluated directly, with the
+// function that fills the table.
+template <int D>
+__device__ __forceinline__ void lane_factors(int g, int py, int px, const BwdArgs& A, float2 (&cf)[D / 4]) {
+  constexpr int QUARTER = D / 4;
+  double2 f[D / 4];
+#pragma unroll
+  for (int i = 0; i < D / 4; ++i) {
+    const int pr = (i >> 3) * 16 + 4 * ((i >> 1) & 3) + 2 * g + (i & 1);
+    const int axis = pr / QUARTER, kk = pr - axis * QUARTER;
+    const int pos = axis ? px : py, pc = pos < A.P ? pos : A.P - 1;
+    f[i] = A.cs[pc * QUARTER + kk];
+  }
+#pragma unroll
+  for (int i = 0; i < D / 4; ++i) {
+    const int pr = (i >> 3) * 16 + 4 * ((i >> 1) & 3) + 2 * g + (i & 1);
+    const int axis = pr / QUARTER, kk = pr - axis * QUARTER;
+    const int pos = axis ? px : py;
+    if (pos >= A.P) f[i] = rope_cos_sin(pos, kk, D / 2, A.log2_theta);
+  }
+#pragma unroll
+  for (int i = 0; i < D / 4; ++i) cf[i] = make_float2(static_cast<float>(f[i].x), static_cast<float>(f[i].y));
+}
+
+// Inverse RoPE of the pair (a, b) with factors (cos, sin), in fp32, then bf16.
+__device__ __forceinline__ uint32_t unrotate_pair(float a, float b, float2 cs) {
+  return pack_bf16x2(a * cs.x + b * cs.y, b * cs.x - a * cs.y);
+}
+
+// One lane's part of an output row (lane: row ql, dims dt*32 + 8 (r/4) + 4 g + r%4 of
+// v[dt][r]), times sc, inverse-rotated for a row at (py, px) when RoPE is on, as bf16.
+template <int D>
+__device__ __forceinline__ void store_row_part(const f32x16 (&v)[D / 32], float sc, int g, int py, int px,
+                                               const BwdArgs& A, bf16_t* orow) {
+  float2 cf[D / 4];
+  if (A.rope_on) lane_factors<D>(g, py, px, A, cf);
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d0 = dt * 32 + 8 * rg + 4 * g, i = 2 * (4 * dt + rg);
+      const float a0 = sc * v[dt][4 * rg], a1 = sc * v[dt][4 * rg + 1];
+      const float a2 = sc * v[dt][4 * rg + 2], a3 = sc * v[dt][4 * rg + 3];
+      const uint32_t w0 = A.rope_on ? unrotate_pair(a0, a1, cf[i]) : pack_bf16x2(a0, a1);
+      const uint32_t w1 = A.rope_on ? unrotate_pair(a2, a3, cf[i + 1]) : pack_bf16x2(a2, a3);
+      *reinterpret_cast<uint2*>(orow + d0) = make_uint2(w0, w1);
+    }
 }
 
 // Token (row of the caller's tensors) and position of valid buffer row `row`.
@@ -737,15 +778,7 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dq_kernel(BwdArgs A) {
   int py, px;
   const int64_t rr = raster_row(qrow, A, py, px);
   bf16_t* orow = A.out0 + ((static_cast<int64_t>(b) * A.L + rr) * A.heads + h) * D;
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const int d0 = dt * 32 + 8 * rg + 4 * g;
-      const uint32_t w0 = unrotate_pair(A.out_scale * acc[dt][4 * rg], A.out_scale * acc[dt][4 * rg + 1], d0 / 2, py, px, A, D);
-      const uint32_t w1 = unrotate_pair(A.out_scale * acc[dt][4 * rg + 2], A.out_scale * acc[dt][4 * rg + 3], d0 / 2 + 1, py, px, A, D);
-      *reinterpret_cast<uint2*>(orow + d0) = make_uint2(w0, w1);
-    }
+  store_row_part<D>(acc, A.out_scale, g, py, px, A, orow);
 }
 
 // ---------------------------------------------------------------- dK, dV (key-outer)
@@ -993,14 +1026,11 @@ __global__ __launch_bounds__(NWAVES * 64) void bwd_dkv_kernel(BwdArgs A) {
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
       const int d0 = dt * 32 + 8 * rg + 4 * g;
-      const float c = A.out_scale;
-      const uint32_t k0 = unrotate_pair(c * dk[dt][4 * rg], c * dk[dt][4 * rg + 1], d0 / 2, py, px, A, D);
-      const uint32_t k1 = unrotate_pair(c * dk[dt][4 * rg + 2], c * dk[dt][4 * rg + 3], d0 / 2 + 1, py, px, A, D);
-      *reinterpret_cast<uint2*>(A.out0 + ro + d0) = make_uint2(k0, k1);
       *reinterpret_cast<uint2*>(A.out1 + ro + d0) =
           make_uint2(pack_bf16x2(dv[dt][4 * rg], dv[dt][4 * rg + 1]),
                      pack_bf16x2(dv[dt][4 * rg + 2], dv[dt][4 * rg + 3]));
     }
+  store_row_part<D>(dk, A.out_scale, g, py, px, A, A.out0 + ro);
 }
 
 // ------------------------------------------------------------------ host side
