@@ -110,6 +110,23 @@ def stratified_rows(g, rng, n_hi, n_lr):
     return np.unique(np.array(picks + lr, dtype=np.int64))
 
 
+@pytest.mark.parametrize("name,g", [
+    # 256 queries of a workgroup span 4 window rows: their Q RoPE factors (4 rows + 64
+    # columns) are staged in LDS
+    ("w64_factors_in_lds", Geometry(B=1, heads=1, head_dim=128, H=64, W=128, w=64, H_lr=16,
+                                    W_lr=32)),
+    # 2 rows + 128 columns of factors exceed the stage buffer: the lanes read the fp64 table
+    ("w128_factors_from_table", Geometry(B=1, heads=1, head_dim=128, H=128, W=128, w=128,
+                                         H_lr=32, W_lr=32)),
+])
+def test_forward_wide_windows_sampled_rows(name, g):
+    say(f"forward wide windows, sampled rows: {name} {g}")
+    q, k, v = make_qkv_bits(g, 4321)
+    got = bf16_f64(from_dev(run_forward(g, q, k, v)))
+    rows = stratified_rows(g, np.random.default_rng(5), 300, 40)
+    check_close(got[0, rows, 0], oracle_rows(g, q, k, v, 0, 0, rows), name)
+
+
 @pytest.mark.parametrize("name,heads_checked,n_hi,n_lr", [
     ("2k", (0, 11, 23), 400, 100),
     ("nonsquare", (0, 23), 300, 60),
