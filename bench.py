@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 8k] [--cpu-seconds S]
                     [--radius R] [--guide-mode M] [--text T] [--backward] [--rope-at-load]
+                    [--permute-free]
 
 A step is one full uhla_forward (cos/sin table -> K, V permutation, K fused with RoPE ->
 hi-res block-sparse attention with Q rotated at load and the inverse permutation fused
@@ -15,7 +16,9 @@ value       effective TFLOP/s of the whole step: algorithmic FLOPs (4 * head_dim
             --backward times a training step instead: uhla_forward_lse then uhla_backward
             (algorithmic FLOPs: 4*d per pair forward, 10*d per pair backward).
             --rope-at-load times uhla_forward_rope_at_load (K rotated at every K tile
-            load instead of once in the prep pass).
+            load instead of once in the prep pass), --permute-free
+            uhla_forward_permute_free (no K/V prep pass: tiles copied from the raster
+            K and V, K rotated at load, V read transposed from LDS).
 roofline    the dominant kernel (hi-res attention pass) against the bf16 MFMA peak:
             its algorithmic FLOPs per launch / its mean launch duration, measured with
             HIP events recorded on the launch stream around each launch in as many steps
@@ -219,6 +222,8 @@ def main():
     ap.add_argument("--backward", action="store_true", help="time forward (with LSE) + backward")
     ap.add_argument("--rope-at-load", action="store_true",
                     help="uhla_forward_rope_at_load: K rotated at every K tile load")
+    ap.add_argument("--permute-free", action="store_true",
+                    help="uhla_forward_permute_free: no K/V prep pass")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -233,7 +238,8 @@ def main():
     g = CONFIGS[args.config].with_(radius=args.radius, guide_mode=args.guide_mode, T=args.text)
     if args.backward:
         return bench_backward(args, g)
-    variant = args.radius != 1 or args.guide_mode != 0 or args.text != 0 or args.rope_at_load
+    variant = (args.radius != 1 or args.guide_mode != 0 or args.text != 0 or args.rope_at_load
+               or args.permute_free)
     log(f"[bench] generating seeded inputs for {g}")
     t0 = time.perf_counter()
     q, k, v = make_qkv_bits(g, CONFIG_SEEDS[args.config])
@@ -243,11 +249,13 @@ def main():
     qt, kt, vt = up(q), up(k), up(v)
     out = torch.empty_like(qt)
     ws = api.alloc_workspace(g.B, g.H, g.W, g.w, g.H_lr, g.W_lr, g.heads, g.head_dim, dev,
-                             rho=g.rho, radius=g.radius, guide_mode=g.guide_mode, T=g.T)
+                             rho=g.rho, radius=g.radius, guide_mode=g.guide_mode, T=g.T,
+                             permute_free=args.permute_free)
     fwd = lambda timer=None: api.forward(qt, kt, vt, g.H, g.W, g.w, g.H_lr, g.W_lr, rho=g.rho,
                                          theta=g.theta, out=out, workspace=ws, timer=timer,
                                          radius=g.radius, guide_mode=g.guide_mode, T=g.T,
-                                         rope_at_load=args.rope_at_load)
+                                         rope_at_load=args.rope_at_load,
+                                         permute_free=args.permute_free)
     for _ in range(args.warmup):
         fwd()
     torch.cuda.synchronize()
@@ -344,7 +352,10 @@ def main():
                    "rho": g.rho, "rope_theta": g.theta, "tokens": g.L,
                    "neighbourhood_radius": g.radius, "guide_mode": g.guide_mode,
                    "text_tokens": g.T,
-                   "k_rope": "at every K tile load" if args.rope_at_load else "once, in the K prep pass",
+                   "k_rope": ("at every K tile load" if args.rope_at_load or args.permute_free
+                              else "once, in the K prep pass"),
+                   "kv_prep": "none: tiles copied from raster K, V" if args.permute_free
+                              else "window-first K (rotated) and V^T tiles",
                    "parallelism": "single GPU"},
         "tokens_per_s": round(g.B * g.L / (ms_step * 1e-3), 1),
         "hi_tokens_per_s": round(g.B * g.N / (ms_step * 1e-3), 1),
@@ -356,7 +367,9 @@ def main():
                              "frac_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4)},
         "stage_ms": {s: round(x, 4) for s, x in stage_avg.items()},
         "roofline": {"kernel": "attn_fwd_kernel<128, 8, hi%s> (hi-res pass)"
-                               % (", K rotated at load" if args.rope_at_load else ""), "bound": "mfma",
+                               % (", raster tiles" if args.permute_free
+                                  else ", K rotated at load" if args.rope_at_load else ""),
+                     "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},

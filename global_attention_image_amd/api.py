@@ -63,6 +63,10 @@ EXPORTS = {
     "uhla_forward_rope_at_load": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_int] * 9
                                   + [ctypes.c_float, ctypes.c_float, ctypes.c_void_p,
                                      ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
+    "uhla_forward_permute_free_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 9),
+    "uhla_forward_permute_free": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_int] * 9
+                                  + [ctypes.c_float, ctypes.c_float, ctypes.c_void_p,
+                                     ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
 }
 
 _lib = None
@@ -214,9 +218,12 @@ def forward_text_workspace_bytes(B, T, H, W, w, H_lr, W_lr, rho, heads, head_dim
 
 
 def alloc_workspace(B, H, W, w, H_lr, W_lr, heads, head_dim, device="cuda", rho=4, radius=1,
-                    guide_mode=0, T=0):
+                    guide_mode=0, T=0, permute_free=False):
     import torch
-    if T:
+    if permute_free:
+        n = load().uhla_forward_permute_free_workspace_bytes(B, H, W, w, H_lr, W_lr, rho, heads,
+                                                             head_dim)
+    elif T:
         n = forward_text_workspace_bytes(B, T, H, W, w, H_lr, W_lr, rho, heads, head_dim, radius,
                                          guide_mode)
     elif radius == 1 and guide_mode == 0:
@@ -260,13 +267,13 @@ class Timer:
 
 def forward(q, k, v, H, W, w, H_lr, W_lr, rho=4, scale=0.0, theta=10000.0, out=None,
             workspace=None, timer: Timer | None = None, radius=1, guide_mode=0, T=0,
-            rope_at_load=False):
+            rope_at_load=False, permute_free=False):
     """Hierarchical local attention forward on bf16 [B, T + H*W + H_lr*W_lr, heads, d] tensors.
 
     radius / guide_mode select the mask variants of uhla_forward_masked and T > 0 the text
     tokens of uhla_forward_text (rows 0..T-1); with the defaults uhla_forward is called.
     rope_at_load selects uhla_forward_rope_at_load (K rotated at every K tile load; default
-    mask only).  A timer records per-stage durations (uhla_forward_timed /
+    mask only), permute_free uhla_forward_permute_free (no K/V prep pass; default mask only).  A timer records per-stage durations (uhla_forward_timed /
     uhla_forward_masked_timed / uhla_forward_text / uhla_forward_rope_at_load)."""
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
@@ -279,18 +286,25 @@ def forward(q, k, v, H, W, w, H_lr, W_lr, rho=4, scale=0.0, theta=10000.0, out=N
     if out is None:
         out = torch.empty_like(q)
     _require(out, "out", torch.bfloat16)
+    if (rope_at_load or permute_free) and (T or radius != 1 or guide_mode != 0):
+        raise ValueError("rope_at_load and permute_free cover the default mask only")
+    if rope_at_load and permute_free:
+        raise ValueError("choose one of rope_at_load and permute_free")
     if workspace is None:
         workspace = alloc_workspace(B, H, W, w, H_lr, W_lr, Hh, d, q.device, rho=rho,
-                                    radius=radius, guide_mode=guide_mode, T=T)
+                                    radius=radius, guide_mode=guide_mode, T=T,
+                                    permute_free=permute_free)
     lib = load()
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, W, w, H_lr, W_lr, rho, Hh, d,
             float(scale), float(theta))
     tail = (_ptr(workspace), workspace.numel(), _stream(q))
     if rope_at_load:
-        if T or radius != 1 or guide_mode != 0:
-            raise ValueError("rope_at_load covers the default mask only")
         st = lib.uhla_forward_rope_at_load(*args, *tail, timer.h if timer is not None else None)
         _check(st, "uhla_forward_rope_at_load")
+        return out
+    if permute_free:
+        st = lib.uhla_forward_permute_free(*args, *tail, timer.h if timer is not None else None)
+        _check(st, "uhla_forward_permute_free")
         return out
     if T:
         st = lib.uhla_forward_text(*args[:5], int(T), *args[5:], int(radius), int(guide_mode),

@@ -415,6 +415,8 @@ struct AttnArgs {
   float* o_part;          // TEXT: [splits][B*heads][q_rows][D] unnormalised partial outputs
   float2* ml_part;        // TEXT: [splits][B*heads][q_rows] (running max, sum)
   float* lse;             // optional [B*heads][out_rows]: natural-log sum of exp(scaled scores)
+  const bf16_t* k_raw;    // RAW: the caller's K and V [B][out_rows][heads][D], read in place
+  const bf16_t* v_raw;
 };
 
 constexpr int kStages = 4;  // LDS ring: tiles t, t+1 are read while t+2, t+3 land
@@ -445,7 +447,15 @@ constexpr int kPvAhead = 4;  // V fragment reads in flight ahead of the PV MFMAs
 // in revolutions, reduced with fract), the rotation in fp32, one rounding to bf16.  Tile
 // t+1 is rotated in iteration t before a mid-iteration barrier, ahead of its first reader
 // (wave B's QK^T_{t+1} in the second half of that iteration).
-template <int D, int NWAVES, bool HI, bool RECT, bool TEXT, bool ROTK = false>
+//
+// RAW (uhla_forward_permute_free): no prep pass at all.  Tiles are copied straight from the
+// caller's raster K and V: a 64-key hi tile is 64 / w window rows of w tokens (or a
+// 64-token piece of one row of a wider window), so this lane's source chunk sits at the
+// same offset from the tile's first token in every hi tile, and a guide tile is 64
+// consecutive guide tokens (the missing keys of the last one re-read its last token and
+// are masked).  K is rotated at load as with ROTK; V lands row-major (chunks swizzled for
+// the transposing LDS read) and its V^T fragments are read with ds_read_b64_tr_b16.
+template <int D, int NWAVES, bool HI, bool RECT, bool TEXT, bool ROTK = false, bool RAW = false>
 __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   constexpr int NT = NWAVES * 64;
   constexpr int TILE_BYTES = kKeyTile * D * 2;       // one K or V tile
@@ -602,14 +612,70 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
     const int vr = slot >> 3, vp = slot & 7;
     v_src[i] = vr * (kKeyTile * 2) + ((vp ^ v_swizzle(vr)) << 4);
   }
+  static_assert(!RAW || (ROTK && !RECT && !TEXT), "raster tiles: K rotated at load, default mask");
+  // RAW: this lane's chunk offsets from a tile's first token in the caller's K and V, for
+  // hi tiles (h) and guide tiles (g)
+  int kh_src[RAW ? CPT : 1], kg_src[RAW ? CPT : 1], vh_src[RAW ? CPT : 1], vg_src[RAW ? CPT : 1];
+  const int rowb = a.heads * (D * 2);  // bytes between consecutive tokens of one head
+  if constexpr (RAW) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int slot = (i * NWAVES + wave) * 64 + lane;
+      const int kr = slot / KCH, kp = slot - kr * KCH;
+      const int rel = a.w <= kKeyTile ? (kr / a.w) * a.W + (kr % a.w) : kr;
+      kh_src[i] = rel * rowb + ((kp ^ k_swizzle<D>(kr)) << 4);
+      kg_src[i] = kr * rowb + ((kp ^ k_swizzle<D>(kr)) << 4);
+      vh_src[i] = rel * rowb + ((kp ^ bwd_swizzle<D>(kr)) << 4);
+      vg_src[i] = kr * rowb + ((kp ^ bwd_swizzle<D>(kr)) << 4);
+    }
+  }
   // Global sources of tile t (K tile, V^T tile).  A V^T tile of 64 keys holds as many bytes
   // as the K tile of the same keys, so one offset serves both.
   const char* k_hi_b = reinterpret_cast<const char*>(a.k_hi) + static_cast<int64_t>(bh) * a.N * (D * 2);
   const char* v_hi_b = reinterpret_cast<const char*>(a.v_hi) + static_cast<int64_t>(bh) * a.N * (D * 2);
   const char* k_lr_b = reinterpret_cast<const char*>(a.k_lr) + static_cast<int64_t>(bh) * a.Mg * (D * 2);
   const char* v_lr_b = reinterpret_cast<const char*>(a.v_lr) + static_cast<int64_t>(bh) * a.Mg * (D * 2);
+  // Keys of tile t that exist (a prefix): only the last guide tile and the last text tile
+  // of the global buffer can be partial, so their tile indices (-1: none) and key counts
+  // are found once and the loop tests two scalars per tile ...
+  int part_t0 = -1, part_v0 = kKeyTile, part_t1 = -1, part_v1 = kKeyTile;
+  if (RECT) {
+    if (a.T % kKeyTile) {
+      part_t1 = n_local + n_rect + static_cast<int>(a.T / kKeyTile);
+      part_v1 = static_cast<int>(a.T % kKeyTile);
+    }
+  } else {
+    const int goff = TEXT ? n_hi_tiles - t_base : n_local;  // tile t = global tile t - goff
+    if (a.M % kKeyTile) {
+      part_t0 = static_cast<int>(a.M / kKeyTile) + goff;
+      part_v0 = static_cast<int>(a.M % kKeyTile);
+    }
+    if (a.T % kKeyTile) {
+      part_t1 = static_cast<int>(a.Mk / kKeyTile + a.T / kKeyTile) + goff;
+      part_v1 = static_cast<int>(a.T % kKeyTile);
+    }
+  }
   // (with RECT, k_lr / v_lr / Mg describe the cell-block buffer)
-  auto tile_src = [&](int t, const char*& kp, const char*& vp) __attribute__((always_inline)) {
+  // RAW tiles also report their kind (0: hi, 1: guide) and how many of their keys exist.
+  const int64_t g_row0 = HI ? a.out_row0 + a.N : a.out_row0;  // row of guide token 0 (RAW)
+  auto tile_src = [&](int t, const char*& kp, const char*& vp, int& kind, int& valid) __attribute__((always_inline)) {
+    kind = 0;
+    valid = kKeyTile;
+    if constexpr (RAW) {
+      int64_t row;  // row of the tile's first token within batch b of the caller's tensors
+      if (HI && t < n_local) {
+        const int p0 = static_cast<int>(__builtin_amdgcn_readfirstlane(tile_off_s[t]) / (D * 2));
+        row = a.out_row0 + window_first_to_raster(p0, a.W, a.w, a.n_wx);
+      } else {
+        row = g_row0 + static_cast<int64_t>(t - (HI ? n_local : 0)) * kKeyTile;
+        kind = 1;
+        valid = t == part_t0 ? part_v0 : kKeyTile;
+      }
+      const int64_t off = ((static_cast<int64_t>(b) * a.out_rows + row) * a.heads + h) * (D * 2);
+      kp = reinterpret_cast<const char*>(a.k_raw) + off;
+      vp = reinterpret_cast<const char*>(a.v_raw) + off;
+      return;
+    }
     if (HI && t < n_local) {
       const uint32_t off = __builtin_amdgcn_readfirstlane(tile_off_s[t]);
       kp = k_hi_b + off;
@@ -631,7 +697,20 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   // DMA instructions [p0, p1) of this thread's share of one K tile and one V tile:
   // instruction p copies K chunk p/2 (p even) from kp into the K half of stage `kdst`, or
   // V chunk p/2 (p odd) from vp into the V half of stage `vdst`; a null source is skipped.
-  auto issue_parts = [&](const char* kp, const char* vp, char* kdst, char* vdst, int p0, int p1) __attribute__((always_inline)) {
+  // Source offset of this lane's chunk of DMA instruction i (K or V half) for a tile of the
+  // given kind; RAW guide tiles with fewer than 64 keys re-read their last key.
+  auto src_off = [&](int i, bool is_v, int kind, int valid) __attribute__((always_inline)) -> int {
+    if constexpr (!RAW) {
+      return is_v ? v_src[i] : k_src[i];
+    } else {
+      if (kind == 0) return is_v ? vh_src[i] : kh_src[i];
+      if (valid >= kKeyTile) return is_v ? vg_src[i] : kg_src[i];
+      const int slot = (i * NWAVES + wave) * 64 + lane, kr = slot / KCH, kp = slot - kr * KCH;
+      return min(kr, valid - 1) * rowb + ((kp ^ (is_v ? bwd_swizzle<D>(kr) : k_swizzle<D>(kr))) << 4);
+    }
+  };
+  auto issue_parts = [&](const char* kp, const char* vp, char* kdst, char* vdst, int p0, int p1,
+                         int kind, int valid) __attribute__((always_inline)) {
     const uint32_t klds = lds_addr(kdst), vlds = lds_addr(vdst) + TILE_BYTES;
 #pragma unroll
     for (int p = 0; p < LOADS_PER_TILE; ++p) {
@@ -639,44 +718,26 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
       const int i = p >> 1;
       const uint32_t off = (i * NWAVES + wave) * 64 * 16;
       if (p & 1) {
-        if (vp) dma_16b(vp, v_src[i], __builtin_amdgcn_readfirstlane(vlds + off));
+        if (vp) dma_16b(vp, src_off(i, true, kind, valid), __builtin_amdgcn_readfirstlane(vlds + off));
       } else {
-        if (kp) dma_16b(kp, k_src[i], __builtin_amdgcn_readfirstlane(klds + off));
+        if (kp) dma_16b(kp, src_off(i, false, kind, valid), __builtin_amdgcn_readfirstlane(klds + off));
       }
     }
   };
   auto issue_k = [&](int t, char* dst) __attribute__((always_inline)) {
     const char* kp;
     const char* vp;
-    tile_src(t, kp, vp);
-    issue_parts(kp, nullptr, dst, dst, 0, LOADS_PER_TILE);
+    int kind, valid;
+    tile_src(t, kp, vp, kind, valid);
+    issue_parts(kp, nullptr, dst, dst, 0, LOADS_PER_TILE, kind, valid);
   };
   auto issue_v = [&](int t, char* dst) __attribute__((always_inline)) {
     const char* kp;
     const char* vp;
-    tile_src(t, kp, vp);
-    issue_parts(nullptr, vp, dst, dst, 0, LOADS_PER_TILE);
+    int kind, valid;
+    tile_src(t, kp, vp, kind, valid);
+    issue_parts(nullptr, vp, dst, dst, 0, LOADS_PER_TILE, kind, valid);
   };
-  // Keys of tile t that exist (a prefix): only the last guide tile and the last text tile
-  // of the global buffer can be partial, so their tile indices (-1: none) and key counts
-  // are found once and the loop tests two scalars per tile ...
-  int part_t0 = -1, part_v0 = kKeyTile, part_t1 = -1, part_v1 = kKeyTile;
-  if (RECT) {
-    if (a.T % kKeyTile) {
-      part_t1 = n_local + n_rect + static_cast<int>(a.T / kKeyTile);
-      part_v1 = static_cast<int>(a.T % kKeyTile);
-    }
-  } else {
-    const int goff = TEXT ? n_hi_tiles - t_base : n_local;  // tile t = global tile t - goff
-    if (a.M % kKeyTile) {
-      part_t0 = static_cast<int>(a.M / kKeyTile) + goff;
-      part_v0 = static_cast<int>(a.M % kKeyTile);
-    }
-    if (a.T % kKeyTile) {
-      part_t1 = static_cast<int>(a.Mk / kKeyTile + a.T / kKeyTile) + goff;
-      part_v1 = static_cast<int>(a.T % kKeyTile);
-    }
-  }
   auto tile_valid = [&](int t) __attribute__((always_inline)) -> int {
     return t == part_t0 ? part_v0 : t == part_t1 ? part_v1 : kKeyTile;
   };
@@ -982,7 +1043,9 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   };
 
   // V^T fragment for key-step ks, output dims 32 dt + ql
+  const TrAddr<D> tra(lane);  // RAW: transposed V^T fragments from the row-major V tile
   auto v_frag = [&](const char* vb, int ks, int dt) __attribute__((always_inline)) -> bf16x8 {
+    if constexpr (RAW) return TrAddr<D>::frag(vb, tra.x, ks, dt);
     const int vr = dt * 32 + ql;
     return *reinterpret_cast<const bf16x8*>(vb + vr * (kKeyTile * 2) + (((2 * ks + g) ^ v_swizzle(vr)) << 4));
   };
@@ -1051,8 +1114,9 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
       const char* kp;
       const char* vp;
       const char* unused;
-      tile_src(t + 3 < n_tiles ? t + 3 : t, kp, unused);
-      tile_src(t + 2 < n_tiles ? t + 2 : t, unused, vp);
+      int k_kind, k_valid, v_kind, v_valid;
+      tile_src(t + 3 < n_tiles ? t + 3 : t, kp, unused, k_kind, k_valid);
+      tile_src(t + 2 < n_tiles ? t + 2 : t, unused, vp, v_kind, v_valid);
       char* kdst = stage((S + 3) & 3);
       char* vdst = stage((S + 2) & 3);
       auto dma_slot = [&](int slot) __attribute__((always_inline)) {
@@ -1061,8 +1125,8 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_kernel(AttnArgs a) {
         for (int p = slot * LOADS_PER_TILE / 4; p < (slot + 1) * LOADS_PER_TILE / 4; ++p) {
           const int i = p >> 1;
           const uint32_t off = (i * NWAVES + wave) * 64 * 16;
-          if (p & 1) dma_16b(vp, v_src[i], __builtin_amdgcn_readfirstlane(vlds + off));
-          else dma_16b(kp, k_src[i], __builtin_amdgcn_readfirstlane(klds + off));
+          if (p & 1) dma_16b(vp, src_off(i, true, v_kind, v_valid), __builtin_amdgcn_readfirstlane(vlds + off));
+          else dma_16b(kp, src_off(i, false, k_kind, k_valid), __builtin_amdgcn_readfirstlane(klds + off));
         }
       };
       dma_slot(0);
@@ -1215,14 +1279,14 @@ __global__ void text_combine_kernel(const float* __restrict__ o_part, const floa
   if (lse && d == 0) lse[bh * out_rows + x] = (mx + __log2f(l)) * 0.69314718055994531f;
 }
 
-template <int D, int NWAVES, bool HI, bool RECT, bool TEXT, bool ROTK = false>
+template <int D, int NWAVES, bool HI, bool RECT, bool TEXT, bool ROTK = false, bool RAW = false>
 static void launch_attn(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, NWAVES, HI, RECT, TEXT, ROTK>), dim3(a.total_blocks),
+  hipLaunchKernelGGL((attn_fwd_kernel<D, NWAVES, HI, RECT, TEXT, ROTK, RAW>), dim3(a.total_blocks),
                      dim3(NWAVES * 64), 0, s, a);
 }
 
 enum PassKind { kPassHi = 0, kPassHiRect = 1, kPassGuide = 2, kPassText = 3, kPassHiRotK = 4,
-                kPassGuideRotK = 5 };
+                kPassGuideRotK = 5, kPassHiRaw = 6, kPassGuideRaw = 7 };
 
 template <int D>
 static void dispatch_attn_d(int nwaves, PassKind kind, const AttnArgs& a, hipStream_t s) {
@@ -1231,6 +1295,8 @@ static void dispatch_attn_d(int nwaves, PassKind kind, const AttnArgs& a, hipStr
     case kPassText: launch_attn<D, 8, false, false, true>(a, s); break;
     case kPassHiRotK: launch_attn<D, 8, true, false, false, true>(a, s); break;
     case kPassGuideRotK: launch_attn<D, 8, false, false, false, true>(a, s); break;
+    case kPassHiRaw: launch_attn<D, 8, true, false, false, true, true>(a, s); break;
+    case kPassGuideRaw: launch_attn<D, 8, false, false, false, true, true>(a, s); break;
     case kPassHiRect:
       nwaves == 8 ? launch_attn<D, 8, true, true, false>(a, s) : launch_attn<D, 2, true, true, false>(a, s);
       break;
@@ -1486,6 +1552,116 @@ size_t workspace_bytes(int B, int64_t T, int H, int W, int w, int H_lr, int W_lr
                nullptr).bytes;
 }
 
+// Permute-free forward (uhla_forward_permute_free): no K/V prep pass; the attention
+// kernels copy their tiles straight from the caller's raster K and V, rotate K at load and
+// read V transposed from LDS.  Workspace: the cos/sin table only.
+static size_t permute_free_workspace(const Geom& g) {
+  return (static_cast<size_t>(g.P) * (g.D / 4) * sizeof(double2) + 255) / 256 * 256;
+}
+
+static int validate_permute_free(const void* q, const void* k, const void* v, void* o, int B,
+                                 int H, int W, int w, int H_lr, int W_lr, int rho, int heads,
+                                 int D) {
+  int st = validate_forward(q, k, v, o, B, 0, H, W, w, H_lr, W_lr, rho, heads, D, 1, 0);
+  if (st) return st;
+  // a 64-key tile must be whole window rows (64 / w of them) or a 64-token piece of one
+  if (w < 16 || (kKeyTile % w != 0 && w % kKeyTile != 0))
+    return fail_unsupported("permute-free forward: window size must be 16, 32, 64 or a multiple of 64");
+  // per-lane chunk offsets from a tile's first token are 32-bit
+  const int64_t rowb = static_cast<int64_t>(heads) * D * 2;
+  const int64_t rows = w <= kKeyTile ? static_cast<int64_t>(kKeyTile / w) * W : kKeyTile;
+  if (rows * rowb >= (int64_t(1) << 31))
+    return fail_unsupported("permute-free forward: rows of the tensors too long for 32-bit tile offsets");
+  return UHLA_OK;
+}
+
+static int forward_permute_free_impl(const void* q, const void* k, const void* v, void* o, int B,
+                                     int H, int W, int w, int H_lr, int W_lr, int rho, int heads,
+                                     int D, float scale, float theta, void* workspace,
+                                     size_t workspace_bytes, void* stream, uhla_timer* timer) {
+  int st = validate_permute_free(q, k, v, o, B, H, W, w, H_lr, W_lr, rho, heads, D);
+  if (st) return st;
+  const Geom g = make_geom(B, H, W, w, H_lr, W_lr, rho, heads, D, 1, 0, 0);
+  const size_t need = permute_free_workspace(g);
+  if (!workspace || workspace_bytes < need) return (set_detail("workspace too small"), UHLA_ERR_WORKSPACE);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail_arg("workspace must be 256-byte aligned");
+  const int64_t L = g.N + g.M;
+  const size_t tensor_bytes = static_cast<size_t>(B) * L * heads * D * 2;
+  if (ranges_overlap(o, tensor_bytes, q, tensor_bytes) || ranges_overlap(o, tensor_bytes, k, tensor_bytes) ||
+      ranges_overlap(o, tensor_bytes, v, tensor_bytes) || ranges_overlap(o, tensor_bytes, workspace, need))
+    return fail_arg("o overlaps an input or the workspace");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  double2* cs = static_cast<double2*>(workspace);
+  const bool rope_on = theta > 0.0f;
+  const float sc = scale > 0.0f ? scale : 1.0f / sqrtf(static_cast<float>(D));
+  const double l2t = rope_on ? log2(static_cast<double>(theta)) : 0.0;
+  if (timer) timer_begin(timer, UHLA_STAGE_TABLES, s);
+  if (rope_on) {
+    const int n = g.P * (D / 4);
+    hipLaunchKernelGGL(cos_sin_table_kernel, dim3((n + 255) / 256), dim3(256), 0, s, cs, g.P, D, l2t);
+    st = check_launch("cos_sin_table_kernel");
+    if (st) return st;
+  }
+  if (timer) {  // no prep and no separate unpermute: their stages stay empty
+    timer_end(timer, UHLA_STAGE_TABLES, s);
+    for (int stage : {UHLA_STAGE_PREP_HI, UHLA_STAGE_PREP_LR}) {
+      timer_begin(timer, stage, s);
+      timer_end(timer, stage, s);
+    }
+  }
+  AttnArgs a{};
+  a.q = static_cast<const bf16_t*>(q);
+  a.k_raw = static_cast<const bf16_t*>(k);
+  a.v_raw = static_cast<const bf16_t*>(v);
+  a.k_hi = a.k_lr = a.k_raw;  // unused by the raster-tile kernels
+  a.v_hi = a.v_lr = a.v_raw;
+  a.cs = cs; a.log2_theta = l2t; a.P = g.P; a.rope_on = rope_on ? 1 : 0;
+  a.q_scale = static_cast<double>(sc) * 1.4426950408889634;
+  a.rho = rho; a.H_lr = H_lr; a.W_lr = W_lr; a.nbj = g.nbj;
+  a.N = g.N; a.M = g.M; a.Mk = g.Mk; a.Mg = g.Mk; a.T = 0; a.Mb = 0;
+  a.heads = heads; a.w2 = w * w;
+  a.out = static_cast<bf16_t*>(o); a.out_rows = L;
+  const int64_t BH = static_cast<int64_t>(B) * heads;
+  if (timer) timer_begin(timer, UHLA_STAGE_ATTN_HI, s);
+  {
+    AttnArgs h = a;
+    h.q_rows = g.N;
+    h.out_row0 = 0;
+    h.W = W; h.w = w; h.n_wx = g.n_wx; h.n_wy = g.n_wy;
+    h.radius = 1;
+    h.q_valid = static_cast<int>(g.N);
+    h.blocks_per_bh = static_cast<int>(g.N / kMaxQuery);
+    h.total_blocks = static_cast<int>(BH * h.blocks_per_bh);
+    dispatch_attn(D, 8, kPassHiRaw, h, s);
+    st = check_launch("attn_fwd_kernel(hi, raster tiles)");
+    if (st) return st;
+  }
+  if (timer) {
+    timer_end(timer, UHLA_STAGE_ATTN_HI, s);
+    timer_begin(timer, UHLA_STAGE_ATTN_LR, s);
+  }
+  if (g.M > 0) {
+    AttnArgs l = a;
+    l.q_rows = g.Mq;
+    l.out_row0 = g.N;
+    l.q_valid = static_cast<int>(g.M);
+    l.blocks_per_bh = static_cast<int>(g.Mq / kMaxQuery);
+    l.total_blocks = static_cast<int>(BH * l.blocks_per_bh);
+    dispatch_attn(D, 8, kPassGuideRaw, l, s);
+    st = check_launch("attn_fwd_kernel(guide, raster tiles)");
+    if (st) return st;
+  }
+  if (timer) {
+    timer_end(timer, UHLA_STAGE_ATTN_LR, s);
+    for (int stage : {UHLA_STAGE_UNPERMUTE, UHLA_STAGE_ATTN_TEXT}) {
+      timer_begin(timer, stage, s);
+      timer_end(timer, stage, s);
+    }
+    return timer_commit(timer);
+  }
+  return UHLA_OK;
+}
+
 }  // namespace uhla
 
 extern "C" size_t uhla_forward_workspace_bytes(int B, int H, int W, int w, int H_lr, int W_lr,
@@ -1570,3 +1746,21 @@ extern "C" int uhla_forward_rope_at_load(const void* q, const void* k, const voi
                             theta, 1, 0, workspace, workspace_bytes, stream, timer, nullptr, true);
 }
 
+
+extern "C" size_t uhla_forward_permute_free_workspace_bytes(int B, int H, int W, int w, int H_lr,
+                                                           int W_lr, int rho, int heads,
+                                                           int head_dim) {
+  if (B < 1 || H < 1 || W < 1 || w < 1 || heads < 1 || H_lr < 0 || W_lr < 0 || head_dim < 1) return 0;
+  return uhla::permute_free_workspace(uhla::make_geom(B, H, W, w, H_lr, W_lr, rho > 0 ? rho : 1,
+                                                      heads, head_dim, 1, 0, 0));
+}
+
+extern "C" int uhla_forward_permute_free(const void* q, const void* k, const void* v, void* o,
+                                         int B, int H, int W, int w, int H_lr, int W_lr, int rho,
+                                         int heads, int head_dim, float scale, float theta,
+                                         void* workspace, size_t workspace_bytes, void* stream,
+                                         uhla_timer* timer) {
+  return uhla::forward_permute_free_impl(q, k, v, o, B, H, W, w, H_lr, W_lr, rho, heads,
+                                         head_dim, scale, theta, workspace, workspace_bytes,
+                                         stream, timer);
+}

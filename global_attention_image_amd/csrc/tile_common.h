@@ -70,4 +70,56 @@ __device__ __forceinline__ void wait_vm_and_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte chunk swizzle of the backward's LDS row tiles: physical chunk = logical chunk ^
+// bwd_swizzle<D>(row).  The tiles are read two ways: 16 lanes reading one chunk of 16
+// consecutive rows (the row fragments) need 16 distinct values over any 16 consecutive
+// rows, and the transposed reads below, where each 32-lane half addresses 4 rows x 4
+// consecutive chunks, need those 16 (row, chunk) pairs in 16 distinct bank groups.  The
+// swizzle puts row bits 0-1 into chunk bits 2-3 and row bits 2-3 into chunk bits 0-1
+// (D = 64: the same on row / 2, two rows sharing a 256-byte bank line), which meets both;
+// XOR with the plain row % 16 would leave chunk bits 2-3 fixed within a half, 4 bank
+// groups for 16 pairs.
+template <int D>
+__device__ __forceinline__ int bwd_swizzle(int row) {
+  const int e = D == 128 ? (row & 15) : ((row >> 1) & 7);
+  return D == 128 ? (((e & 3) << 2) | (e >> 2)) : (((e & 1) << 2) | (e >> 1));
+}
+
+// Transposed MFMA operands from a row-major LDS tile (rows of D bf16, chunks swizzled by
+// bwd_swizzle<D>): A[i][k] = tile[row(k)][32 dt + i], i = lane % 32, for the 16 rows of
+// reduction step ks, in the order of an accumulator converted in place (element jj of
+// lane group g = lane / 32 is row 16 ks + 8 (jj / 4) + 4 g + jj % 4).  Two
+// ds_read_b64_tr_b16 per fragment: within each 16-lane group, lane i' receives element
+// i' % 4 of the 8 bytes addressed by lane 4 j + i' / 4 (j = 0..3), so the group's lanes
+// address 4 rows x 16 consecutive columns and each lane receives one column of those rows.
+// Lane l addresses row 16 ks + 8 b + R0 (R0 = 4 g + r, r = (l % 16) / 4) at logical chunk
+// 4 dt + c (D = 128; D = 64: 4 dt + c as well, chunks of a 128-byte row) with
+// c = 2 ((l / 16) % 2) + (l % 4) / 2, byte 8 (l % 2) of it.  Under the swizzle the byte
+// offset is x ^ (64 dt + 32 b) plus 2048 b + 4096 ks (D = 64: 1024 b + 2048 ks) for a
+// per-lane x: the XOR touches only bits 5-7 of x, so it costs one VALU op per (dt, b).
+template <int D>
+struct TrAddr {
+  int x;  // per-lane byte offset of (ks, dt, b) = (0, 0, 0)
+  __device__ __forceinline__ explicit TrAddr(int lane) {
+    const int g = lane >> 5, r = (lane & 15) >> 2, r0 = 4 * g + r;
+    const int c = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    x = (D == 128 ? 256 * r0 + 64 * r : 128 * r0 + 64 * (r >> 1)) + 16 * (c ^ g) + 8 * (lane & 1);
+  }
+  // `xb` is x, made opaque by the caller where the XORs are to be recomputed
+  __device__ __forceinline__ static bf16x8 frag(const char* tile, int xb, int ks, int dt) {
+    bf16x8 out;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int off = (xb ^ (64 * dt + 32 * b)) + (D == 128 ? 2048 : 1024) * (b + 2 * ks);
+      const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (__attribute__((address_space(3))) bf16x4*)(tile + off));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[4 * b + e] = v[e];
+    }
+    return out;
+  }
+};
+
 }  // namespace uhla

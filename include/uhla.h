@@ -289,6 +289,30 @@ int uhla_forward_rope_at_load(const void* q, const void* k, const void* v, void*
                               uhla_timer* timer);
 
 /*
+ * Permute-free forward: the result of uhla_forward without the window-first copies of K
+ * and V.  The window-first order exists to make every attention block one spatial window
+ * ([UltraGen/it §2], [UltraGen/fr §2.A]); here the attention kernels copy each 64-key tile
+ * straight from the caller's raster K and V (a tile of a w-wide window is 64 / w window
+ * rows, or a 64-token piece of one row when w > 64; a guide tile is 64 consecutive guide
+ * tokens), rotate the K tile in LDS as uhla_forward_rope_at_load does, and read the V^T
+ * operand transposed from the row-major V tile.  Q and O stay in raster order as in
+ * uhla_forward.  Same arguments, layouts and errors as uhla_forward, plus
+ * UHLA_ERR_UNSUPPORTED for a window size other than 16, 32, 64 or a multiple of 64, or for
+ * rows too long for 32-bit tile offsets ((64 / w) * W * heads * head_dim * 2 >= 2^31).
+ * workspace: at least uhla_forward_permute_free_workspace_bytes(...) bytes (the fp64 RoPE
+ * table only; 0 on invalid sizes), 256-byte aligned.  The result equals uhla_forward's up to
+ * the rounding of rotated K (not bit for bit).  timer may be NULL; otherwise stages are
+ * recorded as in uhla_forward_timed (the prep and unpermute stages stay empty).
+ */
+size_t uhla_forward_permute_free_workspace_bytes(int B, int H, int W, int w, int H_lr,
+                                                 int W_lr, int rho, int heads, int head_dim);
+int uhla_forward_permute_free(const void* q, const void* k, const void* v, void* o,
+                              int B, int H, int W, int w, int H_lr, int W_lr, int rho,
+                              int heads, int head_dim, float scale, float theta,
+                              void* workspace, size_t workspace_bytes, void* stream,
+                              uhla_timer* timer);
+
+/*
  * For callers that cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc): uhla_forward without a workspace
  * argument.  Its scratch memory is a 64 MiB (67108864-byte) array in the library's device
