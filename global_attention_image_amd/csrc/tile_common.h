@@ -72,8 +72,9 @@ __device__ __forceinline__ void wait_vm_and_barrier() {
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-// 16-byte chunk swizzle of the backward's LDS row tiles: physical chunk = logical chunk ^
-// bwd_swizzle<D>(row).  The tiles are read two ways: 16 lanes reading one chunk of 16
+// 16-byte chunk swizzle of row-major LDS tiles that are also read transposed (the
+// backward's tiles, the V tiles of the permute-free forward): physical chunk = logical
+// chunk ^ bwd_swizzle<D>(row).  The tiles are read two ways: 16 lanes reading one chunk of 16
 // consecutive rows (the row fragments) need 16 distinct values over any 16 consecutive
 // rows, and the transposed reads below, where each 32-lane half addresses 4 rows x 4
 // consecutive chunks, need those 16 (row, chunk) pairs in 16 distinct bank groups.  The
