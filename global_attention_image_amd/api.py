@@ -217,9 +217,10 @@ def forward_text_workspace_bytes(B, T, H, W, w, H_lr, W_lr, rho, heads, head_dim
                                                         head_dim, radius, guide_mode))
 
 
-def alloc_workspace(B, H, W, w, H_lr, W_lr, heads, head_dim, device="cuda", rho=4, radius=1,
-                    guide_mode=0, T=0, permute_free=False):
-    import torch
+def workspace_bytes_for(B, H, W, w, H_lr, W_lr, heads, head_dim, rho=4, radius=1, guide_mode=0,
+                        T=0, permute_free=False) -> int:
+    """Workspace bytes of the forward entry point that forward() selects for these options
+    (0 when the library rejects the sizes)."""
     if permute_free:
         n = load().uhla_forward_permute_free_workspace_bytes(B, H, W, w, H_lr, W_lr, rho, heads,
                                                              head_dim)
@@ -231,6 +232,14 @@ def alloc_workspace(B, H, W, w, H_lr, W_lr, heads, head_dim, device="cuda", rho=
     else:
         n = forward_masked_workspace_bytes(B, H, W, w, H_lr, W_lr, rho, heads, head_dim, radius,
                                            guide_mode)
+    return int(n)
+
+
+def alloc_workspace(B, H, W, w, H_lr, W_lr, heads, head_dim, device="cuda", rho=4, radius=1,
+                    guide_mode=0, T=0, permute_free=False):
+    import torch
+    n = workspace_bytes_for(B, H, W, w, H_lr, W_lr, heads, head_dim, rho=rho, radius=radius,
+                            guide_mode=guide_mode, T=T, permute_free=permute_free)
     if n == 0:
         raise ValueError("invalid geometry")
     return torch.empty(n, dtype=torch.uint8, device=device)
@@ -290,14 +299,18 @@ def forward(q, k, v, H, W, w, H_lr, W_lr, rho=4, scale=0.0, theta=10000.0, out=N
         raise ValueError("rope_at_load and permute_free cover the default mask only")
     if rope_at_load and permute_free:
         raise ValueError("choose one of rope_at_load and permute_free")
-    if workspace is None:
+    if workspace is None and workspace_bytes_for(B, H, W, w, H_lr, W_lr, Hh, d, rho=rho,
+                                                 radius=radius, guide_mode=guide_mode, T=T,
+                                                 permute_free=permute_free) > 0:
         workspace = alloc_workspace(B, H, W, w, H_lr, W_lr, Hh, d, q.device, rho=rho,
                                     radius=radius, guide_mode=guide_mode, T=T,
                                     permute_free=permute_free)
     lib = load()
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, W, w, H_lr, W_lr, rho, Hh, d,
             float(scale), float(theta))
-    tail = (_ptr(workspace), workspace.numel(), _stream(q))
+    # sizes the library rejects have no workspace: the entry point reports why
+    tail = (_ptr(workspace) if workspace is not None else None,
+            workspace.numel() if workspace is not None else 0, _stream(q))
     if rope_at_load:
         st = lib.uhla_forward_rope_at_load(*args, *tail, timer.h if timer is not None else None)
         _check(st, "uhla_forward_rope_at_load")

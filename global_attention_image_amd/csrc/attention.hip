@@ -1750,7 +1750,9 @@ extern "C" int uhla_forward_rope_at_load(const void* q, const void* k, const voi
 extern "C" size_t uhla_forward_permute_free_workspace_bytes(int B, int H, int W, int w, int H_lr,
                                                            int W_lr, int rho, int heads,
                                                            int head_dim) {
-  if (B < 1 || H < 1 || W < 1 || w < 1 || heads < 1 || H_lr < 0 || W_lr < 0 || head_dim < 1) return 0;
+  // 0 for the sizes uhla_forward_permute_free rejects on their own (its pointer checks aside)
+  if (uhla::workspace_bytes(B, 0, H, W, w, H_lr, W_lr, rho, heads, head_dim, 1, 0) == 0) return 0;
+  if (w < 16 || (uhla::kKeyTile % w != 0 && w % uhla::kKeyTile != 0)) return 0;
   return uhla::permute_free_workspace(uhla::make_geom(B, H, W, w, H_lr, W_lr, rho > 0 ? rho : 1,
                                                       heads, head_dim, 1, 0, 0));
 }

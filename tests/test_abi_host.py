@@ -290,6 +290,50 @@ def test_forward_rope_at_load_rejects(lib):
     assert f(*fwd_args(w=16, wsb=1000)[:17], NULL, NULL) == api.UHLA_ERR_WORKSPACE
 
 
+# uhla_forward_permute_free(q, k, v, o, B, H, W, w, H_lr, W_lr, rho, heads, d, scale, theta,
+#                           ws, bytes, stream, timer): the rejections happen on the host
+@pytest.mark.parametrize("kw,status", [
+    (dict(w=8), api.UHLA_ERR_UNSUPPORTED),  # a 64-key tile would span parts of 8 window rows
+    (dict(H=96, W=96, w=48, H_lr=0, W_lr=0), api.UHLA_ERR_UNSUPPORTED),  # 64 % 48, 48 % 64
+    (dict(w=16, q=NULL), api.UHLA_ERR_ARG),
+    (dict(w=16, d=96), api.UHLA_ERR_UNSUPPORTED),
+    (dict(w=16, H=40), api.UHLA_ERR_ARG),  # w must divide H
+    # per-lane chunk offsets within a tile are 32-bit: 4 window rows of 2048 tokens of
+    # 1024 heads x 128 dims reach 2^31 bytes ...
+    (dict(H=16, W=2048, w=16, H_lr=0, W_lr=0, heads=1024, d=128), api.UHLA_ERR_UNSUPPORTED),
+    # ... one head fewer stays below and stops at the (too small) workspace
+    (dict(H=16, W=2048, w=16, H_lr=0, W_lr=0, heads=1023, d=128, wsb=1000), api.UHLA_ERR_WORKSPACE),
+    (dict(w=16, ws=NULL), api.UHLA_ERR_WORKSPACE),
+    (dict(w=16, wsb=1000), api.UHLA_ERR_WORKSPACE),
+    (dict(w=16, ws=ctypes.c_void_p(0x50000010)), api.UHLA_ERR_ARG),  # misaligned workspace
+    (dict(w=16, o=P), api.UHLA_ERR_ARG),  # aliases q
+])
+def test_forward_permute_free_rejects(lib, kw, status):
+    assert lib.uhla_forward_permute_free(*fwd_args(**kw), NULL) == status
+
+
+@pytest.mark.parametrize("g", [g for g in GEOMS if g[3] >= 16] +
+                         [(1, 64, 128, 32, 16, 16, 4, 64), (1, 128, 64, 64, 0, 0, 2, 128),
+                          (1, 256, 256, 128, 8, 8, 2, 128)])
+def test_forward_permute_free_workspace_bytes(lib, g):
+    """The permute-free forward's workspace is the fp64 cos/sin table alone: max(H, W)
+    positions x d/4 frequency pairs of (cos, sin), 16 bytes each, 256-byte aligned."""
+    B, H, W, w, H_lr, W_lr, heads, d = g
+    got = lib.uhla_forward_permute_free_workspace_bytes(B, H, W, w, H_lr, W_lr, 4, heads, d)
+    assert got == (16 * max(H, W) * (d // 4) + 255) // 256 * 256
+
+
+def test_forward_permute_free_workspace_bytes_invalid(lib):
+    f = lib.uhla_forward_permute_free_workspace_bytes
+    assert f(1, 32, 32, 8, 8, 8, 4, 2, 64) == 0     # w = 8
+    assert f(1, 96, 96, 48, 0, 0, 4, 2, 64) == 0    # w = 48
+    assert f(1, 40, 32, 16, 8, 8, 4, 2, 64) == 0    # w does not divide H
+    assert f(1, 32, 32, 16, 8, 0, 4, 2, 64) == 0    # one guide extent zero
+    assert f(1, 32, 32, 16, 8, 8, 4, 2, 96) == 0    # head_dim
+    assert f(1, 32, 32, 16, 8, 8, 0, 2, 64) == 0    # rho < 1 with guide tokens
+    assert f(0, 32, 32, 16, 8, 8, 4, 2, 64) == 0    # batch
+
+
 def bwd_args(**kw):
     a = dict(q=P, k=P2, v=P3, o=P4, do=ctypes.c_void_p(0x70000000),
              lse=ctypes.c_void_p(0x80000000), dq=ctypes.c_void_p(0x90000000),
@@ -378,3 +422,18 @@ def test_backward_workspace_bytes(lib, g, T, mode):
 ])
 def test_copy_probe_rejects(lib, args, status):
     assert lib.uhla_copy_probe(*args, NULL) == status
+
+
+@pytest.mark.parametrize("w,H,W", [(8, 16, 16), (48, 96, 96)])
+def test_binding_reports_the_library_status_for_rejected_sizes(lib, monkeypatch, w, H, W):
+    """forward() allocates no workspace for sizes whose workspace query returns 0 and lets
+    the entry point say why (here on host tensors: the call is rejected before any pointer
+    is used or any GPU call is made)."""
+    import torch
+    monkeypatch.setattr(api, "_require", lambda t, name, dtype=None: None)
+    monkeypatch.setattr(api, "_stream", lambda t: NULL)
+    L = H * W + 16
+    q = torch.zeros(1, L, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(api.UhlaError) as e:
+        api.forward(q, q.clone(), q.clone(), H, W, w, 4, 4, permute_free=True)
+    assert e.value.status == api.UHLA_ERR_UNSUPPORTED
