@@ -298,7 +298,9 @@ int uhla_forward_rope_at_load(const void* q, const void* k, const void* v, void*
  * operand transposed from the row-major V tile.  Q and O stay in raster order as in
  * uhla_forward.  Same arguments, layouts and errors as uhla_forward, plus
  * UHLA_ERR_UNSUPPORTED for a window size other than 16, 32, 64 or a multiple of 64, or for
- * rows too long for 32-bit tile offsets ((64 / w) * W * heads * head_dim * 2 >= 2^31).
+ * rows too long for 32-bit offsets within a tile (the tokens a tile spans in the raster
+ * tensor, (64 / w) * W for w <= 64 and 64 for w > 64, times heads * head_dim * 2 bytes,
+ * reaching 2^31).
  * workspace: at least uhla_forward_permute_free_workspace_bytes(...) bytes (the fp64 RoPE
  * table only; 0 on invalid sizes), 256-byte aligned.  The result equals uhla_forward's up to
  * the rounding of rotated K (not bit for bit).  timer may be NULL; otherwise stages are
