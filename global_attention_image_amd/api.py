@@ -281,9 +281,12 @@ def forward(q, k, v, H, W, w, H_lr, W_lr, rho=4, scale=0.0, theta=10000.0, out=N
 
     radius / guide_mode select the mask variants of uhla_forward_masked and T > 0 the text
     tokens of uhla_forward_text (rows 0..T-1); with the defaults uhla_forward is called.
-    rope_at_load selects uhla_forward_rope_at_load (K rotated at every K tile load; default
-    mask only), permute_free uhla_forward_permute_free (no K/V prep pass; default mask only).  A timer records per-stage durations (uhla_forward_timed /
-    uhla_forward_masked_timed / uhla_forward_text / uhla_forward_rope_at_load)."""
+    rope_at_load selects uhla_forward_rope_at_load (K rotated at every K tile load) and
+    permute_free uhla_forward_permute_free (no K/V prep pass), both for the default mask
+    only.  A timer records per-stage durations (uhla_forward_timed /
+    uhla_forward_masked_timed / uhla_forward_text / uhla_forward_rope_at_load /
+    uhla_forward_permute_free).  Sizes the library rejects get no workspace, and the
+    entry point's status is raised as UhlaError."""
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _require(t, n, torch.bfloat16)
