@@ -10,8 +10,10 @@ tolerance a mask or alignment error cannot hide.
   tolerance is relative to the output's own scale;
 * the backward at 8K in the launch configuration bench.py --backward times: dK and dV of
   sampled hi-res keys (corner, edge and interior windows, window borders) against the
-  oracle's row backward on two heads, and the uniform-weight probe (Q = 0), whose dV has a
-  closed form for every key (guide keys included) and whose dK is exactly zero.
+  oracle's row backward on two heads; dK and dV of sampled guide keys against oracle rows
+  stored in tests/golden/ (each sums over every query row of its head); and the
+  uniform-weight probe (Q = 0), whose dV has a closed form for every key (guide keys
+  included) and whose dK is exactly zero.
 """
 import numpy as np
 import pytest
@@ -160,6 +162,27 @@ def test_backward_8k_hi_key_rows():
         _, rk, rv = orc.backward_rows(sl(q), sl(k), sl(v), sl(do), g, 0, 0, [], k_rows)
         check_rel(bf16_f64(dk[0, k_rows, h]), rk, f"8k dk h{h} ({len(k_rows)} hi keys)")
         check_rel(bf16_f64(dv[0, k_rows, h]), rv, f"8k dv h{h} ({len(k_rows)} hi keys)")
+
+
+def test_backward_8k_guide_key_rows():
+    """dK and dV of sampled guide keys at 8K (corners and centre of the guide grid, two
+    seeded others; heads 0 and 23) against the oracle values stored by
+    tests/golden/make_backward_8k_guide_keys.py: each guide key's gradient sums over all
+    278 528 query rows of its head, too long to recompute here."""
+    import json
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                        "backward_8k_guide_keys.json")
+    ref = json.load(open(path))
+    g, q, k, v = config_inputs(ref["workload"])
+    say("backward 8k: sampled guide-key dK / dV rows against stored oracle rows")
+    do = make_qkv_bits(g, ref["do_seed"])[0]
+    _, dk, dv = (from_dev(x) for x in run_fwd_bwd(g, to_dev(q), to_dev(k), to_dev(v), to_dev(do)))
+    for h, e in ref["heads"].items():
+        h, rows = int(h), np.array(e["rows"], dtype=np.int64)
+        assert (rows >= g.N).all() and (rows < g.N + g.H_lr * g.W_lr).all()
+        check_rel(bf16_f64(dk[0, rows, h]), np.array(e["dk"]), f"8k dk h{h} ({len(rows)} guide keys)")
+        check_rel(bf16_f64(dv[0, rows, h]), np.array(e["dv"]), f"8k dv h{h} ({len(rows)} guide keys)")
 
 
 def test_backward_8k_uniform_probe():
