@@ -141,7 +141,8 @@ def cpu_baseline(geom, q, k, v, seconds):
             "seconds": round(dt, 3),
             "extrapolated_full_oracle_s": round(full_s, 1),
             "extrapolation": "extrapolated, not measured: mean RoPE time per head x B*heads + "
-                             "mean time per query row x B*heads*L"}
+                             "mean time per query row x B*heads*L; an upper estimate (full "
+                             "oracle runs at 2k and nonsquare took 0.89 and 0.63 of it)"}
 
 
 def bench_backward(args, g):
