@@ -31,6 +31,9 @@ attention_passes  the same FLOPs over the attention passes alone (prep excluded)
 permute     the standalone uhla_window_permute of the Q hi segment in GB/s, beside a plain
             device-to-device copy of the same bytes and uhla_copy_probe of the same bytes
             through each load path (plain, nontemporal, direct-to-LDS).
+prep        the forward's own permutes (K rotated, V as V^T tiles; default mask): their
+            algorithmic bytes (K and V of every row read and written once) over the prep
+            stages' durations.
 """
 from __future__ import annotations
 
@@ -380,6 +383,15 @@ def main():
                     "device_copy_GB/s": round(copy_gbs, 1),
                     "copy_probe_GB/s": copy_paths},
     }
+    if not variant:
+        # the forward's own permutes: K (rotated) and V (as V^T tiles) of every hi and guide
+        # row read and written once, by prep_k_kernel and prep_v_kernel
+        prep_ms = stage_avg["prep_hi"] + stage_avg["prep_lr"]
+        prep_bytes = 2 * 2 * g.B * (g.N + g.H_lr * g.W_lr) * g.heads * g.head_dim * 2
+        prep_gbs = prep_bytes / (prep_ms * 1e-3) / 1e9
+        res["prep"] = {"kernels": "prep_k_kernel + prep_v_kernel", "ms": round(prep_ms, 4),
+                       "algorithmic_bytes": prep_bytes, "GB/s": round(prep_gbs, 1),
+                       "frac_hbm_peak": round(prep_gbs / PEAK_HBM_GBS, 4)}
     if not args.no_cpu_baseline:
         log(f"[bench] CPU baseline: oracle for ~{args.cpu_seconds:.0f} s")
         res["cpu_baseline"] = cpu_baseline(g, q, k, v, args.cpu_seconds)
