@@ -342,9 +342,9 @@ def backward_rows(q, k, v, do, geom, b: int, h: int, q_rows, k_rows, block: int 
     (dQ[q_rows], dK[k_rows], dV[k_rows]), fp64.
 
     The arithmetic of ``backward`` restricted to the query rows that matter: the rows in
-    ``q_rows`` and every query row whose mask row allows one of ``k_rows`` (a key's
-    gradients sum over those rows only; every other entry of its column of P and dS is
-    zero).  For each block of those rows: P = masked softmax of the row block over all L
+    ``q_rows`` and every query row whose mask row allows one of ``k_rows`` and whose dO
+    row is not zero (a key's gradients sum over those rows only; every other entry of its
+    column of P dO and dS is zero).  For each block of those rows: P = masked softmax of the row block over all L
     keys, dP = dO V^T, dS = P * (dP - rowsum(dP * P)); dV[k] and dK~[k] sum P[:, k] dO and
     s dS[:, k] Q~ over the block, dQ~ = s dS K~; dQ, dK rotate back."""
     q_rows = np.asarray(q_rows, dtype=np.int64)
@@ -357,9 +357,12 @@ def backward_rows(q, k, v, do, geom, b: int, h: int, q_rows, k_rows, block: int 
     need = np.zeros(L, dtype=bool)
     need[q_rows] = True
     if len(k_rows):
+        # a row with dO = 0 has dP = 0, a zero row dot and so dS = 0: it adds nothing to
+        # any key's dK or dV, and is skipped (exact)
+        live = np.any(g != 0, axis=1)
         for s0 in range(0, L, 8 * block):
             blk = np.arange(s0, min(L, s0 + 8 * block))
-            need[blk] |= mask_block(geom, blk, k_rows).any(axis=1)
+            need[blk] |= mask_block(geom, blk, k_rows).any(axis=1) & live[blk]
     rows = np.nonzero(need)[0]
     dq = np.zeros((len(q_rows), q.shape[-1]))
     dk = np.zeros((len(k_rows), q.shape[-1]))

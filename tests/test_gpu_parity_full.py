@@ -10,9 +10,9 @@ tolerance a mask or alignment error cannot hide.
   tolerance is relative to the output's own scale;
 * the backward at 8K in the launch configuration bench.py --backward times: dK and dV of
   sampled hi-res keys (corner, edge and interior windows, window borders) against the
-  oracle's row backward on two heads; dK and dV of sampled guide keys against oracle rows
-  stored in tests/golden/ (each sums over every query row of its head); and the
-  uniform-weight probe (Q = 0), whose dV has a closed form for every key (guide keys
+  oracle's row backward on two heads; dK and dV of sampled guide keys (each sums over
+  every query row of its head) with dO zero except on about 1000 sampled query rows, so
+  that the oracle needs only those rows; and the uniform-weight probe (Q = 0), whose dV has a closed form for every key (guide keys
   included) and whose dK is exactly zero.
 """
 import numpy as np
@@ -164,25 +164,37 @@ def test_backward_8k_hi_key_rows():
         check_rel(bf16_f64(dv[0, k_rows, h]), rv, f"8k dv h{h} ({len(k_rows)} hi keys)")
 
 
-def test_backward_8k_guide_key_rows():
-    """dK and dV of sampled guide keys at 8K (corners and centre of the guide grid, two
-    seeded others; heads 0 and 23) against the oracle values stored by
-    tests/golden/make_backward_8k_guide_keys.py: each guide key's gradient sums over all
-    278 528 query rows of its head, too long to recompute here."""
-    import json
-    import os
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
-                        "backward_8k_guide_keys.json")
-    ref = json.load(open(path))
-    g, q, k, v = config_inputs(ref["workload"])
-    say("backward 8k: sampled guide-key dK / dV rows against stored oracle rows")
-    do = make_qkv_bits(g, ref["do_seed"])[0]
-    _, dk, dv = (from_dev(x) for x in run_fwd_bwd(g, to_dev(q), to_dev(k), to_dev(v), to_dev(do)))
-    for h, e in ref["heads"].items():
-        h, rows = int(h), np.array(e["rows"], dtype=np.int64)
-        assert (rows >= g.N).all() and (rows < g.N + g.H_lr * g.W_lr).all()
-        check_rel(bf16_f64(dk[0, rows, h]), np.array(e["dk"]), f"8k dk h{h} ({len(rows)} guide keys)")
-        check_rel(bf16_f64(dv[0, rows, h]), np.array(e["dv"]), f"8k dv h{h} ({len(rows)} guide keys)")
+def test_backward_8k_sparse_cotangent():
+    """dK and dV of guide keys (and of hi keys, and dQ) at 8K against the oracle.  A guide
+    key's gradient sums over every query row of its head, so dO is zero except on about
+    1000 stratified query rows (corner, edge and interior windows, window borders, random
+    hi rows, guide rows); a row with dO = 0 contributes nothing, so the oracle needs only
+    those rows' softmax, while the kernels still walk every query tile of the head."""
+    from test_gpu_forward import stratified_rows
+    g, q, k, v = config_inputs("8k")
+    say("backward 8k: sparse cotangent, guide-key and hi-key dK / dV, dQ of live rows")
+    rng = np.random.default_rng(79)
+    live = stratified_rows(g, rng, 700, 300)
+    do = np.zeros_like(q)
+    do[:, live] = make_qkv_bits(g, 79)[0][:, live]
+    dq, dk, dv = (from_dev(x) for x in run_fwd_bwd(g, to_dev(q), to_dev(k), to_dev(v), to_dev(do)))
+    nwy, nwx = g.H // g.w, g.W // g.w
+    M, W_lr = g.H_lr * g.W_lr, g.W_lr
+    guide = np.array([0, W_lr - 1, M - W_lr, M - 1, (g.H_lr // 2) * W_lr + W_lr // 2]
+                     + list(rng.integers(0, M, 11)))
+    for h in (0, 23):
+        g_rows = np.unique(g.N + guide)
+        h_rows = hi_key_rows(g, [(0, 0), (nwy // 2, nwx // 2), (nwy - 1, nwx - 1)])
+        k_rows = np.concatenate([h_rows, g_rows])
+        q_rows = live[::8]
+        sl = lambda x: bf16_f64(x[:, :, h:h + 1, :])
+        rq, rk, rv = orc.backward_rows(sl(q), sl(k), sl(v), sl(do), g, 0, 0, q_rows, k_rows)
+        nh = len(h_rows)
+        check_rel(bf16_f64(dk[0, g_rows, h]), rk[nh:], f"8k dk h{h} ({len(g_rows)} guide keys)")
+        check_rel(bf16_f64(dv[0, g_rows, h]), rv[nh:], f"8k dv h{h} ({len(g_rows)} guide keys)")
+        check_rel(bf16_f64(dk[0, h_rows, h]), rk[:nh], f"8k dk h{h} ({nh} hi keys, sparse dO)")
+        check_rel(bf16_f64(dv[0, h_rows, h]), rv[:nh], f"8k dv h{h} ({nh} hi keys, sparse dO)")
+        check_rel(bf16_f64(dq[0, q_rows, h]), rq, f"8k dq h{h} ({len(q_rows)} live rows)")
 
 
 def test_backward_8k_uniform_probe():

@@ -711,6 +711,34 @@ def test_backward_rows_match_full_backward():
         assert np.max(np.abs(rv - dv[0, krows, 0])) < 1e-12
 
 
+def test_backward_rows_sparse_cotangent_vs_autograd():
+    """With dO zero on all but a few query rows, backward_rows skips the zero rows; its
+    key gradients must still equal torch autograd of the rotation-matrix forward (which
+    knows nothing of the skip) and the oracle's full backward, for hi, guide and text keys
+    and for query rows with and without a cotangent."""
+    import torch
+    g = small_geom(B=1, heads=2, head_dim=8, H=12, W=16, w=4, H_lr=5, W_lr=7, rho=3,
+                   radius=1, T=3)
+    q, k, v = rand_qkv(g, 61)
+    do = np.zeros_like(q)
+    live = np.array([0, g.T + 2, g.T + 5 * g.W + 9, g.T + g.N - 1, g.T + g.N + 4, g.L - 1])
+    do[0, live, 1] = rand_qkv(g, 62)[0][0, live, 1]
+    qrows = np.array([live[1], live[4], g.T + 7])
+    krows = np.arange(g.L)
+    rq, rk, rv = orc.backward_rows(q, k, v, do, g, 0, 1, qrows, krows, block=4)
+    f = torch_attention_fn(g)
+    tq, tk, tv = (torch.from_numpy(x[0, :, 1].copy()).requires_grad_(True) for x in (q, k, v))
+    o, _ = f(tq, tk, tv)
+    o.backward(torch.from_numpy(do[0, :, 1].copy()))
+    assert np.max(np.abs(rq - tq.grad.numpy()[qrows])) < 1e-10
+    assert np.max(np.abs(rk - tk.grad.numpy()[krows])) < 1e-10
+    assert np.max(np.abs(rv - tv.grad.numpy()[krows])) < 1e-10
+    assert np.abs(rk).max() > 1e-3 and np.abs(rv).max() > 1e-3
+    dq, dk, dv = orc.backward(q, k, v, do, g)
+    assert np.max(np.abs(rk - dk[0, krows, 1])) < 1e-12
+    assert np.max(np.abs(rv - dv[0, krows, 1])) < 1e-12
+
+
 def test_backward_rows_rich_geometry_vs_autograd():
     """backward_rows against torch autograd of the rotation-matrix forward (independent of
     the oracle's own backward) and against the oracle's full backward, on a geometry with
