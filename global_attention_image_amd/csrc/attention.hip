@@ -362,24 +362,29 @@ __global__ __launch_bounds__(kPrepThreads) void prep_v_kernel(
     }
   }
   __syncthreads();
-  // write D rows x 64 keys; each thread writes 8 consecutive slots of one d-row
+  // write D rows x 64 keys; each task takes 8 consecutive slots of two adjacent d-rows:
+  // it reads 4-byte words (dims d, d + 1 of one key) and splits them into the two rows
   const int64_t bh = b * heads + h, tsz = static_cast<int64_t>(D) * kKeyTile;
   bf16_t* dst;
   if (tile_id < n_hi) dst = v_hi + (bh * n_hi + tile_id) * tsz;
   else if (tile_id < n_hi + n_g) dst = v_lr + (bh * n_g + (tile_id - n_hi)) * tsz;
   else dst = v_gb + (bh * (Mbg / kKeyTile) + (tile_id - n_hi - n_g)) * tsz;
-  for (int i = threadIdx.x; i < D * (kKeyTile / 8); i += kPrepThreads) {
-    const int d = i / (kKeyTile / 8), s8 = (i - d * (kKeyTile / 8)) * 8;
-    uint32_t wv[4];
+  for (int i = threadIdx.x; i < (D / 2) * (kKeyTile / 8); i += kPrepThreads) {
+    const int dp = i / (kKeyTile / 8), s8 = (i - dp * (kKeyTile / 8)) * 8;
+    const int d = 2 * dp;
+    uint32_t r0[4], r1[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       // slot s holds key v_slot(s) (the mapping is its own inverse)
-      const uint32_t lo = tile[v_slot(s8 + 2 * e)][d];
-      const uint32_t hi = tile[v_slot(s8 + 2 * e + 1)][d];
-      wv[e] = lo | (hi << 16);
+      const uint32_t lo = *reinterpret_cast<const uint32_t*>(&tile[v_slot(s8 + 2 * e)][d]);
+      const uint32_t hi = *reinterpret_cast<const uint32_t*>(&tile[v_slot(s8 + 2 * e + 1)][d]);
+      r0[e] = (lo & 0xffffu) | (hi << 16);
+      r1[e] = (lo >> 16) | (hi & 0xffff0000u);
     }
-    __builtin_nontemporal_store(u32x4{wv[0], wv[1], wv[2], wv[3]},
-                                reinterpret_cast<u32x4*>(dst + static_cast<int64_t>(d) * kKeyTile + s8));
+    bf16_t* row = dst + static_cast<int64_t>(d) * kKeyTile + s8;
+    __builtin_nontemporal_store(u32x4{r0[0], r0[1], r0[2], r0[3]}, reinterpret_cast<u32x4*>(row));
+    __builtin_nontemporal_store(u32x4{r1[0], r1[1], r1[2], r1[3]},
+                                reinterpret_cast<u32x4*>(row + kKeyTile));
   }
 }
 
