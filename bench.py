@@ -265,15 +265,20 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] warmup done; timing {args.steps} steps")
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        fwd()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    # The spread of per-step device times, from as many steps again with HIP events
+    # around each (kept out of the timed loop above, whose wall time is the value).
     step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)]
-    t0 = time.perf_counter()
     for e_a, e_b in step_ev:
         e_a.record()
         fwd()
         e_b.record()
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
     step_list = sorted(a.elapsed_time(b) for a, b in step_ev)
     # Stage durations (HIP events on the launch stream around each kernel) from as many
     # steps again through the timed entry point.
