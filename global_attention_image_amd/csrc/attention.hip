@@ -191,7 +191,9 @@ __global__ __launch_bounds__(kPrepThreads) void prep_k_kernel(
   __shared__ bf16_t* dq_s[kPrepRows];
   __shared__ int64_t kst_s[kPrepRows], k2st_s[kPrepRows], qst_s[kPrepRows];  // per-head strides
   __shared__ int pos_s[kPrepRows][2];
-  __shared__ double2 cs_s[kPrepRows][2][QUARTER];
+  // RoPE factors of pair 4j + e (pairs of both axes in one list, y first) at [row][e][j]:
+  // the 16-byte reads of the lanes that rotate chunks j = 0, 1, ... are consecutive
+  __shared__ double2 cs_s[kPrepRows][4][CPH];
   const int64_t L = T + N + M;
   const int64_t b = blockIdx.y;
   const int tid = threadIdx.x;
@@ -247,7 +249,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_k_kernel(
     for (int e = tid; e < kPrepRows * 2 * QUARTER; e += kPrepThreads) {
       const int rt = e / (2 * QUARTER), axis = (e / QUARTER) & 1, kk = e % QUARTER;
       const int pos = pos_s[rt][axis];
-      cs_s[rt][axis][kk] = pos < P ? cs[pos * QUARTER + kk] : rope_cos_sin(pos, kk, D / 2, log2_theta);
+      cs_s[rt][kk % 4][(axis * QUARTER + kk) / 4] =
+          pos < P ? cs[pos * QUARTER + kk] : rope_cos_sin(pos, kk, D / 2, log2_theta);
     }
     __syncthreads();
   }
@@ -267,8 +270,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_k_kernel(
       const uint4 ki = make_uint4(kv[0], kv[1], kv[2], kv[3]);
       if (rope_on) {
         // pairs 4j .. 4j+3 lie on one axis (y for the first D/4 pairs)
-        const int axis = (4 * j) / QUARTER, k0 = 4 * j - axis * QUARTER;
-        const double2* f = &cs_s[t][axis][k0];
+        const double2 f[4] = {cs_s[t][0][j], cs_s[t][1][j], cs_s[t][2][j], cs_s[t][3][j]};
         ko = make_uint4(rope_rotate_word(ki.x, f[0]), rope_rotate_word(ki.y, f[1]),
                         rope_rotate_word(ki.z, f[2]), rope_rotate_word(ki.w, f[3]));
         if (dq) {
