@@ -1,9 +1,10 @@
 """Full-size parity gates that bite: checks at the 2K, non-square and 8K workloads whose
 tolerance a mask or alignment error cannot hide.
 
-* every row of one head at 2K, and every row of the border windows (clipped
-  neighbourhoods) of one head per batch at non-square, against the fp64 oracle at the
-  stated tolerance (max-abs 2e-2, mean-abs 2e-3);
+* every row of one head at 2K, every row of the border windows (clipped neighbourhoods)
+  of one head per batch at non-square, every row of three bands of windows and the guide
+  rows of one head at 4K, and stratified rows of every head at 8K, against the fp64
+  oracle at the stated tolerance (max-abs 2e-2, mean-abs 2e-3);
 * a sharp gate: Q scaled by 4 (exact in bf16), so each row's softmax concentrates on a few
   keys and dropping or misplacing any visible window moves those rows' outputs by O(1)
   (the oracle pin test_sharp_gate_catches_a_dropped_neighbour measures that effect); the
@@ -89,6 +90,50 @@ def test_forward_border_windows_nonsquare():
     for b, h in ((0, 0), (1, 23)):
         want = oracle_head_rows(g, q, k, v, b, h, rows)
         check(bf16_f64(got[b, rows, h]), want, f"nonsquare b{b} h{h} ({len(rows)} rows)")
+
+
+def window_band_rows(g, band_rows):
+    """Raster indices of every token in the given window rows (all window columns)."""
+    nwx = g.W // g.w
+    rows = []
+    for wy in band_rows:
+        for wx in range(nwx):
+            iy, ix = np.divmod(np.arange(g.w * g.w), g.w)
+            rows.append((wy * g.w + iy) * g.W + wx * g.w + ix)
+    return np.sort(np.concatenate(rows))
+
+
+def test_forward_window_bands_4k():
+    """Every row of the top, middle and bottom window rows (corner, edge and interior
+    windows, 12 288 hi rows) and every guide row of one head at 4K."""
+    g, q, k, v = config_inputs("4k")
+    h = 17
+    nwy = g.H // g.w
+    say(f"forward 4k: every row of window rows 0, {nwy // 2}, {nwy - 1} and the guide rows, head {h}")
+    got = forward_dev(g, to_dev(q), to_dev(k), to_dev(v))
+    rows = np.concatenate([window_band_rows(g, (0, nwy // 2, nwy - 1)), np.arange(g.N, g.L)])
+    want = oracle_head_rows(g, q, k, v, 0, h, rows)
+    check(bf16_f64(got[0, rows, h]), want, f"4k h{h} ({len(rows)} rows)")
+
+
+def test_forward_every_head_8k():
+    """Stratified rows (corner, edge and interior windows, window borders, guide rows) of
+    every one of the 24 heads at 8K."""
+    from test_gpu_forward import stratified_rows
+    g, q, k, v = config_inputs("8k")
+    say("forward 8k: stratified rows of every head")
+    got = forward_dev(g, to_dev(q), to_dev(k), to_dev(v))
+    rng = np.random.default_rng(46)
+    errs = []
+    for h in range(g.heads):
+        rows = stratified_rows(g, rng, 90, 20)
+        want = oracle_head_rows(g, q, k, v, 0, h, rows)
+        err = np.abs(bf16_f64(got[0, rows, h]) - want)
+        errs.append((h, len(rows), err.max(), err.mean()))
+        assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (h, err.max(), err.mean())
+    say("8k every head: " + ", ".join(f"h{h} {n} rows max-abs {m:.2e}" for h, n, m, _ in errs[::6]))
+    say(f"8k every head ({sum(e[1] for e in errs)} rows): max-abs {max(e[2] for e in errs):.3e} "
+        f"mean-abs {np.mean([e[3] for e in errs]):.3e}")
 
 
 def test_sharp_gate_2k_every_row():
