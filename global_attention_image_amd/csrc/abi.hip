@@ -109,11 +109,23 @@ extern "C" int uhla_timer_create(int max_calls, uhla_timer** out) {
 
 extern "C" int uhla_timer_destroy(uhla_timer* t) {
   if (!t) return UHLA_OK;
+  // every event is destroyed even if one fails; the first failure is reported
+  hipError_t first = hipSuccess;
   for (hipEvent_t e : t->start)
-    if (e) hipEventDestroy(e);
+    if (e) {
+      const hipError_t r = hipEventDestroy(e);
+      if (first == hipSuccess) first = r;
+    }
   for (hipEvent_t e : t->stop)
-    if (e) hipEventDestroy(e);
+    if (e) {
+      const hipError_t r = hipEventDestroy(e);
+      if (first == hipSuccess) first = r;
+    }
   delete t;
+  if (first != hipSuccess) {
+    uhla::set_hip_detail("hipEventDestroy", first);
+    return UHLA_ERR_HIP;
+  }
   return UHLA_OK;
 }
 

@@ -242,6 +242,8 @@ const char* uhla_last_error_detail(void);
  * n_stages, the summed milliseconds over the recorded calls into stage_ms[s], and the
  * number of recorded calls into *calls.  Stages are enumerated by uhla_stage.
  * uhla_timer_reset forgets recorded calls.  A call beyond max_calls is not timed.
+ * uhla_timer_destroy frees the timer and all its events (NULL: no-op); it returns
+ * UHLA_ERR_HIP if destroying an event failed, the timer being freed all the same.
  */
 typedef enum {
   UHLA_STAGE_TABLES = 0,    /* RoPE cos/sin table */
