@@ -1412,10 +1412,17 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, int B, in
       ranges_overlap(o, tensor_bytes, v, tensor_bytes) ||
       ranges_overlap(o, tensor_bytes, workspace, need.bytes))
     return fail_arg("o overlaps an input or the workspace");
+  // the prep pass writes the workspace while the inputs are still being read
+  for (const void* x : {q, k, v})
+    if (ranges_overlap(workspace, need.bytes, x, tensor_bytes))
+      return fail_arg("the workspace overlaps an input");
   const size_t lse_bytes = static_cast<size_t>(B) * heads * L * sizeof(float);
   if (lse && (reinterpret_cast<uintptr_t>(lse) % 4 || ranges_overlap(lse, lse_bytes, o, tensor_bytes) ||
-              ranges_overlap(lse, lse_bytes, workspace, need.bytes)))
-    return fail_arg("lse misaligned or overlapping o or the workspace");
+              ranges_overlap(lse, lse_bytes, workspace, need.bytes) ||
+              ranges_overlap(lse, lse_bytes, q, tensor_bytes) ||
+              ranges_overlap(lse, lse_bytes, k, tensor_bytes) ||
+              ranges_overlap(lse, lse_bytes, v, tensor_bytes)))
+    return fail_arg("lse misaligned or overlapping o, an input or the workspace");
   const Workspace ws = carve(g, workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool rope_on = theta > 0.0f;
@@ -1597,6 +1604,8 @@ static int forward_permute_free_impl(const void* q, const void* k, const void* v
   if (ranges_overlap(o, tensor_bytes, q, tensor_bytes) || ranges_overlap(o, tensor_bytes, k, tensor_bytes) ||
       ranges_overlap(o, tensor_bytes, v, tensor_bytes) || ranges_overlap(o, tensor_bytes, workspace, need))
     return fail_arg("o overlaps an input or the workspace");
+  for (const void* x : {q, k, v})
+    if (ranges_overlap(workspace, need, x, tensor_bytes)) return fail_arg("the workspace overlaps an input");
   hipStream_t s = static_cast<hipStream_t>(stream);
   double2* cs = static_cast<double2*>(workspace);
   const bool rope_on = theta > 0.0f;

@@ -1128,6 +1128,11 @@ extern "C" int uhla_backward(const void* q, const void* k, const void* v, const 
   }
   if (ranges_overlap(dq, tb, dk, tb) || ranges_overlap(dq, tb, dv, tb) || ranges_overlap(dk, tb, dv, tb))
     return fail_arg("gradients overlap each other");
+  // the row-prep pass writes the workspace while the inputs are still being read
+  for (const void* y : ins)
+    if (ranges_overlap(workspace, need.bytes, y, tb)) return fail_arg("the workspace overlaps an input");
+  if (ranges_overlap(workspace, need.bytes, lse, static_cast<size_t>(B) * heads * L * 4))
+    return fail_arg("the workspace overlaps lse");
   const BwdWorkspace ws = carve_bwd(g, workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool rope_on = theta > 0.0f;

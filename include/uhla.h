@@ -121,7 +121,8 @@ size_t uhla_forward_workspace_bytes(int B, int H, int W, int w, int H_lr, int W_
  * workspace: device memory of at least uhla_forward_workspace_bytes(...) bytes, 256-byte
  *   aligned, owned by the caller; its contents are scratch.
  * Errors: UHLA_ERR_ARG (null pointers, sizes < 1, w not dividing H or W, rho < 1 with
- * guide tokens, exactly one of H_lr/W_lr zero, O overlapping Q, K, V or the workspace);
+ * guide tokens, exactly one of H_lr/W_lr zero, O overlapping Q, K, V or the workspace,
+ * the workspace overlapping Q, K or V);
  * UHLA_ERR_UNSUPPORTED (head_dim not in {64, 128}; w not a multiple of 8, or w > 16
  * and not a multiple of 16; more than 1024 key tiles of 64 keys per window, counting
  * the neighbour windows' tiles and, in the masked variant, the guide cell blocks; B or
@@ -194,7 +195,8 @@ int uhla_forward_text(const void* q, const void* k, const void* v, void* o,
  * uhla_forward_lse: uhla_forward_text (T = 0: uhla_forward_masked) that also writes lse,
  *   fp32 [B, heads, T + N + M] in the same row order as O: the natural log of each row's
  *   sum of exp(scale * q.k) over the keys the row sees.  Errors: as uhla_forward_text, plus
- *   UHLA_ERR_ARG for a null or misaligned lse or one overlapping O or the workspace.
+ *   UHLA_ERR_ARG for a null or misaligned lse or one overlapping O, Q, K, V or the
+ *   workspace.
  *
  * uhla_backward: gradients dQ, dK, dV (bf16, layout of Q) of O = uhla_forward_text(Q, K,
  *   V; T, radius, guide_mode) (T = 0: uhla_forward_masked) for the output gradient dO,
@@ -208,7 +210,7 @@ int uhla_forward_text(const void* q, const void* k, const void* v, void* o,
  *   workspace: at least uhla_backward_workspace_bytes(...) bytes, 256-byte aligned.
  *   Errors: UHLA_ERR_ARG (null or misaligned pointers, sizes < 1, T < 0, w not dividing H
  *   or W, radius < 0, guide_mode outside 0..2, gradients overlapping an input, lse, the
- *   workspace or each other); UHLA_ERR_UNSUPPORTED (head_dim not in {64, 128}, w as in
+ *   workspace or each other, the workspace overlapping an input or lse); UHLA_ERR_UNSUPPORTED (head_dim not in {64, 128}, w as in
  *   uhla_forward, more than 1024 key tiles per window or, in guide modes 1 and 2, more
  *   than 1024 tiles in a window's or a cell-block group's tile list, T > 2^24);
  *   UHLA_ERR_WORKSPACE; UHLA_ERR_HIP.

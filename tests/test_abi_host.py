@@ -149,6 +149,8 @@ def fwd_args(**kw):
     (dict(o=P), api.UHLA_ERR_ARG),  # aliases q
     (dict(o=ctypes.c_void_p(0x30000000 + 4096)), api.UHLA_ERR_ARG),  # overlaps v
     (dict(ws=ctypes.c_void_p(0x50000010)), api.UHLA_ERR_ARG),  # misaligned workspace
+    (dict(ws=P2), api.UHLA_ERR_ARG),  # workspace overlaps k
+    (dict(ws=ctypes.c_void_p(0x10000000 + 4096)), api.UHLA_ERR_ARG),  # workspace inside q
 ])
 def test_forward_rejects(lib, kw, status):
     assert lib.uhla_forward(*fwd_args(**kw)) == status
@@ -278,6 +280,7 @@ def test_forward_lse_rejects(lib):
     assert f(*lse_args(lse=NULL)) == api.UHLA_ERR_ARG
     assert f(*lse_args(lse=ctypes.c_void_p(0x60000002))) == api.UHLA_ERR_ARG  # misaligned
     assert f(*lse_args(lse=ctypes.c_void_p(0x40000000 + 64))) == api.UHLA_ERR_ARG  # inside o
+    assert f(*lse_args(lse=ctypes.c_void_p(0x20000000 + 64))) == api.UHLA_ERR_ARG  # inside k
     assert f(*lse_args(q=NULL)) == api.UHLA_ERR_ARG
     assert f(*lse_args(d=96)) == api.UHLA_ERR_UNSUPPORTED
 
@@ -307,6 +310,7 @@ def test_forward_rope_at_load_rejects(lib):
     (dict(w=16, wsb=1000), api.UHLA_ERR_WORKSPACE),
     (dict(w=16, ws=ctypes.c_void_p(0x50000010)), api.UHLA_ERR_ARG),  # misaligned workspace
     (dict(w=16, o=P), api.UHLA_ERR_ARG),  # aliases q
+    (dict(w=16, ws=P3), api.UHLA_ERR_ARG),  # workspace overlaps v
 ])
 def test_forward_permute_free_rejects(lib, kw, status):
     assert lib.uhla_forward_permute_free(*fwd_args(**kw), NULL) == status
@@ -371,6 +375,8 @@ def bwd_args(**kw):
     (dict(dk=ctypes.c_void_p(0x90000000 + 4096)), api.UHLA_ERR_ARG),  # overlaps dq
     (dict(dv=ctypes.c_void_p(0x80000000)), api.UHLA_ERR_ARG),  # overlaps lse
     (dict(dq=ctypes.c_void_p(0x50000000 + 4096)), api.UHLA_ERR_ARG),  # inside the workspace
+    (dict(ws=ctypes.c_void_p(0x70000000)), api.UHLA_ERR_ARG),  # workspace overlaps dO
+    (dict(ws=ctypes.c_void_p(0x80000000)), api.UHLA_ERR_ARG),  # workspace overlaps lse
 ])
 def test_backward_rejects(lib, kw, status):
     assert lib.uhla_backward(*bwd_args(**kw)) == status
