@@ -427,7 +427,7 @@ struct AttnArgs {
 };
 
 constexpr int kStages = 4;  // LDS ring: tiles t, t+1 are read while t+2, t+3 land
-constexpr int kQkAhead = 3;  // K fragment reads in flight ahead of the QK^T MFMAs (steps)
+constexpr int kQkAhead = 2;  // K fragment reads in flight ahead of the QK^T MFMAs (steps)
 constexpr int kPvAhead = 4;  // V fragment reads in flight ahead of the PV MFMAs
 
 // One workgroup = NWAVES waves x 32 queries.  Waves [0, NWAVES/2) ("A") and
